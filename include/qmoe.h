@@ -1,0 +1,187 @@
+/*
+ * qmoe.h -- C ABI of the MI355X (gfx950) quantized top-k Mixture-of-Experts layer.
+ *
+ * The layer is the forward pass of a top-k routed MoE SwiGLU FFN whose experts
+ * hold low-bit weights, as described on the source pages:
+ *   - "Quantized Mixture of Experts (Q-MoE)", section 3 components table: a
+ *     gating network selects the top-k experts per input (e.g. top-2); an expert
+ *     quantizer owns each expert's precision (INT8, FP8, ...); a sparse execution
+ *     engine runs only the activated experts. Section 4: INT4/INT8 quantization.
+ *   - IT Donga article on DREAM-MoE / SRA-MoE, DREAM-MoE section: 4-bit and 3-bit
+ *     weight-quantized MoE LLMs.
+ *   - "FineRMoE" (aitrends), architecture paragraph: an expert is gate, up and
+ *     down projections with an activation; shared experts sit beside sparse
+ *     ones; the selected experts' outputs are mixed by the router's softmax
+ *     probabilities.
+ *   - "OmniMoE", technical summary 2.1 (an always-on shared dense MLP) and 2.2
+ *     (expert-centric scheduling: flatten all routing decisions into a task
+ *     list, group by expert id, order by token id inside each group, then a
+ *     grouped GEMM that loads each expert's weights once for all its tokens).
+ *
+ * The three calls map onto those three components:
+ *   qmoe_pack_experts  -- the expert quantizer (host quantization + device layout)
+ *   qmoe_route_topk    -- the gating network's selection and task list
+ *   qmoe_forward       -- the sparse execution engine (router, dispatch, experts,
+ *                         combine), every step a HIP kernel on the caller's stream
+ *   qmoe_destroy       -- releases what qmoe_pack_experts allocated
+ *
+ * Conventions (all entry points):
+ *   - Return QMOE_OK (0) on success, a negative QMOE_E* code on failure; nothing
+ *     throws across the ABI. qmoe_last_error() returns a thread-local message
+ *     describing the last failure on the calling thread.
+ *   - Asynchronous calls (route, forward) report argument and launch errors at
+ *     once; execution errors surface at the caller's next stream synchronisation.
+ *   - A context serves one stream at a time: its workspace is shared by calls.
+ *   - "device" pointers are HIP device memory on the context's device; "host"
+ *     pointers are ordinary CPU memory. The library never frees caller memory.
+ *   - bf16 values are passed as their 16-bit patterns (uint16_t).
+ */
+#ifndef QMOE_H
+#define QMOE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QMOE_OK 0
+#define QMOE_EINVAL (-1)       /* bad argument: null pointer, shape, T > max_tokens, ... */
+#define QMOE_EHIP (-2)         /* a HIP runtime call or kernel launch failed */
+#define QMOE_ENOMEM (-3)       /* device or host allocation failed */
+#define QMOE_EUNSUPPORTED (-4) /* valid request outside what this build supports */
+
+typedef struct qmoe_ctx qmoe_ctx; /* opaque; owns all device memory it allocates */
+
+/* Expert weight formats (the expert quantizer's precision choices).
+ * Rounding: fp32 arithmetic, round half to even; the stored scale is the one
+ * used to form the codes; a row or group whose stored scale is zero gets
+ * scale 1 and all-zero codes (and zero point 0).
+ *   INT8_SYM_CH       s_n = amax_n/127 (fp32, per output row); q = clamp(rint(w/s), -127, 127)
+ *   INT4_ASYM_G128    per (row, 128-wide group along the input dim): range widened to
+ *                     include 0, s = fp16((max-min)/15), z = clamp(rint(-min/s), 0, 15)
+ *                     stored as fp16, q = clamp(rint(w/s)+z, 0, 15); W = (q-z)*s
+ *   INT4_SYM_G128     s = fp16(amax/7), q = clamp(rint(w/s), -8, 7); W = q*s
+ *   INT3_SYM_G128_IN4 s = fp16(amax/3), q = clamp(rint(w/s), -4, 3), stored in 4-bit
+ *                     containers exactly like INT4_SYM_G128
+ *   FP8E4M3_CH        s_n = amax_n/448 (fp32, per row); q = OCP e4m3fn(w/s), nearest
+ *                     even, saturating at 448; the sign bit follows w/s
+ * fp16 scales saturate at 65504. */
+typedef enum {
+    QMOE_W_INT8_SYM_CH = 0,
+    QMOE_W_INT4_ASYM_G128 = 1,
+    QMOE_W_INT4_SYM_G128 = 2,
+    QMOE_W_INT3_SYM_G128_IN4 = 3,
+    QMOE_W_FP8E4M3_CH = 4
+} qmoe_wformat;
+
+/* Layer configuration, fixed at pack time.
+ *   d_model      input and output width d; multiple of 256
+ *   d_ff         routed expert width F; multiple of 128
+ *   n_experts    routed experts E, 1..1024
+ *   top_k        experts per token k, 1..min(E, 64)
+ *   n_shared     always-on shared experts S >= 0 (mixing weight 1, same format)
+ *   d_ff_shared  shared expert width (multiple of 128; ignored when S = 0)
+ *   wformat      a qmoe_wformat value
+ *   group_size   must be 128 for the group formats (ignored otherwise)
+ *   router_fp32  1: router weight is fp32 [E][d]; 0: bf16 [E][d]
+ *   renormalize  1: weights = softmax over the selected k (they sum to 1);
+ *                0: weights = full-softmax probability of each selected expert
+ *   max_tokens   largest T a forward may pass; sizes the workspace
+ *   device       HIP device ordinal that holds the weights and runs the layer */
+typedef struct {
+    int32_t d_model, d_ff, n_experts, top_k, n_shared, d_ff_shared;
+    int32_t wformat;
+    int32_t group_size;
+    int32_t router_fp32;
+    int32_t renormalize;
+    int32_t max_tokens;
+    int32_t device;
+} qmoe_config;
+
+/* Caller-owned device buffers that receive routing results; any may be NULL.
+ *   logits    [T][E] fp32   router logits x.W_r^T + bias (forward only)
+ *   topk_idx  [T][k] int32  selected experts, descending logit, ties to the
+ *                           lower index
+ *   topk_w    [T][k] fp32   their mixing weights
+ *   counts    [E]    int32  tasks (token, slot) per expert
+ *   offsets   [E+1]  int32  exclusive scan of counts
+ *   perm      [T*k]  int32  task list: perm[row] = t*k + j, rows grouped by
+ *                           expert in expert order, tokens ascending inside */
+typedef struct {
+    float *logits;
+    int32_t *topk_idx;
+    float *topk_w;
+    int32_t *counts;
+    int32_t *offsets;
+    int32_t *perm;
+} qmoe_route_out;
+
+/* The expert quantizer (Q-MoE page, section 3, "Expert Quantizer"; section 4
+ * INT4/INT8 quantization). Synchronous.
+ *   cfg        layer configuration (copied)
+ *   w_gate     host array of E+S host pointers, each fp32 row-major [F][d]
+ *              (routed experts 0..E-1, then shared experts, whose F is d_ff_shared)
+ *   w_up       same shape as w_gate
+ *   w_down     E+S host pointers, each fp32 row-major [d][F]
+ *   w_router   host [E][d], fp32 or bf16 bit patterns per cfg->router_fp32
+ *   router_bias host [E] fp32 added to every logit, or NULL
+ *   out        receives the new context; *out is NULL on failure
+ * Host arrays are only read during the call. Quantizes every matrix on the
+ * host, lays the codes out for the device kernels, allocates the weight arena
+ * and a workspace sized for cfg->max_tokens on cfg->device. */
+int qmoe_pack_experts(const qmoe_config *cfg, const float *const *w_gate, const float *const *w_up,
+                      const float *const *w_down, const void *w_router, const float *router_bias, qmoe_ctx **out);
+
+/* The gating network's selection and the expert-centric task list, from given
+ * logits (Q-MoE page, section 3 "Gating Network"; OmniMoE technical summary
+ * 2.2, task collection and grouping). Asynchronous on `stream`.
+ *   logits  device [T][E] fp32 (any bias already added); finite values only
+ *   T       0 <= T <= max_tokens (T = 0 is a no-op)
+ *   out     device buffers to fill (logits member ignored); NULL members skipped
+ *   stream  hipStream_t (NULL = the null stream) */
+int qmoe_route_topk(qmoe_ctx *ctx, const float *logits, int32_t T, qmoe_route_out *out, void *stream);
+
+/* The sparse execution engine: y = sum_j w_tj * Expert_{e_tj}(x_t) + sum_s Shared_s(x_t),
+ * Expert(x) = W_down (silu(W_gate x) * (W_up x)) on the quantized weights.
+ * Asynchronous on `stream`; never synchronises with the host.
+ *   x       device [T][d] bf16
+ *   T       0 <= T <= max_tokens (T = 0 is a no-op)
+ *   y       device [T][d] bf16 output (may not alias x)
+ *   dbg     NULL, or device buffers that receive this call's routing
+ *   stream  hipStream_t (NULL = the null stream) */
+int qmoe_forward(qmoe_ctx *ctx, const uint16_t *x, int32_t T, uint16_t *y, qmoe_route_out *dbg, void *stream);
+
+/* Frees the context and its device memory. NULL is a no-op. The caller must
+ * have synchronised every stream that used the context. */
+void qmoe_destroy(qmoe_ctx *ctx);
+
+/* Thread-local description of the last failing call on this thread ("" if none). */
+const char *qmoe_last_error(void);
+
+/* Reads one packed matrix back in canonical form (synchronous; for tests).
+ *   expert  0..E-1 routed, E..E+S-1 shared
+ *   matrix  0 gate [F][d], 1 up [F][d], 2 down [d][F]
+ *   codes   host [N][K] int8: signed q (symmetric formats), 0..15 (INT4_ASYM),
+ *           raw e4m3 byte (FP8)
+ *   scales  host fp32 [N][K/128] (group formats) or [N] (per-channel)
+ *   zeros   host, same shape as scales (0 except INT4_ASYM), or NULL */
+int qmoe_export_packed(qmoe_ctx *ctx, int32_t expert, int32_t matrix, int8_t *codes, float *scales, float *zeros);
+
+/* Kernel timing with HIP events recorded on the launch stream around every
+ * kernel of qmoe_forward / qmoe_route_topk (for measurement).
+ *   qmoe_profile_enable   on = 1 starts recording (clears totals), 0 stops
+ *   qmoe_profile_read     synchronises the recorded events and returns, per
+ *                         kernel slot (QMOE_NUM_KERNELS), the summed elapsed
+ *                         milliseconds and the number of launches
+ *   qmoe_kernel_name      name of a kernel slot */
+#define QMOE_NUM_KERNELS 9
+int qmoe_profile_enable(qmoe_ctx *ctx, int32_t on);
+int qmoe_profile_read(qmoe_ctx *ctx, double *total_ms, int64_t *launches);
+const char *qmoe_kernel_name(int32_t slot);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMOE_H */

@@ -1,0 +1,571 @@
+// C-ABI entry points of the quantized top-k MoE layer (see include/qmoe.h).
+//
+// qmoe_pack_experts  : expert quantizer (host) + device weight arena + workspace
+// qmoe_route_topk    : top-k selection and expert-centric task list from logits
+// qmoe_forward       : router -> top-k -> dispatch -> grouped gate/up -> grouped
+//                      down -> combine, all HIP kernels on the caller's stream
+// qmoe_destroy       : frees the context
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include <hip/hip_runtime_api.h>
+
+#include "qmoe_internal.h"
+
+using namespace qmoe;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+const char *kKernelNames[QMOE_NUM_KERNELS] = {"router", "topk", "dispatch_count", "dispatch_scan",
+                                              "dispatch_scatter", "xsum", "gemm_gate_up", "gemm_down", "combine"};
+enum Slot { K_ROUTER = 0, K_TOPK, K_DCOUNT, K_DSCAN, K_DSCATTER, K_XSUM, K_GEMM13, K_GEMM2, K_COMBINE };
+
+struct MatInfo {
+    int N = 0, K = 0;
+    size_t codes_off = 0, codes_bytes = 0;
+    size_t gs_off = 0, gz_off = 0, ps_off = 0;   // byte offsets in the arena (0 = absent)
+    size_t gs_count = 0, ps_count = 0;
+};
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+}  // namespace
+
+struct qmoe_ctx {
+    qmoe_config cfg{};
+    int df = 0;
+    int E = 0, S = 0, F = 0, Fs = 0, d = 0, k = 0;
+    int maxT = 0;
+    // weights
+    uint8_t *arena = nullptr;
+    size_t arena_bytes = 0;
+    std::vector<MatInfo> m13, m2;   // per expert (E + S)
+    ExpertW *d_experts = nullptr;
+    void *router_w = nullptr;       // bf16 [E][d] or fp32 [E][d]
+    float *router_b = nullptr;
+    // workspace
+    float *logits = nullptr, *wpair = nullptr;
+    int32_t *idx = nullptr, *chunk_counts = nullptr, *chunk_base = nullptr, *counts = nullptr, *offsets = nullptr;
+    int32_t *perm = nullptr, *inv = nullptr, *num_tiles = nullptr;
+    Tile *tiles = nullptr;
+    uint16_t *H = nullptr;
+    float *O = nullptr, *xsum = nullptr, *hsum = nullptr;
+    int ldh = 0;
+    size_t tiles_cap = 0;
+    std::vector<void *> allocs;
+    // profiling
+    bool prof = false;
+    struct Rec {
+        int slot;
+        hipEvent_t a, b;
+    };
+    std::vector<Rec> recs;
+    std::vector<hipEvent_t> pool;
+    double tot_ms[QMOE_NUM_KERNELS] = {};
+    int64_t launches[QMOE_NUM_KERNELS] = {};
+    bool debug_sync = false;
+};
+
+namespace {
+
+int dalloc(qmoe_ctx *c, void **p, size_t bytes) {
+    if (bytes == 0) bytes = 256;
+    if (getenv("QMOE_TEST_FAIL_ALLOC")) return fail(QMOE_ENOMEM, "allocation failure injected (QMOE_TEST_FAIL_ALLOC)");
+    hipError_t e = hipMalloc(p, bytes);
+    if (e != hipSuccess) {
+        *p = nullptr;
+        return fail(QMOE_ENOMEM, "hipMalloc(%zu) failed: %s", bytes, hipGetErrorString(e));
+    }
+    c->allocs.push_back(*p);
+    return QMOE_OK;
+}
+
+int validate(const qmoe_config *cfg) {
+    if (!cfg) return fail(QMOE_EINVAL, "cfg is NULL");
+    if (cfg->d_model <= 0 || cfg->d_ff <= 0 || cfg->n_experts <= 0 || cfg->max_tokens <= 0)
+        return fail(QMOE_EINVAL, "d_model, d_ff, n_experts and max_tokens must be positive");
+    if (cfg->top_k < 1 || cfg->top_k > cfg->n_experts)
+        return fail(QMOE_EINVAL, "top_k=%d must be in [1, n_experts=%d]", cfg->top_k, cfg->n_experts);
+    if (cfg->n_shared < 0) return fail(QMOE_EINVAL, "n_shared must be >= 0");
+    if (cfg->n_shared > 0 && cfg->d_ff_shared <= 0) return fail(QMOE_EINVAL, "d_ff_shared must be positive");
+    if (dev_format(cfg->wformat) < 0) return fail(QMOE_EINVAL, "unknown wformat %d", cfg->wformat);
+    if (cfg->d_model % 256 != 0) return fail(QMOE_EUNSUPPORTED, "d_model=%d is not a multiple of 256", cfg->d_model);
+    if (cfg->d_ff % 128 != 0) return fail(QMOE_EUNSUPPORTED, "d_ff=%d is not a multiple of 128", cfg->d_ff);
+    if (cfg->n_shared > 0 && cfg->d_ff_shared % 128 != 0)
+        return fail(QMOE_EUNSUPPORTED, "d_ff_shared=%d is not a multiple of 128", cfg->d_ff_shared);
+    if (is_group_wformat(cfg->wformat) && cfg->group_size != 128)
+        return fail(QMOE_EUNSUPPORTED, "group_size=%d: only 128 is supported", cfg->group_size);
+    if (cfg->n_experts > 1024) return fail(QMOE_EUNSUPPORTED, "n_experts=%d exceeds 1024", cfg->n_experts);
+    if (cfg->top_k > 64) return fail(QMOE_EUNSUPPORTED, "top_k=%d exceeds 64", cfg->top_k);
+    const long long rows = (long long)cfg->max_tokens * (cfg->top_k + cfg->n_shared);
+    if (rows >= (1ll << 30)) return fail(QMOE_EUNSUPPORTED, "max_tokens=%d too large", cfg->max_tokens);
+    if (cfg->renormalize != 0 && cfg->renormalize != 1) return fail(QMOE_EINVAL, "renormalize must be 0 or 1");
+    if (cfg->router_fp32 != 0 && cfg->router_fp32 != 1) return fail(QMOE_EINVAL, "router_fp32 must be 0 or 1");
+    return QMOE_OK;
+}
+
+// Quantize + lay out one expert (all three matrices).
+struct ExpertPack {
+    PackedMatrix w13, w2;
+    int rc = QMOE_OK;
+};
+
+void pack_one(int wformat, int F, int d, const float *wg, const float *wu, const float *wd, ExpertPack &out) {
+    CanonMatrix g, u, dn, w13;
+    int rc = quantize_matrix(wformat, F, d, wg, g);
+    if (rc == QMOE_OK) rc = quantize_matrix(wformat, F, d, wu, u);
+    if (rc == QMOE_OK) rc = quantize_matrix(wformat, d, F, wd, dn);
+    if (rc != QMOE_OK) {
+        out.rc = rc;
+        return;
+    }
+    interleave_gate_up(g, u, w13, is_group_wformat(wformat));
+    layout_matrix(wformat, w13, out.w13);
+    layout_matrix(wformat, dn, out.w2);
+}
+
+MatInfo plan_matrix(const PackedMatrix &p, int N, int K, size_t &cursor) {
+    MatInfo m;
+    m.N = N;
+    m.K = K;
+    m.codes_off = cursor;
+    m.codes_bytes = p.codes.size();
+    cursor = align256(cursor + m.codes_bytes);
+    if (!p.gscale.empty()) {
+        m.gs_off = cursor;
+        m.gs_count = p.gscale.size();
+        cursor = align256(cursor + p.gscale.size() * 2);
+    }
+    if (!p.gzero.empty()) {
+        m.gz_off = cursor;
+        cursor = align256(cursor + p.gzero.size() * 2);
+    }
+    if (!p.pscale.empty()) {
+        m.ps_off = cursor;
+        m.ps_count = p.pscale.size();
+        cursor = align256(cursor + p.pscale.size() * 4);
+    }
+    return m;
+}
+
+int upload_matrix(qmoe_ctx *c, const MatInfo &m, const PackedMatrix &p) {
+    hipError_t e = hipMemcpy(c->arena + m.codes_off, p.codes.data(), p.codes.size(), hipMemcpyHostToDevice);
+    if (e == hipSuccess && m.gs_off)
+        e = hipMemcpy(c->arena + m.gs_off, p.gscale.data(), p.gscale.size() * 2, hipMemcpyHostToDevice);
+    if (e == hipSuccess && m.gz_off)
+        e = hipMemcpy(c->arena + m.gz_off, p.gzero.data(), p.gzero.size() * 2, hipMemcpyHostToDevice);
+    if (e == hipSuccess && m.ps_off)
+        e = hipMemcpy(c->arena + m.ps_off, p.pscale.data(), p.pscale.size() * 4, hipMemcpyHostToDevice);
+    if (e != hipSuccess) return fail(QMOE_EHIP, "hipMemcpy of packed weights failed: %s", hipGetErrorString(e));
+    return QMOE_OK;
+}
+
+void free_ctx(qmoe_ctx *c) {
+    if (!c) return;
+    for (void *p : c->allocs) (void)hipFree(p);
+    for (auto &r : c->recs) {
+        (void)hipEventDestroy(r.a);
+        (void)hipEventDestroy(r.b);
+    }
+    for (auto ev : c->pool) (void)hipEventDestroy(ev);
+    delete c;
+}
+
+hipEvent_t take_event(qmoe_ctx *c) {
+    if (!c->pool.empty()) {
+        hipEvent_t e = c->pool.back();
+        c->pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+// Runs `launch` (returning hipError_t) with optional event timing around it.
+template <typename Fn>
+int timed(qmoe_ctx *c, int slot, hipStream_t s, Fn launch) {
+    hipEvent_t a = nullptr, b = nullptr;
+    if (c->prof) {
+        a = take_event(c);
+        b = take_event(c);
+        if (a && b) (void)hipEventRecord(a, s);
+    }
+    hipError_t e = launch();
+    if (e != hipSuccess) return fail(QMOE_EHIP, "launch of %s failed: %s", kKernelNames[slot], hipGetErrorString(e));
+    if (c->prof && a && b) {
+        (void)hipEventRecord(b, s);
+        c->recs.push_back({slot, a, b});
+    }
+    if (c->debug_sync) {
+        e = hipStreamSynchronize(s);
+        if (e == hipSuccess) e = hipGetLastError();
+        if (e != hipSuccess) return fail(QMOE_EHIP, "%s failed: %s", kKernelNames[slot], hipGetErrorString(e));
+    }
+    return QMOE_OK;
+}
+
+int rows_per_tile(const qmoe_ctx *c, int T) {
+    const long P = (long)T * c->k;
+    const long active = std::min<long>(c->E, P);
+    const double avg = (double)P / (double)std::max<long>(1, active);
+    if (avg <= 16.0) return 16;
+    if (avg <= 96.0) return 64;
+    return 128;
+}
+
+int max_tiles_for(const qmoe_ctx *c, int T, int bm) {
+    const long P = (long)T * c->k;
+    return (int)((P + bm - 1) / bm + std::min<long>(c->E, P) + (long)c->S * ((T + bm - 1) / bm));
+}
+
+// Top-k + dispatch shared by route_topk and forward.
+int run_route(qmoe_ctx *c, const float *logits, int T, int bm, int n_shared, hipStream_t s) {
+    const int P = T * c->k;
+    const int nchunks = (P + kDispatchChunk - 1) / kDispatchChunk;
+    int rc = timed(c, K_TOPK, s, [&] { return launch_topk(logits, T, c->E, c->k, c->cfg.renormalize, c->idx, c->wpair, s); });
+    if (rc) return rc;
+    rc = timed(c, K_DCOUNT, s, [&] { return launch_dispatch_count(c->idx, P, c->E, c->chunk_counts, s); });
+    if (rc) return rc;
+    rc = timed(c, K_DSCAN, s, [&] {
+        return launch_dispatch_scan(c->chunk_counts, nchunks, c->E, P, T, n_shared, bm, c->chunk_base, c->counts,
+                                    c->offsets, c->tiles, c->num_tiles, s);
+    });
+    if (rc) return rc;
+    return timed(c, K_DSCATTER, s,
+                 [&] { return launch_dispatch_scatter(c->idx, P, c->E, c->chunk_base, c->perm, c->inv, s); });
+}
+
+int copy_out(void *dst, const void *src, size_t bytes, hipStream_t s) {
+    if (!dst || bytes == 0) return QMOE_OK;
+    hipError_t e = hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return fail(QMOE_EHIP, "hipMemcpyAsync failed: %s", hipGetErrorString(e));
+    return QMOE_OK;
+}
+
+int copy_route(qmoe_ctx *c, const qmoe_route_out *o, int T, hipStream_t s) {
+    if (!o) return QMOE_OK;
+    const size_t P = (size_t)T * c->k;
+    int rc = copy_out(o->topk_idx, c->idx, P * 4, s);
+    if (!rc) rc = copy_out(o->topk_w, c->wpair, P * 4, s);
+    if (!rc) rc = copy_out(o->counts, c->counts, (size_t)c->E * 4, s);
+    if (!rc) rc = copy_out(o->offsets, c->offsets, (size_t)(c->E + 1) * 4, s);
+    if (!rc) rc = copy_out(o->perm, c->perm, P * 4, s);
+    return rc;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *qmoe_last_error(void) { return g_last_error.c_str(); }
+
+const char *qmoe_kernel_name(int32_t slot) {
+    return (slot >= 0 && slot < QMOE_NUM_KERNELS) ? kKernelNames[slot] : "";
+}
+
+int qmoe_pack_experts(const qmoe_config *cfg, const float *const *w_gate, const float *const *w_up,
+                      const float *const *w_down, const void *w_router, const float *router_bias, qmoe_ctx **out) {
+    g_last_error.clear();
+    if (!out) return fail(QMOE_EINVAL, "out is NULL");
+    *out = nullptr;
+    int rc = validate(cfg);
+    if (rc) return rc;
+    if (!w_gate || !w_up || !w_down || !w_router) return fail(QMOE_EINVAL, "weight array pointer is NULL");
+    const int nexp = cfg->n_experts + cfg->n_shared;
+    for (int i = 0; i < nexp; i++)
+        if (!w_gate[i] || !w_up[i] || !w_down[i]) return fail(QMOE_EINVAL, "weights of expert %d are NULL", i);
+
+    int ndev = 0;
+    hipError_t he = hipGetDeviceCount(&ndev);
+    if (he != hipSuccess || ndev == 0) return fail(QMOE_EHIP, "no HIP device available");
+    if (cfg->device < 0 || cfg->device >= ndev) return fail(QMOE_EINVAL, "device %d out of range", cfg->device);
+    he = hipSetDevice(cfg->device);
+    if (he != hipSuccess) return fail(QMOE_EHIP, "hipSetDevice: %s", hipGetErrorString(he));
+
+    qmoe_ctx *c = new qmoe_ctx();
+    c->cfg = *cfg;
+    c->df = dev_format(cfg->wformat);
+    c->E = cfg->n_experts;
+    c->S = cfg->n_shared;
+    c->F = cfg->d_ff;
+    c->Fs = cfg->n_shared > 0 ? cfg->d_ff_shared : 0;
+    c->d = cfg->d_model;
+    c->k = cfg->top_k;
+    c->maxT = cfg->max_tokens;
+    c->debug_sync = getenv("QMOE_DEBUG") != nullptr;
+
+    // Quantize and lay out every expert on the host, several experts at a time.
+    std::vector<ExpertPack> packs(nexp);
+    {
+        const int nthreads = std::max(1, std::min<int>(nexp, (int)std::thread::hardware_concurrency()));
+        std::vector<std::thread> pool;
+        for (int tid = 0; tid < nthreads; tid++)
+            pool.emplace_back([&, tid] {
+                for (int i = tid; i < nexp; i += nthreads) {
+                    const int f = i < c->E ? c->F : c->Fs;
+                    pack_one(cfg->wformat, f, c->d, w_gate[i], w_up[i], w_down[i], packs[i]);
+                }
+            });
+        for (auto &t : pool) t.join();
+    }
+    for (int i = 0; i < nexp; i++)
+        if (packs[i].rc) {
+            free_ctx(c);
+            return fail(packs[i].rc, "quantization of expert %d failed", i);
+        }
+
+    size_t cursor = 0;
+    c->m13.resize(nexp);
+    c->m2.resize(nexp);
+    for (int i = 0; i < nexp; i++) {
+        const int f = i < c->E ? c->F : c->Fs;
+        c->m13[i] = plan_matrix(packs[i].w13, 2 * f, c->d, cursor);
+        c->m2[i] = plan_matrix(packs[i].w2, c->d, f, cursor);
+    }
+    c->arena_bytes = cursor;
+    rc = dalloc(c, (void **)&c->arena, c->arena_bytes);
+    for (int i = 0; !rc && i < nexp; i++) {
+        rc = upload_matrix(c, c->m13[i], packs[i].w13);
+        if (!rc) rc = upload_matrix(c, c->m2[i], packs[i].w2);
+        packs[i] = ExpertPack();   // release host copies as we go
+    }
+    if (rc) {
+        free_ctx(c);
+        return rc;
+    }
+    std::vector<ExpertW> hexp(nexp);
+    for (int i = 0; i < nexp; i++) {
+        ExpertW &w = hexp[i];
+        const MatInfo &a = c->m13[i], &b = c->m2[i];
+        w.c13 = c->arena + a.codes_off;
+        w.s13 = a.gs_off ? (const uint16_t *)(c->arena + a.gs_off) : nullptr;
+        w.z13 = a.gz_off ? (const uint16_t *)(c->arena + a.gz_off) : nullptr;
+        w.p13 = a.ps_off ? (const float *)(c->arena + a.ps_off) : nullptr;
+        w.c2 = c->arena + b.codes_off;
+        w.s2 = b.gs_off ? (const uint16_t *)(c->arena + b.gs_off) : nullptr;
+        w.z2 = b.gz_off ? (const uint16_t *)(c->arena + b.gz_off) : nullptr;
+        w.p2 = b.ps_off ? (const float *)(c->arena + b.ps_off) : nullptr;
+        w.F = i < c->E ? c->F : c->Fs;
+    }
+    rc = dalloc(c, (void **)&c->d_experts, sizeof(ExpertW) * nexp);
+    if (!rc && hipMemcpy(c->d_experts, hexp.data(), sizeof(ExpertW) * nexp, hipMemcpyHostToDevice) != hipSuccess)
+        rc = fail(QMOE_EHIP, "upload of expert table failed");
+
+    // Router weight and bias.
+    const size_t wr_bytes = (size_t)c->E * c->d * (cfg->router_fp32 ? 4 : 2);
+    if (!rc) rc = dalloc(c, &c->router_w, wr_bytes);
+    if (!rc && hipMemcpy(c->router_w, w_router, wr_bytes, hipMemcpyHostToDevice) != hipSuccess)
+        rc = fail(QMOE_EHIP, "upload of router weight failed");
+    if (!rc && router_bias) {
+        rc = dalloc(c, (void **)&c->router_b, sizeof(float) * c->E);
+        if (!rc && hipMemcpy(c->router_b, router_bias, sizeof(float) * c->E, hipMemcpyHostToDevice) != hipSuccess)
+            rc = fail(QMOE_EHIP, "upload of router bias failed");
+    }
+
+    // Workspace sized for max_tokens.
+    const size_t T = (size_t)c->maxT, P = T * c->k;
+    const size_t nchunks = (P + kDispatchChunk - 1) / kDispatchChunk;
+    const size_t rows_total = P + (size_t)c->S * T;
+    c->ldh = std::max(c->F, c->Fs);
+    c->tiles_cap = (size_t)max_tiles_for(c, c->maxT, 16) + 16;
+    if (!rc) rc = dalloc(c, (void **)&c->logits, T * c->E * 4);
+    if (!rc) rc = dalloc(c, (void **)&c->wpair, P * 4);
+    if (!rc) rc = dalloc(c, (void **)&c->idx, P * 4);
+    if (!rc) rc = dalloc(c, (void **)&c->chunk_counts, nchunks * c->E * 4);
+    if (!rc) rc = dalloc(c, (void **)&c->chunk_base, nchunks * c->E * 4);
+    if (!rc) rc = dalloc(c, (void **)&c->counts, (size_t)c->E * 4);
+    if (!rc) rc = dalloc(c, (void **)&c->offsets, (size_t)(c->E + 1) * 4);
+    if (!rc) rc = dalloc(c, (void **)&c->perm, P * 4);
+    if (!rc) rc = dalloc(c, (void **)&c->inv, P * 4);
+    if (!rc) rc = dalloc(c, (void **)&c->num_tiles, 256);
+    if (!rc) rc = dalloc(c, (void **)&c->tiles, c->tiles_cap * sizeof(Tile));
+    if (!rc) rc = dalloc(c, (void **)&c->H, rows_total * c->ldh * 2);
+    if (!rc) rc = dalloc(c, (void **)&c->O, rows_total * c->d * 4);
+    if (!rc) rc = dalloc(c, (void **)&c->xsum, T * (c->d / 128) * 4);
+    if (!rc) rc = dalloc(c, (void **)&c->hsum, rows_total * (c->ldh / 128) * 4);
+    if (rc) {
+        free_ctx(c);
+        return rc;
+    }
+    *out = c;
+    return QMOE_OK;
+}
+
+void qmoe_destroy(qmoe_ctx *ctx) {
+    if (!ctx) return;
+    (void)hipSetDevice(ctx->cfg.device);
+    free_ctx(ctx);
+}
+
+int qmoe_route_topk(qmoe_ctx *c, const float *logits, int32_t T, qmoe_route_out *out, void *stream) {
+    g_last_error.clear();
+    if (!c) return fail(QMOE_EINVAL, "ctx is NULL");
+    if (T < 0 || T > c->maxT) return fail(QMOE_EINVAL, "T=%d outside [0, max_tokens=%d]", T, c->maxT);
+    if (T == 0) return QMOE_OK;
+    if (!logits) return fail(QMOE_EINVAL, "logits is NULL");
+    hipStream_t s = (hipStream_t)stream;
+    if (hipSetDevice(c->cfg.device) != hipSuccess) return fail(QMOE_EHIP, "hipSetDevice failed");
+    int rc = run_route(c, logits, T, 128, 0, s);
+    if (rc) return rc;
+    return copy_route(c, out, T, s);
+}
+
+int qmoe_forward(qmoe_ctx *c, const uint16_t *x, int32_t T, uint16_t *y, qmoe_route_out *dbg, void *stream) {
+    g_last_error.clear();
+    if (!c) return fail(QMOE_EINVAL, "ctx is NULL");
+    if (T < 0 || T > c->maxT) return fail(QMOE_EINVAL, "T=%d outside [0, max_tokens=%d]", T, c->maxT);
+    if (T == 0) return QMOE_OK;
+    if (!x || !y) return fail(QMOE_EINVAL, "x or y is NULL");
+    if ((const void *)x == (const void *)y) return fail(QMOE_EINVAL, "y may not alias x");
+    hipStream_t s = (hipStream_t)stream;
+    if (hipSetDevice(c->cfg.device) != hipSuccess) return fail(QMOE_EHIP, "hipSetDevice failed");
+
+    const int P = T * c->k;
+    const int bm = rows_per_tile(c, T);
+    const int max_tiles = max_tiles_for(c, T, bm);
+    int rc;
+    if (c->cfg.router_fp32)
+        rc = timed(c, K_ROUTER, s, [&] {
+            return launch_router_f32(x, (const float *)c->router_w, c->router_b, c->logits, T, c->d, c->E, s);
+        });
+    else
+        rc = timed(c, K_ROUTER, s, [&] {
+            return launch_router_bf16(x, (const uint16_t *)c->router_w, c->router_b, c->logits, T, c->d, c->E, s);
+        });
+    if (rc) return rc;
+    rc = run_route(c, c->logits, T, bm, c->S, s);
+    if (rc) return rc;
+    if (is_group_wformat(c->cfg.wformat)) {
+        rc = timed(c, K_XSUM, s, [&] { return launch_xsum(x, T, c->d, c->xsum, s); });
+        if (rc) return rc;
+    }
+
+    GemmArgs a{};
+    a.experts = c->d_experts;
+    a.tiles = c->tiles;
+    a.num_tiles = c->num_tiles;
+    a.perm = c->perm;
+    a.wpair = c->wpair;
+    a.x = x;
+    a.xsum = c->xsum;
+    a.H = c->H;
+    a.hsum = c->hsum;
+    a.O = c->O;
+    a.ldh = c->ldh;
+    a.d = c->d;
+    a.k = c->k;
+    a.P = P;
+    a.T = T;
+    a.E = c->E;
+    const int maxN13 = 2 * std::max(c->F, c->Fs);
+    rc = timed(c, K_GEMM13, s, [&] { return launch_gemm13(c->df, bm, a, max_tiles, maxN13, s); });
+    if (rc) return rc;
+    rc = timed(c, K_GEMM2, s, [&] { return launch_gemm2(c->df, bm, a, max_tiles, s); });
+    if (rc) return rc;
+    rc = timed(c, K_COMBINE, s, [&] { return launch_combine(c->O, c->inv, T, c->d, c->k, P, c->S, y, s); });
+    if (rc) return rc;
+    if (dbg) {
+        rc = copy_out(dbg->logits, c->logits, (size_t)T * c->E * 4, s);
+        if (!rc) rc = copy_route(c, dbg, T, s);
+    }
+    return rc;
+}
+
+int qmoe_export_packed(qmoe_ctx *c, int32_t expert, int32_t matrix, int8_t *codes, float *scales, float *zeros) {
+    g_last_error.clear();
+    if (!c || !codes || !scales) return fail(QMOE_EINVAL, "NULL argument");
+    if (expert < 0 || expert >= c->E + c->S || matrix < 0 || matrix > 2)
+        return fail(QMOE_EINVAL, "expert %d / matrix %d out of range", expert, matrix);
+    if (hipSetDevice(c->cfg.device) != hipSuccess) return fail(QMOE_EHIP, "hipSetDevice failed");
+    const MatInfo &m = matrix == 2 ? c->m2[expert] : c->m13[expert];
+    PackedMatrix p;
+    p.codes.resize(m.codes_bytes);
+    hipError_t e = hipMemcpy(p.codes.data(), c->arena + m.codes_off, m.codes_bytes, hipMemcpyDeviceToHost);
+    if (e == hipSuccess && m.gs_off) {
+        p.gscale.resize(m.gs_count);
+        e = hipMemcpy(p.gscale.data(), c->arena + m.gs_off, m.gs_count * 2, hipMemcpyDeviceToHost);
+    }
+    if (e == hipSuccess && m.gz_off) {
+        p.gzero.resize(m.gs_count);
+        e = hipMemcpy(p.gzero.data(), c->arena + m.gz_off, m.gs_count * 2, hipMemcpyDeviceToHost);
+    }
+    if (e == hipSuccess && m.ps_off) {
+        p.pscale.resize(m.ps_count);
+        e = hipMemcpy(p.pscale.data(), c->arena + m.ps_off, m.ps_count * 4, hipMemcpyDeviceToHost);
+    }
+    if (e != hipSuccess) return fail(QMOE_EHIP, "hipMemcpy D2H failed: %s", hipGetErrorString(e));
+    CanonMatrix full;
+    full.N = m.N;
+    full.K = m.K;
+    unlayout_matrix(c->cfg.wformat, p, full);
+    const int G = is_group_wformat(c->cfg.wformat) ? m.K / kBlockK : 1;
+    // W13 rows alternate gate / up in 16-row blocks; select the requested half.
+    const int outN = matrix == 2 ? m.N : m.N / 2;
+    for (int r = 0; r < outN; r++) {
+        const int src = matrix == 2 ? r : ((r / kBlockRows) * 2 + matrix) * kBlockRows + r % kBlockRows;
+        memcpy(codes + (size_t)r * m.K, &full.q[(size_t)src * m.K], (size_t)m.K);
+        for (int g = 0; g < G; g++) {
+            scales[(size_t)r * G + g] = full.scale[(size_t)src * G + g];
+            if (zeros) zeros[(size_t)r * G + g] = full.zero[(size_t)src * G + g];
+        }
+    }
+    return QMOE_OK;
+}
+
+int qmoe_profile_enable(qmoe_ctx *c, int32_t on) {
+    if (!c) return fail(QMOE_EINVAL, "ctx is NULL");
+    c->prof = on != 0;
+    if (c->prof) {
+        for (auto &r : c->recs) {
+            c->pool.push_back(r.a);
+            c->pool.push_back(r.b);
+        }
+        c->recs.clear();
+        for (int i = 0; i < QMOE_NUM_KERNELS; i++) {
+            c->tot_ms[i] = 0.0;
+            c->launches[i] = 0;
+        }
+    }
+    return QMOE_OK;
+}
+
+int qmoe_profile_read(qmoe_ctx *c, double *total_ms, int64_t *launches) {
+    if (!c || !total_ms || !launches) return fail(QMOE_EINVAL, "NULL argument");
+    for (auto &r : c->recs) {
+        if (hipEventSynchronize(r.b) != hipSuccess) return fail(QMOE_EHIP, "hipEventSynchronize failed");
+        float ms = 0.0f;
+        if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) return fail(QMOE_EHIP, "hipEventElapsedTime failed");
+        c->tot_ms[r.slot] += ms;
+        c->launches[r.slot] += 1;
+        c->pool.push_back(r.a);
+        c->pool.push_back(r.b);
+    }
+    c->recs.clear();
+    for (int i = 0; i < QMOE_NUM_KERNELS; i++) {
+        total_ms[i] = c->tot_ms[i];
+        launches[i] = c->launches[i];
+    }
+    return QMOE_OK;
+}
+
+}  // extern "C"

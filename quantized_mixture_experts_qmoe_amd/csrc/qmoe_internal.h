@@ -1,0 +1,153 @@
+// Internal declarations shared by the HIP library's translation units
+// (packer, kernels, C-ABI layer). Not installed; not part of the ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include <hip/hip_runtime_api.h>
+
+#include "../../include/qmoe.h"
+
+namespace qmoe {
+
+// ---------------------------------------------------------------------------
+// Device weight layout.
+//
+// A packed block covers 16 output rows x 128 input positions (k) of one matrix.
+// 4-bit formats: 1024 bytes. Lane l (0..63) of a wave owns bytes [16l, 16l+16);
+//   its dword s (0..3) holds the eight codes of row (l % 16) at
+//   k = 32s + 8(l/16) + j, j = 0..7. Code j occupies bits [4(j/2), 4(j/2)+4) when
+//   j is even and bits [16 + 4(j/2), 16 + 4(j/2)+4) when j is odd, so that
+//   (dword >> 4i) & 0x000F000F yields codes 2i and 2i+1 in the two 16-bit halves.
+//   Stored values are unsigned: q + 8 for the symmetric formats, q for INT4_ASYM.
+// 8-bit formats: 2048 bytes. Lane l owns bytes [32l, 32l+32); dwords 2s and 2s+1
+//   hold the eight codes of row (l % 16) at k = 32s + 8(l/16) + j in byte j.
+// In both cases a lane's dword pair for step s is exactly the B operand of one
+// v_mfma_f32_16x16x32_bf16 (lane l supplies column l%16, k = 8(l/16)..+8).
+// Blocks are stored row-block major: block (rb, kb) at index rb*(K/128) + kb.
+// Group scales / zeros (fp16 bits): [N/16][K/128][16], the block's 16 rows
+// contiguous. Per-channel scales (fp32): [N].
+//
+// The gate and up matrices of one expert are packed as a single matrix "W13"
+// of 2F rows whose 16-row blocks alternate: block 2b = gate rows 16b..16b+15,
+// block 2b+1 = up rows 16b..16b+15. The down matrix "W2" is [d][F].
+// ---------------------------------------------------------------------------
+constexpr int kBlockRows = 16;
+constexpr int kBlockK = 128;
+
+enum DevFormat : int {
+    DF_INT8 = 0,   // signed int8 codes, fp32 per-row scale
+    DF_I4ASYM = 1, // 4-bit codes, fp16 scale + zero per (row, group)
+    DF_I4SYM = 2,  // 4-bit codes (q+8), fp16 scale per (row, group); INT3 uses it too
+    DF_FP8 = 4     // e4m3 codes, fp32 per-row scale
+};
+
+inline int dev_format(int wformat) {
+    switch (wformat) {
+    case QMOE_W_INT8_SYM_CH: return DF_INT8;
+    case QMOE_W_INT4_ASYM_G128: return DF_I4ASYM;
+    case QMOE_W_INT4_SYM_G128: return DF_I4SYM;
+    case QMOE_W_INT3_SYM_G128_IN4: return DF_I4SYM;
+    case QMOE_W_FP8E4M3_CH: return DF_FP8;
+    default: return -1;
+    }
+}
+inline bool is_group_wformat(int wformat) {
+    return wformat == QMOE_W_INT4_ASYM_G128 || wformat == QMOE_W_INT4_SYM_G128 ||
+           wformat == QMOE_W_INT3_SYM_G128_IN4;
+}
+inline int block_bytes(int df) { return (df == DF_INT8 || df == DF_FP8) ? 2048 : 1024; }
+
+// Per-expert device pointers (one entry per routed expert, then per shared expert).
+struct ExpertW {
+    const uint8_t *c13;   // W13 codes
+    const uint16_t *s13;  // W13 group scales (fp16 bits) or nullptr
+    const uint16_t *z13;  // W13 group zeros (fp16 bits) or nullptr
+    const float *p13;     // W13 per-channel scales [2F] or nullptr
+    const uint8_t *c2;    // W2 codes
+    const uint16_t *s2;
+    const uint16_t *z2;
+    const float *p2;      // W2 per-channel scales [d]
+    int32_t F;            // d_ff of this expert
+    int32_t pad[3];
+};
+
+// One M-tile of the grouped GEMMs: rows [row0, row_end) of expert e.
+struct Tile {
+    int32_t e, row0, row_end, pad;
+};
+
+// ---------------------------------------------------------------------------
+// Host packer (qmoe_pack.cpp)
+// ---------------------------------------------------------------------------
+struct CanonMatrix {      // canonical quantized matrix, row-major [N][K]
+    int N = 0, K = 0;
+    std::vector<int8_t> q;     // codes as exported
+    std::vector<float> scale;  // [N][G] or [N]
+    std::vector<float> zero;   // same shape as scale
+};
+
+// Quantize w[N][K] by the format rules. Returns QMOE_OK or a QMOE_E* code.
+int quantize_matrix(int wformat, int N, int K, const float *w, CanonMatrix &out);
+
+// Device layout of a canonical matrix (codes blocks, group scales/zeros as fp16
+// bits, per-channel scales). For W13 the caller passes the interleaved matrix.
+struct PackedMatrix {
+    std::vector<uint8_t> codes;
+    std::vector<uint16_t> gscale, gzero;
+    std::vector<float> pscale;
+};
+void layout_matrix(int wformat, const CanonMatrix &m, PackedMatrix &out);
+// Build the interleaved W13 canonical matrix from gate and up.
+void interleave_gate_up(const CanonMatrix &gate, const CanonMatrix &up, CanonMatrix &w13, bool group_format);
+// Inverse of layout_matrix (for export): fills codes/scales/zeros of m (N, K preset).
+void unlayout_matrix(int wformat, const PackedMatrix &p, CanonMatrix &m);
+
+// ---------------------------------------------------------------------------
+// Kernel launchers (qmoe_kernels.hip). All asynchronous on `s`.
+// ---------------------------------------------------------------------------
+hipError_t launch_router_bf16(const uint16_t *x, const uint16_t *wr, const float *bias, float *logits, int T, int d,
+                              int E, hipStream_t s);
+hipError_t launch_router_f32(const uint16_t *x, const float *wr, const float *bias, float *logits, int T, int d, int E,
+                             hipStream_t s);
+hipError_t launch_topk(const float *logits, int T, int E, int k, int renorm, int32_t *idx, float *w, hipStream_t s);
+
+// Dispatch: per-chunk histogram, scan + tile list, stable scatter.
+constexpr int kDispatchChunk = 1024;
+hipError_t launch_dispatch_count(const int32_t *idx, int P, int E, int32_t *chunk_counts, hipStream_t s);
+hipError_t launch_dispatch_scan(const int32_t *chunk_counts, int nchunks, int E, int P, int T, int n_shared, int bm,
+                                int32_t *chunk_base, int32_t *counts, int32_t *offsets, Tile *tiles,
+                                int32_t *num_tiles, hipStream_t s);
+hipError_t launch_dispatch_scatter(const int32_t *idx, int P, int E, const int32_t *chunk_base, int32_t *perm,
+                                   int32_t *inv, hipStream_t s);
+
+struct GemmArgs {
+    const ExpertW *experts;
+    const Tile *tiles;
+    const int32_t *num_tiles;
+    const int32_t *perm;     // task list (pair id per routed row)
+    const float *wpair;      // mixing weight per pair [P]
+    const uint16_t *x;       // [T][d] bf16 (gate/up input)
+    const float *xsum;       // [T][d/128] group sums of x
+    uint16_t *H;             // [rows][ldh] bf16 intermediate
+    float *hsum;             // [rows][ldh/128] group sums of H (bf16-rounded values)
+    float *O;                // [rows][d] fp32 weighted expert outputs
+    int32_t ldh;
+    int32_t d;
+    int32_t k;               // top-k
+    int32_t P;               // routed rows (T*k)
+    int32_t T;
+    int32_t E;               // routed experts
+};
+// bm: rows per M-tile (16, 64 or 128); max_tiles: grid bound; maxN13: max 2F.
+hipError_t launch_gemm13(int df, int bm, const GemmArgs &a, int max_tiles, int maxN13, hipStream_t s);
+hipError_t launch_gemm2(int df, int bm, const GemmArgs &a, int max_tiles, hipStream_t s);
+hipError_t launch_combine(const float *O, const int32_t *inv, int T, int d, int k, int P, int n_shared,
+                          uint16_t *y, hipStream_t s);
+hipError_t launch_xsum(const uint16_t *x, int T, int d, float *xsum, hipStream_t s);
+
+}  // namespace qmoe

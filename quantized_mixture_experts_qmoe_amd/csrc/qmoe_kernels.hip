@@ -1,0 +1,801 @@
+// HIP kernels of the quantized top-k MoE layer for gfx950 (CDNA4).
+//
+//   router      logits = x . W_r^T (+ bias): bf16 MFMA with fp32 accumulation
+//               (fp32 router weights: a plain fp32 dot-product kernel)
+//   top-k       one wavefront per token: k rounds of a wave-wide (value, index)
+//               max reduction, lowest index wins ties; softmax over the selection
+//   dispatch    expert-centric task list (OmniMoE page, technical summary 2.2:
+//               collect tasks, group by expert id, token order inside a group):
+//               per-chunk histogram -> scan + M-tile list -> stable scatter
+//   xsum        per-token sums of x over 128-wide groups (offset correction)
+//   gemm13      grouped gate/up GEMM over the task list: packed codes become
+//               exact bf16 MFMA operands in registers (group scales applied in
+//               fp32 per group), gathered token rows are staged in LDS,
+//               SiLU(gate) * up is fused in the epilogue
+//   gemm2       grouped down GEMM; the epilogue applies the mixing weight
+//   combine     y_t = sum_j O[row(t, j)] + sum_s O_shared(t), fp32, bf16 out
+#include <hip/hip_runtime.h>
+
+#include "qmoe_internal.h"
+
+namespace qmoe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16f(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+__device__ __forceinline__ uint16_t to_bf16(float f) {
+    __bf16 h = (__bf16)f;   // round to nearest even (v_cvt_pk_bf16_f32)
+    return __builtin_bit_cast(uint16_t, h);
+}
+__device__ __forceinline__ float half_bits_to_f32(uint16_t b) {
+    return (float)__builtin_bit_cast(_Float16, b);
+}
+
+// ---------------------------------------------------------------------------
+// Router
+// ---------------------------------------------------------------------------
+
+// Workgroup = 4 waves, tile 64 tokens x 64 experts; wave w owns tokens
+// [16w, 16w+16) against all 64 experts (four 16x16 accumulators).
+__global__ __launch_bounds__(256) void k_router_bf16(const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr,
+                                                     const float *__restrict__ bias, float *__restrict__ logits, int T,
+                                                     int d, int E) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int t0 = blockIdx.x * 64 + wave * 16;
+    const int e0 = blockIdx.y * 64;
+    const int kq = (lane >> 4) * 8;
+    const int ar = t0 + (lane & 15);
+    const bool aok = ar < T;
+    const uint16_t *ap = x + (size_t)(aok ? ar : 0) * d + kq;
+    const uint16_t *bp[4];
+    bool bok[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int be = e0 + 16 * i + (lane & 15);
+        bok[i] = be < E;
+        bp[i] = wr + (size_t)(bok[i] ? be : 0) * d + kq;
+    }
+    f32x4 acc[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const uint4 zero4 = make_uint4(0, 0, 0, 0);
+#pragma unroll 4
+    for (int k0 = 0; k0 < d; k0 += 32) {
+        const uint4 av = aok ? *reinterpret_cast<const uint4 *>(ap + k0) : zero4;
+        const bf16x8 a = __builtin_bit_cast(bf16x8, av);
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const uint4 bv = bok[i] ? *reinterpret_cast<const uint4 *>(bp[i] + k0) : zero4;
+            acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, bv), acc[i], 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int e = e0 + 16 * i + (lane & 15);
+        if (e >= E) continue;
+        const float b = bias ? bias[e] : 0.0f;
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const int t = t0 + (lane >> 4) * 4 + r;
+            if (t < T) logits[(size_t)t * E + e] = acc[i][r] + b;
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void k_router_f32(const uint16_t *__restrict__ x, const float *__restrict__ wr,
+                                                    const float *__restrict__ bias, float *__restrict__ logits, int T,
+                                                    int d, int E) {
+    const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (long)T * E) return;
+    const int t = (int)(i / E), e = (int)(i % E);
+    const uint16_t *xr = x + (size_t)t * d;
+    const float *w = wr + (size_t)e * d;
+    float acc = 0.0f;
+    for (int c = 0; c < d; c++) acc = fmaf(bf16f(xr[c]), w[c], acc);
+    logits[i] = acc + (bias ? bias[e] : 0.0f);
+}
+
+// ---------------------------------------------------------------------------
+// Top-k + softmax weights (gating network)
+// ---------------------------------------------------------------------------
+
+// (value, index) order: larger value first, then smaller index. Index INT_MAX
+// marks "no candidate".
+__device__ __forceinline__ bool better(float v, int e, float bv, int be) {
+    return e != INT_MAX && (be == INT_MAX || v > bv || (v == bv && e < be));
+}
+
+template <int EPL>
+__global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, int T, int E, int k, int renorm,
+                                              int32_t *__restrict__ idx, float *__restrict__ w) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int t = blockIdx.x * 4 + wave;
+    if (t >= T) return;   // uniform per wave
+    const float *lt = logits + (size_t)t * E;
+    float v[EPL];
+    uint64_t taken = 0;
+#pragma unroll
+    for (int i = 0; i < EPL; i++) {
+        const int e = lane + 64 * i;
+        v[i] = e < E ? lt[e] : 0.0f;
+        if (e >= E) taken |= 1ull << i;
+    }
+    float my_v = 0.0f, vmax = 0.0f;
+    int my_e = 0;
+    for (int j = 0; j < k; j++) {
+        float bv = 0.0f;
+        int be = INT_MAX;
+#pragma unroll
+        for (int i = 0; i < EPL; i++)
+            if (!((taken >> i) & 1ull) && better(v[i], lane + 64 * i, bv, be)) {
+                bv = v[i];
+                be = lane + 64 * i;
+            }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            const float ov = __shfl_xor(bv, off);
+            const int oe = __shfl_xor(be, off);
+            if (better(ov, oe, bv, be)) {
+                bv = ov;
+                be = oe;
+            }
+        }
+        if ((be & 63) == lane) taken |= 1ull << (be >> 6);
+        if (lane == j) {
+            my_v = bv;
+            my_e = be;
+        }
+        if (j == 0) vmax = bv;
+    }
+    const float ex = lane < k ? expf(my_v - vmax) : 0.0f;
+    float part;
+    if (renorm) {
+        part = ex;
+    } else {
+        part = 0.0f;
+#pragma unroll
+        for (int i = 0; i < EPL; i++)
+            if (lane + 64 * i < E) part += expf(v[i] - vmax);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
+    const float denom = __shfl(part, 0);
+    if (lane < k) {
+        idx[(size_t)t * k + lane] = my_e;
+        w[(size_t)t * k + lane] = ex / denom;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Dispatch: expert-centric task list
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void k_dispatch_count(const int32_t *__restrict__ idx, int P, int E,
+                                                        int32_t *__restrict__ chunk_counts) {
+    extern __shared__ int cnt[];
+    for (int e = threadIdx.x; e < E; e += 256) cnt[e] = 0;
+    __syncthreads();
+    const int p0 = blockIdx.x * kDispatchChunk;
+    for (int i = threadIdx.x; i < kDispatchChunk; i += 256) {
+        const int p = p0 + i;
+        if (p < P) atomicAdd(&cnt[idx[p]], 1);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += 256) chunk_counts[(size_t)blockIdx.x * E + e] = cnt[e];
+}
+
+// Exclusive scan over a 1024-thread workgroup (16 waves).
+__device__ int block_exclusive_scan_1024(int v, int *wsum) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    if (wave == 0) {
+        int s = lane < 16 ? wsum[lane] : 0;
+        int si = s;
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) {
+            const int o = __shfl_up(si, off);
+            if (lane >= off) si += o;
+        }
+        if (lane < 16) wsum[16 + lane] = si - s;   // exclusive wave bases
+    }
+    __syncthreads();
+    const int r = wsum[16 + wave] + incl - v;
+    __syncthreads();
+    return r;
+}
+
+// One workgroup of 1024 threads. Thread i owns experts [i*per, (i+1)*per).
+__global__ __launch_bounds__(1024) void k_dispatch_scan(const int32_t *__restrict__ cc, int nchunks, int E, int P,
+                                                        int T, int n_shared, int bm, int32_t *__restrict__ chunk_base,
+                                                        int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
+                                                        Tile *__restrict__ tiles, int32_t *__restrict__ num_tiles) {
+    __shared__ int wsum[32];
+    const int per = (E + 1023) / 1024;
+    const int e_begin = threadIdx.x * per;
+    int tot_local = 0, tiles_local = 0;
+    for (int i = 0; i < per; i++) {
+        const int e = e_begin + i;
+        if (e >= E) break;
+        int s = 0;
+        for (int b = 0; b < nchunks; b++) s += cc[(size_t)b * E + e];
+        counts[e] = s;
+        tot_local += s;
+        tiles_local += (s + bm - 1) / bm;
+    }
+    const int row_base = block_exclusive_scan_1024(tot_local, wsum);
+    const int tile_base = block_exclusive_scan_1024(tiles_local, wsum);
+    int row = row_base, tile = tile_base;
+    for (int i = 0; i < per; i++) {
+        const int e = e_begin + i;
+        if (e >= E) break;
+        const int c = counts[e];
+        offsets[e] = row;
+        int run = row;
+        for (int b = 0; b < nchunks; b++) {
+            chunk_base[(size_t)b * E + e] = run;
+            run += cc[(size_t)b * E + e];
+        }
+        for (int m = 0; m < c; m += bm) tiles[tile++] = Tile{e, row + m, row + c, 0};
+        row += c;
+    }
+    // the last thread holding experts knows the routed tile total
+    if (threadIdx.x == 1023) {
+        offsets[E] = P;
+        const int routed_tiles = tile_base + tiles_local;
+        int tcount = routed_tiles;
+        for (int s = 0; s < n_shared; s++)
+            for (int m = 0; m < T; m += bm)
+                tiles[tcount++] = Tile{E + s, P + s * T + m, P + (s + 1) * T, 0};
+        *num_tiles = tcount;
+    }
+}
+
+// Stable scatter: ranks inside a chunk follow pair order. Each round takes 256
+// consecutive pairs; ranks inside a wave come from per-expert 64-bit lane masks.
+__global__ __launch_bounds__(256) void k_dispatch_scatter(const int32_t *__restrict__ idx, int P, int E,
+                                                          const int32_t *__restrict__ chunk_base,
+                                                          int32_t *__restrict__ perm, int32_t *__restrict__ inv) {
+    extern __shared__ unsigned long long smem64[];
+    unsigned long long *masks = smem64;                       // [4][E]
+    int *running = reinterpret_cast<int *>(smem64 + 4 * E);  // [E]
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int e = threadIdx.x; e < E; e += 256) {
+        running[e] = chunk_base[(size_t)blockIdx.x * E + e];
+        masks[e] = masks[E + e] = masks[2 * E + e] = masks[3 * E + e] = 0ull;
+    }
+    __syncthreads();
+    for (int round = 0; round < kDispatchChunk / 256; round++) {
+        const int p = blockIdx.x * kDispatchChunk + round * 256 + threadIdx.x;
+        const bool valid = p < P;
+        const int e = valid ? idx[p] : 0;
+        if (valid) atomicOr(&masks[wave * E + e], 1ull << lane);
+        __syncthreads();
+        if (valid) {
+            int rank = __popcll(masks[wave * E + e] & ((1ull << lane) - 1ull));
+            for (int w2 = 0; w2 < wave; w2++) rank += __popcll(masks[w2 * E + e]);
+            const int row = running[e] + rank;
+            perm[row] = p;
+            inv[p] = row;
+        }
+        __syncthreads();
+        for (int e2 = threadIdx.x; e2 < E; e2 += 256) {
+            running[e2] += __popcll(masks[e2]) + __popcll(masks[E + e2]) + __popcll(masks[2 * E + e2]) +
+                           __popcll(masks[3 * E + e2]);
+            masks[e2] = masks[E + e2] = masks[2 * E + e2] = masks[3 * E + e2] = 0ull;
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Row sums over 128-wide groups (the offset correction of the integer-code GEMM)
+// ---------------------------------------------------------------------------
+
+// xsum[t][g] = sum_{c in group g} x[t][c] in fp32. One wave per token row;
+// lane l reads 16-byte chunks l, l+64, ...; the 16 chunks of a group sit in 16
+// consecutive lanes and are reduced with xor shuffles.
+__global__ __launch_bounds__(256) void k_xsum(const uint16_t *__restrict__ x, int T, int d, float *__restrict__ xsum) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int t = blockIdx.x * 4 + wave;
+    if (t >= T) return;
+    const int nchunk = d / 8, G = d / 128;
+    for (int c0 = 0; c0 < nchunk; c0 += 64) {
+        const int c = c0 + lane;
+        const uint4 v = *reinterpret_cast<const uint4 *>(x + (size_t)t * d + c * 8);
+        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+        float s = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; i++) s += bf16f(u[i] & 0xFFFFu) + bf16f(u[i] >> 16);
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) s += __shfl_xor(s, off);
+        if ((lane & 15) == 0) xsum[(size_t)t * G + c / 16] = s;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// B operands
+// ---------------------------------------------------------------------------
+
+// 4-bit codes -> bf16 integers 128 + u (exact): OR-ing a nibble into the low
+// mantissa bits of bf16 128.0 (0x4300) gives 128 + u. One dword holds eight
+// codes; (dword >> 4i) & 0x000F000F yields codes 2i, 2i+1 in its two halves.
+__device__ __forceinline__ bf16x8 nibbles_to_bf16_128(uint32_t d) {
+    uint4 r;
+    r.x = (d & 0x000F000Fu) | 0x43004300u;
+    r.y = ((d >> 4) & 0x000F000Fu) | 0x43004300u;
+    r.z = ((d >> 8) & 0x000F000Fu) | 0x43004300u;
+    r.w = ((d >> 12) & 0x000F000Fu) | 0x43004300u;
+    return __builtin_bit_cast(bf16x8, r);
+}
+
+template <int DF>
+__device__ __forceinline__ bf16x8 codes8_to_bf16(uint32_t d0, uint32_t d1);
+
+// int8: exact in bf16; the per-row scale is applied in the epilogue.
+template <>
+__device__ __forceinline__ bf16x8 codes8_to_bf16<DF_INT8>(uint32_t d0, uint32_t d1) {
+    bf16x8 r;
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        const uint32_t dw = j < 4 ? d0 : d1;
+        const int v = (int)(int8_t)((dw >> (8 * (j & 3))) & 0xFFu);
+        r[j] = (__bf16)(float)v;
+    }
+    return r;
+}
+
+// e4m3: exact in bf16 (sign, exponent re-biased 7 -> 127, 3 mantissa bits;
+// subnormals m * 2^-9 go through fp32); the per-row scale is in the epilogue.
+__device__ __forceinline__ uint16_t e4m3_to_bf16_bits(uint32_t b) {
+    const uint32_t s = (b & 0x80u) << 8, e = (b >> 3) & 15u, m = b & 7u;
+    if (e != 0) return (uint16_t)(s | ((e + 120u) << 7) | (m << 4));
+    const float f = (float)m * 0x1p-9f;   // at most 3 significant bits: exact in bf16
+    return (uint16_t)(s | (__float_as_uint(f) >> 16));
+}
+
+template <>
+__device__ __forceinline__ bf16x8 codes8_to_bf16<DF_FP8>(uint32_t d0, uint32_t d1) {
+    bf16x8 r;
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        const uint32_t dw = j < 4 ? d0 : d1;
+        r[j] = __builtin_bit_cast(__bf16, e4m3_to_bf16_bits((dw >> (8 * (j & 3))) & 0xFFu));
+    }
+    return r;
+}
+
+// ---------------------------------------------------------------------------
+// Grouped GEMMs over the task list
+// ---------------------------------------------------------------------------
+//
+// MODE 0 (gate/up): A = gathered x rows, B = W13 of the tile's expert; output
+//   H[row][F] = silu(gate) * up in bf16 (+ per-group row sums of H for MODE 1).
+// MODE 1 (down): A = H rows of the tile, B = W2; output O[row][d] (fp32) =
+//   (mixing weight of the row's task) * (H . W2^T).
+// Workgroup = 4 waves; tile = BM rows x 256 columns of B's N dimension (for
+// MODE 0 these are 128 gate/up column pairs = one 128-wide group of H). Wave w
+// owns 64 columns = four 16-row packed blocks, so each packed weight is
+// converted by exactly one wave of the workgroup.
+
+struct TileCtx {
+    Tile tl;
+    ExpertW ew;
+    int N, K, n0, rows;
+};
+
+template <int MODE>
+__device__ __forceinline__ bool tile_setup(const GemmArgs &a, TileCtx &c) {
+    if ((int)blockIdx.y >= *a.num_tiles) return false;
+    c.tl = a.tiles[blockIdx.y];
+    c.ew = a.experts[c.tl.e];
+    c.N = MODE == 0 ? 2 * c.ew.F : a.d;
+    c.K = MODE == 0 ? a.d : c.ew.F;
+    c.n0 = blockIdx.x * 256;
+    c.rows = c.tl.row_end - c.tl.row0;
+    return c.n0 < c.N;
+}
+
+// Group formats: the MFMA consumes exact integer codes (128 + u as bf16).
+// Per 128-wide group g and output (m, n):
+//   sum_k a_mk (u_nk - z_ng) = sum_k a_mk (128 + u_nk) - (128 + z_ng) * rowsum_mg
+// The chain of four MFMAs of a group starts from C = -ZC * rowsum (ZC = 136 for
+// the symmetric formats, whose stored u = q + 8; 128 for asymmetric), and the
+// group's result is scaled by s_ng in fp32 into the running accumulator
+// (asymmetric: minus s_ng z_ng rowsum_mg as well).
+template <int DF, int MODE, int MI>
+__global__ __launch_bounds__(256) void k_gemm_g(GemmArgs a) {
+    constexpr int BM = 16 * MI;
+    constexpr int PITCH = 136;   // bf16 per LDS row: 128 + 8 pad (conflict-free MFMA reads)
+    constexpr float ZC = DF == DF_I4SYM ? 136.0f : 128.0f;
+    __shared__ __attribute__((aligned(16))) uint16_t As[BM * PITCH];
+    __shared__ __attribute__((aligned(16))) float Rs[BM];
+
+    TileCtx c;
+    if (!tile_setup<MODE>(a, c)) return;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int KB = c.K / 128;
+    const int lrow = (lane >> 4) * 4;
+
+    const int c16 = threadIdx.x & 15;
+    const uint16_t *asrc[MI];
+    const float *rsrc[MI];
+    bool aok[MI];
+#pragma unroll
+    for (int i = 0; i < MI; i++) {
+        const int r = (threadIdx.x >> 4) + 16 * i;
+        aok[i] = r < c.rows;
+        const int gr = c.tl.row0 + (aok[i] ? r : 0);
+        if (MODE == 0) {
+            const int tok = gr < a.P ? a.perm[gr] / a.k : (gr - a.P) % a.T;
+            asrc[i] = a.x + (size_t)tok * a.d + c16 * 8;
+            rsrc[i] = a.xsum + (size_t)tok * (a.d / 128);
+        } else {
+            asrc[i] = a.H + (size_t)gr * a.ldh + c16 * 8;
+            rsrc[i] = a.hsum + (size_t)gr * (a.ldh / 128);
+        }
+    }
+    const uint8_t *codes = MODE == 0 ? c.ew.c13 : c.ew.c2;
+    const uint16_t *gsc = MODE == 0 ? c.ew.s13 : c.ew.s2;
+    const uint16_t *gzp = MODE == 0 ? c.ew.z13 : c.ew.z2;
+    const int ib0 = c.n0 / 16 + 4 * wave;
+
+    f32x4 acc[MI][4];
+#pragma unroll
+    for (int mi = 0; mi < MI; mi++)
+#pragma unroll
+        for (int nb = 0; nb < 4; nb++) acc[mi][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int kb = 0; kb < KB; kb++) {
+        uint4 braw[4];
+        float bsc[4], bsz[4];
+#pragma unroll
+        for (int nb = 0; nb < 4; nb++) {
+            const size_t blk = (size_t)(ib0 + nb) * KB + kb;
+            braw[nb] = *reinterpret_cast<const uint4 *>(codes + blk * 1024 + lane * 16);
+            bsc[nb] = half_bits_to_f32(gsc[blk * 16 + (lane & 15)]);
+            bsz[nb] = DF == DF_I4ASYM ? -bsc[nb] * half_bits_to_f32(gzp[blk * 16 + (lane & 15)]) : 0.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < MI; i++) {
+            const uint4 v = aok[i] ? *reinterpret_cast<const uint4 *>(asrc[i] + kb * 128) : make_uint4(0, 0, 0, 0);
+            const int r = (threadIdx.x >> 4) + 16 * i;
+            *reinterpret_cast<uint4 *>(&As[r * PITCH + c16 * 8]) = v;
+            if (c16 == 0) Rs[r] = aok[i] ? rsrc[i][kb] : 0.0f;
+        }
+        __syncthreads();
+        bf16x8 bq[4][4];
+#pragma unroll
+        for (int nb = 0; nb < 4; nb++) {
+            bq[nb][0] = nibbles_to_bf16_128(braw[nb].x);
+            bq[nb][1] = nibbles_to_bf16_128(braw[nb].y);
+            bq[nb][2] = nibbles_to_bf16_128(braw[nb].z);
+            bq[nb][3] = nibbles_to_bf16_128(braw[nb].w);
+        }
+#pragma unroll
+        for (int mi = 0; mi < MI; mi++) {
+            const f32x4 rs = *reinterpret_cast<const f32x4 *>(&Rs[mi * 16 + lrow]);
+            const f32x4 cinit = rs * -ZC;
+            bf16x8 af[4];
+#pragma unroll
+            for (int s = 0; s < 4; s++)
+                af[s] = *reinterpret_cast<const bf16x8 *>(&As[(mi * 16 + (lane & 15)) * PITCH + s * 32 + (lane >> 4) * 8]);
+            f32x4 p[4];
+#pragma unroll
+            for (int nb = 0; nb < 4; nb++) p[nb] = cinit;
+#pragma unroll
+            for (int s = 0; s < 4; s++)
+#pragma unroll
+                for (int nb = 0; nb < 4; nb++)
+                    p[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s], bq[nb][s], p[nb], 0, 0, 0);
+#pragma unroll
+            for (int nb = 0; nb < 4; nb++) {
+                acc[mi][nb] += bsc[nb] * p[nb];
+                if (DF == DF_I4ASYM) acc[mi][nb] += bsz[nb] * rs;
+            }
+        }
+        __syncthreads();
+    }
+
+    if (MODE == 0) {
+        float hs[MI][4];
+#pragma unroll
+        for (int mi = 0; mi < MI; mi++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) hs[mi][r] = 0.0f;
+#pragma unroll
+        for (int pr = 0; pr < 2; pr++) {
+            const int col = ((ib0 + 2 * pr) >> 1) * 16 + (lane & 15);
+#pragma unroll
+            for (int mi = 0; mi < MI; mi++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    const int row = mi * 16 + lrow + r;
+                    const float g = acc[mi][2 * pr][r];
+                    const float u = acc[mi][2 * pr + 1][r];
+                    const uint16_t hb = to_bf16(g / (1.0f + __expf(-g)) * u);
+                    hs[mi][r] += bf16f(hb);
+                    if (row < c.rows) a.H[(size_t)(c.tl.row0 + row) * a.ldh + col] = hb;
+                }
+        }
+        // row sums of this workgroup's 128 H columns (one group of the down GEMM)
+        float *red = reinterpret_cast<float *>(As);   // [4][BM]
+#pragma unroll
+        for (int mi = 0; mi < MI; mi++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                float v = hs[mi][r];
+#pragma unroll
+                for (int off = 1; off < 16; off <<= 1) v += __shfl_xor(v, off);
+                if ((lane & 15) == 0) red[wave * BM + mi * 16 + lrow + r] = v;
+            }
+        __syncthreads();
+        if ((int)threadIdx.x < BM && (int)threadIdx.x < c.rows) {
+            const int row = threadIdx.x;
+            const float v = red[row] + red[BM + row] + red[2 * BM + row] + red[3 * BM + row];
+            a.hsum[(size_t)(c.tl.row0 + row) * (a.ldh / 128) + c.n0 / 256] = v;
+        }
+    } else {
+#pragma unroll
+        for (int mi = 0; mi < MI; mi++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int row = mi * 16 + lrow + r;
+                if (row >= c.rows) continue;
+                const int gr = c.tl.row0 + row;
+                const float wt = gr < a.P ? a.wpair[a.perm[gr]] : 1.0f;
+#pragma unroll
+                for (int nb = 0; nb < 4; nb++) {
+                    const int n = c.n0 + 64 * wave + 16 * nb + (lane & 15);
+                    a.O[(size_t)gr * a.d + n] = acc[mi][nb][r] * wt;
+                }
+            }
+    }
+}
+
+// Per-channel formats (int8, e4m3): codes convert exactly to bf16 and the
+// per-row scale multiplies the finished accumulator.
+template <int DF, int MODE, int MI>
+__global__ __launch_bounds__(256) void k_gemm_c(GemmArgs a) {
+    constexpr int BM = 16 * MI;
+    constexpr int PITCH = 136;
+    __shared__ __attribute__((aligned(16))) uint16_t As[BM * PITCH];
+
+    TileCtx c;
+    if (!tile_setup<MODE>(a, c)) return;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int KB = c.K / 128;
+    const int lrow = (lane >> 4) * 4;
+    const int c16 = threadIdx.x & 15;
+    const uint16_t *asrc[MI];
+    bool aok[MI];
+#pragma unroll
+    for (int i = 0; i < MI; i++) {
+        const int r = (threadIdx.x >> 4) + 16 * i;
+        aok[i] = r < c.rows;
+        const int gr = c.tl.row0 + (aok[i] ? r : 0);
+        if (MODE == 0) {
+            const int tok = gr < a.P ? a.perm[gr] / a.k : (gr - a.P) % a.T;
+            asrc[i] = a.x + (size_t)tok * a.d + c16 * 8;
+        } else {
+            asrc[i] = a.H + (size_t)gr * a.ldh + c16 * 8;
+        }
+    }
+    const uint8_t *codes = MODE == 0 ? c.ew.c13 : c.ew.c2;
+    const int ib0 = c.n0 / 16 + 4 * wave;
+
+    f32x4 acc[MI][4];
+#pragma unroll
+    for (int mi = 0; mi < MI; mi++)
+#pragma unroll
+        for (int nb = 0; nb < 4; nb++) acc[mi][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int kb = 0; kb < KB; kb++) {
+        uint4 braw[4][2];
+#pragma unroll
+        for (int nb = 0; nb < 4; nb++) {
+            const uint8_t *bp = codes + ((size_t)(ib0 + nb) * KB + kb) * 2048 + lane * 32;
+            braw[nb][0] = *reinterpret_cast<const uint4 *>(bp);
+            braw[nb][1] = *reinterpret_cast<const uint4 *>(bp + 16);
+        }
+#pragma unroll
+        for (int i = 0; i < MI; i++) {
+            const uint4 v = aok[i] ? *reinterpret_cast<const uint4 *>(asrc[i] + kb * 128) : make_uint4(0, 0, 0, 0);
+            *reinterpret_cast<uint4 *>(&As[((threadIdx.x >> 4) + 16 * i) * PITCH + c16 * 8]) = v;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int s = 0; s < 4; s++) {
+            bf16x8 bfr[4];
+#pragma unroll
+            for (int nb = 0; nb < 4; nb++) {
+                const uint4 q = braw[nb][s >> 1];
+                bfr[nb] = codes8_to_bf16<DF>((s & 1) ? q.z : q.x, (s & 1) ? q.w : q.y);
+            }
+#pragma unroll
+            for (int mi = 0; mi < MI; mi++) {
+                const bf16x8 af =
+                    *reinterpret_cast<const bf16x8 *>(&As[(mi * 16 + (lane & 15)) * PITCH + s * 32 + (lane >> 4) * 8]);
+#pragma unroll
+                for (int nb = 0; nb < 4; nb++)
+                    acc[mi][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr[nb], acc[mi][nb], 0, 0, 0);
+            }
+        }
+        __syncthreads();
+    }
+
+    if (MODE == 0) {
+        const float *ps = c.ew.p13;
+#pragma unroll
+        for (int pr = 0; pr < 2; pr++) {
+            const int ibg = ib0 + 2 * pr;
+            const int col = (ibg >> 1) * 16 + (lane & 15);
+            const float sg = ps[ibg * 16 + (lane & 15)];
+            const float su = ps[(ibg + 1) * 16 + (lane & 15)];
+#pragma unroll
+            for (int mi = 0; mi < MI; mi++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    const int row = mi * 16 + lrow + r;
+                    if (row < c.rows) {
+                        const float g = acc[mi][2 * pr][r] * sg;
+                        const float u = acc[mi][2 * pr + 1][r] * su;
+                        a.H[(size_t)(c.tl.row0 + row) * a.ldh + col] = to_bf16(g / (1.0f + __expf(-g)) * u);
+                    }
+                }
+        }
+    } else {
+        const float *ps = c.ew.p2;
+        float sn[4];
+#pragma unroll
+        for (int nb = 0; nb < 4; nb++) sn[nb] = ps[c.n0 + 64 * wave + 16 * nb + (lane & 15)];
+#pragma unroll
+        for (int mi = 0; mi < MI; mi++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int row = mi * 16 + lrow + r;
+                if (row >= c.rows) continue;
+                const int gr = c.tl.row0 + row;
+                const float wt = gr < a.P ? a.wpair[a.perm[gr]] : 1.0f;
+#pragma unroll
+                for (int nb = 0; nb < 4; nb++) {
+                    const int n = c.n0 + 64 * wave + 16 * nb + (lane & 15);
+                    a.O[(size_t)gr * a.d + n] = acc[mi][nb][r] * sn[nb] * wt;
+                }
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Combine
+// ---------------------------------------------------------------------------
+
+// y[t] = sum_j O[inv[t*k+j]] + sum_s O[P + s*T + t], summed in fp32 in slot
+// order, rounded once to bf16.
+__global__ __launch_bounds__(256) void k_combine(const float *__restrict__ O, const int32_t *__restrict__ inv, int T,
+                                                 int d, int k, int P, int n_shared, uint16_t *__restrict__ y) {
+    const int t = blockIdx.x;
+    for (int c4 = threadIdx.x; c4 < d / 4; c4 += 256) {
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        const int nrows = k + n_shared;
+        for (int j = 0; j < nrows; j++) {
+            const size_t row = j < k ? (size_t)inv[(size_t)t * k + j] : (size_t)P + (size_t)(j - k) * T + t;
+            const float4 v = *reinterpret_cast<const float4 *>(O + row * d + c4 * 4);
+            acc.x += v.x;
+            acc.y += v.y;
+            acc.z += v.z;
+            acc.w += v.w;
+        }
+        uint2 out;
+        out.x = (uint32_t)to_bf16(acc.x) | ((uint32_t)to_bf16(acc.y) << 16);
+        out.y = (uint32_t)to_bf16(acc.z) | ((uint32_t)to_bf16(acc.w) << 16);
+        *reinterpret_cast<uint2 *>(y + (size_t)t * d + c4 * 4) = out;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+
+hipError_t launch_router_bf16(const uint16_t *x, const uint16_t *wr, const float *bias, float *logits, int T, int d,
+                              int E, hipStream_t s) {
+    dim3 grid((T + 63) / 64, (E + 63) / 64);
+    hipLaunchKernelGGL(k_router_bf16, grid, dim3(256), 0, s, x, wr, bias, logits, T, d, E);
+    return hipGetLastError();
+}
+
+hipError_t launch_router_f32(const uint16_t *x, const float *wr, const float *bias, float *logits, int T, int d, int E,
+                             hipStream_t s) {
+    const long n = (long)T * E;
+    hipLaunchKernelGGL(k_router_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, x, wr, bias, logits, T, d, E);
+    return hipGetLastError();
+}
+
+hipError_t launch_topk(const float *logits, int T, int E, int k, int renorm, int32_t *idx, float *w, hipStream_t s) {
+    dim3 grid((T + 3) / 4);
+    if (E <= 64)
+        hipLaunchKernelGGL(k_topk<1>, grid, dim3(256), 0, s, logits, T, E, k, renorm, idx, w);
+    else if (E <= 128)
+        hipLaunchKernelGGL(k_topk<2>, grid, dim3(256), 0, s, logits, T, E, k, renorm, idx, w);
+    else if (E <= 256)
+        hipLaunchKernelGGL(k_topk<4>, grid, dim3(256), 0, s, logits, T, E, k, renorm, idx, w);
+    else if (E <= 512)
+        hipLaunchKernelGGL(k_topk<8>, grid, dim3(256), 0, s, logits, T, E, k, renorm, idx, w);
+    else
+        hipLaunchKernelGGL(k_topk<16>, grid, dim3(256), 0, s, logits, T, E, k, renorm, idx, w);
+    return hipGetLastError();
+}
+
+hipError_t launch_dispatch_count(const int32_t *idx, int P, int E, int32_t *chunk_counts, hipStream_t s) {
+    const int nchunks = (P + kDispatchChunk - 1) / kDispatchChunk;
+    hipLaunchKernelGGL(k_dispatch_count, dim3(nchunks), dim3(256), E * sizeof(int), s, idx, P, E, chunk_counts);
+    return hipGetLastError();
+}
+
+hipError_t launch_dispatch_scan(const int32_t *chunk_counts, int nchunks, int E, int P, int T, int n_shared, int bm,
+                                int32_t *chunk_base, int32_t *counts, int32_t *offsets, Tile *tiles,
+                                int32_t *num_tiles, hipStream_t s) {
+    hipLaunchKernelGGL(k_dispatch_scan, dim3(1), dim3(1024), 0, s, chunk_counts, nchunks, E, P, T, n_shared, bm,
+                       chunk_base, counts, offsets, tiles, num_tiles);
+    return hipGetLastError();
+}
+
+hipError_t launch_dispatch_scatter(const int32_t *idx, int P, int E, const int32_t *chunk_base, int32_t *perm,
+                                   int32_t *inv, hipStream_t s) {
+    const int nchunks = (P + kDispatchChunk - 1) / kDispatchChunk;
+    const size_t lds = (size_t)E * (4 * sizeof(unsigned long long) + sizeof(int));
+    hipLaunchKernelGGL(k_dispatch_scatter, dim3(nchunks), dim3(256), lds, s, idx, P, E, chunk_base, perm, inv);
+    return hipGetLastError();
+}
+
+template <int MODE, int MI>
+static hipError_t launch_gemm_df(int df, dim3 grid, const GemmArgs &a, hipStream_t s) {
+    switch (df) {
+    case DF_INT8: hipLaunchKernelGGL((k_gemm_c<DF_INT8, MODE, MI>), grid, dim3(256), 0, s, a); break;
+    case DF_I4ASYM: hipLaunchKernelGGL((k_gemm_g<DF_I4ASYM, MODE, MI>), grid, dim3(256), 0, s, a); break;
+    case DF_I4SYM: hipLaunchKernelGGL((k_gemm_g<DF_I4SYM, MODE, MI>), grid, dim3(256), 0, s, a); break;
+    case DF_FP8: hipLaunchKernelGGL((k_gemm_c<DF_FP8, MODE, MI>), grid, dim3(256), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <int MODE>
+static hipError_t launch_gemm_bm(int df, int bm, dim3 grid, const GemmArgs &a, hipStream_t s) {
+    switch (bm) {
+    case 16: return launch_gemm_df<MODE, 1>(df, grid, a, s);
+    case 64: return launch_gemm_df<MODE, 4>(df, grid, a, s);
+    case 128: return launch_gemm_df<MODE, 8>(df, grid, a, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_gemm13(int df, int bm, const GemmArgs &a, int max_tiles, int maxN13, hipStream_t s) {
+    dim3 grid((maxN13 + 255) / 256, max_tiles);
+    return launch_gemm_bm<0>(df, bm, grid, a, s);
+}
+
+hipError_t launch_gemm2(int df, int bm, const GemmArgs &a, int max_tiles, hipStream_t s) {
+    dim3 grid((a.d + 255) / 256, max_tiles);
+    return launch_gemm_bm<1>(df, bm, grid, a, s);
+}
+
+hipError_t launch_xsum(const uint16_t *x, int T, int d, float *xsum, hipStream_t s) {
+    hipLaunchKernelGGL(k_xsum, dim3((T + 3) / 4), dim3(256), 0, s, x, T, d, xsum);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine(const float *O, const int32_t *inv, int T, int d, int k, int P, int n_shared,
+                          uint16_t *y, hipStream_t s) {
+    hipLaunchKernelGGL(k_combine, dim3(T), dim3(256), 0, s, O, inv, T, d, k, P, n_shared, y);
+    return hipGetLastError();
+}
+
+}  // namespace qmoe

@@ -18,3 +18,13 @@ def oracle_mod():
     from oracle import oracle as O
     O.lib()
     return O
+
+
+@pytest.fixture(scope="session")
+def qmoe_lib():
+    """The HIP library (built in-tree first if it is missing)."""
+    import quantized_mixture_experts_qmoe_amd as Q
+    if not os.path.exists(Q.LIB_PATH):
+        from quantized_mixture_experts_qmoe_amd import build
+        build.build()
+    return Q.load()

@@ -1,0 +1,88 @@
+"""Host-side checks of the C-ABI library that need no GPU: it loads, exports
+every symbol include/qmoe.h declares, and rejects bad arguments with the
+documented codes before touching a device."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import quantized_mixture_experts_qmoe_amd as Q
+from quantized_mixture_experts_qmoe_amd.inputs import CONFIGS
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "qmoe.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qmoe_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_abi():
+    names = header_functions()
+    for n in ("qmoe_pack_experts", "qmoe_route_topk", "qmoe_forward", "qmoe_destroy"):
+        assert n in names
+    assert set(names) == set(Q.ABI_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(qmoe_lib):
+    for n in header_functions():
+        assert hasattr(qmoe_lib, n), n
+
+
+def _pack(cfg, weights=True):
+    n = cfg.n_experts + cfg.n_shared
+    f = np.zeros((max(cfg.d_ff, 1), max(cfg.d_model, 1)), np.float32)
+    arrs = [f] * max(n, 1)
+    p, keep = Q._ptr_array(arrs)
+    wr = np.zeros((max(cfg.n_experts, 1), max(cfg.d_model, 1)), np.float32)
+    ctx = C.c_void_p()
+    rc = Q.qmoe_pack_experts(cfg, p if weights else None, p, p, wr.ctypes.data, None, C.byref(ctx))
+    return rc, ctx
+
+
+def base_cfg(**kw):
+    c = Q.make_config(CONFIGS["tiny"], max_tokens=64)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+@pytest.mark.parametrize("kw,rc", [
+    (dict(top_k=0), Q.QMOE_EINVAL),
+    (dict(top_k=9), Q.QMOE_EINVAL),              # k > E
+    (dict(d_model=0), Q.QMOE_EINVAL),
+    (dict(max_tokens=0), Q.QMOE_EINVAL),
+    (dict(wformat=7), Q.QMOE_EINVAL),
+    (dict(n_shared=-1), Q.QMOE_EINVAL),
+    (dict(n_shared=1, d_ff_shared=0), Q.QMOE_EINVAL),
+    (dict(renormalize=2), Q.QMOE_EINVAL),
+    (dict(d_model=320), Q.QMOE_EUNSUPPORTED),     # not a multiple of 256
+    (dict(d_ff=200), Q.QMOE_EUNSUPPORTED),        # not a multiple of 128
+    (dict(wformat=2, group_size=64), Q.QMOE_EUNSUPPORTED),
+    (dict(n_experts=2048, top_k=2), Q.QMOE_EUNSUPPORTED),
+    (dict(n_experts=128, top_k=65), Q.QMOE_EUNSUPPORTED),
+])
+def test_pack_rejects_bad_configs(qmoe_lib, kw, rc):
+    got, ctx = _pack(base_cfg(**kw))
+    assert got == rc
+    assert not ctx.value
+    assert Q.qmoe_last_error() != ""
+
+
+def test_pack_rejects_null_weights(qmoe_lib):
+    got, ctx = _pack(base_cfg(), weights=False)
+    assert got == Q.QMOE_EINVAL and not ctx.value
+
+
+def test_null_context_calls(qmoe_lib):
+    Q.qmoe_destroy(None)                                   # no-op
+    assert Q.qmoe_forward(None, None, 4, None, None, None) == Q.QMOE_EINVAL
+    assert "ctx" in Q.qmoe_last_error()
+    assert Q.qmoe_route_topk(None, None, 4, None, None) == Q.QMOE_EINVAL
+    assert Q.qmoe_export_packed(None, 0, 0, None, None, None) == Q.QMOE_EINVAL
+    assert Q.qmoe_profile_enable(None, 1) == Q.QMOE_EINVAL
+    assert [Q.qmoe_kernel_name(i) for i in range(Q.QMOE_NUM_KERNELS)][0] == "router"
+    assert Q.qmoe_kernel_name(99) == ""
