@@ -1,0 +1,187 @@
+"""Benchmark of the quantized top-k MoE layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+
+A step is one qmoe_forward (router, top-k, dispatch, grouped gate/up GEMM,
+grouped down GEMM, combine) over one batch of seeded synthetic tokens whose
+inputs are already resident in HBM. The default workload is the Mixtral-shaped
+prefill layer (T=4096, d=4096, 8 experts top-2, d_ff=14336, INT4 asymmetric
+group-128 weights). Prints ONE JSON line on stdout; progress goes to stderr.
+
+The roofline object is for the dominant kernel (grouped gate/up GEMM for the
+prefill workloads, the same kernel's weight stream for decode): algorithmic
+FLOPs (or bytes) per launch divided by its average duration, measured with HIP
+events recorded on the launch stream around every launch inside the timed
+region. The CPU baseline times the fp64 oracle on a bounded token sample of the
+same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+METRIC = "MoE-layer tokens/s (1 GPU) + % of MFMA peak (prefill) / % HBM BW (decode)"
+
+
+def log(msg: str) -> None:
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic_work(cfg):
+    """FLOPs of the whole layer and of one launch of each grouped GEMM, and the
+    bytes of packed weights (all experts) for reference."""
+    P = cfg.T * cfg.k
+    fl13 = 2.0 * P * cfg.d * 2 * cfg.F + 2.0 * cfg.T * cfg.S * cfg.d * 2 * cfg.Fs
+    fl2 = 2.0 * P * cfg.F * cfg.d + 2.0 * cfg.T * cfg.S * cfg.Fs * cfg.d
+    return dict(layer=cfg.expert_flops(), gemm_gate_up=fl13, gemm_down=fl2)
+
+
+def packed_bytes_per_expert(cfg, f):
+    n = 3 * cfg.d * f
+    if cfg.wformat in ("int4_asym_g128", "int4_sym_g128", "int3_sym_g128"):
+        groups = n // 128
+        return n // 2 + groups * 2 * (2 if cfg.wformat == "int4_asym_g128" else 1)
+    return n + 4 * (2 * f + cfg.d)
+
+
+def cpu_baseline(inp, n_tokens: int):
+    from oracle import oracle as O
+    cfg = inp.cfg
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
+    log(f"cpu baseline: quantizing the oracle's copy of the layer ({threads} threads)")
+    layer = O.OracleLayer(inp)
+    rng = np.random.default_rng(123)
+    toks = np.sort(rng.choice(cfg.T, size=min(n_tokens, cfg.T), replace=False)).astype(np.int32)
+    log(f"cpu baseline: oracle forward on {len(toks)} sampled tokens")
+    t0 = time.perf_counter()
+    layer.forward(inp.x, tokens=toks)
+    dt = time.perf_counter() - t0
+    layer.close()
+    return {"value": len(toks) / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(toks)} of {cfg.T} tokens of the same layer (fp64 forward incl. per-expert "
+                      f"dequantization; quantization setup untimed), {dt:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="mixtral_prefill")
+    ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (0 = per-config default)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--flush-mb", type=int, default=-1,
+                    help="write this many MiB between timed decode steps to evict the 256 MB MALL "
+                         "(default: 1024 for decode workloads, 0 otherwise)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              f"(the layer is not sharded; see the design notes for how it would shard).", file=sys.stderr)
+        return 2
+
+    import torch
+    import quantized_mixture_experts_qmoe_amd as Q
+    from quantized_mixture_experts_qmoe_amd.inputs import CONFIGS, make_inputs
+
+    cfg = CONFIGS[args.config]
+    decode = cfg.T <= 64
+    log(f"workload {cfg.name}: generating seeded inputs")
+    inp = make_inputs(cfg, seed=0)
+    log("packing experts (host quantizer -> device arena)")
+    layer = Q.QMoE(inp, max_tokens=cfg.T, device=0)
+    x = torch.from_numpy(inp.x.view(np.int16)).view(torch.bfloat16).cuda()
+    y = torch.empty_like(x)
+    stream = torch.cuda.current_stream()
+    flush_mb = args.flush_mb if args.flush_mb >= 0 else (1024 if decode else 0)
+    scratch = torch.empty(flush_mb * 1024 * 1024 // 4, dtype=torch.float32, device="cuda") if flush_mb else None
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        layer.forward(x, y=y, stream=stream)
+    torch.cuda.synchronize()
+
+    log(f"timing {args.steps} steps")
+    layer.profile_enable(True)
+    if scratch is None:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            layer.forward(x, y=y, stream=stream)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+    else:
+        # decode: evict the MALL before each step and time each step with events
+        elapsed = 0.0
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        for _ in range(args.steps):
+            scratch.fill_(1.0)
+            ev0.record(stream)
+            layer.forward(x, y=y, stream=stream)
+            ev1.record(stream)
+            ev1.synchronize()
+            elapsed += ev0.elapsed_time(ev1) / 1e3
+    prof = layer.profile_read()
+    layer.profile_enable(False)
+
+    ms_per_step = 1e3 * elapsed / args.steps
+    value = cfg.T * args.steps / elapsed
+    work = algorithmic_work(cfg)
+    kernels = {k: {"avg_us": 1e3 * v[0] / max(v[1], 1), "launches": v[1]} for k, v in prof.items() if v[1]}
+    k13 = kernels["gemm_gate_up"]["avg_us"]
+    if not decode:
+        achieved = work["gemm_gate_up"] / (k13 * 1e-6) / 1e12
+        roof = {"bound": "mfma", "kernel": "gemm_gate_up", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                "per_launch": f"{work['gemm_gate_up']:.4e} FLOP"}
+    else:
+        # bytes of the gate/up weights of the distinct experts this batch selects
+        route = Q.QMoE.route_buffers(cfg.T, cfg.E, cfg.k)
+        layer.forward(x, y=y, route=route)
+        torch.cuda.synchronize()
+        used = np.unique(route["topk_idx"].cpu().numpy())
+        per_exp13 = packed_bytes_per_expert(cfg, cfg.F) * 2 // 3
+        b13 = len(used) * per_exp13 + cfg.T * cfg.d * 2
+        achieved = b13 / (k13 * 1e-6) / 1e9
+        roof = {"bound": "hbm", "kernel": "gemm_gate_up", "achieved": achieved, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": None,
+                "per_launch": f"{b13} B ({len(used)} distinct experts)"}
+    layer_tflops = work["layer"] / (ms_per_step * 1e-3) / 1e12
+    log(f"{value:.4g} tokens/s, {ms_per_step:.3f} ms/step, layer {layer_tflops:.1f} TFLOP/s; kernels: "
+        + ", ".join(f"{k}={v['avg_us']:.1f}us" for k, v in kernels.items()))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        n = args.cpu_tokens or (48 if cfg.d * cfg.F >= 4096 * 8192 else 256)
+        cpu = cpu_baseline(inp, n)
+        log(f"cpu baseline {cpu['value']:.3g} tokens/s on {cpu['cores']} threads")
+
+    out = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.name, "T": cfg.T, "d_model": cfg.d, "experts": cfg.E, "top_k": cfg.k,
+                   "d_ff": cfg.F, "shared": cfg.S, "weights": cfg.wformat, "parallelism": "none (1 GPU)"},
+        "layer_tflops": layer_tflops,
+        "layer_mfma_frac": layer_tflops / PEAK_BF16_TFLOPS,
+        "kernels_us": {k: round(v["avg_us"], 2) for k, v in kernels.items()},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    layer.close()
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -229,8 +229,7 @@ int rows_per_tile(const qmoe_ctx *c, int T) {
     const long active = std::min<long>(c->E, P);
     const double avg = (double)P / (double)std::max<long>(1, active);
     if (avg <= 16.0) return 16;
-    if (avg <= 96.0) return 64;
-    return 128;
+    return 64;
 }
 
 int max_tiles_for(const qmoe_ctx *c, int T, int bm) {
@@ -443,6 +442,10 @@ int qmoe_forward(qmoe_ctx *c, const uint16_t *x, int32_t T, uint16_t *y, qmoe_ro
     const int P = T * c->k;
     const int bm = rows_per_tile(c, T);
     const int max_tiles = max_tiles_for(c, T, bm);
+    const bool grouped = is_group_wformat(c->cfg.wformat);
+    const float zc = c->df == DF_I4SYM ? -136.0f : -128.0f;   // row-sum scale of the integer-code GEMM
+    // the bf16 router emits the row sums when each of its four waves covers whole 128-wide groups
+    const bool fused_sums = grouped && !c->cfg.router_fp32 && c->d % 512 == 0;
     int rc;
     if (c->cfg.router_fp32)
         rc = timed(c, K_ROUTER, s, [&] {
@@ -450,13 +453,14 @@ int qmoe_forward(qmoe_ctx *c, const uint16_t *x, int32_t T, uint16_t *y, qmoe_ro
         });
     else
         rc = timed(c, K_ROUTER, s, [&] {
-            return launch_router_bf16(x, (const uint16_t *)c->router_w, c->router_b, c->logits, T, c->d, c->E, s);
+            return launch_router_bf16(x, (const uint16_t *)c->router_w, c->router_b, c->logits,
+                                      fused_sums ? c->xsum : nullptr, zc, T, c->d, c->E, s);
         });
     if (rc) return rc;
     rc = run_route(c, c->logits, T, bm, c->S, s);
     if (rc) return rc;
-    if (is_group_wformat(c->cfg.wformat)) {
-        rc = timed(c, K_XSUM, s, [&] { return launch_xsum(x, T, c->d, c->xsum, s); });
+    if (grouped && !fused_sums) {
+        rc = timed(c, K_XSUM, s, [&] { return launch_xsum(x, T, c->d, zc, c->xsum, s); });
         if (rc) return rc;
     }
 

@@ -110,8 +110,9 @@ void unlayout_matrix(int wformat, const PackedMatrix &p, CanonMatrix &m);
 // ---------------------------------------------------------------------------
 // Kernel launchers (qmoe_kernels.hip). All asynchronous on `s`.
 // ---------------------------------------------------------------------------
-hipError_t launch_router_bf16(const uint16_t *x, const uint16_t *wr, const float *bias, float *logits, int T, int d,
-                              int E, hipStream_t s);
+// xsum (may be NULL): receives xscale * per-128-group row sums of x.
+hipError_t launch_router_bf16(const uint16_t *x, const uint16_t *wr, const float *bias, float *logits, float *xsum,
+                              float xscale, int T, int d, int E, hipStream_t s);
 hipError_t launch_router_f32(const uint16_t *x, const float *wr, const float *bias, float *logits, int T, int d, int E,
                              hipStream_t s);
 hipError_t launch_topk(const float *logits, int T, int E, int k, int renorm, int32_t *idx, float *w, hipStream_t s);
@@ -142,12 +143,13 @@ struct GemmArgs {
     int32_t P;               // routed rows (T*k)
     int32_t T;
     int32_t E;               // routed experts
+    int32_t n_tiles;         // 256-column N-tiles of the widest expert (set by the launcher)
 };
 // bm: rows per M-tile (16, 64 or 128); max_tiles: grid bound; maxN13: max 2F.
 hipError_t launch_gemm13(int df, int bm, const GemmArgs &a, int max_tiles, int maxN13, hipStream_t s);
 hipError_t launch_gemm2(int df, int bm, const GemmArgs &a, int max_tiles, hipStream_t s);
 hipError_t launch_combine(const float *O, const int32_t *inv, int T, int d, int k, int P, int n_shared,
                           uint16_t *y, hipStream_t s);
-hipError_t launch_xsum(const uint16_t *x, int T, int d, float *xsum, hipStream_t s);
+hipError_t launch_xsum(const uint16_t *x, int T, int d, float scale, float *xsum, hipStream_t s);
 
 }  // namespace qmoe

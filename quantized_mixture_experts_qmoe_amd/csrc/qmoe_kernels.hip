@@ -36,51 +36,103 @@ __device__ __forceinline__ float half_bits_to_f32(uint16_t b) {
 // Router
 // ---------------------------------------------------------------------------
 
-// Workgroup = 4 waves, tile 64 tokens x 64 experts; wave w owns tokens
-// [16w, 16w+16) against all 64 experts (four 16x16 accumulators).
+// Workgroup = 4 waves over one tile of 16*MT tokens x 16*NT experts; the waves
+// split d into four quarters (more independent loads in flight per workgroup)
+// and combine their partial tiles through LDS. Workgroups of the first expert
+// tile also emit the per-128-group row sums of x (times xscale) that the
+// integer-code expert GEMM uses (xsum may be NULL).
+template <int MT, int NT>
 __global__ __launch_bounds__(256) void k_router_bf16(const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr,
-                                                     const float *__restrict__ bias, float *__restrict__ logits, int T,
-                                                     int d, int E) {
+                                                     const float *__restrict__ bias, float *__restrict__ logits,
+                                                     float *__restrict__ xsum, float xscale, int T, int d, int E) {
+    __shared__ f32x4 red[3][MT * NT][64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int t0 = blockIdx.x * 64 + wave * 16;
-    const int e0 = blockIdx.y * 64;
+    const int t0 = blockIdx.x * 16 * MT;
+    const int e0 = blockIdx.y * 16 * NT;
     const int kq = (lane >> 4) * 8;
-    const int ar = t0 + (lane & 15);
-    const bool aok = ar < T;
-    const uint16_t *ap = x + (size_t)(aok ? ar : 0) * d + kq;
-    const uint16_t *bp[4];
-    bool bok[4];
+    const uint16_t *ap[MT];
+    bool aok[MT];
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const int be = e0 + 16 * i + (lane & 15);
-        bok[i] = be < E;
-        bp[i] = wr + (size_t)(bok[i] ? be : 0) * d + kq;
+    for (int i = 0; i < MT; i++) {
+        const int t = t0 + 16 * i + (lane & 15);
+        aok[i] = t < T;
+        ap[i] = x + (size_t)(aok[i] ? t : 0) * d + kq;
     }
-    f32x4 acc[4];
+    const uint16_t *bp[NT];
+    bool bok[NT];
 #pragma unroll
-    for (int i = 0; i < 4; i++) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const uint4 zero4 = make_uint4(0, 0, 0, 0);
-#pragma unroll 4
-    for (int k0 = 0; k0 < d; k0 += 32) {
-        const uint4 av = aok ? *reinterpret_cast<const uint4 *>(ap + k0) : zero4;
-        const bf16x8 a = __builtin_bit_cast(bf16x8, av);
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const uint4 bv = bok[i] ? *reinterpret_cast<const uint4 *>(bp[i] + k0) : zero4;
-            acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, bv), acc[i], 0, 0, 0);
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
+    for (int i = 0; i < NT; i++) {
         const int e = e0 + 16 * i + (lane & 15);
-        if (e >= E) continue;
-        const float b = bias ? bias[e] : 0.0f;
+        bok[i] = e < E;
+        bp[i] = wr + (size_t)(bok[i] ? e : 0) * d + kq;
+    }
+    f32x4 acc[MT][NT];
 #pragma unroll
-        for (int r = 0; r < 4; r++) {
-            const int t = t0 + (lane >> 4) * 4 + r;
-            if (t < T) logits[(size_t)t * E + e] = acc[i][r] + b;
+    for (int i = 0; i < MT; i++)
+#pragma unroll
+        for (int j = 0; j < NT; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const bool do_sum = xsum != nullptr && blockIdx.y == 0;
+    float gs[MT];
+#pragma unroll
+    for (int i = 0; i < MT; i++) gs[i] = 0.0f;
+    const uint4 zero4 = make_uint4(0, 0, 0, 0);
+    const int kw = d / 4, kbeg = wave * kw;
+#pragma unroll 4
+    for (int k0 = kbeg; k0 < kbeg + kw; k0 += 32) {
+        uint4 av[MT];
+#pragma unroll
+        for (int i = 0; i < MT; i++) av[i] = aok[i] ? *reinterpret_cast<const uint4 *>(ap[i] + k0) : zero4;
+#pragma unroll
+        for (int j = 0; j < NT; j++) {
+            const uint4 bv = bok[j] ? *reinterpret_cast<const uint4 *>(bp[j] + k0) : zero4;
+#pragma unroll
+            for (int i = 0; i < MT; i++)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[i]),
+                                                                    __builtin_bit_cast(bf16x8, bv), acc[i][j], 0, 0, 0);
+        }
+        if (do_sum) {
+#pragma unroll
+            for (int i = 0; i < MT; i++) {
+                const uint32_t u[4] = {av[i].x, av[i].y, av[i].z, av[i].w};
+#pragma unroll
+                for (int q = 0; q < 4; q++) gs[i] += bf16f(u[q] & 0xFFFFu) + bf16f(u[q] >> 16);
+            }
+            if (((k0 + 32) & 127) == 0) {
+#pragma unroll
+                for (int i = 0; i < MT; i++) {
+                    float v = gs[i];
+                    v += __shfl_xor(v, 16);
+                    v += __shfl_xor(v, 32);
+                    const int t = t0 + 16 * i + lane;
+                    if (lane < 16 && t < T) xsum[(size_t)t * (d / 128) + k0 / 128] = v * xscale;
+                    gs[i] = 0.0f;
+                }
+            }
         }
     }
+    if (wave > 0) {
+#pragma unroll
+        for (int i = 0; i < MT; i++)
+#pragma unroll
+            for (int j = 0; j < NT; j++) red[wave - 1][i * NT + j][lane] = acc[i][j];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int i = 0; i < MT; i++)
+#pragma unroll
+        for (int j = 0; j < NT; j++) {
+            const f32x4 v = acc[i][j] + red[0][i * NT + j][lane] + red[1][i * NT + j][lane] +
+                            red[2][i * NT + j][lane];
+            const int e = e0 + 16 * j + (lane & 15);
+            if (e >= E) continue;
+            const float b = bias ? bias[e] : 0.0f;
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int t = t0 + 16 * i + (lane >> 4) * 4 + r;
+                if (t < T) logits[(size_t)t * E + e] = v[r] + b;
+            }
+        }
 }
 
 __global__ __launch_bounds__(256) void k_router_f32(const uint16_t *__restrict__ x, const float *__restrict__ wr,
@@ -299,10 +351,12 @@ __global__ __launch_bounds__(256) void k_dispatch_scatter(const int32_t *__restr
 // Row sums over 128-wide groups (the offset correction of the integer-code GEMM)
 // ---------------------------------------------------------------------------
 
-// xsum[t][g] = sum_{c in group g} x[t][c] in fp32. One wave per token row;
+// xsum[t][g] = scale * sum_{c in group g} x[t][c] in fp32 (scale = -ZC, see the
+// grouped GEMM). One wave per token row;
 // lane l reads 16-byte chunks l, l+64, ...; the 16 chunks of a group sit in 16
 // consecutive lanes and are reduced with xor shuffles.
-__global__ __launch_bounds__(256) void k_xsum(const uint16_t *__restrict__ x, int T, int d, float *__restrict__ xsum) {
+__global__ __launch_bounds__(256) void k_xsum(const uint16_t *__restrict__ x, int T, int d, float scale,
+                                              float *__restrict__ xsum) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int t = blockIdx.x * 4 + wave;
     if (t >= T) return;
@@ -316,7 +370,7 @@ __global__ __launch_bounds__(256) void k_xsum(const uint16_t *__restrict__ x, in
         for (int i = 0; i < 4; i++) s += bf16f(u[i] & 0xFFFFu) + bf16f(u[i] >> 16);
 #pragma unroll
         for (int off = 1; off < 16; off <<= 1) s += __shfl_xor(s, off);
-        if ((lane & 15) == 0) xsum[(size_t)t * G + c / 16] = s;
+        if ((lane & 15) == 0) xsum[(size_t)t * G + c / 16] = s * scale;
     }
 }
 
@@ -409,12 +463,19 @@ __device__ __forceinline__ bool tile_setup(const GemmArgs &a, TileCtx &c) {
 // The chain of four MFMAs of a group starts from C = -ZC * rowsum (ZC = 136 for
 // the symmetric formats, whose stored u = q + 8; 128 for asymmetric), and the
 // group's result is scaled by s_ng in fp32 into the running accumulator
-// (asymmetric: minus s_ng z_ng rowsum_mg as well).
+// (asymmetric: minus s_ng z_ng rowsum_mg as well). Row sums are stored already
+// multiplied by -ZC ("nrs"), so the asymmetric term is (s z / 128) * nrs.
+template <int DF>
+struct GroupConst {
+    static constexpr float ZC = DF == DF_I4SYM ? 136.0f : 128.0f;
+};
+
+// 16-row tiles (decode-shaped batches): one workgroup per (tile, 256 columns).
 template <int DF, int MODE, int MI>
 __global__ __launch_bounds__(256) void k_gemm_g(GemmArgs a) {
     constexpr int BM = 16 * MI;
     constexpr int PITCH = 136;   // bf16 per LDS row: 128 + 8 pad (conflict-free MFMA reads)
-    constexpr float ZC = DF == DF_I4SYM ? 136.0f : 128.0f;
+    constexpr float ZC = GroupConst<DF>::ZC;
     __shared__ __attribute__((aligned(16))) uint16_t As[BM * PITCH];
     __shared__ __attribute__((aligned(16))) float Rs[BM];
 
@@ -461,7 +522,8 @@ __global__ __launch_bounds__(256) void k_gemm_g(GemmArgs a) {
             const size_t blk = (size_t)(ib0 + nb) * KB + kb;
             braw[nb] = *reinterpret_cast<const uint4 *>(codes + blk * 1024 + lane * 16);
             bsc[nb] = half_bits_to_f32(gsc[blk * 16 + (lane & 15)]);
-            bsz[nb] = DF == DF_I4ASYM ? -bsc[nb] * half_bits_to_f32(gzp[blk * 16 + (lane & 15)]) : 0.0f;
+            bsz[nb] = DF == DF_I4ASYM ? bsc[nb] * half_bits_to_f32(gzp[blk * 16 + (lane & 15)]) * (1.0f / 128.0f)
+                                      : 0.0f;
         }
 #pragma unroll
         for (int i = 0; i < MI; i++) {
@@ -481,8 +543,8 @@ __global__ __launch_bounds__(256) void k_gemm_g(GemmArgs a) {
         }
 #pragma unroll
         for (int mi = 0; mi < MI; mi++) {
-            const f32x4 rs = *reinterpret_cast<const f32x4 *>(&Rs[mi * 16 + lrow]);
-            const f32x4 cinit = rs * -ZC;
+            const f32x4 rs = *reinterpret_cast<const f32x4 *>(&Rs[mi * 16 + lrow]);   // -ZC * rowsum
+            const f32x4 cinit = rs;
             bf16x8 af[4];
 #pragma unroll
             for (int s = 0; s < 4; s++)
@@ -540,7 +602,7 @@ __global__ __launch_bounds__(256) void k_gemm_g(GemmArgs a) {
         if ((int)threadIdx.x < BM && (int)threadIdx.x < c.rows) {
             const int row = threadIdx.x;
             const float v = red[row] + red[BM + row] + red[2 * BM + row] + red[3 * BM + row];
-            a.hsum[(size_t)(c.tl.row0 + row) * (a.ldh / 128) + c.n0 / 256] = v;
+            a.hsum[(size_t)(c.tl.row0 + row) * (a.ldh / 128) + c.n0 / 256] = -ZC * v;
         }
     } else {
 #pragma unroll
@@ -554,6 +616,217 @@ __global__ __launch_bounds__(256) void k_gemm_g(GemmArgs a) {
 #pragma unroll
                 for (int nb = 0; nb < 4; nb++) {
                     const int n = c.n0 + 64 * wave + 16 * nb + (lane & 15);
+                    a.O[(size_t)gr * a.d + n] = acc[mi][nb][r] * wt;
+                }
+            }
+    }
+}
+
+// ---- 64-row tiles (prefill): pipelined, XCD-aware -------------------------
+//
+// Work items (M-tile of the task list, 256-column N-tile) are numbered in bands
+// of 4 N-tiles with the M-tile slower inside a band, so concurrently running
+// workgroups share both activation rows and packed weights; the numbering is
+// split into 8 contiguous chunks, one per XCD (workgroup L runs on XCD L % 8),
+// so each XCD's L2 sees a contiguous window of the work.
+__device__ __forceinline__ bool map_work(int L, int ntiles, int NT, int &tile, int &nt) {
+    const int total = ntiles * NT;
+    const int C = (total + 7) >> 3;
+    if ((L >> 3) >= C) return false;
+    const int w = (L & 7) * C + (L >> 3);
+    if (w >= total) return false;
+    constexpr int GN = 4;
+    const int band = w / (ntiles * GN);
+    const int rem = w - band * ntiles * GN;
+    const int gw = min(GN, NT - band * GN);
+    tile = rem / gw;
+    nt = band * GN + rem % gw;
+    return true;
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void gbl_void_t;
+
+// Asynchronous global -> LDS copies (gfx950 global_load_lds_dword{,x4}): lane l
+// of the wave writes its `size` bytes at lds_wave_base + l * size.
+__device__ __forceinline__ void lds_dma16(const void *g, void *lds_wave_base) {
+    __builtin_amdgcn_global_load_lds((gbl_void_t *)g, (lds_void_t *)lds_wave_base, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_dma4(const void *g, void *lds_wave_base) {
+    __builtin_amdgcn_global_load_lds((gbl_void_t *)g, (lds_void_t *)lds_wave_base, 4, 0, 0);
+}
+
+// Activation tile in LDS: 64 rows x 128 bf16 (256 B per row, no padding); the
+// 16-byte chunk c of row r is stored at chunk position c ^ (r & 15), so the 16
+// rows an MFMA operand read touches fall in 16 different bank groups.
+// Double-buffered; the next group's rows, row sums and packed codes are in
+// flight while the current group is computed; one barrier per group.
+template <int DF, int MODE>
+__global__ __launch_bounds__(256, 2) void k_gemm_g64(GemmArgs a) {
+    constexpr int MI = 4, BM = 64;
+    constexpr float ZC = GroupConst<DF>::ZC;
+    __shared__ __attribute__((aligned(1024))) uint16_t As[2][BM * 128];
+    __shared__ __attribute__((aligned(256))) float Rs[2][BM];
+
+    int tile_id, ntile;
+    if (!map_work(blockIdx.x, *a.num_tiles, a.n_tiles, tile_id, ntile)) return;
+    const Tile tl = a.tiles[tile_id];
+    const ExpertW ew = a.experts[tl.e];
+    const int N = MODE == 0 ? 2 * ew.F : a.d;
+    const int K = MODE == 0 ? a.d : ew.F;
+    const int n0 = ntile * 256;
+    if (n0 >= N) return;
+    const int rows = tl.row_end - tl.row0;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int KB = K / 128;
+    const int lrow = (lane >> 4) * 4;
+
+    // sources of this lane's four 16-byte activation chunks per group
+    const uint16_t *abase = MODE == 0 ? a.x : a.H;
+    const int lda = MODE == 0 ? a.d : a.ldh;
+    uint32_t aoff[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int row = 16 * wave + 4 * i + (lane >> 4);
+        const int gr = tl.row0 + (row < rows ? row : 0);
+        const int src = MODE == 0 ? (gr < a.P ? a.perm[gr] / a.k : (gr - a.P) % a.T) : gr;
+        aoff[i] = (uint32_t)src * (uint32_t)lda + (uint32_t)(((lane & 15) ^ (row & 15)) * 8);
+    }
+    const float *rbase = MODE == 0 ? a.xsum : a.hsum;
+    const int ldr = MODE == 0 ? a.d / 128 : a.ldh / 128;
+    uint32_t roff;
+    {
+        const int gr = tl.row0 + (lane < rows ? lane : 0);
+        const int src = MODE == 0 ? (gr < a.P ? a.perm[gr] / a.k : (gr - a.P) % a.T) : gr;
+        roff = (uint32_t)src * (uint32_t)ldr;
+    }
+    const uint8_t *codes = MODE == 0 ? ew.c13 : ew.c2;
+    const uint16_t *gsc = MODE == 0 ? ew.s13 : ew.s2;
+    const uint16_t *gzp = MODE == 0 ? ew.z13 : ew.z2;
+    const int ib0 = n0 / 16 + 4 * wave;
+
+    auto issue_a = [&](int kb, int buf) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) lds_dma16(abase + aoff[i] + kb * 128, &As[buf][(16 * wave + 4 * i) * 128]);
+        if (wave == 0) lds_dma4(rbase + roff + kb, &Rs[buf][0]);
+    };
+    uint4 braw[4];
+    float bsc[4], bsz[4];
+    auto load_b = [&](int kb) {
+#pragma unroll
+        for (int nb = 0; nb < 4; nb++) {
+            const size_t blk = (size_t)(ib0 + nb) * KB + kb;
+            braw[nb] = *reinterpret_cast<const uint4 *>(codes + blk * 1024 + lane * 16);
+            bsc[nb] = half_bits_to_f32(gsc[blk * 16 + (lane & 15)]);
+            bsz[nb] = DF == DF_I4ASYM ? bsc[nb] * half_bits_to_f32(gzp[blk * 16 + (lane & 15)]) * (1.0f / 128.0f)
+                                      : 0.0f;
+        }
+    };
+
+    f32x4 acc[MI][4];
+#pragma unroll
+    for (int mi = 0; mi < MI; mi++)
+#pragma unroll
+        for (int nb = 0; nb < 4; nb++) acc[mi][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    issue_a(0, 0);
+    load_b(0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    for (int kb = 0; kb < KB; kb++) {
+        const int cur = kb & 1;
+        // this group's codes become MFMA operands; their registers then take the
+        // next group's codes, which arrive during this group's MFMAs
+        bf16x8 bq[4][4];
+        float csc[4], csz[4];
+#pragma unroll
+        for (int nb = 0; nb < 4; nb++) {
+            bq[nb][0] = nibbles_to_bf16_128(braw[nb].x);
+            bq[nb][1] = nibbles_to_bf16_128(braw[nb].y);
+            bq[nb][2] = nibbles_to_bf16_128(braw[nb].z);
+            bq[nb][3] = nibbles_to_bf16_128(braw[nb].w);
+            csc[nb] = bsc[nb];
+            csz[nb] = bsz[nb];
+        }
+        if (kb + 1 < KB) {
+            issue_a(kb + 1, cur ^ 1);
+            load_b(kb + 1);
+        }
+        const uint16_t *Ab = As[cur];
+#pragma unroll
+        for (int mi = 0; mi < MI; mi++) {
+            const f32x4 nrs = *reinterpret_cast<const f32x4 *>(&Rs[cur][mi * 16 + lrow]);
+            f32x4 p[4];
+#pragma unroll
+            for (int nb = 0; nb < 4; nb++) p[nb] = nrs;
+#pragma unroll
+            for (int s = 0; s < 4; s++) {
+                const int pc = (s * 4 + (lane >> 4)) ^ (lane & 15);
+                const bf16x8 af = *reinterpret_cast<const bf16x8 *>(&Ab[(mi * 16 + (lane & 15)) * 128 + pc * 8]);
+#pragma unroll
+                for (int nb = 0; nb < 4; nb++)
+                    p[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bq[nb][s], p[nb], 0, 0, 0);
+            }
+#pragma unroll
+            for (int nb = 0; nb < 4; nb++) {
+                acc[mi][nb] += csc[nb] * p[nb];
+                if (DF == DF_I4ASYM) acc[mi][nb] += csz[nb] * nrs;
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+
+    if (MODE == 0) {
+        float hs[MI][4];
+#pragma unroll
+        for (int mi = 0; mi < MI; mi++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) hs[mi][r] = 0.0f;
+#pragma unroll
+        for (int pr = 0; pr < 2; pr++) {
+            const int col = ((ib0 + 2 * pr) >> 1) * 16 + (lane & 15);
+#pragma unroll
+            for (int mi = 0; mi < MI; mi++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    const int row = mi * 16 + lrow + r;
+                    const float g = acc[mi][2 * pr][r];
+                    const float u = acc[mi][2 * pr + 1][r];
+                    const uint16_t hb = to_bf16(g / (1.0f + __expf(-g)) * u);
+                    hs[mi][r] += bf16f(hb);
+                    if (row < rows) a.H[(size_t)(tl.row0 + row) * a.ldh + col] = hb;
+                }
+        }
+        float *red = reinterpret_cast<float *>(&As[0][0]);   // [4][BM]; the last barrier freed the tiles
+#pragma unroll
+        for (int mi = 0; mi < MI; mi++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                float v = hs[mi][r];
+#pragma unroll
+                for (int off = 1; off < 16; off <<= 1) v += __shfl_xor(v, off);
+                if ((lane & 15) == 0) red[wave * BM + mi * 16 + lrow + r] = v;
+            }
+        __syncthreads();
+        if ((int)threadIdx.x < BM && (int)threadIdx.x < rows) {
+            const int row = threadIdx.x;
+            const float v = red[row] + red[BM + row] + red[2 * BM + row] + red[3 * BM + row];
+            a.hsum[(size_t)(tl.row0 + row) * (a.ldh / 128) + n0 / 256] = -ZC * v;
+        }
+    } else {
+#pragma unroll
+        for (int mi = 0; mi < MI; mi++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int row = mi * 16 + lrow + r;
+                if (row >= rows) continue;
+                const int gr = tl.row0 + row;
+                const float wt = gr < a.P ? a.wpair[a.perm[gr]] : 1.0f;
+#pragma unroll
+                for (int nb = 0; nb < 4; nb++) {
+                    const int n = n0 + 64 * wave + 16 * nb + (lane & 15);
                     a.O[(size_t)gr * a.d + n] = acc[mi][nb][r] * wt;
                 }
             }
@@ -704,10 +977,15 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ O, co
 // Launchers
 // ---------------------------------------------------------------------------
 
-hipError_t launch_router_bf16(const uint16_t *x, const uint16_t *wr, const float *bias, float *logits, int T, int d,
-                              int E, hipStream_t s) {
-    dim3 grid((T + 63) / 64, (E + 63) / 64);
-    hipLaunchKernelGGL(k_router_bf16, grid, dim3(256), 0, s, x, wr, bias, logits, T, d, E);
+hipError_t launch_router_bf16(const uint16_t *x, const uint16_t *wr, const float *bias, float *logits, float *xsum,
+                              float xscale, int T, int d, int E, hipStream_t s) {
+    if (T >= 256) {
+        dim3 grid((T + 31) / 32, (E + 31) / 32);
+        hipLaunchKernelGGL((k_router_bf16<2, 2>), grid, dim3(256), 0, s, x, wr, bias, logits, xsum, xscale, T, d, E);
+    } else {
+        dim3 grid((T + 15) / 16, (E + 31) / 32);
+        hipLaunchKernelGGL((k_router_bf16<1, 2>), grid, dim3(256), 0, s, x, wr, bias, logits, xsum, xscale, T, d, E);
+    }
     return hipGetLastError();
 }
 
@@ -768,7 +1046,19 @@ static hipError_t launch_gemm_df(int df, dim3 grid, const GemmArgs &a, hipStream
 }
 
 template <int MODE>
-static hipError_t launch_gemm_bm(int df, int bm, dim3 grid, const GemmArgs &a, hipStream_t s) {
+static hipError_t launch_gemm(int df, int bm, int max_tiles, int maxN, const GemmArgs &a0, hipStream_t s) {
+    GemmArgs a = a0;
+    a.n_tiles = (maxN + 255) / 256;
+    if (bm == 64 && (df == DF_I4SYM || df == DF_I4ASYM)) {
+        const long total = (long)max_tiles * a.n_tiles;
+        dim3 grid((unsigned)(8 * ((total + 7) / 8)));
+        if (df == DF_I4SYM)
+            hipLaunchKernelGGL((k_gemm_g64<DF_I4SYM, MODE>), grid, dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((k_gemm_g64<DF_I4ASYM, MODE>), grid, dim3(256), 0, s, a);
+        return hipGetLastError();
+    }
+    dim3 grid(a.n_tiles, max_tiles);
     switch (bm) {
     case 16: return launch_gemm_df<MODE, 1>(df, grid, a, s);
     case 64: return launch_gemm_df<MODE, 4>(df, grid, a, s);
@@ -778,17 +1068,15 @@ static hipError_t launch_gemm_bm(int df, int bm, dim3 grid, const GemmArgs &a, h
 }
 
 hipError_t launch_gemm13(int df, int bm, const GemmArgs &a, int max_tiles, int maxN13, hipStream_t s) {
-    dim3 grid((maxN13 + 255) / 256, max_tiles);
-    return launch_gemm_bm<0>(df, bm, grid, a, s);
+    return launch_gemm<0>(df, bm, max_tiles, maxN13, a, s);
 }
 
 hipError_t launch_gemm2(int df, int bm, const GemmArgs &a, int max_tiles, hipStream_t s) {
-    dim3 grid((a.d + 255) / 256, max_tiles);
-    return launch_gemm_bm<1>(df, bm, grid, a, s);
+    return launch_gemm<1>(df, bm, max_tiles, a.d, a, s);
 }
 
-hipError_t launch_xsum(const uint16_t *x, int T, int d, float *xsum, hipStream_t s) {
-    hipLaunchKernelGGL(k_xsum, dim3((T + 3) / 4), dim3(256), 0, s, x, T, d, xsum);
+hipError_t launch_xsum(const uint16_t *x, int T, int d, float scale, float *xsum, hipStream_t s) {
+    hipLaunchKernelGGL(k_xsum, dim3((T + 3) / 4), dim3(256), 0, s, x, T, d, scale, xsum);
     return hipGetLastError();
 }
 
