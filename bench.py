@@ -83,7 +83,20 @@ def main() -> int:
     ap.add_argument("--flush-mb", type=int, default=-1,
                     help="write this many MiB between timed decode steps to evict the 256 MB MALL "
                          "(default: 1024 for decode workloads, 0 otherwise)")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB (3 times), the "
+                         "reference for scaling HBM byte counters")
     args = ap.parse_args()
+    if args.copy_calibration_mb:
+        import torch
+        n = args.copy_calibration_mb * 1024 * 1024 // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "launches": 3}))
+        return 0
     if args.gpus != 1:
         print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported "
               f"(the layer is not sharded; see the design notes for how it would shard).", file=sys.stderr)

@@ -16,7 +16,8 @@ from typing import Optional, Sequence
 
 import numpy as np
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqmoe.so")
+# QMOE_LIBRARY may point at another build of the same library (e.g. a tuning build).
+LIB_PATH = os.environ.get("QMOE_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqmoe.so")
 
 QMOE_OK = 0
 QMOE_EINVAL = -1

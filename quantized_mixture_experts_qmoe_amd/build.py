@@ -15,9 +15,12 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqmoe.so")
 
 ARCH = "gfx950"
-# Packed-FP32 VALU forms are kept out of every kernel (see DESIGN notes).
+# Packed-FP32 VALU instructions are disabled in every kernel.
+# MFMA results are kept in architectural VGPRs (the grouped GEMMs scale them
+# with VALU FMAs every group; AGPR placement would add a read per element).
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
-             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-mllvm", "-amdgpu-mfma-vgpr-form"]
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC"]
 
 

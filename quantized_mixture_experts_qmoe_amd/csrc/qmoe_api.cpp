@@ -42,7 +42,7 @@ enum Slot { K_ROUTER = 0, K_TOPK, K_DCOUNT, K_DSCAN, K_DSCATTER, K_XSUM, K_GEMM1
 struct MatInfo {
     int N = 0, K = 0;
     size_t codes_off = 0, codes_bytes = 0;
-    size_t gs_off = 0, gz_off = 0, ps_off = 0;   // byte offsets in the arena (0 = absent)
+    size_t gs_off = 0, gz_off = 0, ps_off = 0, zc_off = 0;   // byte offsets in the arena (0 = absent)
     size_t gs_count = 0, ps_count = 0;
 };
 
@@ -83,6 +83,7 @@ struct qmoe_ctx {
     double tot_ms[QMOE_NUM_KERNELS] = {};
     int64_t launches[QMOE_NUM_KERNELS] = {};
     bool debug_sync = false;
+    int gemm_bm = 64;   // rows per M-tile of the prefill GEMMs (group formats): 64, 96 or 128
 };
 
 namespace {
@@ -164,6 +165,10 @@ MatInfo plan_matrix(const PackedMatrix &p, int N, int K, size_t &cursor) {
         m.ps_count = p.pscale.size();
         cursor = align256(cursor + p.pscale.size() * 4);
     }
+    if (!p.zc.empty()) {
+        m.zc_off = cursor;
+        cursor = align256(cursor + p.zc.size() * 2);
+    }
     return m;
 }
 
@@ -175,6 +180,8 @@ int upload_matrix(qmoe_ctx *c, const MatInfo &m, const PackedMatrix &p) {
         e = hipMemcpy(c->arena + m.gz_off, p.gzero.data(), p.gzero.size() * 2, hipMemcpyHostToDevice);
     if (e == hipSuccess && m.ps_off)
         e = hipMemcpy(c->arena + m.ps_off, p.pscale.data(), p.pscale.size() * 4, hipMemcpyHostToDevice);
+    if (e == hipSuccess && m.zc_off)
+        e = hipMemcpy(c->arena + m.zc_off, p.zc.data(), p.zc.size() * 2, hipMemcpyHostToDevice);
     if (e != hipSuccess) return fail(QMOE_EHIP, "hipMemcpy of packed weights failed: %s", hipGetErrorString(e));
     return QMOE_OK;
 }
@@ -229,7 +236,8 @@ int rows_per_tile(const qmoe_ctx *c, int T) {
     const long active = std::min<long>(c->E, P);
     const double avg = (double)P / (double)std::max<long>(1, active);
     if (avg <= 16.0) return 16;
-    return 64;
+    if (!is_group_wformat(c->cfg.wformat)) return 64;
+    return c->gemm_bm;
 }
 
 int max_tiles_for(const qmoe_ctx *c, int T, int bm) {
@@ -312,6 +320,10 @@ int qmoe_pack_experts(const qmoe_config *cfg, const float *const *w_gate, const 
     c->k = cfg->top_k;
     c->maxT = cfg->max_tokens;
     c->debug_sync = getenv("QMOE_DEBUG") != nullptr;
+    if (const char *bmenv = getenv("QMOE_PREFILL_TILE_ROWS")) {   // tuning knob: 64, 96 or 128
+        const int v = atoi(bmenv);
+        if (v == 64 || v == 96 || v == 128) c->gemm_bm = v;
+    }
 
     // Quantize and lay out every expert on the host, several experts at a time.
     std::vector<ExpertPack> packs(nexp);
@@ -360,10 +372,12 @@ int qmoe_pack_experts(const qmoe_config *cfg, const float *const *w_gate, const 
         w.s13 = a.gs_off ? (const uint16_t *)(c->arena + a.gs_off) : nullptr;
         w.z13 = a.gz_off ? (const uint16_t *)(c->arena + a.gz_off) : nullptr;
         w.p13 = a.ps_off ? (const float *)(c->arena + a.ps_off) : nullptr;
+        w.zc13 = a.zc_off ? (const uint16_t *)(c->arena + a.zc_off) : nullptr;
         w.c2 = c->arena + b.codes_off;
         w.s2 = b.gs_off ? (const uint16_t *)(c->arena + b.gs_off) : nullptr;
         w.z2 = b.gz_off ? (const uint16_t *)(c->arena + b.gz_off) : nullptr;
         w.p2 = b.ps_off ? (const float *)(c->arena + b.ps_off) : nullptr;
+        w.zc2 = b.zc_off ? (const uint16_t *)(c->arena + b.zc_off) : nullptr;
         w.F = i < c->E ? c->F : c->Fs;
     }
     rc = dalloc(c, (void **)&c->d_experts, sizeof(ExpertW) * nexp);

@@ -31,6 +31,11 @@ namespace qmoe {
 // Blocks are stored row-block major: block (rb, kb) at index rb*(K/128) + kb.
 // Group scales / zeros (fp16 bits): [N/16][K/128][16], the block's 16 rows
 // contiguous. Per-channel scales (fp32): [N].
+// Zero-point correction operand (INT4_ASYM only): v_ng = s_ng * z_ng / 128 split
+// exactly into bf16 hi + lo and laid out as MFMA B operands over the group
+// index: block (rb, gs) of 1024 bf16 = hi[64 lanes][8] then lo[64 lanes][8];
+// lane l holds row rb*16 + l%16, groups g = 32gs + 8(l/16) + j (0 past the last
+// group).
 //
 // The gate and up matrices of one expert are packed as a single matrix "W13"
 // of 2F rows whose 16-row blocks alternate: block 2b = gate rows 16b..16b+15,
@@ -68,10 +73,12 @@ struct ExpertW {
     const uint16_t *s13;  // W13 group scales (fp16 bits) or nullptr
     const uint16_t *z13;  // W13 group zeros (fp16 bits) or nullptr
     const float *p13;     // W13 per-channel scales [2F] or nullptr
+    const uint16_t *zc13; // W13 zero-point correction operand (INT4_ASYM) or nullptr
     const uint8_t *c2;    // W2 codes
     const uint16_t *s2;
     const uint16_t *z2;
     const float *p2;      // W2 per-channel scales [d]
+    const uint16_t *zc2;
     int32_t F;            // d_ff of this expert
     int32_t pad[3];
 };
@@ -100,6 +107,7 @@ struct PackedMatrix {
     std::vector<uint8_t> codes;
     std::vector<uint16_t> gscale, gzero;
     std::vector<float> pscale;
+    std::vector<uint16_t> zc;   // zero-point correction operand (INT4_ASYM)
 };
 void layout_matrix(int wformat, const CanonMatrix &m, PackedMatrix &out);
 // Build the interleaved W13 canonical matrix from gate and up.

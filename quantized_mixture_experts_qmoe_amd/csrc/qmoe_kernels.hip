@@ -31,6 +31,22 @@ __device__ __forceinline__ uint16_t to_bf16(float f) {
 __device__ __forceinline__ float half_bits_to_f32(uint16_t b) {
     return (float)__builtin_bit_cast(_Float16, b);
 }
+// Loads through the global address space (global_load rather than flat_load, so
+// outstanding loads count only against vmcnt and never delay LDS waits).
+template <typename T>
+__device__ __forceinline__ T gload(const T *p) {
+    return *(const __attribute__((address_space(1))) T *)p;
+}
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 gload16(const void *p) {
+    const u32x4 v = *(const __attribute__((address_space(1))) u32x4 *)p;
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+// bf16 hi + lo split of an fp32 value (hi = nearest bf16, lo = nearest bf16 of the rest).
+__device__ __forceinline__ void split_bf16(float v, __bf16 &hi, __bf16 &lo) {
+    hi = (__bf16)v;
+    lo = (__bf16)(v - (float)hi);
+}
 
 // ---------------------------------------------------------------------------
 // Router
@@ -390,6 +406,28 @@ __device__ __forceinline__ bf16x8 nibbles_to_bf16_128(uint32_t d) {
     return __builtin_bit_cast(bf16x8, r);
 }
 
+// Same conversion with the mask and the magic held in registers: gfx9 VOP3
+// instructions cannot encode literals, so with register operands each pair of
+// codes costs one v_and_or_b32 (plus one shift for the upper three pairs).
+struct NibbleConst {
+    uint32_t mask;    // 0x000F000F (scalar register)
+    uint32_t magic;   // 0x43004300 (vector register)
+};
+__device__ __forceinline__ NibbleConst nibble_const() {
+    NibbleConst c;
+    asm volatile("s_mov_b32 %0, 0xf000f" : "=s"(c.mask));
+    asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(c.magic));
+    return c;
+}
+__device__ __forceinline__ bf16x8 nibbles_to_bf16_128(uint32_t d, NibbleConst c) {
+    uint4 r;
+    r.x = (d & c.mask) | c.magic;
+    r.y = ((d >> 4) & c.mask) | c.magic;
+    r.z = ((d >> 8) & c.mask) | c.magic;
+    r.w = ((d >> 12) & c.mask) | c.magic;
+    return __builtin_bit_cast(bf16x8, r);
+}
+
 template <int DF>
 __device__ __forceinline__ bf16x8 codes8_to_bf16(uint32_t d0, uint32_t d1);
 
@@ -644,29 +682,48 @@ __device__ __forceinline__ bool map_work(int L, int ntiles, int NT, int &tile, i
     return true;
 }
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) const void gbl_void_t;
-
-// Asynchronous global -> LDS copies (gfx950 global_load_lds_dword{,x4}): lane l
-// of the wave writes its `size` bytes at lds_wave_base + l * size.
-__device__ __forceinline__ void lds_dma16(const void *g, void *lds_wave_base) {
-    __builtin_amdgcn_global_load_lds((gbl_void_t *)g, (lds_void_t *)lds_wave_base, 16, 0, 0);
+// s_waitcnt immediate (gfx9 encoding): wait until at most `vm` vector-memory
+// operations are outstanding and all LDS operations have completed.
+template <int VM>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+    static_assert(VM >= 0 && VM < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | (0 << 8) | ((VM >> 4) << 14));
 }
-__device__ __forceinline__ void lds_dma4(const void *g, void *lds_wave_base) {
-    __builtin_amdgcn_global_load_lds((gbl_void_t *)g, (lds_void_t *)lds_wave_base, 4, 0, 0);
+// Workgroup barrier without the compiler's fence (which would drain every
+// outstanding load); the memory clobber keeps LDS accesses on their side.
+__device__ __forceinline__ void raw_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// ---- 64/96/128-row tiles (prefill): global -> LDS ring, XCD-aware ----------
+//
+// Every transfer of the K loop is an asynchronous global -> LDS copy issued
+// from inline assembly (so the compiler neither waits on it before LDS reads
+// nor counts it): per wave and group exactly 14 copies -- 8 x 1 KB of gathered
+// activation rows, 4 x 1 KB of its own packed codes, the fp16 scales of its
+// four 16-row blocks and 32 row sums. A three-stage ring gives a prefetch
+// distance of two groups; at the end of group g, "vmcnt <= 14" means group g+1
+// has landed, and one barrier publishes it to the workgroup.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+__device__ __forceinline__ void dma16(const void *g, uint32_t lds) {
+    const uint32_t base = __builtin_amdgcn_readfirstlane(lds);   // wave-uniform by construction
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(base) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void *g, uint32_t lds) {
+    const uint32_t base = __builtin_amdgcn_readfirstlane(lds);
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(base) : "memory", "m0");
 }
 
-// Activation tile in LDS: 64 rows x 128 bf16 (256 B per row, no padding); the
-// 16-byte chunk c of row r is stored at chunk position c ^ (r & 15), so the 16
-// rows an MFMA operand read touches fall in 16 different bank groups.
-// Double-buffered; the next group's rows, row sums and packed codes are in
-// flight while the current group is computed; one barrier per group.
-template <int DF, int MODE>
-__global__ __launch_bounds__(256, 2) void k_gemm_g64(GemmArgs a) {
-    constexpr int MI = 4, BM = 64;
+template <int DF, int MODE, int MI, int NW, int NST, int OCC>
+__global__ __launch_bounds__(64 * NW, OCC) void k_gemm_gpf(GemmArgs a) {
+    constexpr int BM = 16 * MI, RPW = BM / NW;   // activation rows copied per wave
+    constexpr int ADMA = RPW / 4;                 // 1 KB activation copies per wave
+    constexpr int DMA_PER_GROUP = ADMA + 4 + 2;
+    constexpr int ST_A = 0, ST_B = BM * 256, ST_S = ST_B + NW * 4096, ST_R = ST_S + NW * 128,
+                  ST_BYTES = ST_R + BM * 4;
+    constexpr int NTILE = 64 * NW;                // B columns per workgroup
     constexpr float ZC = GroupConst<DF>::ZC;
-    __shared__ __attribute__((aligned(1024))) uint16_t As[2][BM * 128];
-    __shared__ __attribute__((aligned(256))) float Rs[2][BM];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[NST * ST_BYTES];
 
     int tile_id, ntile;
     if (!map_work(blockIdx.x, *a.num_tiles, a.n_tiles, tile_id, ntile)) return;
@@ -674,20 +731,22 @@ __global__ __launch_bounds__(256, 2) void k_gemm_g64(GemmArgs a) {
     const ExpertW ew = a.experts[tl.e];
     const int N = MODE == 0 ? 2 * ew.F : a.d;
     const int K = MODE == 0 ? a.d : ew.F;
-    const int n0 = ntile * 256;
+    const int n0 = ntile * NTILE;
     if (n0 >= N) return;
     const int rows = tl.row_end - tl.row0;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int KB = K / 128;
     const int lrow = (lane >> 4) * 4;
+    const uint32_t lds0 = lds_addr(lds);
 
-    // sources of this lane's four 16-byte activation chunks per group
+    // sources of this lane's ADMA 16-byte activation chunks per group: rows
+    // RPW*w + 4i + lane/16, chunk (lane & 15) ^ (row & 15) (the swizzle)
     const uint16_t *abase = MODE == 0 ? a.x : a.H;
     const int lda = MODE == 0 ? a.d : a.ldh;
-    uint32_t aoff[4];
+    uint32_t aoff[ADMA];
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const int row = 16 * wave + 4 * i + (lane >> 4);
+    for (int i = 0; i < ADMA; i++) {
+        const int row = RPW * wave + 4 * i + (lane >> 4);
         const int gr = tl.row0 + (row < rows ? row : 0);
         const int src = MODE == 0 ? (gr < a.P ? a.perm[gr] / a.k : (gr - a.P) % a.T) : gr;
         aoff[i] = (uint32_t)src * (uint32_t)lda + (uint32_t)(((lane & 15) ^ (row & 15)) * 8);
@@ -696,89 +755,140 @@ __global__ __launch_bounds__(256, 2) void k_gemm_g64(GemmArgs a) {
     const int ldr = MODE == 0 ? a.d / 128 : a.ldh / 128;
     uint32_t roff;
     {
-        const int gr = tl.row0 + (lane < rows ? lane : 0);
+        const int row = RPW * wave + (lane < RPW ? lane : 0);
+        const int gr = tl.row0 + (row < rows ? row : 0);
         const int src = MODE == 0 ? (gr < a.P ? a.perm[gr] / a.k : (gr - a.P) % a.T) : gr;
         roff = (uint32_t)src * (uint32_t)ldr;
     }
     const uint8_t *codes = MODE == 0 ? ew.c13 : ew.c2;
     const uint16_t *gsc = MODE == 0 ? ew.s13 : ew.s2;
-    const uint16_t *gzp = MODE == 0 ? ew.z13 : ew.z2;
-    const int ib0 = n0 / 16 + 4 * wave;
+    // a wave whose 64 columns lie past N (last N-tile of a narrower matrix)
+    // copies block 0 instead to keep its copy count, and computes nothing
+    const bool wave_on = n0 + 64 * wave < N;
+    const int ib0 = wave_on ? n0 / 16 + 4 * wave : 0;
+    // scale copy: lane i (< 32) brings the scales of rows 2(i&7), 2(i&7)+1 of block i>>3
+    const int snb = (lane >> 3) & 3, spair = lane & 7;
 
-    auto issue_a = [&](int kb, int buf) {
+    auto issue = [&](int kb, int st) {
+        const uint32_t sb = lds0 + st * ST_BYTES;
 #pragma unroll
-        for (int i = 0; i < 4; i++) lds_dma16(abase + aoff[i] + kb * 128, &As[buf][(16 * wave + 4 * i) * 128]);
-        if (wave == 0) lds_dma4(rbase + roff + kb, &Rs[buf][0]);
-    };
-    uint4 braw[4];
-    float bsc[4], bsz[4];
-    auto load_b = [&](int kb) {
+        for (int i = 0; i < ADMA; i++) dma16(abase + aoff[i] + kb * 128, sb + ST_A + (RPW * wave + 4 * i) * 256);
 #pragma unroll
-        for (int nb = 0; nb < 4; nb++) {
-            const size_t blk = (size_t)(ib0 + nb) * KB + kb;
-            braw[nb] = *reinterpret_cast<const uint4 *>(codes + blk * 1024 + lane * 16);
-            bsc[nb] = half_bits_to_f32(gsc[blk * 16 + (lane & 15)]);
-            bsz[nb] = DF == DF_I4ASYM ? bsc[nb] * half_bits_to_f32(gzp[blk * 16 + (lane & 15)]) * (1.0f / 128.0f)
-                                      : 0.0f;
-        }
+        for (int nb = 0; nb < 4; nb++)
+            dma16(codes + ((size_t)(ib0 + nb) * KB + kb) * 1024 + lane * 16, sb + ST_B + (wave * 4 + nb) * 1024);
+        if (lane < 32) dma4(gsc + ((size_t)(ib0 + snb) * KB + kb) * 16 + 2 * spair, sb + ST_S + wave * 128);
+        if (lane < RPW) dma4(rbase + roff + kb, sb + ST_R + wave * RPW * 4);
     };
+    const int last = KB - 1;
 
     f32x4 acc[MI][4];
 #pragma unroll
     for (int mi = 0; mi < MI; mi++)
 #pragma unroll
         for (int nb = 0; nb < 4; nb++) acc[mi][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const NibbleConst nc = nibble_const();
 
-    issue_a(0, 0);
-    load_b(0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    // prologue: groups 0 .. NST-2 in flight, then group 0 must land
+#pragma unroll
+    for (int j = 0; j < NST - 1; j++) issue(min(j, last), j);
+    wait_vm_lgkm0<DMA_PER_GROUP * (NST - 2)>();
+    raw_barrier();
 
+    int st = 0;
     for (int kb = 0; kb < KB; kb++) {
-        const int cur = kb & 1;
-        // this group's codes become MFMA operands; their registers then take the
-        // next group's codes, which arrive during this group's MFMAs
+        issue(min(kb + NST - 1, last), st == 0 ? NST - 1 : st - 1);   // stage (kb + NST - 1) % NST
+        const uint8_t *S = lds + st * ST_BYTES;
+        // this wave's packed codes and scales of the group
         bf16x8 bq[4][4];
-        float csc[4], csz[4];
+        float sc[4];
 #pragma unroll
         for (int nb = 0; nb < 4; nb++) {
-            bq[nb][0] = nibbles_to_bf16_128(braw[nb].x);
-            bq[nb][1] = nibbles_to_bf16_128(braw[nb].y);
-            bq[nb][2] = nibbles_to_bf16_128(braw[nb].z);
-            bq[nb][3] = nibbles_to_bf16_128(braw[nb].w);
-            csc[nb] = bsc[nb];
-            csz[nb] = bsz[nb];
+            const uint4 raw = *reinterpret_cast<const uint4 *>(S + ST_B + (wave * 4 + nb) * 1024 + lane * 16);
+            bq[nb][0] = nibbles_to_bf16_128(raw.x, nc);
+            bq[nb][1] = nibbles_to_bf16_128(raw.y, nc);
+            bq[nb][2] = nibbles_to_bf16_128(raw.z, nc);
+            bq[nb][3] = nibbles_to_bf16_128(raw.w, nc);
+            sc[nb] = half_bits_to_f32(*reinterpret_cast<const uint16_t *>(S + ST_S + wave * 128 + nb * 32 +
+                                                                          (lane & 15) * 2));
         }
-        if (kb + 1 < KB) {
-            issue_a(kb + 1, cur ^ 1);
-            load_b(kb + 1);
-        }
-        const uint16_t *Ab = As[cur];
-#pragma unroll
-        for (int mi = 0; mi < MI; mi++) {
-            const f32x4 nrs = *reinterpret_cast<const f32x4 *>(&Rs[cur][mi * 16 + lrow]);
-            f32x4 p[4];
-#pragma unroll
-            for (int nb = 0; nb < 4; nb++) p[nb] = nrs;
+        const uint16_t *Ab = reinterpret_cast<const uint16_t *>(S + ST_A);
+        const float *Rb = reinterpret_cast<const float *>(S + ST_R);
+        if (wave_on) {
+            // k-step outer: the 4*MI MFMA chains of the group advance together, so
+            // consecutive MFMAs of a chain are 4*MI instructions apart, and the
+            // scale FMAs at the end read chains that finished long before
+            f32x4 p[MI][4];
 #pragma unroll
             for (int s = 0; s < 4; s++) {
                 const int pc = (s * 4 + (lane >> 4)) ^ (lane & 15);
-                const bf16x8 af = *reinterpret_cast<const bf16x8 *>(&Ab[(mi * 16 + (lane & 15)) * 128 + pc * 8]);
 #pragma unroll
-                for (int nb = 0; nb < 4; nb++)
-                    p[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bq[nb][s], p[nb], 0, 0, 0);
+                for (int mi = 0; mi < MI; mi++) {
+                    const bf16x8 af = *reinterpret_cast<const bf16x8 *>(&Ab[(mi * 16 + (lane & 15)) * 128 + pc * 8]);
+                    const f32x4 c0 = s == 0 ? *reinterpret_cast<const f32x4 *>(&Rb[mi * 16 + lrow]) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int nb = 0; nb < 4; nb++)
+                        p[mi][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bq[nb][s], s == 0 ? c0 : p[mi][nb], 0, 0, 0);
+                }
             }
+#pragma unroll
+            for (int mi = 0; mi < MI; mi++)
+#pragma unroll
+                for (int nb = 0; nb < 4; nb++) acc[mi][nb] += sc[nb] * p[mi][nb];
+        }
+        wait_vm_lgkm0<DMA_PER_GROUP * (NST - 2)>();   // group kb+1 has landed
+        raw_barrier();
+        st = st == NST - 1 ? 0 : st + 1;
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    raw_barrier();
+
+    if (DF == DF_I4ASYM && wave_on) {
+        // zero points: acc[m][n] += sum_g (s_ng z_ng / 128) * nrs_mg, one MFMA
+        // contraction over the group index with bf16 hi/lo splits of both sides
+        // (hi*hi + hi*lo + lo*hi; relative error ~2^-16 of the correction)
+        const uint16_t *zcp = MODE == 0 ? ew.zc13 : ew.zc2;
+        const int GS = (KB + 31) / 32;
+        uint32_t zrow[MI];
+#pragma unroll
+        for (int mi = 0; mi < MI; mi++) {
+            const int row = mi * 16 + (lane & 15);
+            const int gr = tl.row0 + (row < rows ? row : 0);
+            const int src = MODE == 0 ? (gr < a.P ? a.perm[gr] / a.k : (gr - a.P) % a.T) : gr;
+            zrow[mi] = (uint32_t)src * (uint32_t)ldr;
+        }
+        for (int gs = 0; gs < GS; gs++) {
+            bf16x8 bh[4], bl[4];
 #pragma unroll
             for (int nb = 0; nb < 4; nb++) {
-                acc[mi][nb] += csc[nb] * p[nb];
-                if (DF == DF_I4ASYM) acc[mi][nb] += csz[nb] * nrs;
+                const uint16_t *q = zcp + ((size_t)(ib0 + nb) * GS + gs) * 1024 + lane * 8;
+                bh[nb] = __builtin_bit_cast(bf16x8, gload16(q));
+                bl[nb] = __builtin_bit_cast(bf16x8, gload16(q + 512));
+            }
+            const int g0 = gs * 32 + (lane >> 4) * 8;
+#pragma unroll
+            for (int mi = 0; mi < MI; mi++) {
+                bf16x8 ah, al;
+#pragma unroll
+                for (int j = 0; j < 8; j++) {
+                    const float v = g0 + j < KB ? gload(rbase + zrow[mi] + g0 + j) : 0.0f;
+                    __bf16 h, l;
+                    split_bf16(v, h, l);
+                    ah[j] = h;
+                    al[j] = l;
+                }
+#pragma unroll
+                for (int nb = 0; nb < 4; nb++) {
+                    acc[mi][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh[nb], acc[mi][nb], 0, 0, 0);
+                    acc[mi][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl[nb], acc[mi][nb], 0, 0, 0);
+                    acc[mi][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh[nb], acc[mi][nb], 0, 0, 0);
+                }
             }
         }
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
     }
 
     if (MODE == 0) {
+        // H = silu(gate) * up; the workgroup's columns are NW/4 groups of 128 H
+        // columns, whose per-row sums (of the bf16 values) feed the down GEMM
         float hs[MI][4];
 #pragma unroll
         for (int mi = 0; mi < MI; mi++)
@@ -796,10 +906,10 @@ __global__ __launch_bounds__(256, 2) void k_gemm_g64(GemmArgs a) {
                     const float u = acc[mi][2 * pr + 1][r];
                     const uint16_t hb = to_bf16(g / (1.0f + __expf(-g)) * u);
                     hs[mi][r] += bf16f(hb);
-                    if (row < rows) a.H[(size_t)(tl.row0 + row) * a.ldh + col] = hb;
+                    if (wave_on && row < rows) a.H[(size_t)(tl.row0 + row) * a.ldh + col] = hb;
                 }
         }
-        float *red = reinterpret_cast<float *>(&As[0][0]);   // [4][BM]; the last barrier freed the tiles
+        float *red = reinterpret_cast<float *>(lds);   // [NW][BM]; the last barrier freed the ring
 #pragma unroll
         for (int mi = 0; mi < MI; mi++)
 #pragma unroll
@@ -810,10 +920,14 @@ __global__ __launch_bounds__(256, 2) void k_gemm_g64(GemmArgs a) {
                 if ((lane & 15) == 0) red[wave * BM + mi * 16 + lrow + r] = v;
             }
         __syncthreads();
-        if ((int)threadIdx.x < BM && (int)threadIdx.x < rows) {
-            const int row = threadIdx.x;
-            const float v = red[row] + red[BM + row] + red[2 * BM + row] + red[3 * BM + row];
-            a.hsum[(size_t)(tl.row0 + row) * (a.ldh / 128) + n0 / 256] = -ZC * v;
+        if ((int)threadIdx.x < BM * (NW / 4)) {
+            const int h = threadIdx.x / BM, row = threadIdx.x % BM;
+            const int grp = n0 / 256 + h;   // 128-wide H group
+            if (row < rows && grp < ew.F / 128) {
+                const float *rr = red + 4 * h * BM + row;
+                const float v = rr[0] + rr[BM] + rr[2 * BM] + rr[3 * BM];
+                a.hsum[(size_t)(tl.row0 + row) * (a.ldh / 128) + grp] = -ZC * v;
+            }
         }
     } else {
 #pragma unroll
@@ -827,7 +941,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_g64(GemmArgs a) {
 #pragma unroll
                 for (int nb = 0; nb < 4; nb++) {
                     const int n = n0 + 64 * wave + 16 * nb + (lane & 15);
-                    a.O[(size_t)gr * a.d + n] = acc[mi][nb][r] * wt;
+                    if (wave_on) a.O[(size_t)gr * a.d + n] = acc[mi][nb][r] * wt;
                 }
             }
     }
@@ -1049,13 +1163,27 @@ template <int MODE>
 static hipError_t launch_gemm(int df, int bm, int max_tiles, int maxN, const GemmArgs &a0, hipStream_t s) {
     GemmArgs a = a0;
     a.n_tiles = (maxN + 255) / 256;
-    if (bm == 64 && (df == DF_I4SYM || df == DF_I4ASYM)) {
+    if ((bm == 64 || bm == 96 || bm == 128) && (df == DF_I4SYM || df == DF_I4ASYM)) {
+        // prefill tiles: 8 waves (two per SIMD) over bm rows x 512 columns,
+        // double-buffered; 64-row tiles use 4 waves x 256 columns, 3 stages
+        const int cols = bm == 64 ? 256 : 512;
+        a.n_tiles = (maxN + cols - 1) / cols;
         const long total = (long)max_tiles * a.n_tiles;
         dim3 grid((unsigned)(8 * ((total + 7) / 8)));
-        if (df == DF_I4SYM)
-            hipLaunchKernelGGL((k_gemm_g64<DF_I4SYM, MODE>), grid, dim3(256), 0, s, a);
-        else
-            hipLaunchKernelGGL((k_gemm_g64<DF_I4ASYM, MODE>), grid, dim3(256), 0, s, a);
+        const bool sym = df == DF_I4SYM;
+        switch (bm) {
+        case 64:   // two workgroups per CU (<= 256 VGPRs, 67 KB LDS each)
+            if (sym) hipLaunchKernelGGL((k_gemm_gpf<DF_I4SYM, MODE, 4, 4, 2, 2>), grid, dim3(256), 0, s, a);
+            else hipLaunchKernelGGL((k_gemm_gpf<DF_I4ASYM, MODE, 4, 4, 2, 2>), grid, dim3(256), 0, s, a);
+            break;
+        case 96:
+            if (sym) hipLaunchKernelGGL((k_gemm_gpf<DF_I4SYM, MODE, 6, 8, 2, 1>), grid, dim3(512), 0, s, a);
+            else hipLaunchKernelGGL((k_gemm_gpf<DF_I4ASYM, MODE, 6, 8, 2, 1>), grid, dim3(512), 0, s, a);
+            break;
+        default:
+            if (sym) hipLaunchKernelGGL((k_gemm_gpf<DF_I4SYM, MODE, 8, 8, 2, 1>), grid, dim3(512), 0, s, a);
+            else hipLaunchKernelGGL((k_gemm_gpf<DF_I4ASYM, MODE, 8, 8, 2, 1>), grid, dim3(512), 0, s, a);
+        }
         return hipGetLastError();
     }
     dim3 grid(a.n_tiles, max_tiles);

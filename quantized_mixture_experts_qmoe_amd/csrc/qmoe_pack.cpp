@@ -70,6 +70,20 @@ uint8_t e4m3_bits(float v) {
 
 inline float clampf(float v, float lo, float hi) { return std::min(std::max(v, lo), hi); }
 
+// bf16 bits of a finite float, round to nearest even.
+uint16_t bf16_rne_bits(float v) {
+    uint32_t u;
+    memcpy(&u, &v, 4);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+float bf16_value(uint16_t b) {
+    const uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
 }  // namespace
 
 int quantize_matrix(int wformat, int N, int K, const float *w, CanonMatrix &out) {
@@ -206,6 +220,27 @@ void layout_matrix(int wformat, const CanonMatrix &m, PackedMatrix &out) {
                 }
     } else {
         out.pscale.assign(m.scale.begin(), m.scale.end());
+    }
+    out.zc.clear();
+    if (df == DF_I4ASYM) {
+        // s * z / 128 is exact in fp32 (11-bit scale times a 4-bit zero); its
+        // bf16 remainder after the rounded high part fits a bf16 exactly.
+        const int GS = (KB + 31) / 32;
+        out.zc.assign((size_t)NB * GS * 1024, 0);
+        for (int rb = 0; rb < NB; rb++)
+            for (int gs = 0; gs < GS; gs++) {
+                uint16_t *blk = &out.zc[((size_t)rb * GS + gs) * 1024];
+                for (int lane = 0; lane < 64; lane++)
+                    for (int j = 0; j < 8; j++) {
+                        const int n = rb * kBlockRows + lane % 16;
+                        const int g = gs * 32 + 8 * (lane / 16) + j;
+                        const float v = g < KB ? m.scale[(size_t)n * KB + g] * m.zero[(size_t)n * KB + g] / 128.0f : 0.0f;
+                        const uint16_t hi = bf16_rne_bits(v);
+                        const uint16_t lo = bf16_rne_bits(v - bf16_value(hi));
+                        blk[lane * 8 + j] = hi;
+                        blk[512 + lane * 8 + j] = lo;
+                    }
+            }
     }
 }
 
