@@ -54,6 +54,23 @@ def packed_bytes_per_expert(cfg, f):
     return n + 4 * (2 * f + cfg.d)
 
 
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    copy-calibrated FETCH_SIZE + WRITE_SIZE counter runs, or None when no run
+    covers it or the kernel source has changed since the counters were taken."""
+    import hashlib
+    rec_path = os.path.join(ROOT, "profiles", "traffic.json")
+    src = os.path.join(ROOT, "quantized_mixture_experts_qmoe_amd", "csrc", "qmoe_kernels.hip")
+    try:
+        rec = json.load(open(rec_path))
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    if rec.get("kernel_source_sha256") != sha:
+        return None
+    return rec.get("kernels", {}).get(kernel, {}).get(workload)
+
+
 def cpu_baseline(inp, n_tokens: int):
     from oracle import oracle as O
     cfg = inp.cfg
@@ -155,7 +172,8 @@ def main() -> int:
     if not decode:
         achieved = work["gemm_gate_up"] / (k13 * 1e-6) / 1e12
         roof = {"bound": "mfma", "kernel": "gemm_gate_up", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                "traffic": measured_traffic("gemm_gate_up", cfg.name), "traffic_unit": "bytes/launch",
                 "per_launch": f"{work['gemm_gate_up']:.4e} FLOP"}
     else:
         # bytes of the gate/up weights of the distinct experts this batch selects
@@ -167,7 +185,8 @@ def main() -> int:
         b13 = len(used) * per_exp13 + cfg.T * cfg.d * 2
         achieved = b13 / (k13 * 1e-6) / 1e9
         roof = {"bound": "hbm", "kernel": "gemm_gate_up", "achieved": achieved, "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": None,
+                "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+                "traffic": measured_traffic("gemm_gate_up", cfg.name), "traffic_unit": "bytes/launch",
                 "per_launch": f"{b13} B ({len(used)} distinct experts)"}
     layer_tflops = work["layer"] / (ms_per_step * 1e-3) / 1e12
     log(f"{value:.4g} tokens/s, {ms_per_step:.3f} ms/step, layer {layer_tflops:.1f} TFLOP/s; kernels: "

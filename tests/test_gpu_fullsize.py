@@ -1,0 +1,62 @@
+"""Full-size GPU parity: every benchmark layer at its real shape, run as one
+qmoe_forward over the whole batch (the launch configuration bench.py times).
+The oracle evaluates a sample of tokens one by one; routing and the task list
+are checked on every token."""
+import numpy as np
+import pytest
+import torch
+
+from quantized_mixture_experts_qmoe_amd import QMoE
+from quantized_mixture_experts_qmoe_amd.inputs import CONFIGS, make_inputs
+from gpu_util import assert_output_close, bf16_tensor_to_f64, check_own_routing, logit_bound, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def sample_tokens(T, n, seed=0):
+    if T <= n:
+        return np.arange(T, dtype=np.int32)
+    rng = np.random.default_rng(seed)
+    mid = rng.choice(np.arange(1, T - 1), size=n - 2, replace=False)
+    return np.sort(np.concatenate([[0, T - 1], mid])).astype(np.int32)
+
+
+@pytest.mark.parametrize("name", ["tiny", "mixtral_prefill", "qwen3_prefill", "dsv2lite_prefill", "qwen3_decode",
+                                  "qwen3_decode_fp8"])
+def test_full_size_layer(oracle_mod, name):
+    O = oracle_mod
+    cfg = CONFIGS[name]
+    print(f"[case] full-size {name}", flush=True)
+    inp = make_inputs(cfg, seed=0)
+    layer = QMoE(inp, max_tokens=cfg.T)
+    x = to_dev_bf16(inp.x)
+    route = QMoE.route_buffers(cfg.T, cfg.E, cfg.k)
+    y = layer.forward(x, route=route)
+    torch.cuda.synchronize()
+    y_gpu = bf16_tensor_to_f64(y)
+    idx = route["topk_idx"].cpu().numpy()
+    w = route["topk_w"].cpu().numpy().astype(np.float64)
+    lg = route["logits"].cpu().numpy()
+    layer.close()
+
+    # every token: distinct experts, weights sum to 1, task list bit-exact
+    assert np.all(np.sort(idx, axis=1)[:, 1:] != np.sort(idx, axis=1)[:, :-1])
+    assert np.all((idx >= 0) & (idx < cfg.E))
+    assert np.all(np.abs(w.sum(1) - 1.0) <= 1e-5)
+    counts, offsets, perm, _ = O.dispatch(idx, cfg.E)
+    assert np.array_equal(route["counts"].cpu().numpy(), counts)
+    assert np.array_equal(route["offsets"].cpu().numpy(), offsets)
+    assert np.array_equal(route["perm"].cpu().numpy(), perm)
+
+    # sampled tokens against the oracle
+    oracle = O.OracleLayer(inp)
+    toks = sample_tokens(cfg.T, 40)
+    ref = oracle.forward(inp.x, tokens=toks)
+    bound = logit_bound(inp.x[toks], inp.w_router, cfg.router_fp32)
+    diff = check_own_routing(ref, lg[toks], idx[toks], w[toks], bound, inp.bias)
+    y_ref = ref["y"].copy()
+    if diff:
+        alt = oracle.forward(inp.x, tokens=toks[diff], given=idx[toks][diff])
+        y_ref[diff] = alt["y"]
+    assert_output_close(y_gpu[toks], y_ref, f"full-size {name} ({len(toks)} sampled tokens)")
+    oracle.close()
