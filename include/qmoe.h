@@ -170,13 +170,18 @@ int qmoe_export_packed(qmoe_ctx *ctx, int32_t expert, int32_t matrix, int8_t *co
 
 /* Kernel timing with HIP events recorded on the launch stream around every
  * kernel of qmoe_forward / qmoe_route_topk (for measurement).
- *   qmoe_profile_enable   on = 1 starts recording (clears totals), 0 stops
+ *   qmoe_profile_enable   slot_mask != 0 starts recording the kernel slots
+ *                         whose bits are set (bit i = slot i; -1 = all) and
+ *                         clears the totals; 0 stops. Each recorded launch
+ *                         adds two event records to the stream, which delay
+ *                         the next kernel by a few microseconds: time only the
+ *                         slots of interest when the step time matters.
  *   qmoe_profile_read     synchronises the recorded events and returns, per
  *                         kernel slot (QMOE_NUM_KERNELS), the summed elapsed
  *                         milliseconds and the number of launches
  *   qmoe_kernel_name      name of a kernel slot */
-#define QMOE_NUM_KERNELS 9
-int qmoe_profile_enable(qmoe_ctx *ctx, int32_t on);
+#define QMOE_NUM_KERNELS 10
+int qmoe_profile_enable(qmoe_ctx *ctx, int32_t slot_mask);
 int qmoe_profile_read(qmoe_ctx *ctx, double *total_ms, int64_t *launches);
 const char *qmoe_kernel_name(int32_t slot);
 

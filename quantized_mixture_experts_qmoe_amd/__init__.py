@@ -24,7 +24,7 @@ QMOE_EINVAL = -1
 QMOE_EHIP = -2
 QMOE_ENOMEM = -3
 QMOE_EUNSUPPORTED = -4
-QMOE_NUM_KERNELS = 9
+QMOE_NUM_KERNELS = 10
 
 WFORMAT_CODES = {"int8_sym_ch": 0, "int4_asym_g128": 1, "int4_sym_g128": 2, "int3_sym_g128": 3,
                  "fp8e4m3_ch": 4}
@@ -232,8 +232,19 @@ class QMoE:
         _check(rc, "qmoe_export_packed")
         return q, s, z
 
-    def profile_enable(self, on: bool = True) -> None:
-        _check(qmoe_profile_enable(self.ctx, int(on)), "qmoe_profile_enable")
+    def profile_enable(self, on=True) -> None:
+        """True: time every kernel slot; False: stop; an iterable of slot names:
+        time only those (each timed launch costs two event records)."""
+        if on is True:
+            mask = -1
+        elif on is False or on is None:
+            mask = 0
+        else:
+            names = [qmoe_kernel_name(i) for i in range(QMOE_NUM_KERNELS)]
+            mask = 0
+            for n in on:
+                mask |= 1 << names.index(n)
+        _check(qmoe_profile_enable(self.ctx, mask), "qmoe_profile_enable")
 
     def profile_read(self):
         ms = np.zeros(QMOE_NUM_KERNELS, np.float64)

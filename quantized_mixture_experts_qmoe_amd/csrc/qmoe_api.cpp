@@ -35,9 +35,10 @@ int fail(int code, const char *fmt, ...) {
     return code;
 }
 
-const char *kKernelNames[QMOE_NUM_KERNELS] = {"router", "topk", "dispatch_count", "dispatch_scan",
-                                              "dispatch_scatter", "xsum", "gemm_gate_up", "gemm_down", "combine"};
-enum Slot { K_ROUTER = 0, K_TOPK, K_DCOUNT, K_DSCAN, K_DSCATTER, K_XSUM, K_GEMM13, K_GEMM2, K_COMBINE };
+const char *kKernelNames[QMOE_NUM_KERNELS] = {"router",     "topk",         "dispatch_count", "dispatch_scan",
+                                              "dispatch_scatter", "xsum", "gemm_gate_up", "gemm_down",
+                                              "combine",    "topk_dispatch"};
+enum Slot { K_ROUTER = 0, K_TOPK, K_DCOUNT, K_DSCAN, K_DSCATTER, K_XSUM, K_GEMM13, K_GEMM2, K_COMBINE, K_TOPKD };
 
 struct MatInfo {
     int N = 0, K = 0;
@@ -73,7 +74,7 @@ struct qmoe_ctx {
     size_t tiles_cap = 0;
     std::vector<void *> allocs;
     // profiling
-    bool prof = false;
+    uint32_t prof = 0;   // bit i: time kernel slot i
     struct Rec {
         int slot;
         hipEvent_t a, b;
@@ -203,8 +204,10 @@ hipEvent_t take_event(qmoe_ctx *c) {
         c->pool.pop_back();
         return e;
     }
+    // timing-only events: no system-scope fence (no cache writeback or
+    // invalidation between the timed kernels)
     hipEvent_t e = nullptr;
-    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
     return e;
 }
 
@@ -212,14 +215,15 @@ hipEvent_t take_event(qmoe_ctx *c) {
 template <typename Fn>
 int timed(qmoe_ctx *c, int slot, hipStream_t s, Fn launch) {
     hipEvent_t a = nullptr, b = nullptr;
-    if (c->prof) {
+    const bool on = (c->prof >> slot) & 1u;
+    if (on) {
         a = take_event(c);
         b = take_event(c);
         if (a && b) (void)hipEventRecord(a, s);
     }
     hipError_t e = launch();
     if (e != hipSuccess) return fail(QMOE_EHIP, "launch of %s failed: %s", kKernelNames[slot], hipGetErrorString(e));
-    if (c->prof && a && b) {
+    if (on && a && b) {
         (void)hipEventRecord(b, s);
         c->recs.push_back({slot, a, b});
     }
@@ -248,6 +252,11 @@ int max_tiles_for(const qmoe_ctx *c, int T, int bm) {
 // Top-k + dispatch shared by route_topk and forward.
 int run_route(qmoe_ctx *c, const float *logits, int T, int bm, int n_shared, hipStream_t s) {
     const int P = T * c->k;
+    if (T <= kSmallRouteMaxT && c->E <= kSmallRouteMaxE)
+        return timed(c, K_TOPKD, s, [&] {
+            return launch_route_small(logits, T, c->E, c->k, c->cfg.renormalize, n_shared, bm, c->idx, c->wpair,
+                                      c->counts, c->offsets, c->tiles, c->num_tiles, c->perm, c->inv, s);
+        });
     const int nchunks = (P + kDispatchChunk - 1) / kDispatchChunk;
     int rc = timed(c, K_TOPK, s, [&] { return launch_topk(logits, T, c->E, c->k, c->cfg.renormalize, c->idx, c->wpair, s); });
     if (rc) return rc;
@@ -458,12 +467,21 @@ int qmoe_forward(qmoe_ctx *c, const uint16_t *x, int32_t T, uint16_t *y, qmoe_ro
     const int max_tiles = max_tiles_for(c, T, bm);
     const bool grouped = is_group_wformat(c->cfg.wformat);
     const float zc = c->df == DF_I4SYM ? -136.0f : -128.0f;   // row-sum scale of the integer-code GEMM
+    // Row sums of x: the prefill GEMMs of the group formats read them; the
+    // decode kernel (bm == 16) computes its own while staging rows.
+    const bool need_sums = grouped && bm > 16;
+    // small batches: a router grid of 16 x 16 tiles without the row sums
+    const bool small_router = !c->cfg.router_fp32 && T <= kSmallRouteMaxT;
     // the bf16 router emits the row sums when each of its four waves covers whole 128-wide groups
-    const bool fused_sums = grouped && !c->cfg.router_fp32 && c->d % 512 == 0;
+    const bool fused_sums = need_sums && !small_router && !c->cfg.router_fp32 && c->d % 512 == 0;
     int rc;
     if (c->cfg.router_fp32)
         rc = timed(c, K_ROUTER, s, [&] {
             return launch_router_f32(x, (const float *)c->router_w, c->router_b, c->logits, T, c->d, c->E, s);
+        });
+    else if (small_router)
+        rc = timed(c, K_ROUTER, s, [&] {
+            return launch_router_small(x, (const uint16_t *)c->router_w, c->router_b, c->logits, T, c->d, c->E, s);
         });
     else
         rc = timed(c, K_ROUTER, s, [&] {
@@ -473,7 +491,7 @@ int qmoe_forward(qmoe_ctx *c, const uint16_t *x, int32_t T, uint16_t *y, qmoe_ro
     if (rc) return rc;
     rc = run_route(c, c->logits, T, bm, c->S, s);
     if (rc) return rc;
-    if (grouped && !fused_sums) {
+    if (need_sums && !fused_sums) {
         rc = timed(c, K_XSUM, s, [&] { return launch_xsum(x, T, c->d, zc, c->xsum, s); });
         if (rc) return rc;
     }
@@ -550,9 +568,9 @@ int qmoe_export_packed(qmoe_ctx *c, int32_t expert, int32_t matrix, int8_t *code
     return QMOE_OK;
 }
 
-int qmoe_profile_enable(qmoe_ctx *c, int32_t on) {
+int qmoe_profile_enable(qmoe_ctx *c, int32_t slot_mask) {
     if (!c) return fail(QMOE_EINVAL, "ctx is NULL");
-    c->prof = on != 0;
+    c->prof = (uint32_t)slot_mask & ((1u << QMOE_NUM_KERNELS) - 1u);
     if (c->prof) {
         for (auto &r : c->recs) {
             c->pool.push_back(r.a);

@@ -124,15 +124,24 @@ hipError_t launch_router_bf16(const uint16_t *x, const uint16_t *wr, const float
 hipError_t launch_router_f32(const uint16_t *x, const float *wr, const float *bias, float *logits, int T, int d, int E,
                              hipStream_t s);
 hipError_t launch_topk(const float *logits, int T, int E, int k, int renorm, int32_t *idx, float *w, hipStream_t s);
-
+// Small batches (T <= kSmallRouteMaxT): bf16 MFMA router without row sums.
+hipError_t launch_router_small(const uint16_t *x, const uint16_t *wr, const float *bias, float *logits, int T, int d,
+                               int E, hipStream_t s);
 // Dispatch: per-chunk histogram, scan + tile list, stable scatter.
 constexpr int kDispatchChunk = 1024;
+// One-workgroup top-k + dispatch for small batches.
+constexpr int kSmallRouteMaxT = 64;
+constexpr int kSmallRouteMaxE = 256;
 hipError_t launch_dispatch_count(const int32_t *idx, int P, int E, int32_t *chunk_counts, hipStream_t s);
 hipError_t launch_dispatch_scan(const int32_t *chunk_counts, int nchunks, int E, int P, int T, int n_shared, int bm,
                                 int32_t *chunk_base, int32_t *counts, int32_t *offsets, Tile *tiles,
                                 int32_t *num_tiles, hipStream_t s);
 hipError_t launch_dispatch_scatter(const int32_t *idx, int P, int E, const int32_t *chunk_base, int32_t *perm,
                                    int32_t *inv, hipStream_t s);
+// Top-k and the whole dispatch in one workgroup (T <= kSmallRouteMaxT, E <= kSmallRouteMaxE).
+hipError_t launch_route_small(const float *logits, int T, int E, int k, int renorm, int n_shared, int bm,
+                              int32_t *idx, float *w, int32_t *counts, int32_t *offsets, Tile *tiles,
+                              int32_t *num_tiles, int32_t *perm, int32_t *inv, hipStream_t s);
 
 struct GemmArgs {
     const ExpertW *experts;
@@ -153,7 +162,8 @@ struct GemmArgs {
     int32_t E;               // routed experts
     int32_t n_tiles;         // 256-column N-tiles of the widest expert (set by the launcher)
 };
-// bm: rows per M-tile (16, 64 or 128); max_tiles: grid bound; maxN13: max 2F.
+// bm: rows per M-tile (16: weight-streaming decode kernel; 64, 96, 128: prefill
+// kernels); max_tiles: grid bound; maxN13: max 2F.
 hipError_t launch_gemm13(int df, int bm, const GemmArgs &a, int max_tiles, int maxN13, hipStream_t s);
 hipError_t launch_gemm2(int df, int bm, const GemmArgs &a, int max_tiles, hipStream_t s);
 hipError_t launch_combine(const float *O, const int32_t *inv, int T, int d, int k, int P, int n_shared,

@@ -2,8 +2,10 @@
 //
 //   router      logits = x . W_r^T (+ bias): bf16 MFMA with fp32 accumulation
 //               (fp32 router weights: a plain fp32 dot-product kernel)
-//   top-k       one wavefront per token: k rounds of a wave-wide (value, index)
-//               max reduction, lowest index wins ties; softmax over the selection
+//   top-k       one wavefront per token: k rounds of a wave-wide maximum of
+//               (logit, ~index) keys on DPP, lowest index wins ties; softmax
+//               over the selection. Small batches: top-k and dispatch in one
+//               workgroup
 //   dispatch    expert-centric task list (OmniMoE page, technical summary 2.2:
 //               collect tasks, group by expert id, token order inside a group):
 //               per-chunk histogram -> scan + M-tile list -> stable scatter
@@ -164,59 +166,147 @@ __global__ __launch_bounds__(256) void k_router_f32(const uint16_t *__restrict__
     logits[i] = acc + (bias ? bias[e] : 0.0f);
 }
 
+// Small batches (T <= 64): one workgroup per 16 tokens x 16 experts. The four
+// waves split d into quarters and keep up to 16 MFMA k-steps of x and W_r
+// operands in flight straight from memory; partial tiles meet in LDS and are
+// summed in wave order.
+__global__ __launch_bounds__(256) void k_router_small(const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr,
+                                                      const float *__restrict__ bias, float *__restrict__ logits,
+                                                      int T, int d, int E) {
+    constexpr int STEPS = 16;
+    __shared__ float part[4][256];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int t = blockIdx.x * 16 + (lane & 15);
+    const int e = blockIdx.y * 16 + (lane & 15);
+    const bool t_ok = t < T, e_ok = e < E;
+    const int q = d / 4;   // a multiple of 64
+    const uint16_t *xa = x + (size_t)(t_ok ? t : 0) * d + wave * q + (lane >> 4) * 8;
+    const uint16_t *wb = wr + (size_t)(e_ok ? e : 0) * d + wave * q + (lane >> 4) * 8;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < q; k0 += STEPS * 32) {
+        uint4 va[STEPS], vb[STEPS];
+#pragma unroll
+        for (int s = 0; s < STEPS; s++) {
+            const bool in = k0 + s * 32 < q;
+            va[s] = (in && t_ok) ? gload16(xa + k0 + s * 32) : make_uint4(0, 0, 0, 0);
+            vb[s] = (in && e_ok) ? gload16(wb + k0 + s * 32) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int s = 0; s < STEPS; s++)
+            if (k0 + s * 32 < q)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va[s]),
+                                                              __builtin_bit_cast(bf16x8, vb[s]), acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++) part[wave][(4 * (lane >> 4) + i) * 16 + (lane & 15)] = acc[i];
+    __syncthreads();
+    const int row = threadIdx.x >> 4, col = threadIdx.x & 15;
+    const int tt = blockIdx.x * 16 + row, ee = blockIdx.y * 16 + col;
+    if (tt < T && ee < E) {
+        const float v = ((part[0][threadIdx.x] + part[1][threadIdx.x]) + part[2][threadIdx.x]) + part[3][threadIdx.x];
+        logits[(size_t)tt * E + ee] = v + (bias ? bias[ee] : 0.0f);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Top-k + softmax weights (gating network)
 // ---------------------------------------------------------------------------
 
-// (value, index) order: larger value first, then smaller index. Index INT_MAX
-// marks "no candidate".
-__device__ __forceinline__ bool better(float v, int e, float bv, int be) {
-    return e != INT_MAX && (be == INT_MAX || v > bv || (v == bv && e < be));
+// Wave-wide reductions on DPP (row shifts within 16-lane rows, then the
+// row-15 and row-31 broadcasts): each step is a VALU op, not an LDS round trip.
+// After the six steps lane 63 holds the result.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_keep(uint32_t v) {   // lanes without a source keep their own value
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_zero(float v) {         // lanes without a source read 0
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF, true));
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t max_step(uint64_t key) {
+    const uint64_t o = ((uint64_t)dpp_keep<CTRL, ROW_MASK>((uint32_t)(key >> 32)) << 32) | dpp_keep<CTRL, ROW_MASK>((uint32_t)key);
+    return o > key ? o : key;
+}
+constexpr int kDppShr1 = 0x111, kDppShr2 = 0x112, kDppShr4 = 0x114, kDppShr8 = 0x118;
+constexpr int kDppBcast15 = 0x142, kDppBcast31 = 0x143;
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t key) {
+    key = max_step<kDppShr1, 0xF>(key);
+    key = max_step<kDppShr2, 0xF>(key);
+    key = max_step<kDppShr4, 0xF>(key);
+    key = max_step<kDppShr8, 0xF>(key);
+    key = max_step<kDppBcast15, 0xA>(key);
+    key = max_step<kDppBcast31, 0xC>(key);
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)key, 63);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(key >> 32), 63);
+    return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ float wave_sum_f32(float v) {
+    v += dpp_zero<kDppShr1, 0xF>(v);
+    v += dpp_zero<kDppShr2, 0xF>(v);
+    v += dpp_zero<kDppShr4, 0xF>(v);
+    v += dpp_zero<kDppShr8, 0xF>(v);
+    v += dpp_zero<kDppBcast15, 0xA>(v);
+    v += dpp_zero<kDppBcast31, 0xC>(v);
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+// Inclusive prefix sum over the wave (lane i: sum of lanes 0..i).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, kDppShr1, 0xF, 0xF, true);
+    v += __builtin_amdgcn_update_dpp(0, v, kDppShr2, 0xF, 0xF, true);
+    v += __builtin_amdgcn_update_dpp(0, v, kDppShr4, 0xF, 0xF, true);
+    v += __builtin_amdgcn_update_dpp(0, v, kDppShr8, 0xF, 0xF, true);
+    v += __builtin_amdgcn_update_dpp(0, v, kDppBcast15, 0xA, 0xF, true);
+    v += __builtin_amdgcn_update_dpp(0, v, kDppBcast31, 0xC, 0xF, true);
+    return v;
 }
 
+// Selection key of (logit, expert): larger logit first, then lower index. The
+// logit is mapped to an order-preserving unsigned integer (+0.0 and -0.0 made
+// equal first); the low word holds ~index. 0 means "no candidate".
+__device__ __forceinline__ uint64_t select_key(float v, int e) {
+    uint32_t u = __float_as_uint(v + 0.0f);
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)u << 32) | (uint32_t)~(uint32_t)e;
+}
+__device__ __forceinline__ float key_value(uint64_t key) {
+    const uint32_t u = (uint32_t)(key >> 32);
+    return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+}
+__device__ __forceinline__ int key_expert(uint64_t key) { return (int)~(uint32_t)key; }
+
+// Top-k of one token by one wavefront: k rounds of a wave-wide key maximum;
+// lane j ends holding slot j. Weights: softmax over the k selected logits
+// (renorm) or the full-softmax probabilities of the selected. Writes
+// idx_out[0..k) and w_out[0..k); returns this lane's expert (slot = lane) or -1
+// for lanes >= k.
 template <int EPL>
-__global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, int T, int E, int k, int renorm,
-                                              int32_t *__restrict__ idx, float *__restrict__ w) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int t = blockIdx.x * 4 + wave;
-    if (t >= T) return;   // uniform per wave
-    const float *lt = logits + (size_t)t * E;
+__device__ __forceinline__ int topk_token(const float *__restrict__ lt, int E, int k, int renorm, int lane,
+                                          int32_t *__restrict__ idx_out, float *__restrict__ w_out) {
     float v[EPL];
-    uint64_t taken = 0;
+    uint64_t key[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; i++) {
         const int e = lane + 64 * i;
         v[i] = e < E ? lt[e] : 0.0f;
-        if (e >= E) taken |= 1ull << i;
+        key[i] = e < E ? select_key(v[i], e) : 0ull;
     }
-    float my_v = 0.0f, vmax = 0.0f;
-    int my_e = 0;
+    uint64_t mine = 0, first = 0;
     for (int j = 0; j < k; j++) {
-        float bv = 0.0f;
-        int be = INT_MAX;
+        uint64_t best = key[0];
+#pragma unroll
+        for (int i = 1; i < EPL; i++) best = key[i] > best ? key[i] : best;
+        const uint64_t wbest = wave_max_u64(best);
+        const int be = key_expert(wbest);
 #pragma unroll
         for (int i = 0; i < EPL; i++)
-            if (!((taken >> i) & 1ull) && better(v[i], lane + 64 * i, bv, be)) {
-                bv = v[i];
-                be = lane + 64 * i;
-            }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            const float ov = __shfl_xor(bv, off);
-            const int oe = __shfl_xor(be, off);
-            if (better(ov, oe, bv, be)) {
-                bv = ov;
-                be = oe;
-            }
-        }
-        if ((be & 63) == lane) taken |= 1ull << (be >> 6);
-        if (lane == j) {
-            my_v = bv;
-            my_e = be;
-        }
-        if (j == 0) vmax = bv;
+            if (be == lane + 64 * i) key[i] = 0ull;
+        if (lane == j) mine = wbest;
+        if (j == 0) first = wbest;
     }
-    const float ex = lane < k ? expf(my_v - vmax) : 0.0f;
+    const float vmax = key_value(first);
+    const float ex = lane < k ? expf(key_value(mine) - vmax) : 0.0f;
     float part;
     if (renorm) {
         part = ex;
@@ -226,13 +316,23 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, 
         for (int i = 0; i < EPL; i++)
             if (lane + 64 * i < E) part += expf(v[i] - vmax);
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
-    const float denom = __shfl(part, 0);
+    const float denom = wave_sum_f32(part);
     if (lane < k) {
-        idx[(size_t)t * k + lane] = my_e;
-        w[(size_t)t * k + lane] = ex / denom;
+        const int my_e = key_expert(mine);
+        idx_out[lane] = my_e;
+        w_out[lane] = ex / denom;
+        return my_e;
     }
+    return -1;
+}
+
+template <int EPL>
+__global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, int T, int E, int k, int renorm,
+                                              int32_t *__restrict__ idx, float *__restrict__ w) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int t = blockIdx.x * 4 + wave;
+    if (t >= T) return;   // uniform per wave
+    topk_token<EPL>(logits + (size_t)t * E, E, k, renorm, lane, idx + (size_t)t * k, w + (size_t)t * k);
 }
 
 // ---------------------------------------------------------------------------
@@ -253,25 +353,16 @@ __global__ __launch_bounds__(256) void k_dispatch_count(const int32_t *__restric
     for (int e = threadIdx.x; e < E; e += 256) chunk_counts[(size_t)blockIdx.x * E + e] = cnt[e];
 }
 
-// Exclusive scan over a 1024-thread workgroup (16 waves).
+// Exclusive scan over a 1024-thread workgroup (16 waves): DPP scans inside the
+// waves, then one wave scans the 16 wave totals.
 __device__ int block_exclusive_scan_1024(int v, int *wsum) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int incl = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int o = __shfl_up(incl, off);
-        if (lane >= off) incl += o;
-    }
+    const int incl = wave_incl_scan(v);
     if (lane == 63) wsum[wave] = incl;
     __syncthreads();
     if (wave == 0) {
-        int s = lane < 16 ? wsum[lane] : 0;
-        int si = s;
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) {
-            const int o = __shfl_up(si, off);
-            if (lane >= off) si += o;
-        }
+        const int s = lane < 16 ? wsum[lane] : 0;
+        const int si = wave_incl_scan(s);
         if (lane < 16) wsum[16 + lane] = si - s;   // exclusive wave bases
     }
     __syncthreads();
@@ -363,6 +454,94 @@ __global__ __launch_bounds__(256) void k_dispatch_scatter(const int32_t *__restr
     }
 }
 
+// Small batches (T <= 64, E <= 256): top-k and the whole dispatch (histogram,
+// scan, tile list, stable scatter) in one workgroup of 16 waves, with the same
+// outputs as k_topk followed by the three dispatch kernels.
+struct RouteSmallSmem {
+    int sidx[kSmallRouteMaxT * 64];
+    unsigned long long masks[16][kSmallRouteMaxE];
+    int base[kSmallRouteMaxE];
+    int wsum[32];
+};
+
+template <int EPL>
+__device__ void route_small_body(RouteSmallSmem &sm, const float *__restrict__ logits, int T, int E, int k,
+                                 int renorm, int n_shared, int bm, int32_t *__restrict__ idx, float *__restrict__ w,
+                                 int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
+                                 Tile *__restrict__ tiles, int32_t *__restrict__ num_tiles,
+                                 int32_t *__restrict__ perm, int32_t *__restrict__ inv) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int P = T * k;
+    for (int e = tid; e < E; e += 1024) sm.base[e] = 0;
+    for (int i = tid; i < 16 * kSmallRouteMaxE; i += 1024) (&sm.masks[0][0])[i] = 0ull;
+    __syncthreads();
+    for (int t = wave; t < T; t += 16) {
+        const int e = topk_token<EPL>(logits + (size_t)t * E, E, k, renorm, lane, idx + (size_t)t * k,
+                                      w + (size_t)t * k);
+        if (e >= 0) {
+            sm.sidx[t * k + lane] = e;
+            atomicAdd(&sm.base[e], 1);
+        }
+    }
+    __syncthreads();
+    // thread e owns expert e
+    const int cnt = tid < E ? sm.base[tid] : 0;
+    const int ntile = (cnt + bm - 1) / bm;
+    const int row0 = block_exclusive_scan_1024(cnt, sm.wsum);
+    const int tile0 = block_exclusive_scan_1024(ntile, sm.wsum);
+    if (tid < E) {
+        counts[tid] = cnt;
+        offsets[tid] = row0;
+        for (int m = 0; m < cnt; m += bm) tiles[tile0 + m / bm] = Tile{tid, row0 + m, row0 + cnt, 0};
+        sm.base[tid] = row0;
+    }
+    if (tid == E - 1) {
+        offsets[E] = P;
+        int tcount = tile0 + ntile;
+        for (int s = 0; s < n_shared; s++)
+            for (int m = 0; m < T; m += bm) tiles[tcount++] = Tile{E + s, P + s * T + m, P + (s + 1) * T, 0};
+        *num_tiles = tcount;
+    }
+    __syncthreads();
+    // stable scatter, 1024 pairs per round: rank = earlier pairs of the same expert
+    for (int r0 = 0; r0 < P; r0 += 1024) {
+        const int p = r0 + tid;
+        const bool valid = p < P;
+        const int e = valid ? sm.sidx[p] : 0;
+        if (valid) atomicOr(&sm.masks[wave][e], 1ull << lane);
+        __syncthreads();
+        if (valid) {
+            int rank = __popcll(sm.masks[wave][e] & ((1ull << lane) - 1ull));
+            for (int w2 = 0; w2 < wave; w2++) rank += __popcll(sm.masks[w2][e]);
+            const int row = sm.base[e] + rank;
+            perm[row] = p;
+            inv[p] = row;
+        }
+        __syncthreads();
+        if (tid < E) {
+            int add = 0;
+            for (int w2 = 0; w2 < 16; w2++) {
+                add += __popcll(sm.masks[w2][tid]);
+                sm.masks[w2][tid] = 0ull;
+            }
+            sm.base[tid] += add;
+        }
+        __syncthreads();
+    }
+}
+
+template <int EPL>
+__global__ __launch_bounds__(1024) void k_route_small(const float *__restrict__ logits, int T, int E, int k,
+                                                      int renorm, int n_shared, int bm, int32_t *__restrict__ idx,
+                                                      float *__restrict__ w, int32_t *__restrict__ counts,
+                                                      int32_t *__restrict__ offsets, Tile *__restrict__ tiles,
+                                                      int32_t *__restrict__ num_tiles, int32_t *__restrict__ perm,
+                                                      int32_t *__restrict__ inv) {
+    __shared__ RouteSmallSmem sm;
+    route_small_body<EPL>(sm, logits, T, E, k, renorm, n_shared, bm, idx, w, counts, offsets, tiles, num_tiles, perm,
+                          inv);
+}
+
 // ---------------------------------------------------------------------------
 // Row sums over 128-wide groups (the offset correction of the integer-code GEMM)
 // ---------------------------------------------------------------------------
@@ -444,24 +623,25 @@ __device__ __forceinline__ bf16x8 codes8_to_bf16<DF_INT8>(uint32_t d0, uint32_t 
     return r;
 }
 
-// e4m3: exact in bf16 (sign, exponent re-biased 7 -> 127, 3 mantissa bits;
-// subnormals m * 2^-9 go through fp32); the per-row scale is in the epilogue.
-__device__ __forceinline__ uint16_t e4m3_to_bf16_bits(uint32_t b) {
-    const uint32_t s = (b & 0x80u) << 8, e = (b >> 3) & 15u, m = b & 7u;
-    if (e != 0) return (uint16_t)(s | ((e + 120u) << 7) | (m << 4));
-    const float f = (float)m * 0x1p-9f;   // at most 3 significant bits: exact in bf16
-    return (uint16_t)(s | (__float_as_uint(f) >> 16));
+// e4m3 (OCP e4m3fn): exact in bf16. The hardware converts two codes to fp32
+// (v_cvt_pk_f32_fp8) and packs two fp32 into bf16 (v_cvt_pk_bf16_f32), one
+// instruction per code; the per-row scale is applied in the epilogue.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+template <bool HI_WORD>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t dw) {
+    const f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8(dw, HI_WORD);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
 }
 
 template <>
 __device__ __forceinline__ bf16x8 codes8_to_bf16<DF_FP8>(uint32_t d0, uint32_t d1) {
-    bf16x8 r;
-#pragma unroll
-    for (int j = 0; j < 8; j++) {
-        const uint32_t dw = j < 4 ? d0 : d1;
-        r[j] = __builtin_bit_cast(__bf16, e4m3_to_bf16_bits((dw >> (8 * (j & 3))) & 0xFFu));
-    }
-    return r;
+    uint4 r;
+    r.x = e4m3x2_to_bf16x2<false>(d0);
+    r.y = e4m3x2_to_bf16x2<true>(d0);
+    r.z = e4m3x2_to_bf16x2<false>(d1);
+    r.w = e4m3x2_to_bf16x2<true>(d1);
+    return __builtin_bit_cast(bf16x8, r);
 }
 
 // ---------------------------------------------------------------------------
@@ -508,155 +688,224 @@ struct GroupConst {
     static constexpr float ZC = DF == DF_I4SYM ? 136.0f : 128.0f;
 };
 
-// 16-row tiles (decode-shaped batches): one workgroup per (tile, 256 columns).
-template <int DF, int MODE, int MI>
-__global__ __launch_bounds__(256) void k_gemm_g(GemmArgs a) {
-    constexpr int BM = 16 * MI;
-    constexpr int PITCH = 136;   // bf16 per LDS row: 128 + 8 pad (conflict-free MFMA reads)
+// ---- decode-shaped batches: tiles of at most 16 rows ----------------------
+//
+// Here the packed weights are the whole cost, so the kernel is built to keep
+// HBM busy. Workgroup = 4 waves over one tile and 256 columns of B's N
+// dimension; each wave owns four 16-row packed blocks (for the gate/up GEMM two
+// gate/up pairs) and streams their K blocks through a register ring DEPTH K
+// blocks deep, so every load of the ring is in flight at once. The tile's
+// activation rows (at most 16) are staged in LDS in chunks of four K blocks,
+// double-buffered; the next chunk's loads are issued before the weight loads
+// of the current chunk, so waiting for them never drains the weight ring.
+// Group formats take their per-128-group row sums from the staged rows.
+template <int DF>
+struct DecodeCfg {
+    static constexpr bool kGroup = DF == DF_I4SYM || DF == DF_I4ASYM;
+    static constexpr int kWords = kGroup ? 1 : 2;   // 16-byte words per lane per block and K block
+    static constexpr int kDepth = kGroup ? 4 : 2;   // K blocks in flight per wave
+};
+
+template <int DF, int MODE>
+__global__ __launch_bounds__(256) void k_gemm_dec(GemmArgs a) {
+    using CF = DecodeCfg<DF>;
+    constexpr int NB = 4;                  // 16-row blocks per wave
+    constexpr int KC = 4;                  // K blocks per staged chunk
+    constexpr int PITCH = KC * 128 + 8;    // bf16 per LDS row: rows 16 bytes apart in the bank space
     constexpr float ZC = GroupConst<DF>::ZC;
-    __shared__ __attribute__((aligned(16))) uint16_t As[BM * PITCH];
-    __shared__ __attribute__((aligned(16))) float Rs[BM];
+    static_assert(KC % CF::kDepth == 0, "the ring slot must be static inside a chunk");
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][16 * PITCH];
+    __shared__ __attribute__((aligned(16))) float Rs[2][KC][16];
 
     TileCtx c;
     if (!tile_setup<MODE>(a, c)) return;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int KB = c.K / 128;
-    const int lrow = (lane >> 4) * 4;
+    const int NC = (KB + KC - 1) / KC;
 
-    const int c16 = threadIdx.x & 15;
-    const uint16_t *asrc[MI];
-    const float *rsrc[MI];
-    bool aok[MI];
-#pragma unroll
-    for (int i = 0; i < MI; i++) {
-        const int r = (threadIdx.x >> 4) + 16 * i;
-        aok[i] = r < c.rows;
-        const int gr = c.tl.row0 + (aok[i] ? r : 0);
+    // Every path through the K loop issues the same loads (addresses clamped to
+    // valid memory, unused data zeroed by selects), so the compiler's wait
+    // counts stay exact and the ring keeps its depth.
+    // Staging role: row tid/16, 32 consecutive k at 32 * (tid % 16) of the
+    // chunk; rows past the tile read its first row and stage zeros.
+    const int sr = tid >> 4, sk = (tid & 15) * 32;
+    const bool srow = sr < c.rows;
+    const uint16_t *asrc;
+    {
+        const int gr = c.tl.row0 + (srow ? sr : 0);
         if (MODE == 0) {
             const int tok = gr < a.P ? a.perm[gr] / a.k : (gr - a.P) % a.T;
-            asrc[i] = a.x + (size_t)tok * a.d + c16 * 8;
-            rsrc[i] = a.xsum + (size_t)tok * (a.d / 128);
+            asrc = a.x + (size_t)tok * a.d;
         } else {
-            asrc[i] = a.H + (size_t)gr * a.ldh + c16 * 8;
-            rsrc[i] = a.hsum + (size_t)gr * (a.ldh / 128);
+            asrc = a.H + (size_t)gr * a.ldh;
         }
     }
+    uint4 av[4];
+    bool aok = false;
+    auto stage_load = [&](int ch) {
+        const int k0 = ch * (KC * 128) + sk;
+        aok = srow && k0 < c.K;
+        const int kc = min(k0, c.K - 32);
+#pragma unroll
+        for (int i = 0; i < 4; i++) av[i] = gload16(asrc + kc + 8 * i);
+    };
+    auto stage_store = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            av[i].x = aok ? av[i].x : 0u;
+            av[i].y = aok ? av[i].y : 0u;
+            av[i].z = aok ? av[i].z : 0u;
+            av[i].w = aok ? av[i].w : 0u;
+            *reinterpret_cast<uint4 *>(&As[buf][sr * PITCH + sk + 8 * i]) = av[i];
+        }
+        if (CF::kGroup) {
+            float sum = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const uint32_t u[4] = {av[i].x, av[i].y, av[i].z, av[i].w};
+#pragma unroll
+                for (int j = 0; j < 4; j++) sum += bf16f(u[j] & 0xFFFFu) + bf16f(u[j] >> 16);
+            }
+            // the four threads of a 128-wide group are consecutive lanes
+            sum += __shfl_xor(sum, 1);
+            sum += __shfl_xor(sum, 2);
+            if ((tid & 3) == 0) Rs[buf][(tid & 15) >> 2][sr] = -ZC * sum;
+        }
+    };
+
     const uint8_t *codes = MODE == 0 ? c.ew.c13 : c.ew.c2;
     const uint16_t *gsc = MODE == 0 ? c.ew.s13 : c.ew.s2;
     const uint16_t *gzp = MODE == 0 ? c.ew.z13 : c.ew.z2;
-    const int ib0 = c.n0 / 16 + 4 * wave;
-
-    f32x4 acc[MI][4];
+    const int ib0 = c.n0 / 16 + NB * wave;
+    // Scales and zeros travel as the aligned dword holding this lane's fp16
+    // value and its neighbour's; `hsel` picks the half.
+    uint4 ring[CF::kDepth][NB][CF::kWords];
+    uint32_t rsc[CF::kDepth][NB], rzp[CF::kDepth][NB];
+    const int spair = (lane & 15) & ~1;
+    const uint32_t hsel = (lane & 1) * 16;
+    auto issue = [&](int kb, int slot) {
 #pragma unroll
-    for (int mi = 0; mi < MI; mi++)
-#pragma unroll
-        for (int nb = 0; nb < 4; nb++) acc[mi][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    for (int kb = 0; kb < KB; kb++) {
-        uint4 braw[4];
-        float bsc[4], bsz[4];
-#pragma unroll
-        for (int nb = 0; nb < 4; nb++) {
+        for (int nb = 0; nb < NB; nb++) {
             const size_t blk = (size_t)(ib0 + nb) * KB + kb;
-            braw[nb] = *reinterpret_cast<const uint4 *>(codes + blk * 1024 + lane * 16);
-            bsc[nb] = half_bits_to_f32(gsc[blk * 16 + (lane & 15)]);
-            bsz[nb] = DF == DF_I4ASYM ? bsc[nb] * half_bits_to_f32(gzp[blk * 16 + (lane & 15)]) * (1.0f / 128.0f)
-                                      : 0.0f;
-        }
-#pragma unroll
-        for (int i = 0; i < MI; i++) {
-            const uint4 v = aok[i] ? *reinterpret_cast<const uint4 *>(asrc[i] + kb * 128) : make_uint4(0, 0, 0, 0);
-            const int r = (threadIdx.x >> 4) + 16 * i;
-            *reinterpret_cast<uint4 *>(&As[r * PITCH + c16 * 8]) = v;
-            if (c16 == 0) Rs[r] = aok[i] ? rsrc[i][kb] : 0.0f;
-        }
-        __syncthreads();
-        bf16x8 bq[4][4];
-#pragma unroll
-        for (int nb = 0; nb < 4; nb++) {
-            bq[nb][0] = nibbles_to_bf16_128(braw[nb].x);
-            bq[nb][1] = nibbles_to_bf16_128(braw[nb].y);
-            bq[nb][2] = nibbles_to_bf16_128(braw[nb].z);
-            bq[nb][3] = nibbles_to_bf16_128(braw[nb].w);
-        }
-#pragma unroll
-        for (int mi = 0; mi < MI; mi++) {
-            const f32x4 rs = *reinterpret_cast<const f32x4 *>(&Rs[mi * 16 + lrow]);   // -ZC * rowsum
-            const f32x4 cinit = rs;
-            bf16x8 af[4];
-#pragma unroll
-            for (int s = 0; s < 4; s++)
-                af[s] = *reinterpret_cast<const bf16x8 *>(&As[(mi * 16 + (lane & 15)) * PITCH + s * 32 + (lane >> 4) * 8]);
-            f32x4 p[4];
-#pragma unroll
-            for (int nb = 0; nb < 4; nb++) p[nb] = cinit;
-#pragma unroll
-            for (int s = 0; s < 4; s++)
-#pragma unroll
-                for (int nb = 0; nb < 4; nb++)
-                    p[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s], bq[nb][s], p[nb], 0, 0, 0);
-#pragma unroll
-            for (int nb = 0; nb < 4; nb++) {
-                acc[mi][nb] += bsc[nb] * p[nb];
-                if (DF == DF_I4ASYM) acc[mi][nb] += bsz[nb] * rs;
+            if constexpr (CF::kGroup) {
+                ring[slot][nb][0] = gload16(codes + blk * 1024 + lane * 16);
+                rsc[slot][nb] = gload(reinterpret_cast<const uint32_t *>(gsc + blk * 16 + spair));
+                if constexpr (DF == DF_I4ASYM)
+                    rzp[slot][nb] = gload(reinterpret_cast<const uint32_t *>(gzp + blk * 16 + spair));
+            } else {
+                ring[slot][nb][0] = gload16(codes + blk * 2048 + lane * 32);
+                ring[slot][nb][1] = gload16(codes + blk * 2048 + lane * 32 + 16);
             }
         }
+    };
+
+    f32x4 acc[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](int j, int buf, int slot) {
+        bf16x8 af[4];
+#pragma unroll
+        for (int s = 0; s < 4; s++)
+            af[s] = *reinterpret_cast<const bf16x8 *>(&As[buf][(lane & 15) * PITCH + j * 128 + s * 32 + (lane >> 4) * 8]);
+        if constexpr (CF::kGroup) {
+            const f32x4 rs = *reinterpret_cast<const f32x4 *>(&Rs[buf][j][(lane >> 4) * 4]);   // -ZC * rowsum
+#pragma unroll
+            for (int nb = 0; nb < NB; nb++) {
+                const uint4 q = ring[slot][nb][0];
+                f32x4 p = rs;
+                p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[0], nibbles_to_bf16_128(q.x), p, 0, 0, 0);
+                p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[1], nibbles_to_bf16_128(q.y), p, 0, 0, 0);
+                p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[2], nibbles_to_bf16_128(q.z), p, 0, 0, 0);
+                p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[3], nibbles_to_bf16_128(q.w), p, 0, 0, 0);
+                const float sc = half_bits_to_f32((uint16_t)(rsc[slot][nb] >> hsel));
+                acc[nb] += sc * p;
+                if (DF == DF_I4ASYM)
+                    acc[nb] += (sc * half_bits_to_f32((uint16_t)(rzp[slot][nb] >> hsel)) * (1.0f / 128.0f)) * rs;
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < 4; s++)
+#pragma unroll
+                for (int nb = 0; nb < NB; nb++) {
+                    const uint4 q = ring[slot][nb][s >> 1];
+                    acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        af[s], codes8_to_bf16<DF>((s & 1) ? q.z : q.x, (s & 1) ? q.w : q.y), acc[nb], 0, 0, 0);
+                }
+        }
+        // Materialise the accumulators here: otherwise IR-level sinking moves the
+        // scale updates (and the last use of the ring's scale registers) to the
+        // end of the chunk, past the refills of the same slots.
+#pragma unroll
+        for (int nb = 0; nb < NB; nb++) asm volatile("" : "+v"(acc[nb]));
+    };
+
+    // K blocks past the end (the last chunk's padding) compute on zero rows with
+    // a copy of the last block: they add exactly zero.
+    // The scheduling barriers keep each refill right after the compute that
+    // frees its ring slot: left alone, the scheduler sinks all refills to the
+    // end of the chunk (loads stop overlapping compute) or lifts a refill above
+    // the last use of its slot (the registers cannot be reused and the loop
+    // back-edge gains copies that wait for every load).
+    stage_load(0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < CF::kDepth; i++) {
+        issue(min(i, KB - 1), i);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    stage_store(0);
+    __syncthreads();
+    for (int ch = 0; ch < NC; ch++) {
+        const int buf = ch & 1;
+        stage_load(ch + 1);   // past the last chunk: zeros, never read
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < KC; j++) {
+            const int kb = ch * KC + j;
+            compute(j, buf, j % CF::kDepth);
+            __builtin_amdgcn_sched_barrier(0);
+            issue(min(kb + CF::kDepth, KB - 1), j % CF::kDepth);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        stage_store(buf ^ 1);
         __syncthreads();
     }
 
+    const int lrow = (lane >> 4) * 4;
     if (MODE == 0) {
-        float hs[MI][4];
-#pragma unroll
-        for (int mi = 0; mi < MI; mi++)
-#pragma unroll
-            for (int r = 0; r < 4; r++) hs[mi][r] = 0.0f;
 #pragma unroll
         for (int pr = 0; pr < 2; pr++) {
-            const int col = ((ib0 + 2 * pr) >> 1) * 16 + (lane & 15);
-#pragma unroll
-            for (int mi = 0; mi < MI; mi++)
-#pragma unroll
-                for (int r = 0; r < 4; r++) {
-                    const int row = mi * 16 + lrow + r;
-                    const float g = acc[mi][2 * pr][r];
-                    const float u = acc[mi][2 * pr + 1][r];
-                    const uint16_t hb = to_bf16(g / (1.0f + __expf(-g)) * u);
-                    hs[mi][r] += bf16f(hb);
-                    if (row < c.rows) a.H[(size_t)(c.tl.row0 + row) * a.ldh + col] = hb;
-                }
-        }
-        // row sums of this workgroup's 128 H columns (one group of the down GEMM)
-        float *red = reinterpret_cast<float *>(As);   // [4][BM]
-#pragma unroll
-        for (int mi = 0; mi < MI; mi++)
+            const int ibg = ib0 + 2 * pr;
+            const int col = (ibg >> 1) * 16 + (lane & 15);
+            const float sg = CF::kGroup ? 1.0f : c.ew.p13[ibg * 16 + (lane & 15)];
+            const float su = CF::kGroup ? 1.0f : c.ew.p13[(ibg + 1) * 16 + (lane & 15)];
 #pragma unroll
             for (int r = 0; r < 4; r++) {
-                float v = hs[mi][r];
-#pragma unroll
-                for (int off = 1; off < 16; off <<= 1) v += __shfl_xor(v, off);
-                if ((lane & 15) == 0) red[wave * BM + mi * 16 + lrow + r] = v;
+                const int row = lrow + r;
+                if (row < c.rows) {
+                    const float g = acc[2 * pr][r] * sg;
+                    const float u = acc[2 * pr + 1][r] * su;
+                    a.H[(size_t)(c.tl.row0 + row) * a.ldh + col] = to_bf16(g / (1.0f + __expf(-g)) * u);
+                }
             }
-        __syncthreads();
-        if ((int)threadIdx.x < BM && (int)threadIdx.x < c.rows) {
-            const int row = threadIdx.x;
-            const float v = red[row] + red[BM + row] + red[2 * BM + row] + red[3 * BM + row];
-            a.hsum[(size_t)(c.tl.row0 + row) * (a.ldh / 128) + c.n0 / 256] = -ZC * v;
         }
     } else {
+        float sn[NB];
 #pragma unroll
-        for (int mi = 0; mi < MI; mi++)
+        for (int nb = 0; nb < NB; nb++)
+            sn[nb] = CF::kGroup ? 1.0f : c.ew.p2[c.n0 + 64 * wave + 16 * nb + (lane & 15)];
 #pragma unroll
-            for (int r = 0; r < 4; r++) {
-                const int row = mi * 16 + lrow + r;
-                if (row >= c.rows) continue;
-                const int gr = c.tl.row0 + row;
-                const float wt = gr < a.P ? a.wpair[a.perm[gr]] : 1.0f;
+        for (int r = 0; r < 4; r++) {
+            const int row = lrow + r;
+            if (row >= c.rows) continue;
+            const int gr = c.tl.row0 + row;
+            const float wt = gr < a.P ? a.wpair[a.perm[gr]] : 1.0f;
 #pragma unroll
-                for (int nb = 0; nb < 4; nb++) {
-                    const int n = c.n0 + 64 * wave + 16 * nb + (lane & 15);
-                    a.O[(size_t)gr * a.d + n] = acc[mi][nb][r] * wt;
-                }
+            for (int nb = 0; nb < NB; nb++) {
+                const int n = c.n0 + 64 * wave + 16 * nb + (lane & 15);
+                a.O[(size_t)gr * a.d + n] = acc[nb][r] * sn[nb] * wt;
             }
+        }
     }
 }
 
@@ -1069,7 +1318,8 @@ __global__ __launch_bounds__(256) void k_gemm_c(GemmArgs a) {
 __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ O, const int32_t *__restrict__ inv, int T,
                                                  int d, int k, int P, int n_shared, uint16_t *__restrict__ y) {
     const int t = blockIdx.x;
-    for (int c4 = threadIdx.x; c4 < d / 4; c4 += 256) {
+    const int c4 = blockIdx.y * 256 + threadIdx.x;   // one 4-column chunk per thread
+    if (c4 < d / 4) {
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
         const int nrows = k + n_shared;
         for (int j = 0; j < nrows; j++) {
@@ -1103,6 +1353,13 @@ hipError_t launch_router_bf16(const uint16_t *x, const uint16_t *wr, const float
     return hipGetLastError();
 }
 
+hipError_t launch_router_small(const uint16_t *x, const uint16_t *wr, const float *bias, float *logits, int T, int d,
+                               int E, hipStream_t s) {
+    dim3 grid((T + 15) / 16, (E + 15) / 16);
+    hipLaunchKernelGGL(k_router_small, grid, dim3(256), 0, s, x, wr, bias, logits, T, d, E);
+    return hipGetLastError();
+}
+
 hipError_t launch_router_f32(const uint16_t *x, const float *wr, const float *bias, float *logits, int T, int d, int E,
                              hipStream_t s) {
     const long n = (long)T * E;
@@ -1122,6 +1379,22 @@ hipError_t launch_topk(const float *logits, int T, int E, int k, int renorm, int
         hipLaunchKernelGGL(k_topk<8>, grid, dim3(256), 0, s, logits, T, E, k, renorm, idx, w);
     else
         hipLaunchKernelGGL(k_topk<16>, grid, dim3(256), 0, s, logits, T, E, k, renorm, idx, w);
+    return hipGetLastError();
+}
+
+hipError_t launch_route_small(const float *logits, int T, int E, int k, int renorm, int n_shared, int bm,
+                              int32_t *idx, float *w, int32_t *counts, int32_t *offsets, Tile *tiles,
+                              int32_t *num_tiles, int32_t *perm, int32_t *inv, hipStream_t s) {
+    if (T > kSmallRouteMaxT || E > kSmallRouteMaxE) return hipErrorInvalidValue;
+    if (E <= 64)
+        hipLaunchKernelGGL(k_route_small<1>, dim3(1), dim3(1024), 0, s, logits, T, E, k, renorm, n_shared, bm, idx, w,
+                           counts, offsets, tiles, num_tiles, perm, inv);
+    else if (E <= 128)
+        hipLaunchKernelGGL(k_route_small<2>, dim3(1), dim3(1024), 0, s, logits, T, E, k, renorm, n_shared, bm, idx, w,
+                           counts, offsets, tiles, num_tiles, perm, inv);
+    else
+        hipLaunchKernelGGL(k_route_small<4>, dim3(1), dim3(1024), 0, s, logits, T, E, k, renorm, n_shared, bm, idx, w,
+                           counts, offsets, tiles, num_tiles, perm, inv);
     return hipGetLastError();
 }
 
@@ -1147,13 +1420,13 @@ hipError_t launch_dispatch_scatter(const int32_t *idx, int P, int E, const int32
     return hipGetLastError();
 }
 
-template <int MODE, int MI>
-static hipError_t launch_gemm_df(int df, dim3 grid, const GemmArgs &a, hipStream_t s) {
+template <int MODE>
+static hipError_t launch_gemm_dec(int df, dim3 grid, const GemmArgs &a, hipStream_t s) {
     switch (df) {
-    case DF_INT8: hipLaunchKernelGGL((k_gemm_c<DF_INT8, MODE, MI>), grid, dim3(256), 0, s, a); break;
-    case DF_I4ASYM: hipLaunchKernelGGL((k_gemm_g<DF_I4ASYM, MODE, MI>), grid, dim3(256), 0, s, a); break;
-    case DF_I4SYM: hipLaunchKernelGGL((k_gemm_g<DF_I4SYM, MODE, MI>), grid, dim3(256), 0, s, a); break;
-    case DF_FP8: hipLaunchKernelGGL((k_gemm_c<DF_FP8, MODE, MI>), grid, dim3(256), 0, s, a); break;
+    case DF_INT8: hipLaunchKernelGGL((k_gemm_dec<DF_INT8, MODE>), grid, dim3(256), 0, s, a); break;
+    case DF_I4ASYM: hipLaunchKernelGGL((k_gemm_dec<DF_I4ASYM, MODE>), grid, dim3(256), 0, s, a); break;
+    case DF_I4SYM: hipLaunchKernelGGL((k_gemm_dec<DF_I4SYM, MODE>), grid, dim3(256), 0, s, a); break;
+    case DF_FP8: hipLaunchKernelGGL((k_gemm_dec<DF_FP8, MODE>), grid, dim3(256), 0, s, a); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -1187,12 +1460,15 @@ static hipError_t launch_gemm(int df, int bm, int max_tiles, int maxN, const Gem
         return hipGetLastError();
     }
     dim3 grid(a.n_tiles, max_tiles);
-    switch (bm) {
-    case 16: return launch_gemm_df<MODE, 1>(df, grid, a, s);
-    case 64: return launch_gemm_df<MODE, 4>(df, grid, a, s);
-    case 128: return launch_gemm_df<MODE, 8>(df, grid, a, s);
+    if (bm == 16) return launch_gemm_dec<MODE>(df, grid, a, s);
+    // per-channel formats, 64-row tiles
+    if (bm != 64) return hipErrorInvalidValue;
+    switch (df) {
+    case DF_INT8: hipLaunchKernelGGL((k_gemm_c<DF_INT8, MODE, 4>), grid, dim3(256), 0, s, a); break;
+    case DF_FP8: hipLaunchKernelGGL((k_gemm_c<DF_FP8, MODE, 4>), grid, dim3(256), 0, s, a); break;
     default: return hipErrorInvalidValue;
     }
+    return hipGetLastError();
 }
 
 hipError_t launch_gemm13(int df, int bm, const GemmArgs &a, int max_tiles, int maxN13, hipStream_t s) {
@@ -1210,7 +1486,7 @@ hipError_t launch_xsum(const uint16_t *x, int T, int d, float scale, float *xsum
 
 hipError_t launch_combine(const float *O, const int32_t *inv, int T, int d, int k, int P, int n_shared,
                           uint16_t *y, hipStream_t s) {
-    hipLaunchKernelGGL(k_combine, dim3(T), dim3(256), 0, s, O, inv, T, d, k, P, n_shared, y);
+    hipLaunchKernelGGL(k_combine, dim3(T, (d / 4 + 255) / 256), dim3(256), 0, s, O, inv, T, d, k, P, n_shared, y);
     return hipGetLastError();
 }
 

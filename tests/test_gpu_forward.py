@@ -66,6 +66,16 @@ def test_forward_tile_shapes(oracle_mod, fmt, T, E, k):
     run_and_check(oracle_mod, small(fmt, T=T, E=E, k=k, d=256, F=384), seed=T + E, tag=f"{fmt} T={T} E={E} k={k}")
 
 
+@pytest.mark.parametrize("T,E,k,fmt", [(64, 256, 8, "int4_sym_g128"), (64, 256, 8, "fp8e4m3_ch"),
+                                        (8, 300, 6, "int4_asym_g128"), (3, 16, 16, "int4_sym_g128")])
+def test_forward_small_batch_router_limits(oracle_mod, T, E, k, fmt):
+    """Small batches route in one launch up to 64 tokens and 256 experts; past
+    256 experts the separate router / top-k / dispatch kernels take over; k = E
+    selects every expert."""
+    cfg = small(fmt, T=T, E=E, k=k, d=512, F=256, bias=True)
+    run_and_check(oracle_mod, cfg, seed=T * E + k, tag=f"small-batch T={T} E={E} k={k} {fmt}")
+
+
 @pytest.mark.parametrize("fmt", ["int3_sym_g128", "int8_sym_ch", "fp8e4m3_ch"])
 def test_forward_shared_experts_and_bias(oracle_mod, fmt):
     cfg = small(fmt, T=257, E=12, k=3, S=2, Fs=384, bias=True)
