@@ -60,7 +60,8 @@ struct qmoe_ctx {
     uint8_t *arena = nullptr;
     size_t arena_bytes = 0;
     std::vector<MatInfo> m13, m2;   // per expert (E + S)
-    ExpertW *d_experts = nullptr;
+    ExpertW ex0[2] = {};            // routed expert 0, shared expert 0
+    int64_t ex_stride[2] = {0, 0};  // byte stride between consecutive experts of each group
     void *router_w = nullptr;       // bf16 [E][d] or fp32 [E][d]
     float *router_b = nullptr;
     // workspace
@@ -389,9 +390,26 @@ int qmoe_pack_experts(const qmoe_config *cfg, const float *const *w_gate, const 
         w.zc2 = b.zc_off ? (const uint16_t *)(c->arena + b.zc_off) : nullptr;
         w.F = i < c->E ? c->F : c->Fs;
     }
-    rc = dalloc(c, (void **)&c->d_experts, sizeof(ExpertW) * nexp);
-    if (!rc && hipMemcpy(c->d_experts, hexp.data(), sizeof(ExpertW) * nexp, hipMemcpyHostToDevice) != hipSuccess)
-        rc = fail(QMOE_EHIP, "upload of expert table failed");
+    // uniform strides of the routed and of the shared experts in the arena
+    for (int grp = 0; grp < 2 && !rc; grp++) {
+        const int first = grp == 0 ? 0 : c->E, count = grp == 0 ? c->E : c->S;
+        if (count == 0) continue;
+        c->ex0[grp] = hexp[first];
+        c->ex_stride[grp] = count > 1 ? (int64_t)(c->m13[first + 1].codes_off - c->m13[first].codes_off) : 0;
+        for (int i = 1; i < count && !rc; i++) {
+            const int64_t off = c->ex_stride[grp] * i;
+            const MatInfo &a0 = c->m13[first], &b0 = c->m2[first], &a = c->m13[first + i], &b = c->m2[first + i];
+            const size_t z0[10] = {a0.codes_off, a0.gs_off, a0.gz_off, a0.ps_off, a0.zc_off,
+                                   b0.codes_off, b0.gs_off, b0.gz_off, b0.ps_off, b0.zc_off};
+            const size_t zi[10] = {a.codes_off, a.gs_off, a.gz_off, a.ps_off, a.zc_off,
+                                   b.codes_off, b.gs_off, b.gz_off, b.ps_off, b.zc_off};
+            // fields 0 and 5 (codes) are always present (offset 0 is valid there);
+            // for the others offset 0 means "absent"
+            for (int f = 0; f < 10; f++)
+                if ((f % 5 && (z0[f] == 0) != (zi[f] == 0)) || ((f % 5 == 0 || z0[f]) && (int64_t)(zi[f] - z0[f]) != off))
+                    rc = fail(QMOE_EHIP, "internal: expert %d is not uniformly strided in the arena", first + i);
+        }
+    }
 
     // Router weight and bias.
     const size_t wr_bytes = (size_t)c->E * c->d * (cfg->router_fp32 ? 4 : 2);
@@ -497,7 +515,10 @@ int qmoe_forward(qmoe_ctx *c, const uint16_t *x, int32_t T, uint16_t *y, qmoe_ro
     }
 
     GemmArgs a{};
-    a.experts = c->d_experts;
+    a.ex0[0] = c->ex0[0];
+    a.ex0[1] = c->ex0[1];
+    a.ex_stride[0] = c->ex_stride[0];
+    a.ex_stride[1] = c->ex_stride[1];
     a.tiles = c->tiles;
     a.num_tiles = c->num_tiles;
     a.perm = c->perm;

@@ -67,7 +67,7 @@ inline bool is_group_wformat(int wformat) {
 }
 inline int block_bytes(int df) { return (df == DF_INT8 || df == DF_FP8) ? 2048 : 1024; }
 
-// Per-expert device pointers (one entry per routed expert, then per shared expert).
+// Device pointers of one expert's packed matrices.
 struct ExpertW {
     const uint8_t *c13;   // W13 codes
     const uint16_t *s13;  // W13 group scales (fp16 bits) or nullptr
@@ -144,7 +144,11 @@ hipError_t launch_route_small(const float *logits, int T, int E, int k, int reno
                               int32_t *num_tiles, int32_t *perm, int32_t *inv, hipStream_t s);
 
 struct GemmArgs {
-    const ExpertW *experts;
+    // Expert pointers without a table lookup: expert e < E is ex0[0] advanced
+    // by e * ex_stride[0] bytes (routed experts are laid out uniformly in the
+    // arena); shared expert E + i is ex0[1] advanced by i * ex_stride[1].
+    ExpertW ex0[2];
+    int64_t ex_stride[2];
     const Tile *tiles;
     const int32_t *num_tiles;
     const int32_t *perm;     // task list (pair id per routed row)

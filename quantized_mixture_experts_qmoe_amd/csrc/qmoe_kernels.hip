@@ -657,6 +657,27 @@ __device__ __forceinline__ bf16x8 codes8_to_bf16<DF_FP8>(uint32_t d0, uint32_t d
 // owns 64 columns = four 16-row packed blocks, so each packed weight is
 // converted by exactly one wave of the workgroup.
 
+// Pointers of expert e from the kernel arguments (no dependent global load).
+__device__ __forceinline__ ExpertW expert_at(const GemmArgs &a, int e) {
+    const int sh = e >= a.E;
+    const ExpertW &b = a.ex0[sh];
+    const int64_t off = a.ex_stride[sh] * (int64_t)(sh ? e - a.E : e);
+    auto adv = [off](auto *p) { return p ? (decltype(p))((const uint8_t *)p + off) : p; };
+    ExpertW w;
+    w.c13 = adv(b.c13);
+    w.s13 = adv(b.s13);
+    w.z13 = adv(b.z13);
+    w.p13 = adv(b.p13);
+    w.zc13 = adv(b.zc13);
+    w.c2 = adv(b.c2);
+    w.s2 = adv(b.s2);
+    w.z2 = adv(b.z2);
+    w.p2 = adv(b.p2);
+    w.zc2 = adv(b.zc2);
+    w.F = b.F;
+    return w;
+}
+
 struct TileCtx {
     Tile tl;
     ExpertW ew;
@@ -665,9 +686,10 @@ struct TileCtx {
 
 template <int MODE>
 __device__ __forceinline__ bool tile_setup(const GemmArgs &a, TileCtx &c) {
-    if ((int)blockIdx.y >= *a.num_tiles) return false;
+    const int ntiles = *a.num_tiles;   // issued together with the tile load
     c.tl = a.tiles[blockIdx.y];
-    c.ew = a.experts[c.tl.e];
+    if ((int)blockIdx.y >= ntiles) return false;
+    c.ew = expert_at(a, c.tl.e);
     c.N = MODE == 0 ? 2 * c.ew.F : a.d;
     c.K = MODE == 0 ? a.d : c.ew.F;
     c.n0 = blockIdx.x * 256;
@@ -689,6 +711,7 @@ struct GroupConst {
 };
 
 // ---- decode-shaped batches: tiles of at most 16 rows ----------------------
+constexpr int kDecodeBlocksPerWave = 4;
 //
 // Here the packed weights are the whole cost, so the kernel is built to keep
 // HBM busy. Workgroup = 4 waves over one tile and 256 columns of B's N
@@ -703,14 +726,18 @@ template <int DF>
 struct DecodeCfg {
     static constexpr bool kGroup = DF == DF_I4SYM || DF == DF_I4ASYM;
     static constexpr int kWords = kGroup ? 1 : 2;   // 16-byte words per lane per block and K block
-    static constexpr int kDepth = kGroup ? 4 : 2;   // K blocks in flight per wave
+    static constexpr int kDepth = 1;                // K blocks in flight per wave, beyond the one computed
+    static constexpr int kNB = kDecodeBlocksPerWave;
+    static constexpr int kKC = 2;                   // K blocks per staged chunk
 };
 
 template <int DF, int MODE>
 __global__ __launch_bounds__(256) void k_gemm_dec(GemmArgs a) {
     using CF = DecodeCfg<DF>;
-    constexpr int NB = 4;                  // 16-row blocks per wave
-    constexpr int KC = 4;                  // K blocks per staged chunk
+    constexpr int NB = CF::kNB;            // 16-row blocks per wave
+    constexpr int KC = CF::kKC;            // K blocks per staged chunk
+    constexpr int WG_COLS = 4 * NB * 16;   // columns of B's N dimension per workgroup
+    static_assert(NB % 2 == 0 && 256 % WG_COLS == 0, "a wave owns whole gate/up pairs; N % 256 == 0 covers the grid");
     constexpr int PITCH = KC * 128 + 8;    // bf16 per LDS row: rows 16 bytes apart in the bank space
     constexpr float ZC = GroupConst<DF>::ZC;
     static_assert(KC % CF::kDepth == 0, "the ring slot must be static inside a chunk");
@@ -718,7 +745,15 @@ __global__ __launch_bounds__(256) void k_gemm_dec(GemmArgs a) {
     __shared__ __attribute__((aligned(16))) float Rs[2][KC][16];
 
     TileCtx c;
-    if (!tile_setup<MODE>(a, c)) return;
+    const int ntiles = *a.num_tiles;   // issued together with the tile load
+    c.tl = a.tiles[blockIdx.y];
+    if ((int)blockIdx.y >= ntiles) return;
+    c.ew = expert_at(a, c.tl.e);
+    c.N = MODE == 0 ? 2 * c.ew.F : a.d;
+    c.K = MODE == 0 ? a.d : c.ew.F;
+    c.n0 = blockIdx.x * WG_COLS;
+    c.rows = c.tl.row_end - c.tl.row0;
+    if (c.n0 >= c.N) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int KB = c.K / 128;
     const int NC = (KB + KC - 1) / KC;
@@ -726,9 +761,13 @@ __global__ __launch_bounds__(256) void k_gemm_dec(GemmArgs a) {
     // Every path through the K loop issues the same loads (addresses clamped to
     // valid memory, unused data zeroed by selects), so the compiler's wait
     // counts stay exact and the ring keeps its depth.
-    // Staging role: row tid/16, 32 consecutive k at 32 * (tid % 16) of the
+    // Staging role: row tid/16, SPT consecutive k at SPT * (tid % 16) of the
     // chunk; rows past the tile read its first row and stage zeros.
-    const int sr = tid >> 4, sk = (tid & 15) * 32;
+    constexpr int SPT = KC * 128 / 16;     // k per staging thread
+    constexpr int NV = SPT / 8;            // 16-byte words per staging thread
+    constexpr int TPG = 128 / SPT;         // staging threads per 128-wide group
+    static_assert(SPT % 8 == 0 && TPG >= 1, "chunk size");
+    const int sr = tid >> 4, sk = (tid & 15) * SPT;
     const bool srow = sr < c.rows;
     const uint16_t *asrc;
     {
@@ -740,18 +779,18 @@ __global__ __launch_bounds__(256) void k_gemm_dec(GemmArgs a) {
             asrc = a.H + (size_t)gr * a.ldh;
         }
     }
-    uint4 av[4];
+    uint4 av[NV];
     bool aok = false;
     auto stage_load = [&](int ch) {
         const int k0 = ch * (KC * 128) + sk;
         aok = srow && k0 < c.K;
-        const int kc = min(k0, c.K - 32);
+        const int kc = min(k0, c.K - SPT);
 #pragma unroll
-        for (int i = 0; i < 4; i++) av[i] = gload16(asrc + kc + 8 * i);
+        for (int i = 0; i < NV; i++) av[i] = gload16(asrc + kc + 8 * i);
     };
     auto stage_store = [&](int buf) {
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
+        for (int i = 0; i < NV; i++) {
             av[i].x = aok ? av[i].x : 0u;
             av[i].y = aok ? av[i].y : 0u;
             av[i].z = aok ? av[i].z : 0u;
@@ -761,15 +800,15 @@ __global__ __launch_bounds__(256) void k_gemm_dec(GemmArgs a) {
         if (CF::kGroup) {
             float sum = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
+            for (int i = 0; i < NV; i++) {
                 const uint32_t u[4] = {av[i].x, av[i].y, av[i].z, av[i].w};
 #pragma unroll
                 for (int j = 0; j < 4; j++) sum += bf16f(u[j] & 0xFFFFu) + bf16f(u[j] >> 16);
             }
-            // the four threads of a 128-wide group are consecutive lanes
-            sum += __shfl_xor(sum, 1);
-            sum += __shfl_xor(sum, 2);
-            if ((tid & 3) == 0) Rs[buf][(tid & 15) >> 2][sr] = -ZC * sum;
+            // the TPG threads of a 128-wide group are consecutive lanes
+#pragma unroll
+            for (int off = 1; off < TPG; off <<= 1) sum += __shfl_xor(sum, off);
+            if ((tid & (TPG - 1)) == 0) Rs[buf][(tid & 15) / TPG][sr] = -ZC * sum;
         }
     };
 
@@ -874,7 +913,7 @@ __global__ __launch_bounds__(256) void k_gemm_dec(GemmArgs a) {
     const int lrow = (lane >> 4) * 4;
     if (MODE == 0) {
 #pragma unroll
-        for (int pr = 0; pr < 2; pr++) {
+        for (int pr = 0; pr < NB / 2; pr++) {
             const int ibg = ib0 + 2 * pr;
             const int col = (ibg >> 1) * 16 + (lane & 15);
             const float sg = CF::kGroup ? 1.0f : c.ew.p13[ibg * 16 + (lane & 15)];
@@ -893,7 +932,7 @@ __global__ __launch_bounds__(256) void k_gemm_dec(GemmArgs a) {
         float sn[NB];
 #pragma unroll
         for (int nb = 0; nb < NB; nb++)
-            sn[nb] = CF::kGroup ? 1.0f : c.ew.p2[c.n0 + 64 * wave + 16 * nb + (lane & 15)];
+            sn[nb] = CF::kGroup ? 1.0f : c.ew.p2[c.n0 + NB * 16 * wave + 16 * nb + (lane & 15)];
 #pragma unroll
         for (int r = 0; r < 4; r++) {
             const int row = lrow + r;
@@ -902,7 +941,7 @@ __global__ __launch_bounds__(256) void k_gemm_dec(GemmArgs a) {
             const float wt = gr < a.P ? a.wpair[a.perm[gr]] : 1.0f;
 #pragma unroll
             for (int nb = 0; nb < NB; nb++) {
-                const int n = c.n0 + 64 * wave + 16 * nb + (lane & 15);
+                const int n = c.n0 + NB * 16 * wave + 16 * nb + (lane & 15);
                 a.O[(size_t)gr * a.d + n] = acc[nb][r] * sn[nb] * wt;
             }
         }
@@ -977,7 +1016,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void k_gemm_gpf(GemmArgs a) {
     int tile_id, ntile;
     if (!map_work(blockIdx.x, *a.num_tiles, a.n_tiles, tile_id, ntile)) return;
     const Tile tl = a.tiles[tile_id];
-    const ExpertW ew = a.experts[tl.e];
+    const ExpertW ew = expert_at(a, tl.e);
     const int N = MODE == 0 ? 2 * ew.F : a.d;
     const int K = MODE == 0 ? a.d : ew.F;
     const int n0 = ntile * NTILE;
@@ -1459,8 +1498,11 @@ static hipError_t launch_gemm(int df, int bm, int max_tiles, int maxN, const Gem
         }
         return hipGetLastError();
     }
+    if (bm == 16) {
+        const int cols = 4 * kDecodeBlocksPerWave * 16;
+        return launch_gemm_dec<MODE>(df, dim3((maxN + cols - 1) / cols, max_tiles), a, s);
+    }
     dim3 grid(a.n_tiles, max_tiles);
-    if (bm == 16) return launch_gemm_dec<MODE>(df, grid, a, s);
     // per-channel formats, 64-row tiles
     if (bm != 64) return hipErrorInvalidValue;
     switch (df) {
