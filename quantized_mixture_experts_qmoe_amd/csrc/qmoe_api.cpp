@@ -65,7 +65,7 @@ struct qmoe_ctx {
     void *router_w = nullptr;       // bf16 [E][d] or fp32 [E][d]
     float *router_b = nullptr;
     // workspace
-    float *logits = nullptr, *wpair = nullptr;
+    float *logits = nullptr, *wpair = nullptr, *wrow = nullptr;
     int32_t *idx = nullptr, *chunk_counts = nullptr, *chunk_base = nullptr, *counts = nullptr, *offsets = nullptr;
     int32_t *perm = nullptr, *inv = nullptr, *num_tiles = nullptr;
     Tile *tiles = nullptr;
@@ -256,7 +256,7 @@ int run_route(qmoe_ctx *c, const float *logits, int T, int bm, int n_shared, hip
     if (T <= kSmallRouteMaxT && c->E <= kSmallRouteMaxE)
         return timed(c, K_TOPKD, s, [&] {
             return launch_route_small(logits, T, c->E, c->k, c->cfg.renormalize, n_shared, bm, c->idx, c->wpair,
-                                      c->counts, c->offsets, c->tiles, c->num_tiles, c->perm, c->inv, s);
+                                      c->counts, c->offsets, c->tiles, c->num_tiles, c->perm, c->inv, c->wrow, s);
         });
     const int nchunks = (P + kDispatchChunk - 1) / kDispatchChunk;
     int rc = timed(c, K_TOPK, s, [&] { return launch_topk(logits, T, c->E, c->k, c->cfg.renormalize, c->idx, c->wpair, s); });
@@ -269,7 +269,7 @@ int run_route(qmoe_ctx *c, const float *logits, int T, int bm, int n_shared, hip
     });
     if (rc) return rc;
     return timed(c, K_DSCATTER, s,
-                 [&] { return launch_dispatch_scatter(c->idx, P, c->E, c->chunk_base, c->perm, c->inv, s); });
+                 [&] { return launch_dispatch_scatter(c->idx, c->wpair, P, c->E, c->chunk_base, c->perm, c->inv, c->wrow, s); });
 }
 
 int copy_out(void *dst, const void *src, size_t bytes, hipStream_t s) {
@@ -430,6 +430,7 @@ int qmoe_pack_experts(const qmoe_config *cfg, const float *const *w_gate, const 
     c->tiles_cap = (size_t)max_tiles_for(c, c->maxT, 16) + 16;
     if (!rc) rc = dalloc(c, (void **)&c->logits, T * c->E * 4);
     if (!rc) rc = dalloc(c, (void **)&c->wpair, P * 4);
+    if (!rc) rc = dalloc(c, (void **)&c->wrow, P * 4);
     if (!rc) rc = dalloc(c, (void **)&c->idx, P * 4);
     if (!rc) rc = dalloc(c, (void **)&c->chunk_counts, nchunks * c->E * 4);
     if (!rc) rc = dalloc(c, (void **)&c->chunk_base, nchunks * c->E * 4);
@@ -522,7 +523,7 @@ int qmoe_forward(qmoe_ctx *c, const uint16_t *x, int32_t T, uint16_t *y, qmoe_ro
     a.tiles = c->tiles;
     a.num_tiles = c->num_tiles;
     a.perm = c->perm;
-    a.wpair = c->wpair;
+    a.wrow = c->wrow;
     a.x = x;
     a.xsum = c->xsum;
     a.H = c->H;

@@ -136,12 +136,13 @@ hipError_t launch_dispatch_count(const int32_t *idx, int P, int E, int32_t *chun
 hipError_t launch_dispatch_scan(const int32_t *chunk_counts, int nchunks, int E, int P, int T, int n_shared, int bm,
                                 int32_t *chunk_base, int32_t *counts, int32_t *offsets, Tile *tiles,
                                 int32_t *num_tiles, hipStream_t s);
-hipError_t launch_dispatch_scatter(const int32_t *idx, int P, int E, const int32_t *chunk_base, int32_t *perm,
-                                   int32_t *inv, hipStream_t s);
+// Also writes wrow[row] = w[pair of row] (the mixing weight in row order).
+hipError_t launch_dispatch_scatter(const int32_t *idx, const float *w, int P, int E, const int32_t *chunk_base,
+                                   int32_t *perm, int32_t *inv, float *wrow, hipStream_t s);
 // Top-k and the whole dispatch in one workgroup (T <= kSmallRouteMaxT, E <= kSmallRouteMaxE).
 hipError_t launch_route_small(const float *logits, int T, int E, int k, int renorm, int n_shared, int bm,
                               int32_t *idx, float *w, int32_t *counts, int32_t *offsets, Tile *tiles,
-                              int32_t *num_tiles, int32_t *perm, int32_t *inv, hipStream_t s);
+                              int32_t *num_tiles, int32_t *perm, int32_t *inv, float *wrow, hipStream_t s);
 
 struct GemmArgs {
     // Expert pointers without a table lookup: expert e < E is ex0[0] advanced
@@ -152,7 +153,7 @@ struct GemmArgs {
     const Tile *tiles;
     const int32_t *num_tiles;
     const int32_t *perm;     // task list (pair id per routed row)
-    const float *wpair;      // mixing weight per pair [P]
+    const float *wrow;       // mixing weight per routed row [P] (row order)
     const uint16_t *x;       // [T][d] bf16 (gate/up input)
     const float *xsum;       // [T][d/128] group sums of x
     uint16_t *H;             // [rows][ldh] bf16 intermediate

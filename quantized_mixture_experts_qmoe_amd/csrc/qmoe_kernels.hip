@@ -371,57 +371,68 @@ __device__ int block_exclusive_scan_1024(int v, int *wsum) {
     return r;
 }
 
-// One workgroup of 1024 threads. Thread i owns experts [i*per, (i+1)*per).
+// One workgroup of 1024 threads; G = 1024 / next_pow2(E) threads per expert
+// (thread e * G + g), each owning a contiguous range of chunks. One exclusive
+// scan of the range sums in (expert, range) order gives every range's first
+// row directly -- the expert's offset plus the rows of its earlier ranges --
+// and the experts' offsets and counts with it; a second scan places the tiles.
 __global__ __launch_bounds__(1024) void k_dispatch_scan(const int32_t *__restrict__ cc, int nchunks, int E, int P,
                                                         int T, int n_shared, int bm, int32_t *__restrict__ chunk_base,
                                                         int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
                                                         Tile *__restrict__ tiles, int32_t *__restrict__ num_tiles) {
     __shared__ int wsum[32];
-    const int per = (E + 1023) / 1024;
-    const int e_begin = threadIdx.x * per;
-    int tot_local = 0, tiles_local = 0;
-    for (int i = 0; i < per; i++) {
-        const int e = e_begin + i;
-        if (e >= E) break;
-        int s = 0;
-        for (int b = 0; b < nchunks; b++) s += cc[(size_t)b * E + e];
-        counts[e] = s;
-        tot_local += s;
-        tiles_local += (s + bm - 1) / bm;
+    __shared__ int ebase[1025];
+    int E2 = 1;
+    while (E2 < E) E2 <<= 1;
+    const int G = 1024 / E2;
+    const int tid = threadIdx.x, e = tid / G, g = tid % G;
+    const bool live = e < E;
+    const int b0 = (int)((long)nchunks * g / G), b1 = (int)((long)nchunks * (g + 1) / G);
+    int s = 0;
+    if (live) {
+        int b = b0;
+        for (; b + 4 <= b1; b += 4) {
+            const int v0 = cc[(size_t)b * E + e], v1 = cc[(size_t)(b + 1) * E + e];
+            const int v2 = cc[(size_t)(b + 2) * E + e], v3 = cc[(size_t)(b + 3) * E + e];
+            s += (v0 + v1) + (v2 + v3);
+        }
+        for (; b < b1; b++) s += cc[(size_t)b * E + e];
     }
-    const int row_base = block_exclusive_scan_1024(tot_local, wsum);
-    const int tile_base = block_exclusive_scan_1024(tiles_local, wsum);
-    int row = row_base, tile = tile_base;
-    for (int i = 0; i < per; i++) {
-        const int e = e_begin + i;
-        if (e >= E) break;
-        const int c = counts[e];
-        offsets[e] = row;
-        int run = row;
-        for (int b = 0; b < nchunks; b++) {
+    const int first_row = block_exclusive_scan_1024(s, wsum);
+    if (live && g == 0) ebase[e] = first_row;
+    if (tid == 0) ebase[E] = P;
+    __syncthreads();
+    const int cnt = (live && g == 0) ? ebase[e + 1] - first_row : 0;
+    const int ntile = (cnt + bm - 1) / bm;
+    const int tile_base = block_exclusive_scan_1024(ntile, wsum);
+    if (live && g == 0) {
+        counts[e] = cnt;
+        offsets[e] = first_row;
+        for (int m = 0; m < cnt; m += bm) tiles[tile_base + m / bm] = Tile{e, first_row + m, first_row + cnt, 0};
+    }
+    if (live) {
+        int run = first_row;
+        for (int b = b0; b < b1; b++) {
             chunk_base[(size_t)b * E + e] = run;
             run += cc[(size_t)b * E + e];
         }
-        for (int m = 0; m < c; m += bm) tiles[tile++] = Tile{e, row + m, row + c, 0};
-        row += c;
     }
-    // the last thread holding experts knows the routed tile total
-    if (threadIdx.x == 1023) {
+    // the last expert's first thread knows the routed tile total
+    if (live && g == 0 && e == E - 1) {
         offsets[E] = P;
-        const int routed_tiles = tile_base + tiles_local;
-        int tcount = routed_tiles;
-        for (int s = 0; s < n_shared; s++)
-            for (int m = 0; m < T; m += bm)
-                tiles[tcount++] = Tile{E + s, P + s * T + m, P + (s + 1) * T, 0};
+        int tcount = tile_base + ntile;
+        for (int sh = 0; sh < n_shared; sh++)
+            for (int m = 0; m < T; m += bm) tiles[tcount++] = Tile{E + sh, P + sh * T + m, P + (sh + 1) * T, 0};
         *num_tiles = tcount;
     }
 }
 
 // Stable scatter: ranks inside a chunk follow pair order. Each round takes 256
 // consecutive pairs; ranks inside a wave come from per-expert 64-bit lane masks.
-__global__ __launch_bounds__(256) void k_dispatch_scatter(const int32_t *__restrict__ idx, int P, int E,
-                                                          const int32_t *__restrict__ chunk_base,
-                                                          int32_t *__restrict__ perm, int32_t *__restrict__ inv) {
+__global__ __launch_bounds__(256) void k_dispatch_scatter(const int32_t *__restrict__ idx, const float *__restrict__ w,
+                                                          int P, int E, const int32_t *__restrict__ chunk_base,
+                                                          int32_t *__restrict__ perm, int32_t *__restrict__ inv,
+                                                          float *__restrict__ wrow) {
     extern __shared__ unsigned long long smem64[];
     unsigned long long *masks = smem64;                       // [4][E]
     int *running = reinterpret_cast<int *>(smem64 + 4 * E);  // [E]
@@ -435,6 +446,7 @@ __global__ __launch_bounds__(256) void k_dispatch_scatter(const int32_t *__restr
         const int p = blockIdx.x * kDispatchChunk + round * 256 + threadIdx.x;
         const bool valid = p < P;
         const int e = valid ? idx[p] : 0;
+        const float wp = valid ? w[p] : 0.0f;
         if (valid) atomicOr(&masks[wave * E + e], 1ull << lane);
         __syncthreads();
         if (valid) {
@@ -443,6 +455,7 @@ __global__ __launch_bounds__(256) void k_dispatch_scatter(const int32_t *__restr
             const int row = running[e] + rank;
             perm[row] = p;
             inv[p] = row;
+            wrow[row] = wp;
         }
         __syncthreads();
         for (int e2 = threadIdx.x; e2 < E; e2 += 256) {
@@ -459,6 +472,7 @@ __global__ __launch_bounds__(256) void k_dispatch_scatter(const int32_t *__restr
 // outputs as k_topk followed by the three dispatch kernels.
 struct RouteSmallSmem {
     int sidx[kSmallRouteMaxT * 64];
+    float sw[kSmallRouteMaxT * 64];
     unsigned long long masks[16][kSmallRouteMaxE];
     int base[kSmallRouteMaxE];
     int wsum[32];
@@ -469,7 +483,7 @@ __device__ void route_small_body(RouteSmallSmem &sm, const float *__restrict__ l
                                  int renorm, int n_shared, int bm, int32_t *__restrict__ idx, float *__restrict__ w,
                                  int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
                                  Tile *__restrict__ tiles, int32_t *__restrict__ num_tiles,
-                                 int32_t *__restrict__ perm, int32_t *__restrict__ inv) {
+                                 int32_t *__restrict__ perm, int32_t *__restrict__ inv, float *__restrict__ wrow) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int P = T * k;
     for (int e = tid; e < E; e += 1024) sm.base[e] = 0;
@@ -480,6 +494,7 @@ __device__ void route_small_body(RouteSmallSmem &sm, const float *__restrict__ l
                                       w + (size_t)t * k);
         if (e >= 0) {
             sm.sidx[t * k + lane] = e;
+            sm.sw[t * k + lane] = w[(size_t)t * k + lane];   // written by this lane above
             atomicAdd(&sm.base[e], 1);
         }
     }
@@ -516,6 +531,7 @@ __device__ void route_small_body(RouteSmallSmem &sm, const float *__restrict__ l
             const int row = sm.base[e] + rank;
             perm[row] = p;
             inv[p] = row;
+            wrow[row] = sm.sw[p];
         }
         __syncthreads();
         if (tid < E) {
@@ -536,10 +552,10 @@ __global__ __launch_bounds__(1024) void k_route_small(const float *__restrict__ 
                                                       float *__restrict__ w, int32_t *__restrict__ counts,
                                                       int32_t *__restrict__ offsets, Tile *__restrict__ tiles,
                                                       int32_t *__restrict__ num_tiles, int32_t *__restrict__ perm,
-                                                      int32_t *__restrict__ inv) {
+                                                      int32_t *__restrict__ inv, float *__restrict__ wrow) {
     __shared__ RouteSmallSmem sm;
     route_small_body<EPL>(sm, logits, T, E, k, renorm, n_shared, bm, idx, w, counts, offsets, tiles, num_tiles, perm,
-                          inv);
+                          inv, wrow);
 }
 
 // ---------------------------------------------------------------------------
@@ -938,7 +954,7 @@ __global__ __launch_bounds__(256) void k_gemm_dec(GemmArgs a) {
             const int row = lrow + r;
             if (row >= c.rows) continue;
             const int gr = c.tl.row0 + row;
-            const float wt = gr < a.P ? a.wpair[a.perm[gr]] : 1.0f;
+            const float wt = gr < a.P ? a.wrow[gr] : 1.0f;
 #pragma unroll
             for (int nb = 0; nb < NB; nb++) {
                 const int n = c.n0 + NB * 16 * wave + 16 * nb + (lane & 15);
@@ -946,6 +962,15 @@ __global__ __launch_bounds__(256) void k_gemm_dec(GemmArgs a) {
             }
         }
     }
+}
+
+// Expert outputs are written once and read once (by the combine).
+constexpr bool kStoreONT = false;
+__device__ __forceinline__ void store_o(float *p, float v) {
+    if (kStoreONT)
+        __builtin_nontemporal_store(v, p);
+    else
+        *p = v;
 }
 
 // ---- 64-row tiles (prefill): pipelined, XCD-aware -------------------------
@@ -1225,11 +1250,11 @@ __global__ __launch_bounds__(64 * NW, OCC) void k_gemm_gpf(GemmArgs a) {
                 const int row = mi * 16 + lrow + r;
                 if (row >= rows) continue;
                 const int gr = tl.row0 + row;
-                const float wt = gr < a.P ? a.wpair[a.perm[gr]] : 1.0f;
+                const float wt = gr < a.P ? a.wrow[gr] : 1.0f;
 #pragma unroll
                 for (int nb = 0; nb < 4; nb++) {
                     const int n = n0 + 64 * wave + 16 * nb + (lane & 15);
-                    if (wave_on) a.O[(size_t)gr * a.d + n] = acc[mi][nb][r] * wt;
+                    if (wave_on) store_o(a.O + (size_t)gr * a.d + n, acc[mi][nb][r] * wt);
                 }
             }
     }
@@ -1338,7 +1363,7 @@ __global__ __launch_bounds__(256) void k_gemm_c(GemmArgs a) {
                 const int row = mi * 16 + lrow + r;
                 if (row >= c.rows) continue;
                 const int gr = c.tl.row0 + row;
-                const float wt = gr < a.P ? a.wpair[a.perm[gr]] : 1.0f;
+                const float wt = gr < a.P ? a.wrow[gr] : 1.0f;
 #pragma unroll
                 for (int nb = 0; nb < 4; nb++) {
                     const int n = c.n0 + 64 * wave + 16 * nb + (lane & 15);
@@ -1353,25 +1378,58 @@ __global__ __launch_bounds__(256) void k_gemm_c(GemmArgs a) {
 // ---------------------------------------------------------------------------
 
 // y[t] = sum_j O[inv[t*k+j]] + sum_s O[P + s*T + t], summed in fp32 in slot
-// order, rounded once to bf16.
+// order, rounded once to bf16. CPT 4-column chunks per thread, 256 columns
+// apart; the rows are loaded eight at a time so that the loads overlap. O is
+// read exactly once: non-temporal loads keep it from displacing cached data.
+constexpr int kCombineCPT = 1;
+constexpr bool kCombineNT = true;
+__device__ __forceinline__ float4 load_o(const float *p) {
+    if (kCombineNT) {
+        const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
+        return make_float4(v[0], v[1], v[2], v[3]);
+    }
+    return *reinterpret_cast<const float4 *>(p);
+}
 __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ O, const int32_t *__restrict__ inv, int T,
                                                  int d, int k, int P, int n_shared, uint16_t *__restrict__ y) {
+    constexpr int CPT = kCombineCPT;
     const int t = blockIdx.x;
-    const int c4 = blockIdx.y * 256 + threadIdx.x;   // one 4-column chunk per thread
-    if (c4 < d / 4) {
-        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-        const int nrows = k + n_shared;
-        for (int j = 0; j < nrows; j++) {
-            const size_t row = j < k ? (size_t)inv[(size_t)t * k + j] : (size_t)P + (size_t)(j - k) * T + t;
-            const float4 v = *reinterpret_cast<const float4 *>(O + row * d + c4 * 4);
-            acc.x += v.x;
-            acc.y += v.y;
-            acc.z += v.z;
-            acc.w += v.w;
+    const int d4 = d / 4;
+    const int c0 = blockIdx.y * 256 * CPT + threadIdx.x;
+    const int nrows = k + n_shared;
+    float4 acc[CPT];
+#pragma unroll
+    for (int c = 0; c < CPT; c++) acc[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j0 = 0; j0 < nrows; j0 += 8) {
+        float4 v[8][CPT];
+#pragma unroll
+        for (int u = 0; u < 8; u++) {
+            const int j = j0 + u;
+            if (j < nrows) {
+                const size_t row = j < k ? (size_t)inv[(size_t)t * k + j] : (size_t)P + (size_t)(j - k) * T + t;
+#pragma unroll
+                for (int c = 0; c < CPT; c++)
+                    if (c0 + 256 * c < d4) v[u][c] = load_o(O + row * d + (c0 + 256 * c) * 4);
+            }
         }
+#pragma unroll
+        for (int u = 0; u < 8; u++)
+            if (j0 + u < nrows)
+#pragma unroll
+                for (int c = 0; c < CPT; c++) {
+                    acc[c].x += v[u][c].x;
+                    acc[c].y += v[u][c].y;
+                    acc[c].z += v[u][c].z;
+                    acc[c].w += v[u][c].w;
+                }
+    }
+#pragma unroll
+    for (int c = 0; c < CPT; c++) {
+        const int c4 = c0 + 256 * c;
+        if (c4 >= d4) continue;
         uint2 out;
-        out.x = (uint32_t)to_bf16(acc.x) | ((uint32_t)to_bf16(acc.y) << 16);
-        out.y = (uint32_t)to_bf16(acc.z) | ((uint32_t)to_bf16(acc.w) << 16);
+        out.x = (uint32_t)to_bf16(acc[c].x) | ((uint32_t)to_bf16(acc[c].y) << 16);
+        out.y = (uint32_t)to_bf16(acc[c].z) | ((uint32_t)to_bf16(acc[c].w) << 16);
         *reinterpret_cast<uint2 *>(y + (size_t)t * d + c4 * 4) = out;
     }
 }
@@ -1380,15 +1438,25 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ O, co
 // Launchers
 // ---------------------------------------------------------------------------
 
+// Expert tiles of 32 (16 when E <= 16: no idle half tile).
+template <int MT>
+static void launch_router_mt(const uint16_t *x, const uint16_t *wr, const float *bias, float *logits, float *xsum,
+                             float xscale, int T, int d, int E, hipStream_t s) {
+    const int gx = (T + 16 * MT - 1) / (16 * MT);
+    if (E > 16)
+        hipLaunchKernelGGL((k_router_bf16<MT, 2>), dim3(gx, (E + 31) / 32), dim3(256), 0, s, x, wr, bias, logits, xsum,
+                           xscale, T, d, E);
+    else
+        hipLaunchKernelGGL((k_router_bf16<MT, 1>), dim3(gx, 1), dim3(256), 0, s, x, wr, bias, logits, xsum, xscale,
+                           T, d, E);
+}
+
 hipError_t launch_router_bf16(const uint16_t *x, const uint16_t *wr, const float *bias, float *logits, float *xsum,
                               float xscale, int T, int d, int E, hipStream_t s) {
-    if (T >= 256) {
-        dim3 grid((T + 31) / 32, (E + 31) / 32);
-        hipLaunchKernelGGL((k_router_bf16<2, 2>), grid, dim3(256), 0, s, x, wr, bias, logits, xsum, xscale, T, d, E);
-    } else {
-        dim3 grid((T + 15) / 16, (E + 31) / 32);
-        hipLaunchKernelGGL((k_router_bf16<1, 2>), grid, dim3(256), 0, s, x, wr, bias, logits, xsum, xscale, T, d, E);
-    }
+    if (T >= 256)
+        launch_router_mt<2>(x, wr, bias, logits, xsum, xscale, T, d, E, s);
+    else
+        launch_router_mt<1>(x, wr, bias, logits, xsum, xscale, T, d, E, s);
     return hipGetLastError();
 }
 
@@ -1423,17 +1491,17 @@ hipError_t launch_topk(const float *logits, int T, int E, int k, int renorm, int
 
 hipError_t launch_route_small(const float *logits, int T, int E, int k, int renorm, int n_shared, int bm,
                               int32_t *idx, float *w, int32_t *counts, int32_t *offsets, Tile *tiles,
-                              int32_t *num_tiles, int32_t *perm, int32_t *inv, hipStream_t s) {
+                              int32_t *num_tiles, int32_t *perm, int32_t *inv, float *wrow, hipStream_t s) {
     if (T > kSmallRouteMaxT || E > kSmallRouteMaxE) return hipErrorInvalidValue;
     if (E <= 64)
         hipLaunchKernelGGL(k_route_small<1>, dim3(1), dim3(1024), 0, s, logits, T, E, k, renorm, n_shared, bm, idx, w,
-                           counts, offsets, tiles, num_tiles, perm, inv);
+                           counts, offsets, tiles, num_tiles, perm, inv, wrow);
     else if (E <= 128)
         hipLaunchKernelGGL(k_route_small<2>, dim3(1), dim3(1024), 0, s, logits, T, E, k, renorm, n_shared, bm, idx, w,
-                           counts, offsets, tiles, num_tiles, perm, inv);
+                           counts, offsets, tiles, num_tiles, perm, inv, wrow);
     else
         hipLaunchKernelGGL(k_route_small<4>, dim3(1), dim3(1024), 0, s, logits, T, E, k, renorm, n_shared, bm, idx, w,
-                           counts, offsets, tiles, num_tiles, perm, inv);
+                           counts, offsets, tiles, num_tiles, perm, inv, wrow);
     return hipGetLastError();
 }
 
@@ -1451,11 +1519,11 @@ hipError_t launch_dispatch_scan(const int32_t *chunk_counts, int nchunks, int E,
     return hipGetLastError();
 }
 
-hipError_t launch_dispatch_scatter(const int32_t *idx, int P, int E, const int32_t *chunk_base, int32_t *perm,
-                                   int32_t *inv, hipStream_t s) {
+hipError_t launch_dispatch_scatter(const int32_t *idx, const float *w, int P, int E, const int32_t *chunk_base,
+                                   int32_t *perm, int32_t *inv, float *wrow, hipStream_t s) {
     const int nchunks = (P + kDispatchChunk - 1) / kDispatchChunk;
     const size_t lds = (size_t)E * (4 * sizeof(unsigned long long) + sizeof(int));
-    hipLaunchKernelGGL(k_dispatch_scatter, dim3(nchunks), dim3(256), lds, s, idx, P, E, chunk_base, perm, inv);
+    hipLaunchKernelGGL(k_dispatch_scatter, dim3(nchunks), dim3(256), lds, s, idx, w, P, E, chunk_base, perm, inv, wrow);
     return hipGetLastError();
 }
 
@@ -1528,7 +1596,8 @@ hipError_t launch_xsum(const uint16_t *x, int T, int d, float scale, float *xsum
 
 hipError_t launch_combine(const float *O, const int32_t *inv, int T, int d, int k, int P, int n_shared,
                           uint16_t *y, hipStream_t s) {
-    hipLaunchKernelGGL(k_combine, dim3(T, (d / 4 + 255) / 256), dim3(256), 0, s, O, inv, T, d, k, P, n_shared, y);
+    hipLaunchKernelGGL(k_combine, dim3(T, (d / 4 + 256 * kCombineCPT - 1) / (256 * kCombineCPT)), dim3(256), 0, s, O, inv,
+                       T, d, k, P, n_shared, y);
     return hipGetLastError();
 }
 
