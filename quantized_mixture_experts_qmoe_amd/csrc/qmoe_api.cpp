@@ -85,7 +85,7 @@ struct qmoe_ctx {
     double tot_ms[QMOE_NUM_KERNELS] = {};
     int64_t launches[QMOE_NUM_KERNELS] = {};
     bool debug_sync = false;
-    int gemm_bm = 64;   // rows per M-tile of the prefill GEMMs (group formats): 64, 96 or 128
+    int gemm_bm = 64;   // rows per M-tile of the prefill GEMMs
 };
 
 namespace {
@@ -330,10 +330,6 @@ int qmoe_pack_experts(const qmoe_config *cfg, const float *const *w_gate, const 
     c->k = cfg->top_k;
     c->maxT = cfg->max_tokens;
     c->debug_sync = getenv("QMOE_DEBUG") != nullptr;
-    if (const char *bmenv = getenv("QMOE_PREFILL_TILE_ROWS")) {   // tuning knob: 64, 96 or 128
-        const int v = atoi(bmenv);
-        if (v == 64 || v == 96 || v == 128) c->gemm_bm = v;
-    }
 
     // Quantize and lay out every expert on the host, several experts at a time.
     std::vector<ExpertPack> packs(nexp);

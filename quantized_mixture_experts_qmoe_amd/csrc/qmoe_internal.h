@@ -167,7 +167,7 @@ struct GemmArgs {
     int32_t E;               // routed experts
     int32_t n_tiles;         // 256-column N-tiles of the widest expert (set by the launcher)
 };
-// bm: rows per M-tile (16: weight-streaming decode kernel; 64, 96, 128: prefill
+// bm: rows per M-tile (16: weight-streaming decode kernel; 64: prefill
 // kernels); max_tiles: grid bound; maxN13: max 2F.
 hipError_t launch_gemm13(int df, int bm, const GemmArgs &a, int max_tiles, int maxN13, hipStream_t s);
 hipError_t launch_gemm2(int df, int bm, const GemmArgs &a, int max_tiles, hipStream_t s);

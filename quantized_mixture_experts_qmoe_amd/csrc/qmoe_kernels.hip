@@ -1026,6 +1026,16 @@ __device__ __forceinline__ void dma4(const void *g, uint32_t lds) {
     const uint32_t base = __builtin_amdgcn_readfirstlane(lds);
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(base) : "memory", "m0");
 }
+// Same copies addressed as a wave-uniform 64-bit base in SGPRs plus a 32-bit
+// per-lane byte offset: advancing through K moves only the scalar base.
+__device__ __forceinline__ void dma16s(const void *sbase, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void dma4s(const void *sbase, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
+                 : "memory", "m0");
+}
 
 template <int DF, int MODE, int MI, int NW, int NST, int OCC>
 __global__ __launch_bounds__(64 * NW, OCC) void k_gemm_gpf(GemmArgs a) {
@@ -1047,7 +1057,8 @@ __global__ __launch_bounds__(64 * NW, OCC) void k_gemm_gpf(GemmArgs a) {
     const int n0 = ntile * NTILE;
     if (n0 >= N) return;
     const int rows = tl.row_end - tl.row0;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform, kept in an SGPR
     const int KB = K / 128;
     const int lrow = (lane >> 4) * 4;
     const uint32_t lds0 = lds_addr(lds);
@@ -1082,15 +1093,25 @@ __global__ __launch_bounds__(64 * NW, OCC) void k_gemm_gpf(GemmArgs a) {
     // scale copy: lane i (< 32) brings the scales of rows 2(i&7), 2(i&7)+1 of block i>>3
     const int snb = (lane >> 3) & 3, spair = lane & 7;
 
+    // per-lane byte offsets of the copies (constant through K; only the scalar
+    // bases advance with the group index)
+    uint32_t aoffb[ADMA], boffb[4];
+#pragma unroll
+    for (int i = 0; i < ADMA; i++) aoffb[i] = aoff[i] * 2u;
+#pragma unroll
+    for (int nb = 0; nb < 4; nb++) boffb[nb] = (uint32_t)(ib0 + nb) * (uint32_t)KB * 1024u + lane * 16u;
+    const uint32_t soffb = ((uint32_t)(ib0 + snb) * (uint32_t)KB * 16u + 2u * spair) * 2u;
+    const uint32_t roffb = roff * 4u;
     auto issue = [&](int kb, int st) {
         const uint32_t sb = lds0 + st * ST_BYTES;
+        const uint16_t *as = abase + kb * 128;
+        const uint8_t *bs = codes + (size_t)kb * 1024;
 #pragma unroll
-        for (int i = 0; i < ADMA; i++) dma16(abase + aoff[i] + kb * 128, sb + ST_A + (RPW * wave + 4 * i) * 256);
+        for (int i = 0; i < ADMA; i++) dma16s(as, aoffb[i], sb + ST_A + (RPW * wave + 4 * i) * 256);
 #pragma unroll
-        for (int nb = 0; nb < 4; nb++)
-            dma16(codes + ((size_t)(ib0 + nb) * KB + kb) * 1024 + lane * 16, sb + ST_B + (wave * 4 + nb) * 1024);
-        if (lane < 32) dma4(gsc + ((size_t)(ib0 + snb) * KB + kb) * 16 + 2 * spair, sb + ST_S + wave * 128);
-        if (lane < RPW) dma4(rbase + roff + kb, sb + ST_R + wave * RPW * 4);
+        for (int nb = 0; nb < 4; nb++) dma16s(bs, boffb[nb], sb + ST_B + (wave * 4 + nb) * 1024);
+        if (lane < 32) dma4s(gsc + kb * 16, soffb, sb + ST_S + wave * 128);
+        if (lane < RPW) dma4s(rbase + kb, roffb, sb + ST_R + wave * RPW * 4);
     };
     const int last = KB - 1;
 
@@ -1543,27 +1564,14 @@ template <int MODE>
 static hipError_t launch_gemm(int df, int bm, int max_tiles, int maxN, const GemmArgs &a0, hipStream_t s) {
     GemmArgs a = a0;
     a.n_tiles = (maxN + 255) / 256;
-    if ((bm == 64 || bm == 96 || bm == 128) && (df == DF_I4SYM || df == DF_I4ASYM)) {
-        // prefill tiles: 8 waves (two per SIMD) over bm rows x 512 columns,
-        // double-buffered; 64-row tiles use 4 waves x 256 columns, 3 stages
-        const int cols = bm == 64 ? 256 : 512;
-        a.n_tiles = (maxN + cols - 1) / cols;
+    if (bm == 64 && (df == DF_I4SYM || df == DF_I4ASYM)) {
+        // prefill tiles: 64 rows x 256 columns, 4 waves, two stages, two
+        // workgroups per CU (<= 256 VGPRs, 67 KB LDS each)
+        a.n_tiles = (maxN + 255) / 256;
         const long total = (long)max_tiles * a.n_tiles;
         dim3 grid((unsigned)(8 * ((total + 7) / 8)));
-        const bool sym = df == DF_I4SYM;
-        switch (bm) {
-        case 64:   // two workgroups per CU (<= 256 VGPRs, 67 KB LDS each)
-            if (sym) hipLaunchKernelGGL((k_gemm_gpf<DF_I4SYM, MODE, 4, 4, 2, 2>), grid, dim3(256), 0, s, a);
-            else hipLaunchKernelGGL((k_gemm_gpf<DF_I4ASYM, MODE, 4, 4, 2, 2>), grid, dim3(256), 0, s, a);
-            break;
-        case 96:
-            if (sym) hipLaunchKernelGGL((k_gemm_gpf<DF_I4SYM, MODE, 6, 8, 2, 1>), grid, dim3(512), 0, s, a);
-            else hipLaunchKernelGGL((k_gemm_gpf<DF_I4ASYM, MODE, 6, 8, 2, 1>), grid, dim3(512), 0, s, a);
-            break;
-        default:
-            if (sym) hipLaunchKernelGGL((k_gemm_gpf<DF_I4SYM, MODE, 8, 8, 2, 1>), grid, dim3(512), 0, s, a);
-            else hipLaunchKernelGGL((k_gemm_gpf<DF_I4ASYM, MODE, 8, 8, 2, 1>), grid, dim3(512), 0, s, a);
-        }
+        if (df == DF_I4SYM) hipLaunchKernelGGL((k_gemm_gpf<DF_I4SYM, MODE, 4, 4, 2, 2>), grid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((k_gemm_gpf<DF_I4ASYM, MODE, 4, 4, 2, 2>), grid, dim3(256), 0, s, a);
         return hipGetLastError();
     }
     if (bm == 16) {
