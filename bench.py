@@ -71,14 +71,24 @@ def measured_traffic(kernel: str, workload: str):
     return rec.get("kernels", {}).get(kernel, {}).get(workload)
 
 
-def cpu_baseline(inp, n_tokens: int):
+def cpu_baseline(inp, n_tokens: int = 0, target_s: float = 15.0):
+    """The fp64 oracle on a token sample of the same layer: 16 tokens are timed
+    first to size the sample for about `target_s` seconds (or `n_tokens` when
+    given); the rate is taken over the second, sized run."""
     from oracle import oracle as O
     cfg = inp.cfg
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
     log(f"cpu baseline: quantizing the oracle's copy of the layer ({threads} threads)")
     layer = O.OracleLayer(inp)
     rng = np.random.default_rng(123)
-    toks = np.sort(rng.choice(cfg.T, size=min(n_tokens, cfg.T), replace=False)).astype(np.int32)
+    order = rng.permutation(cfg.T).astype(np.int32)
+    if not n_tokens:
+        probe = np.sort(order[:min(16, cfg.T)])
+        t0 = time.perf_counter()
+        layer.forward(inp.x, tokens=probe)
+        per_token = (time.perf_counter() - t0) / len(probe)
+        n_tokens = int(min(cfg.T, max(16, target_s / max(per_token, 1e-9))))
+    toks = np.sort(order[:min(n_tokens, cfg.T)])
     log(f"cpu baseline: oracle forward on {len(toks)} sampled tokens")
     t0 = time.perf_counter()
     layer.forward(inp.x, tokens=toks)
@@ -95,7 +105,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="mixtral_prefill")
-    ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (0 = per-config default)")
+    ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (0: sized for about 15 s)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--flush-mb", type=int, default=-1,
                     help="read this many MiB between timed decode steps to evict the 256 MB MALL "
@@ -212,8 +222,7 @@ def main() -> int:
 
     cpu = None
     if not args.no_cpu_baseline:
-        n = args.cpu_tokens or (48 if cfg.d * cfg.F >= 4096 * 8192 else 256)
-        cpu = cpu_baseline(inp, n)
+        cpu = cpu_baseline(inp, args.cpu_tokens)
         log(f"cpu baseline {cpu['value']:.3g} tokens/s on {cpu['cores']} threads")
 
     out = {
