@@ -1095,22 +1095,20 @@ __global__ __launch_bounds__(64 * NW, OCC) void k_gemm_gpf(GemmArgs a) {
 
     // per-lane byte offsets of the copies (constant through K; only the scalar
     // bases advance with the group index)
-    uint32_t aoffb[ADMA], boffb[4];
+    uint32_t aoffb[ADMA];
 #pragma unroll
     for (int i = 0; i < ADMA; i++) aoffb[i] = aoff[i] * 2u;
-#pragma unroll
-    for (int nb = 0; nb < 4; nb++) boffb[nb] = (uint32_t)(ib0 + nb) * (uint32_t)KB * 1024u + lane * 16u;
-    const uint32_t soffb = ((uint32_t)(ib0 + snb) * (uint32_t)KB * 16u + 2u * spair) * 2u;
+    const uint32_t soffb = ((uint32_t)snb * (uint32_t)KB * 16u + 2u * spair) * 2u;
     const uint32_t roffb = roff * 4u;
     auto issue = [&](int kb, int st) {
         const uint32_t sb = lds0 + st * ST_BYTES;
         const uint16_t *as = abase + kb * 128;
-        const uint8_t *bs = codes + (size_t)kb * 1024;
 #pragma unroll
         for (int i = 0; i < ADMA; i++) dma16s(as, aoffb[i], sb + ST_A + (RPW * wave + 4 * i) * 256);
 #pragma unroll
-        for (int nb = 0; nb < 4; nb++) dma16s(bs, boffb[nb], sb + ST_B + (wave * 4 + nb) * 1024);
-        if (lane < 32) dma4s(gsc + kb * 16, soffb, sb + ST_S + wave * 128);
+        for (int nb = 0; nb < 4; nb++)
+            dma16s(codes + ((size_t)(ib0 + nb) * KB + kb) * 1024, lane * 16u, sb + ST_B + (wave * 4 + nb) * 1024);
+        if (lane < 32) dma4s(gsc + ((size_t)ib0 * KB + kb) * 16, soffb, sb + ST_S + wave * 128);
         if (lane < RPW) dma4s(rbase + kb, roffb, sb + ST_R + wave * RPW * 4);
     };
     const int last = KB - 1;
