@@ -1006,28 +1006,21 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
 // outstanding load); the memory clobber keeps LDS accesses on their side.
 __device__ __forceinline__ void raw_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-// ---- 64/96/128-row tiles (prefill): global -> LDS ring, XCD-aware ----------
+// ---- 64-row tiles (prefill): activation ring in LDS, XCD-aware ------------
 //
-// Every transfer of the K loop is an asynchronous global -> LDS copy issued
-// from inline assembly (so the compiler neither waits on it before LDS reads
-// nor counts it): per wave and group exactly 14 copies -- 8 x 1 KB of gathered
-// activation rows, 4 x 1 KB of its own packed codes, the fp16 scales of its
-// four 16-row blocks and 32 row sums. A three-stage ring gives a prefetch
-// distance of two groups; at the end of group g, "vmcnt <= 14" means group g+1
-// has landed, and one barrier publishes it to the workgroup.
+// Per wave and group (128 K positions): the gathered activation rows and their
+// row sums travel as asynchronous global -> LDS copies issued from inline
+// assembly (so the compiler neither waits on them before LDS reads nor counts
+// them), one group ahead in a two-stage ring; the wave's own packed codes and
+// scales are ordinary loads into a two-slot register ring, also one group
+// ahead. Every group ends with all loads landed (vmcnt 0) and one barrier that
+// publishes the next activation tile to the workgroup.
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
 }
-__device__ __forceinline__ void dma16(const void *g, uint32_t lds) {
-    const uint32_t base = __builtin_amdgcn_readfirstlane(lds);   // wave-uniform by construction
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(base) : "memory", "m0");
-}
-__device__ __forceinline__ void dma4(const void *g, uint32_t lds) {
-    const uint32_t base = __builtin_amdgcn_readfirstlane(lds);
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(base) : "memory", "m0");
-}
-// Same copies addressed as a wave-uniform 64-bit base in SGPRs plus a 32-bit
-// per-lane byte offset: advancing through K moves only the scalar base.
+// Global -> LDS copies (16 or 4 bytes per lane; LDS destination in M0)
+// addressed as a wave-uniform 64-bit base in SGPRs plus a 32-bit per-lane
+// byte offset: advancing through K moves only the scalar base.
 __device__ __forceinline__ void dma16s(const void *sbase, uint32_t voff, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
                  : "memory", "m0");
@@ -1041,9 +1034,11 @@ template <int DF, int MODE, int MI, int NW, int NST, int OCC>
 __global__ __launch_bounds__(64 * NW, OCC) void k_gemm_gpf(GemmArgs a) {
     constexpr int BM = 16 * MI, RPW = BM / NW;   // activation rows copied per wave
     constexpr int ADMA = RPW / 4;                 // 1 KB activation copies per wave
-    constexpr int DMA_PER_GROUP = ADMA + 4 + 2;
-    constexpr int ST_A = 0, ST_B = BM * 256, ST_S = ST_B + NW * 4096, ST_R = ST_S + NW * 128,
-                  ST_BYTES = ST_R + BM * 4;
+    // Packed codes and scales go straight to registers (each wave owns its B
+    // blocks, so nothing would be shared through LDS); the stages hold only the
+    // activation tile and its row sums.
+    static_assert(NST == 2, "the register ring of B runs one group ahead");
+    constexpr int ST_A = 0, ST_R = BM * 256, ST_BYTES = ST_R + BM * 4;
     constexpr int NTILE = 64 * NW;                // B columns per workgroup
     constexpr float ZC = GroupConst<DF>::ZC;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[NST * ST_BYTES];
@@ -1087,29 +1082,36 @@ __global__ __launch_bounds__(64 * NW, OCC) void k_gemm_gpf(GemmArgs a) {
     const uint8_t *codes = MODE == 0 ? ew.c13 : ew.c2;
     const uint16_t *gsc = MODE == 0 ? ew.s13 : ew.s2;
     // a wave whose 64 columns lie past N (last N-tile of a narrower matrix)
-    // copies block 0 instead to keep its copy count, and computes nothing
+    // loads block 0 instead to keep its load count, and computes nothing
     const bool wave_on = n0 + 64 * wave < N;
     const int ib0 = wave_on ? n0 / 16 + 4 * wave : 0;
-    // scale copy: lane i (< 32) brings the scales of rows 2(i&7), 2(i&7)+1 of block i>>3
-    const int snb = (lane >> 3) & 3, spair = lane & 7;
 
     // per-lane byte offsets of the copies (constant through K; only the scalar
     // bases advance with the group index)
     uint32_t aoffb[ADMA];
 #pragma unroll
     for (int i = 0; i < ADMA; i++) aoffb[i] = aoff[i] * 2u;
-    const uint32_t soffb = ((uint32_t)snb * (uint32_t)KB * 16u + 2u * spair) * 2u;
     const uint32_t roffb = roff * 4u;
     auto issue = [&](int kb, int st) {
         const uint32_t sb = lds0 + st * ST_BYTES;
         const uint16_t *as = abase + kb * 128;
 #pragma unroll
         for (int i = 0; i < ADMA; i++) dma16s(as, aoffb[i], sb + ST_A + (RPW * wave + 4 * i) * 256);
-#pragma unroll
-        for (int nb = 0; nb < 4; nb++)
-            dma16s(codes + ((size_t)(ib0 + nb) * KB + kb) * 1024, lane * 16u, sb + ST_B + (wave * 4 + nb) * 1024);
-        if (lane < 32) dma4s(gsc + ((size_t)ib0 * KB + kb) * 16, soffb, sb + ST_S + wave * 128);
         if (lane < RPW) dma4s(rbase + kb, roffb, sb + ST_R + wave * RPW * 4);
+    };
+    // B register ring: codes, and the dword holding this lane's fp16 scale and
+    // its neighbour's
+    uint4 bring[2][4];
+    uint32_t sring[2][4];
+    const int spair2 = (lane & 15) & ~1;
+    const uint32_t hsel = (lane & 1) * 16;
+    auto load_b = [&](int kb, int slot) {
+#pragma unroll
+        for (int nb = 0; nb < 4; nb++) {
+            const size_t blk = (size_t)(ib0 + nb) * KB + kb;
+            bring[slot][nb] = gload16(codes + blk * 1024 + lane * 16);
+            sring[slot][nb] = gload(reinterpret_cast<const uint32_t *>(gsc + blk * 16 + spair2));
+        }
     };
     const int last = KB - 1;
 
@@ -1120,28 +1122,20 @@ __global__ __launch_bounds__(64 * NW, OCC) void k_gemm_gpf(GemmArgs a) {
         for (int nb = 0; nb < 4; nb++) acc[mi][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
     const NibbleConst nc = nibble_const();
 
-    // prologue: groups 0 .. NST-2 in flight, then group 0 must land
-#pragma unroll
-    for (int j = 0; j < NST - 1; j++) issue(min(j, last), j);
-    wait_vm_lgkm0<DMA_PER_GROUP * (NST - 2)>();
-    raw_barrier();
-
-    int st = 0;
-    for (int kb = 0; kb < KB; kb++) {
-        issue(min(kb + NST - 1, last), st == 0 ? NST - 1 : st - 1);   // stage (kb + NST - 1) % NST
+    // one group: the next group's copies, then this group's MFMAs
+    auto group = [&](int kb, int st, int slot) {
         const uint8_t *S = lds + st * ST_BYTES;
         // this wave's packed codes and scales of the group
         bf16x8 bq[4][4];
         float sc[4];
 #pragma unroll
         for (int nb = 0; nb < 4; nb++) {
-            const uint4 raw = *reinterpret_cast<const uint4 *>(S + ST_B + (wave * 4 + nb) * 1024 + lane * 16);
+            const uint4 raw = bring[slot][nb];
             bq[nb][0] = nibbles_to_bf16_128(raw.x, nc);
             bq[nb][1] = nibbles_to_bf16_128(raw.y, nc);
             bq[nb][2] = nibbles_to_bf16_128(raw.z, nc);
             bq[nb][3] = nibbles_to_bf16_128(raw.w, nc);
-            sc[nb] = half_bits_to_f32(*reinterpret_cast<const uint16_t *>(S + ST_S + wave * 128 + nb * 32 +
-                                                                          (lane & 15) * 2));
+            sc[nb] = half_bits_to_f32((uint16_t)(sring[slot][nb] >> hsel));
         }
         const uint16_t *Ab = reinterpret_cast<const uint16_t *>(S + ST_A);
         const float *Rb = reinterpret_cast<const float *>(S + ST_R);
@@ -1167,10 +1161,27 @@ __global__ __launch_bounds__(64 * NW, OCC) void k_gemm_gpf(GemmArgs a) {
 #pragma unroll
                 for (int nb = 0; nb < 4; nb++) acc[mi][nb] += sc[nb] * p[mi][nb];
         }
-        wait_vm_lgkm0<DMA_PER_GROUP * (NST - 2)>();   // group kb+1 has landed
+    };
+
+    // two stages, B one group ahead in registers; every group ends with all
+    // copies landed (vmcnt 0), so the compiler's own waits are already met
+    load_b(0, 0);
+    issue(0, 0);
+    wait_vm_lgkm0<0>();
+    raw_barrier();
+    auto step = [&](int kb, int st, int slot) {
+        load_b(min(kb + 1, last), slot ^ 1);
+        issue(min(kb + 1, last), st ^ 1);
+        group(kb, st, slot);
+        wait_vm_lgkm0<0>();
         raw_barrier();
-        st = st == NST - 1 ? 0 : st + 1;
+    };
+    int kb = 0;
+    for (; kb + 1 < KB; kb += 2) {
+        step(kb, 0, 0);
+        step(kb + 1, 1, 1);
     }
+    if (kb < KB) step(kb, 0, 0);
     __builtin_amdgcn_s_waitcnt(0);
     raw_barrier();
 
