@@ -119,8 +119,11 @@ int validate(const qmoe_config *cfg) {
         return fail(QMOE_EUNSUPPORTED, "group_size=%d: only 128 is supported", cfg->group_size);
     if (cfg->n_experts > 1024) return fail(QMOE_EUNSUPPORTED, "n_experts=%d exceeds 1024", cfg->n_experts);
     if (cfg->top_k > 64) return fail(QMOE_EUNSUPPORTED, "top_k=%d exceeds 64", cfg->top_k);
+    // launch grids index token tiles and M-tiles in their y dimension (< 65536)
     const long long rows = (long long)cfg->max_tokens * (cfg->top_k + cfg->n_shared);
-    if (rows >= (1ll << 30)) return fail(QMOE_EUNSUPPORTED, "max_tokens=%d too large", cfg->max_tokens);
+    if (cfg->max_tokens > (1 << 20) || rows > (1ll << 21))
+        return fail(QMOE_EUNSUPPORTED, "max_tokens=%d too large (max_tokens <= 2^20 and max_tokens * (top_k + "
+                                       "n_shared) <= 2^21)", cfg->max_tokens);
     if (cfg->renormalize != 0 && cfg->renormalize != 1) return fail(QMOE_EINVAL, "renormalize must be 0 or 1");
     if (cfg->router_fp32 != 0 && cfg->router_fp32 != 1) return fail(QMOE_EINVAL, "router_fp32 must be 0 or 1");
     return QMOE_OK;

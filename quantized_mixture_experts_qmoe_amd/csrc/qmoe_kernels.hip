@@ -65,66 +65,80 @@ __global__ __launch_bounds__(256) void k_router_bf16(const uint16_t *__restrict_
                                                      float *__restrict__ xsum, float xscale, int T, int d, int E) {
     __shared__ f32x4 red[3][MT * NT][64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int t0 = blockIdx.x * 16 * MT;
-    const int e0 = blockIdx.y * 16 * NT;
+    // XCD-aware numbering (workgroup L runs on XCD L % 8): the expert tiles of
+    // one token tile are consecutive workgroups of one XCD, so its L2 fetches
+    // the tile's x rows once; the grid's y extent is padded to a multiple of 8
+    const int L = blockIdx.x + blockIdx.y * gridDim.x;
+    const int xcd = L & 7, j = L >> 3;
+    const int et = j % gridDim.x, tt = (j / gridDim.x) * 8 + xcd;
+    const int t0 = tt * 16 * MT;
+    const int e0 = et * 16 * NT;
+    if (t0 >= T) return;
     const int kq = (lane >> 4) * 8;
     const uint16_t *ap[MT];
-    bool aok[MT];
 #pragma unroll
     for (int i = 0; i < MT; i++) {
         const int t = t0 + 16 * i + (lane & 15);
-        aok[i] = t < T;
-        ap[i] = x + (size_t)(aok[i] ? t : 0) * d + kq;
+        ap[i] = x + (size_t)(t < T ? t : 0) * d + kq;
     }
     const uint16_t *bp[NT];
-    bool bok[NT];
 #pragma unroll
     for (int i = 0; i < NT; i++) {
         const int e = e0 + 16 * i + (lane & 15);
-        bok[i] = e < E;
-        bp[i] = wr + (size_t)(bok[i] ? e : 0) * d + kq;
+        bp[i] = wr + (size_t)(e < E ? e : 0) * d + kq;
     }
     f32x4 acc[MT][NT];
 #pragma unroll
     for (int i = 0; i < MT; i++)
 #pragma unroll
         for (int j = 0; j < NT; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const bool do_sum = xsum != nullptr && blockIdx.y == 0;
-    float gs[MT];
+    const bool do_sum = xsum != nullptr && et == 0;
+    // One 128-wide group (4 k-steps) per iteration: every load of the group is
+    // issued before its MFMAs. Loads are unconditional: rows past T and
+    // experts past E read row 0 / expert 0 and only feed outputs that are not
+    // stored; k-steps past this wave's range read its last step and are skipped.
+    const int kw = d / 4, kbeg = wave * kw, kend = kbeg + kw;
+    for (int k0 = kbeg; k0 < kend; k0 += 128) {
+        uint4 av[4][MT], bv[4][NT];
 #pragma unroll
-    for (int i = 0; i < MT; i++) gs[i] = 0.0f;
-    const uint4 zero4 = make_uint4(0, 0, 0, 0);
-    const int kw = d / 4, kbeg = wave * kw;
-#pragma unroll 4
-    for (int k0 = kbeg; k0 < kbeg + kw; k0 += 32) {
-        uint4 av[MT];
+        for (int u = 0; u < 4; u++) {
+            const int kk = min(k0 + 32 * u, kend - 32);
 #pragma unroll
-        for (int i = 0; i < MT; i++) av[i] = aok[i] ? *reinterpret_cast<const uint4 *>(ap[i] + k0) : zero4;
+            for (int i = 0; i < MT; i++) av[u][i] = gload16(ap[i] + kk);
 #pragma unroll
-        for (int j = 0; j < NT; j++) {
-            const uint4 bv = bok[j] ? *reinterpret_cast<const uint4 *>(bp[j] + k0) : zero4;
-#pragma unroll
-            for (int i = 0; i < MT; i++)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[i]),
-                                                                    __builtin_bit_cast(bf16x8, bv), acc[i][j], 0, 0, 0);
+            for (int j = 0; j < NT; j++) bv[u][j] = gload16(bp[j] + kk);
         }
+        float gs[MT];
+#pragma unroll
+        for (int i = 0; i < MT; i++) gs[i] = 0.0f;
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            if (k0 + 32 * u >= kend) continue;   // uniform
+#pragma unroll
+            for (int j = 0; j < NT; j++)
+#pragma unroll
+                for (int i = 0; i < MT; i++)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[u][i]),
+                                                                        __builtin_bit_cast(bf16x8, bv[u][j]),
+                                                                        acc[i][j], 0, 0, 0);
+            if (do_sum) {
+#pragma unroll
+                for (int i = 0; i < MT; i++) {
+                    const uint32_t q[4] = {av[u][i].x, av[u][i].y, av[u][i].z, av[u][i].w};
+#pragma unroll
+                    for (int c = 0; c < 4; c++) gs[i] += bf16f(q[c] & 0xFFFFu) + bf16f(q[c] >> 16);
+                }
+            }
+        }
+        // the fused row sums need whole groups per wave (d % 512 == 0)
         if (do_sum) {
 #pragma unroll
             for (int i = 0; i < MT; i++) {
-                const uint32_t u[4] = {av[i].x, av[i].y, av[i].z, av[i].w};
-#pragma unroll
-                for (int q = 0; q < 4; q++) gs[i] += bf16f(u[q] & 0xFFFFu) + bf16f(u[q] >> 16);
-            }
-            if (((k0 + 32) & 127) == 0) {
-#pragma unroll
-                for (int i = 0; i < MT; i++) {
-                    float v = gs[i];
-                    v += __shfl_xor(v, 16);
-                    v += __shfl_xor(v, 32);
-                    const int t = t0 + 16 * i + lane;
-                    if (lane < 16 && t < T) xsum[(size_t)t * (d / 128) + k0 / 128] = v * xscale;
-                    gs[i] = 0.0f;
-                }
+                float v = gs[i];
+                v += __shfl_xor(v, 16);
+                v += __shfl_xor(v, 32);
+                const int t = t0 + 16 * i + lane;
+                if (lane < 16 && t < T) xsum[(size_t)t * (d / 128) + k0 / 128] = v * xscale;
             }
         }
     }
@@ -1468,16 +1482,19 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ O, co
 // Launchers
 // ---------------------------------------------------------------------------
 
-// Expert tiles of 32 (16 when E <= 16: no idle half tile).
+// Expert tiles of 64 for many experts, 32, or 16 when E <= 16 (no idle half tile).
 template <int MT>
 static void launch_router_mt(const uint16_t *x, const uint16_t *wr, const float *bias, float *logits, float *xsum,
                              float xscale, int T, int d, int E, hipStream_t s) {
-    const int gx = (T + 16 * MT - 1) / (16 * MT);
-    if (E > 16)
-        hipLaunchKernelGGL((k_router_bf16<MT, 2>), dim3(gx, (E + 31) / 32), dim3(256), 0, s, x, wr, bias, logits, xsum,
+    const int gx = 8 * ((T + 16 * MT * 8 - 1) / (16 * MT * 8));   // token tiles, padded to a multiple of 8
+    if (E > 64)
+        hipLaunchKernelGGL((k_router_bf16<MT, 4>), dim3((E + 63) / 64, gx), dim3(256), 0, s, x, wr, bias, logits, xsum,
+                           xscale, T, d, E);
+    else if (E > 16)
+        hipLaunchKernelGGL((k_router_bf16<MT, 2>), dim3((E + 31) / 32, gx), dim3(256), 0, s, x, wr, bias, logits, xsum,
                            xscale, T, d, E);
     else
-        hipLaunchKernelGGL((k_router_bf16<MT, 1>), dim3(gx, 1), dim3(256), 0, s, x, wr, bias, logits, xsum, xscale,
+        hipLaunchKernelGGL((k_router_bf16<MT, 1>), dim3(1, gx), dim3(256), 0, s, x, wr, bias, logits, xsum, xscale,
                            T, d, E);
 }
 

@@ -64,6 +64,8 @@ def base_cfg(**kw):
     (dict(wformat=2, group_size=64), Q.QMOE_EUNSUPPORTED),
     (dict(n_experts=2048, top_k=2), Q.QMOE_EUNSUPPORTED),
     (dict(n_experts=128, top_k=65), Q.QMOE_EUNSUPPORTED),
+    (dict(max_tokens=(1 << 20) + 1), Q.QMOE_EUNSUPPORTED),
+    (dict(max_tokens=(1 << 20), top_k=3), Q.QMOE_EUNSUPPORTED),   # 3 * 2^20 rows
 ])
 def test_pack_rejects_bad_configs(qmoe_lib, kw, rc):
     got, ctx = _pack(base_cfg(**kw))
