@@ -21,6 +21,9 @@ CASES = [  # (T, E, k, kind)
     (1, 8, 2, "normal"), (7, 8, 2, "grid"), (63, 16, 4, "equal"), (65, 16, 4, "hot"), (1000, 64, 6, "grid"),
     (4096, 128, 8, "normal"), (4096, 128, 8, "grid"), (3000, 128, 8, "sparse"), (513, 5, 5, "normal"),
     (200, 300, 8, "grid"), (129, 64, 1, "hot"), (2048, 8, 2, "sparse"),
+    # one-workgroup path at its limits (T <= 64, E <= 256), the decode shape,
+    # and a small batch with too many experts for it
+    (64, 256, 8, "equal"), (64, 256, 64, "grid"), (16, 128, 8, "normal"), (40, 300, 8, "grid"),
 ]
 
 
