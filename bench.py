@@ -54,19 +54,29 @@ def packed_bytes_per_expert(cfg, f):
     return n + 4 * (2 * f + cfg.d)
 
 
+def kernel_code_digest(path: str) -> str:
+    """SHA-256 of a C++/HIP source with its comments and whitespace removed, so
+    that only a change to the code itself retires counters taken on it."""
+    import hashlib
+    import re
+    text = open(path, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return hashlib.sha256(" ".join(text.split()).encode()).hexdigest()
+
+
 def measured_traffic(kernel: str, workload: str):
     """HBM bytes per launch of `kernel` on `workload` from the committed
     copy-calibrated FETCH_SIZE + WRITE_SIZE counter runs, or None when no run
-    covers it or the kernel source has changed since the counters were taken."""
-    import hashlib
+    covers it or the kernel code has changed since the counters were taken."""
     rec_path = os.path.join(ROOT, "profiles", "traffic.json")
     src = os.path.join(ROOT, "quantized_mixture_experts_qmoe_amd", "csrc", "qmoe_kernels.hip")
     try:
         rec = json.load(open(rec_path))
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        digest = kernel_code_digest(src)
     except OSError:
         return None
-    if rec.get("kernel_source_sha256") != sha:
+    if rec.get("kernel_code_digest") != digest:
         return None
     return rec.get("kernels", {}).get(kernel, {}).get(workload)
 

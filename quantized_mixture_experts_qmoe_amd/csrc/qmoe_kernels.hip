@@ -1592,8 +1592,7 @@ static hipError_t launch_gemm(int df, int bm, int max_tiles, int maxN, const Gem
     a.n_tiles = (maxN + 255) / 256;
     if (bm == 64 && (df == DF_I4SYM || df == DF_I4ASYM)) {
         // prefill tiles: 64 rows x 256 columns, 4 waves, two stages, two
-        // workgroups per CU (<= 256 VGPRs, 67 KB LDS each)
-        a.n_tiles = (maxN + 255) / 256;
+        // workgroups per CU (<= 256 VGPRs, 33 KB LDS each)
         const long total = (long)max_tiles * a.n_tiles;
         dim3 grid((unsigned)(8 * ((total + 7) / 8)));
         if (df == DF_I4SYM) hipLaunchKernelGGL((k_gemm_gpf<DF_I4SYM, MODE, 4, 4, 2, 2>), grid, dim3(256), 0, s, a);
