@@ -245,6 +245,10 @@ int rows_per_tile(const qmoe_ctx *c, int T) {
     const double avg = (double)P / (double)std::max<long>(1, active);
     if (avg <= 16.0) return 16;
     if (!is_group_wformat(c->cfg.wformat)) return 64;
+    // 96-row tiles convert each packed code for 1.5x more MFMA work, which pays
+    // once an expert's rows fill several tiles; below that their ragged tails
+    // cost more than the conversions save
+    if (avg >= 512.0) return 96;
     return c->gemm_bm;
 }
 

@@ -1044,18 +1044,23 @@ __device__ __forceinline__ void dma4s(const void *sbase, uint32_t voff, uint32_t
                  : "memory", "m0");
 }
 
-template <int DF, int MODE, int MI, int NW, int NST, int OCC>
-__global__ __launch_bounds__(64 * NW, OCC) void k_gemm_gpf(GemmArgs a) {
+template <int DF, int MODE, int MI, int NB, int NW, bool ROW_OUTER>
+__global__ __launch_bounds__(64 * NW, 2) void k_gemm_gpf(GemmArgs a) {
     constexpr int BM = 16 * MI, RPW = BM / NW;   // activation rows copied per wave
+    static_assert(RPW % 4 == 0 && RPW <= 64, "each wave copies whole 4-row slabs");
     constexpr int ADMA = RPW / 4;                 // 1 KB activation copies per wave
     // Packed codes and scales go straight to registers (each wave owns its B
-    // blocks, so nothing would be shared through LDS); the stages hold only the
-    // activation tile and its row sums.
-    static_assert(NST == 2, "the register ring of B runs one group ahead");
+    // blocks, so nothing would be shared through LDS); the two stages hold only
+    // the activation tile and its row sums.
     constexpr int ST_A = 0, ST_R = BM * 256, ST_BYTES = ST_R + BM * 4;
-    constexpr int NTILE = 64 * NW;                // B columns per workgroup
+    constexpr int WCOLS = 16 * NB;                // B columns per wave
+    constexpr int NTILE = WCOLS * NW;             // B columns per workgroup
+    // Row-block-outer order keeps one row block of chain partials live instead
+    // of all of them; its B ring has one slot, refilled once the group's codes
+    // are converted. Row-block-inner order double-buffers the ring.
+    constexpr int RS = ROW_OUTER ? 1 : 2;
     constexpr float ZC = GroupConst<DF>::ZC;
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[NST * ST_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * ST_BYTES];
 
     int tile_id, ntile;
     if (!map_work(blockIdx.x, *a.num_tiles, a.n_tiles, tile_id, ntile)) return;
@@ -1076,36 +1081,32 @@ __global__ __launch_bounds__(64 * NW, OCC) void k_gemm_gpf(GemmArgs a) {
     // RPW*w + 4i + lane/16, chunk (lane & 15) ^ (row & 15) (the swizzle)
     const uint16_t *abase = MODE == 0 ? a.x : a.H;
     const int lda = MODE == 0 ? a.d : a.ldh;
-    uint32_t aoff[ADMA];
+    uint32_t aoffb[ADMA];
 #pragma unroll
     for (int i = 0; i < ADMA; i++) {
         const int row = RPW * wave + 4 * i + (lane >> 4);
         const int gr = tl.row0 + (row < rows ? row : 0);
         const int src = MODE == 0 ? (gr < a.P ? a.perm[gr] / a.k : (gr - a.P) % a.T) : gr;
-        aoff[i] = (uint32_t)src * (uint32_t)lda + (uint32_t)(((lane & 15) ^ (row & 15)) * 8);
+        aoffb[i] = 2u * ((uint32_t)src * (uint32_t)lda + (uint32_t)(((lane & 15) ^ (row & 15)) * 8));
     }
     const float *rbase = MODE == 0 ? a.xsum : a.hsum;
     const int ldr = MODE == 0 ? a.d / 128 : a.ldh / 128;
-    uint32_t roff;
+    uint32_t roffb;
     {
         const int row = RPW * wave + (lane < RPW ? lane : 0);
         const int gr = tl.row0 + (row < rows ? row : 0);
         const int src = MODE == 0 ? (gr < a.P ? a.perm[gr] / a.k : (gr - a.P) % a.T) : gr;
-        roff = (uint32_t)src * (uint32_t)ldr;
+        roffb = 4u * (uint32_t)src * (uint32_t)ldr;
     }
     const uint8_t *codes = MODE == 0 ? ew.c13 : ew.c2;
     const uint16_t *gsc = MODE == 0 ? ew.s13 : ew.s2;
-    // a wave whose 64 columns lie past N (last N-tile of a narrower matrix)
-    // loads block 0 instead to keep its load count, and computes nothing
-    const bool wave_on = n0 + 64 * wave < N;
-    const int ib0 = wave_on ? n0 / 16 + 4 * wave : 0;
+    // a wave whose columns lie past N (last N-tile of a narrower matrix) loads
+    // blocks 0.. instead to keep its load count, and computes nothing
+    const bool wave_on = n0 + WCOLS * wave < N;
+    const int ib0 = wave_on ? n0 / 16 + NB * wave : 0;
 
-    // per-lane byte offsets of the copies (constant through K; only the scalar
-    // bases advance with the group index)
-    uint32_t aoffb[ADMA];
-#pragma unroll
-    for (int i = 0; i < ADMA; i++) aoffb[i] = aoff[i] * 2u;
-    const uint32_t roffb = roff * 4u;
+    // the copies' per-lane byte offsets are constant through K; only the
+    // scalar bases advance with the group index
     auto issue = [&](int kb, int st) {
         const uint32_t sb = lds0 + st * ST_BYTES;
         const uint16_t *as = abase + kb * 128;
@@ -1115,13 +1116,13 @@ __global__ __launch_bounds__(64 * NW, OCC) void k_gemm_gpf(GemmArgs a) {
     };
     // B register ring: codes, and the dword holding this lane's fp16 scale and
     // its neighbour's
-    uint4 bring[2][4];
-    uint32_t sring[2][4];
+    uint4 bring[RS][NB];
+    uint32_t sring[RS][NB];
     const int spair2 = (lane & 15) & ~1;
     const uint32_t hsel = (lane & 1) * 16;
     auto load_b = [&](int kb, int slot) {
 #pragma unroll
-        for (int nb = 0; nb < 4; nb++) {
+        for (int nb = 0; nb < NB; nb++) {
             const size_t blk = (size_t)(ib0 + nb) * KB + kb;
             bring[slot][nb] = gload16(codes + blk * 1024 + lane * 16);
             sring[slot][nb] = gload(reinterpret_cast<const uint32_t *>(gsc + blk * 16 + spair2));
@@ -1129,21 +1130,20 @@ __global__ __launch_bounds__(64 * NW, OCC) void k_gemm_gpf(GemmArgs a) {
     };
     const int last = KB - 1;
 
-    f32x4 acc[MI][4];
+    f32x4 acc[MI][NB];
 #pragma unroll
     for (int mi = 0; mi < MI; mi++)
 #pragma unroll
-        for (int nb = 0; nb < 4; nb++) acc[mi][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int nb = 0; nb < NB; nb++) acc[mi][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
     const NibbleConst nc = nibble_const();
 
-    // one group: the next group's copies, then this group's MFMAs
-    auto group = [&](int kb, int st, int slot) {
+    // one group: this wave's codes and scales, then the group's MFMAs
+    auto group = [&](int st, int slot, int next_kb) {
         const uint8_t *S = lds + st * ST_BYTES;
-        // this wave's packed codes and scales of the group
-        bf16x8 bq[4][4];
-        float sc[4];
+        bf16x8 bq[NB][4];
+        float sc[NB];
 #pragma unroll
-        for (int nb = 0; nb < 4; nb++) {
+        for (int nb = 0; nb < NB; nb++) {
             const uint4 raw = bring[slot][nb];
             bq[nb][0] = nibbles_to_bf16_128(raw.x, nc);
             bq[nb][1] = nibbles_to_bf16_128(raw.y, nc);
@@ -1151,13 +1151,35 @@ __global__ __launch_bounds__(64 * NW, OCC) void k_gemm_gpf(GemmArgs a) {
             bq[nb][3] = nibbles_to_bf16_128(raw.w, nc);
             sc[nb] = half_bits_to_f32((uint16_t)(sring[slot][nb] >> hsel));
         }
+        if constexpr (RS == 1) load_b(next_kb, 0);
         const uint16_t *Ab = reinterpret_cast<const uint16_t *>(S + ST_A);
         const float *Rb = reinterpret_cast<const float *>(S + ST_R);
-        if (wave_on) {
-            // k-step outer: the 4*MI MFMA chains of the group advance together, so
-            // consecutive MFMAs of a chain are 4*MI instructions apart, and the
-            // scale FMAs at the end read chains that finished long before
-            f32x4 p[MI][4];
+        if (!wave_on) return;
+        if constexpr (ROW_OUTER) {
+            // row block outer: NB chains per row block, each 4 MFMAs deep
+#pragma unroll
+            for (int mi = 0; mi < MI; mi++) {
+                bf16x8 af[4];
+#pragma unroll
+                for (int s = 0; s < 4; s++) {
+                    const int pc = (s * 4 + (lane >> 4)) ^ (lane & 15);
+                    af[s] = *reinterpret_cast<const bf16x8 *>(&Ab[(mi * 16 + (lane & 15)) * 128 + pc * 8]);
+                }
+                const f32x4 c0 = *reinterpret_cast<const f32x4 *>(&Rb[mi * 16 + lrow]);
+                f32x4 p[NB];
+#pragma unroll
+                for (int s = 0; s < 4; s++)
+#pragma unroll
+                    for (int nb = 0; nb < NB; nb++)
+                        p[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s], bq[nb][s], s == 0 ? c0 : p[nb], 0, 0, 0);
+#pragma unroll
+                for (int nb = 0; nb < NB; nb++) acc[mi][nb] += sc[nb] * p[nb];
+            }
+        } else {
+            // k-step outer: the MI*NB MFMA chains of the group advance together,
+            // so consecutive MFMAs of a chain are MI*NB instructions apart, and
+            // the scale FMAs at the end read chains that finished long before
+            f32x4 p[MI][NB];
 #pragma unroll
             for (int s = 0; s < 4; s++) {
                 const int pc = (s * 4 + (lane >> 4)) ^ (lane & 15);
@@ -1166,14 +1188,14 @@ __global__ __launch_bounds__(64 * NW, OCC) void k_gemm_gpf(GemmArgs a) {
                     const bf16x8 af = *reinterpret_cast<const bf16x8 *>(&Ab[(mi * 16 + (lane & 15)) * 128 + pc * 8]);
                     const f32x4 c0 = s == 0 ? *reinterpret_cast<const f32x4 *>(&Rb[mi * 16 + lrow]) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int nb = 0; nb < 4; nb++)
+                    for (int nb = 0; nb < NB; nb++)
                         p[mi][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bq[nb][s], s == 0 ? c0 : p[mi][nb], 0, 0, 0);
                 }
             }
 #pragma unroll
             for (int mi = 0; mi < MI; mi++)
 #pragma unroll
-                for (int nb = 0; nb < 4; nb++) acc[mi][nb] += sc[nb] * p[mi][nb];
+                for (int nb = 0; nb < NB; nb++) acc[mi][nb] += sc[nb] * p[mi][nb];
         }
     };
 
@@ -1184,16 +1206,17 @@ __global__ __launch_bounds__(64 * NW, OCC) void k_gemm_gpf(GemmArgs a) {
     wait_vm_lgkm0<0>();
     raw_barrier();
     auto step = [&](int kb, int st, int slot) {
-        load_b(min(kb + 1, last), slot ^ 1);
-        issue(min(kb + 1, last), st ^ 1);
-        group(kb, st, slot);
+        const int nk = min(kb + 1, last);
+        if constexpr (RS == 2) load_b(nk, slot ^ 1);
+        issue(nk, st ^ 1);
+        group(st, slot, nk);
         wait_vm_lgkm0<0>();
         raw_barrier();
     };
     int kb = 0;
     for (; kb + 1 < KB; kb += 2) {
         step(kb, 0, 0);
-        step(kb + 1, 1, 1);
+        step(kb + 1, 1, RS - 1);
     }
     if (kb < KB) step(kb, 0, 0);
     __builtin_amdgcn_s_waitcnt(0);
@@ -1214,9 +1237,9 @@ __global__ __launch_bounds__(64 * NW, OCC) void k_gemm_gpf(GemmArgs a) {
             zrow[mi] = (uint32_t)src * (uint32_t)ldr;
         }
         for (int gs = 0; gs < GS; gs++) {
-            bf16x8 bh[4], bl[4];
+            bf16x8 bh[NB], bl[NB];
 #pragma unroll
-            for (int nb = 0; nb < 4; nb++) {
+            for (int nb = 0; nb < NB; nb++) {
                 const uint16_t *q = zcp + ((size_t)(ib0 + nb) * GS + gs) * 1024 + lane * 8;
                 bh[nb] = __builtin_bit_cast(bf16x8, gload16(q));
                 bl[nb] = __builtin_bit_cast(bf16x8, gload16(q + 512));
@@ -1234,7 +1257,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void k_gemm_gpf(GemmArgs a) {
                     al[j] = l;
                 }
 #pragma unroll
-                for (int nb = 0; nb < 4; nb++) {
+                for (int nb = 0; nb < NB; nb++) {
                     acc[mi][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh[nb], acc[mi][nb], 0, 0, 0);
                     acc[mi][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl[nb], acc[mi][nb], 0, 0, 0);
                     acc[mi][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh[nb], acc[mi][nb], 0, 0, 0);
@@ -1244,15 +1267,18 @@ __global__ __launch_bounds__(64 * NW, OCC) void k_gemm_gpf(GemmArgs a) {
     }
 
     if (MODE == 0) {
-        // H = silu(gate) * up; the workgroup's columns are NW/4 groups of 128 H
-        // columns, whose per-row sums (of the bf16 values) feed the down GEMM
+        // H = silu(gate) * up; the workgroup's columns are NTILE/256 groups of
+        // 128 H columns, whose per-row sums (of the bf16 values) feed the down
+        // GEMM's zero-offset term
+        constexpr int WPG = 16 / NB;   // waves per 128-wide H group
+        static_assert(NB % 2 == 0 && NW % WPG == 0, "a workgroup covers whole 128-wide H groups");
         float hs[MI][4];
 #pragma unroll
         for (int mi = 0; mi < MI; mi++)
 #pragma unroll
             for (int r = 0; r < 4; r++) hs[mi][r] = 0.0f;
 #pragma unroll
-        for (int pr = 0; pr < 2; pr++) {
+        for (int pr = 0; pr < NB / 2; pr++) {
             const int col = ((ib0 + 2 * pr) >> 1) * 16 + (lane & 15);
 #pragma unroll
             for (int mi = 0; mi < MI; mi++)
@@ -1277,12 +1303,14 @@ __global__ __launch_bounds__(64 * NW, OCC) void k_gemm_gpf(GemmArgs a) {
                 if ((lane & 15) == 0) red[wave * BM + mi * 16 + lrow + r] = v;
             }
         __syncthreads();
-        if ((int)threadIdx.x < BM * (NW / 4)) {
-            const int h = threadIdx.x / BM, row = threadIdx.x % BM;
+        for (int t = threadIdx.x; t < BM * (NW / WPG); t += 64 * NW) {
+            const int h = t / BM, row = t % BM;
             const int grp = n0 / 256 + h;   // 128-wide H group
             if (row < rows && grp < ew.F / 128) {
-                const float *rr = red + 4 * h * BM + row;
-                const float v = rr[0] + rr[BM] + rr[2 * BM] + rr[3 * BM];
+                const float *rr = red + WPG * h * BM + row;
+                float v = 0.0f;
+#pragma unroll
+                for (int w = 0; w < WPG; w++) v += rr[w * BM];
                 a.hsum[(size_t)(tl.row0 + row) * (a.ldh / 128) + grp] = -ZC * v;
             }
         }
@@ -1296,8 +1324,8 @@ __global__ __launch_bounds__(64 * NW, OCC) void k_gemm_gpf(GemmArgs a) {
                 const int gr = tl.row0 + row;
                 const float wt = gr < a.P ? a.wrow[gr] : 1.0f;
 #pragma unroll
-                for (int nb = 0; nb < 4; nb++) {
-                    const int n = n0 + 64 * wave + 16 * nb + (lane & 15);
+                for (int nb = 0; nb < NB; nb++) {
+                    const int n = n0 + WCOLS * wave + 16 * nb + (lane & 15);
                     if (wave_on) store_o(a.O + (size_t)gr * a.d + n, acc[mi][nb][r] * wt);
                 }
             }
@@ -1590,13 +1618,18 @@ template <int MODE>
 static hipError_t launch_gemm(int df, int bm, int max_tiles, int maxN, const GemmArgs &a0, hipStream_t s) {
     GemmArgs a = a0;
     a.n_tiles = (maxN + 255) / 256;
-    if (bm == 64 && (df == DF_I4SYM || df == DF_I4ASYM)) {
-        // prefill tiles: 64 rows x 256 columns, 4 waves, two stages, two
-        // workgroups per CU (<= 256 VGPRs, 33 KB LDS each)
+    if ((bm == 64 || bm == 96) && (df == DF_I4SYM || df == DF_I4ASYM)) {
+        // prefill tiles: bm rows x 256 columns, 4 waves of bm x 64, two stages,
+        // two workgroups per CU (<= 256 VGPRs; 33 KB / 50 KB LDS each)
         const long total = (long)max_tiles * a.n_tiles;
         dim3 grid((unsigned)(8 * ((total + 7) / 8)));
-        if (df == DF_I4SYM) hipLaunchKernelGGL((k_gemm_gpf<DF_I4SYM, MODE, 4, 4, 2, 2>), grid, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((k_gemm_gpf<DF_I4ASYM, MODE, 4, 4, 2, 2>), grid, dim3(256), 0, s, a);
+        if (bm == 64) {
+            if (df == DF_I4SYM) hipLaunchKernelGGL((k_gemm_gpf<DF_I4SYM, MODE, 4, 4, 4, false>), grid, dim3(256), 0, s, a);
+            else hipLaunchKernelGGL((k_gemm_gpf<DF_I4ASYM, MODE, 4, 4, 4, false>), grid, dim3(256), 0, s, a);
+        } else {
+            if (df == DF_I4SYM) hipLaunchKernelGGL((k_gemm_gpf<DF_I4SYM, MODE, 6, 4, 4, true>), grid, dim3(256), 0, s, a);
+            else hipLaunchKernelGGL((k_gemm_gpf<DF_I4ASYM, MODE, 6, 4, 4, true>), grid, dim3(256), 0, s, a);
+        }
         return hipGetLastError();
     }
     if (bm == 16) {

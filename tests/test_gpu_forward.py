@@ -66,6 +66,16 @@ def test_forward_tile_shapes(oracle_mod, fmt, T, E, k):
     run_and_check(oracle_mod, small(fmt, T=T, E=E, k=k, d=256, F=384), seed=T + E, tag=f"{fmt} T={T} E={E} k={k}")
 
 
+@pytest.mark.parametrize("fmt", ["int4_asym_g128", "int4_sym_g128", "int3_sym_g128"])
+@pytest.mark.parametrize("S", [0, 1])
+def test_forward_96_row_tiles(oracle_mod, fmt, S):
+    # 650 routed rows per expert on average: the grouped formats take 96-row
+    # M-tiles (6 full tiles and a 74-row tail per expert, a 52-row tail per
+    # shared expert); F = 384 gives the down GEMM an odd number of K groups
+    cfg = small(fmt, name=f"tiles96_{fmt}_S{S}", T=1300, E=2, k=1, F=384, S=S, Fs=256 if S else 0)
+    run_and_check(oracle_mod, cfg, tag=f"96-row tiles {fmt} S={S}")
+
+
 @pytest.mark.parametrize("T,E,k,fmt", [(64, 256, 8, "int4_sym_g128"), (64, 256, 8, "fp8e4m3_ch"),
                                         (8, 300, 6, "int4_asym_g128"), (3, 16, 16, "int4_sym_g128")])
 def test_forward_small_batch_router_limits(oracle_mod, T, E, k, fmt):
