@@ -51,20 +51,53 @@ __device__ __forceinline__ void split_bf16(float v, __bf16 &hi, __bf16 &lo) {
 }
 
 // ---------------------------------------------------------------------------
+// Asynchronous global -> LDS copies and raw waits
+// ---------------------------------------------------------------------------
+
+// s_waitcnt immediate (gfx9 encoding): wait until at most `vm` vector-memory
+// operations are outstanding and all LDS operations have completed.
+template <int VM>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+    static_assert(VM >= 0 && VM < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | (0 << 8) | ((VM >> 4) << 14));
+}
+// Workgroup barrier without the compiler's fence (which would drain every
+// outstanding load); the memory clobber keeps LDS accesses on their side.
+__device__ __forceinline__ void raw_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+// Global -> LDS copies (16 or 4 bytes per lane; LDS destination in M0)
+// addressed as a wave-uniform 64-bit base in SGPRs plus a 32-bit per-lane
+// byte offset: advancing through K moves only the scalar base.
+__device__ __forceinline__ void dma16s(const void *sbase, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void dma4s(const void *sbase, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
+                 : "memory", "m0");
+}
+
+// ---------------------------------------------------------------------------
 // Router
 // ---------------------------------------------------------------------------
 
-// Workgroup = 4 waves over one tile of 16*MT tokens x 16*NT experts; the waves
-// split d into four quarters (more independent loads in flight per workgroup)
-// and combine their partial tiles through LDS. Workgroups of the first expert
-// tile also emit the per-128-group row sums of x (times xscale) that the
-// integer-code expert GEMM uses (xsum may be NULL).
-template <int MT, int NT>
-__global__ __launch_bounds__(256) void k_router_bf16(const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr,
-                                                     const float *__restrict__ bias, float *__restrict__ logits,
-                                                     float *__restrict__ xsum, float xscale, int T, int d, int E) {
-    __shared__ f32x4 red[3][MT * NT][64];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// Workgroup = NW waves over one tile of 16*MT tokens x 16*NT experts; the
+// waves split d into NW slices and combine their partial tiles through LDS.
+// Each wave streams its slice one 128-wide group per iteration through a
+// two-slot register ring, the next group's loads issued before the current
+// group's MFMAs. Workgroups of the first expert tile also emit the
+// per-128-group row sums of x (times xscale) that the integer-code expert
+// GEMM uses (xsum may be NULL; needs d % (128 * NW) == 0).
+template <int MT, int NT, int NW>
+__global__ __launch_bounds__(64 * NW) void k_router_bf16(const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr,
+                                                         const float *__restrict__ bias, float *__restrict__ logits,
+                                                         float *__restrict__ xsum, float xscale, int T, int d, int E) {
+    __shared__ f32x4 red[NW - 1][MT * NT][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     // XCD-aware numbering (workgroup L runs on XCD L % 8): the expert tiles of
     // one token tile are consecutive workgroups of one XCD, so its L2 fetches
     // the tile's x rows once; the grid's y extent is padded to a multiple of 8
@@ -74,18 +107,21 @@ __global__ __launch_bounds__(256) void k_router_bf16(const uint16_t *__restrict_
     const int t0 = tt * 16 * MT;
     const int e0 = et * 16 * NT;
     if (t0 >= T) return;
+    // rows past T read the tile's first row and experts past E read the first
+    // expert of the tile; both only feed outputs that are not stored
     const int kq = (lane >> 4) * 8;
-    const uint16_t *ap[MT];
+    const uint16_t *xb = x + (size_t)t0 * d;
+    const uint16_t *wb = wr + (size_t)e0 * d;
+    uint32_t aoff[MT], boff[NT];
 #pragma unroll
     for (int i = 0; i < MT; i++) {
-        const int t = t0 + 16 * i + (lane & 15);
-        ap[i] = x + (size_t)(t < T ? t : 0) * d + kq;
+        const int r = 16 * i + (lane & 15);
+        aoff[i] = (uint32_t)((t0 + r < T ? r : 0) * d + kq);
     }
-    const uint16_t *bp[NT];
 #pragma unroll
     for (int i = 0; i < NT; i++) {
-        const int e = e0 + 16 * i + (lane & 15);
-        bp[i] = wr + (size_t)(e < E ? e : 0) * d + kq;
+        const int r = 16 * i + (lane & 15);
+        boff[i] = (uint32_t)((e0 + r < E ? r : 0) * d + kq);
     }
     f32x4 acc[MT][NT];
 #pragma unroll
@@ -93,21 +129,24 @@ __global__ __launch_bounds__(256) void k_router_bf16(const uint16_t *__restrict_
 #pragma unroll
         for (int j = 0; j < NT; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     const bool do_sum = xsum != nullptr && et == 0;
-    // One 128-wide group (4 k-steps) per iteration: every load of the group is
-    // issued before its MFMAs. Loads are unconditional: rows past T and
-    // experts past E read row 0 / expert 0 and only feed outputs that are not
-    // stored; k-steps past this wave's range read its last step and are skipped.
-    const int kw = d / 4, kbeg = wave * kw, kend = kbeg + kw;
-    for (int k0 = kbeg; k0 < kend; k0 += 128) {
-        uint4 av[4][MT], bv[4][NT];
+    const int kw = d / NW, kbeg = wave * kw, kend = kbeg + kw;
+    const int nit = (kw + 127) / 128;
+    // every iteration issues the same loads: k-steps past the slice read its
+    // last step (and are skipped), iterations past the last reread it
+    uint4 av[2][4][MT], bv[2][4][NT];
+    auto load = [&](int it, int slot) {
+        const int k0 = kbeg + 128 * min(it, nit - 1);
 #pragma unroll
         for (int u = 0; u < 4; u++) {
             const int kk = min(k0 + 32 * u, kend - 32);
 #pragma unroll
-            for (int i = 0; i < MT; i++) av[u][i] = gload16(ap[i] + kk);
+            for (int i = 0; i < MT; i++) av[slot][u][i] = gload16(xb + aoff[i] + kk);
 #pragma unroll
-            for (int j = 0; j < NT; j++) bv[u][j] = gload16(bp[j] + kk);
+            for (int j = 0; j < NT; j++) bv[slot][u][j] = gload16(wb + boff[j] + kk);
         }
+    };
+    auto compute = [&](int it, int slot) {
+        const int k0 = kbeg + 128 * it;
         float gs[MT];
 #pragma unroll
         for (int i = 0; i < MT; i++) gs[i] = 0.0f;
@@ -118,19 +157,19 @@ __global__ __launch_bounds__(256) void k_router_bf16(const uint16_t *__restrict_
             for (int j = 0; j < NT; j++)
 #pragma unroll
                 for (int i = 0; i < MT; i++)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[u][i]),
-                                                                        __builtin_bit_cast(bf16x8, bv[u][j]),
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[slot][u][i]),
+                                                                        __builtin_bit_cast(bf16x8, bv[slot][u][j]),
                                                                         acc[i][j], 0, 0, 0);
             if (do_sum) {
 #pragma unroll
                 for (int i = 0; i < MT; i++) {
-                    const uint32_t q[4] = {av[u][i].x, av[u][i].y, av[u][i].z, av[u][i].w};
+                    const uint4 q4 = av[slot][u][i];
+                    const uint32_t q[4] = {q4.x, q4.y, q4.z, q4.w};
 #pragma unroll
                     for (int c = 0; c < 4; c++) gs[i] += bf16f(q[c] & 0xFFFFu) + bf16f(q[c] >> 16);
                 }
             }
         }
-        // the fused row sums need whole groups per wave (d % 512 == 0)
         if (do_sum) {
 #pragma unroll
             for (int i = 0; i < MT; i++) {
@@ -141,7 +180,17 @@ __global__ __launch_bounds__(256) void k_router_bf16(const uint16_t *__restrict_
                 if (lane < 16 && t < T) xsum[(size_t)t * (d / 128) + k0 / 128] = v * xscale;
             }
         }
+    };
+    load(0, 0);
+    int it = 0;
+    for (; it + 1 < nit; it += 2) {
+        load(it + 1, 1);
+        compute(it, 0);
+        load(it + 2, 0);
+        compute(it + 1, 1);
     }
+    if (it < nit) compute(it, 0);
+
     if (wave > 0) {
 #pragma unroll
         for (int i = 0; i < MT; i++)
@@ -154,8 +203,9 @@ __global__ __launch_bounds__(256) void k_router_bf16(const uint16_t *__restrict_
     for (int i = 0; i < MT; i++)
 #pragma unroll
         for (int j = 0; j < NT; j++) {
-            const f32x4 v = acc[i][j] + red[0][i * NT + j][lane] + red[1][i * NT + j][lane] +
-                            red[2][i * NT + j][lane];
+            f32x4 v = acc[i][j];
+#pragma unroll
+            for (int w = 0; w < NW - 1; w++) v += red[w][i * NT + j][lane];
             const int e = e0 + 16 * j + (lane & 15);
             if (e >= E) continue;
             const float b = bias ? bias[e] : 0.0f;
@@ -165,6 +215,168 @@ __global__ __launch_bounds__(256) void k_router_bf16(const uint16_t *__restrict_
                 if (t < T) logits[(size_t)t * E + e] = v[r] + b;
             }
         }
+}
+
+// Router for larger batches: a tile of BT tokens x BE experts per workgroup.
+// The x rows and router rows of each 128-wide K group are copied into LDS with
+// asynchronous global -> LDS copies, whole 256-byte row segments per 16 lanes
+// (fragment-shaped global loads of 64 bytes per row run at a third of the L2
+// bandwidth), XOR-swizzled (chunk c of row r at c ^ (r & 15)) so the MFMA
+// fragment reads are conflict-free, NST groups in flight.
+//   WE > 1 (shared): the waves split the tile's experts WE ways and copy each
+//     group together, one barrier per group.
+//   WE = 1 (streams): every wave computes the whole tile over every fourth
+//     group, staged in its own LDS ring with no barrier; the four partial
+//     tiles are added through LDS at the end.
+// Workgroups of the first expert tile also emit the per-group row sums of x
+// (times xscale) read from the staged tile.
+template <int BT, int BE, int WE, int NST>
+__global__ __launch_bounds__(256) void k_router_lds(const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr,
+                                                    const float *__restrict__ bias, float *__restrict__ logits,
+                                                    float *__restrict__ xsum, float xscale, int T, int d, int E) {
+    constexpr bool STREAMS = WE == 1;
+    static_assert(WE == 1 || WE == 4, "four waves: streams or a four-way expert split");
+    constexpr int MT = BT / 16, NT = BE / (16 * WE);
+    static_assert(MT * 16 == BT && NT * 16 * WE == BE, "whole 16-blocks per wave");
+    constexpr int ROWS = BT + BE;                       // staged rows per group, x first
+    constexpr int CPW = STREAMS ? ROWS / 4 : ROWS / 16;   // 1 KB copies per wave per group
+    static_assert(ROWS % (STREAMS ? 4 : 16) == 0, "whole 4-row copies per wave");
+    constexpr int ST = ROWS * 256;                      // bytes per stage
+    constexpr int RINGS = STREAMS ? 4 : 1;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[RINGS * NST * ST + (STREAMS ? 3 * MT * NT * 1024 : 0)];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int L = blockIdx.x + blockIdx.y * gridDim.x;
+    const int xcd = L & 7, j = L >> 3;
+    const int et = j % gridDim.x, tt = (j / gridDim.x) * 8 + xcd;
+    const int t0 = tt * BT;
+    const int e0 = et * BE;
+    if (t0 >= T) return;
+    const uint32_t ring0 = lds_addr(lds) + (STREAMS ? wave * NST * ST : 0);
+    const uint8_t *ringp = lds + (STREAMS ? wave * NST * ST : 0);
+    const int G = d / 128;
+    // groups this wave takes: all (shared) or wave, wave + 4, ... (streams)
+    const int gstep = STREAMS ? 4 : 1, gfirst = STREAMS ? wave : 0;
+    const int ng = STREAMS ? (G - wave + 3) / 4 : G;
+
+    // copy sources: 4-row slabs, each wholly x or wholly router rows, as the
+    // tile's first row in SGPRs plus a per-lane byte offset below 256 * d;
+    // rows past T / E read the tile's first row (their results are not stored)
+    uint32_t soff[CPW];
+    const uint16_t *sbase[CPW];
+    const uint16_t *xt = x + (size_t)t0 * d, *wt0 = wr + (size_t)e0 * d;
+    const int slab0 = STREAMS ? 0 : CPW * wave;
+#pragma unroll
+    for (int i = 0; i < CPW; i++) {
+        const int row = 4 * (slab0 + i) + (lane >> 4);   // staged row
+        const int sw = ((lane & 15) ^ (row & 15)) * 16;   // source chunk of this lane's LDS slot
+        const bool is_x = 4 * (slab0 + i) < BT;           // uniform over the slab
+        const int r = is_x ? row : row - BT;
+        const bool ok = is_x ? t0 + r < T : e0 + r < E;
+        sbase[i] = is_x ? xt : wt0;
+        soff[i] = (uint32_t)(ok ? r : 0) * (uint32_t)d * 2u + (uint32_t)sw;
+    }
+    // copies of this wave's q-th group (clamped to its last) into stage st
+    auto issue = [&](int q, int st) {
+        const int g = gfirst + gstep * min(q, ng - 1);
+        const uint32_t sb = ring0 + st * ST;
+#pragma unroll
+        for (int i = 0; i < CPW; i++)
+            dma16s(reinterpret_cast<const uint8_t *>(sbase[i]) + g * 256, soff[i], sb + (slab0 + i) * 1024);
+    };
+
+    f32x4 acc[MT][NT];
+#pragma unroll
+    for (int i = 0; i < MT; i++)
+#pragma unroll
+        for (int jj = 0; jj < NT; jj++) acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const bool do_sum = xsum != nullptr && et == 0;
+    const int we = STREAMS ? 0 : wave;
+
+    if (ng > 0) {   // uniform; a stream with no group (G < 4) only adds zeros
+#pragma unroll
+        for (int p = 0; p < NST - 1; p++) issue(p, p);
+        for (int q = 0; q < ng; q++) {
+            wait_vm_lgkm0<(NST - 2) * CPW>();
+            if constexpr (!STREAMS) raw_barrier();
+            const int st = q % NST;
+            // refill the stage read one group ago (in shared mode every wave
+            // passed this group's barrier, so all are done with it)
+            issue(q + NST - 1, (q + NST - 1) % NST);
+            const uint16_t *S = reinterpret_cast<const uint16_t *>(ringp + st * ST);
+#pragma unroll
+            for (int s = 0; s < 4; s++) {
+                const int pc = (s * 4 + (lane >> 4)) ^ (lane & 15);
+                bf16x8 af[MT], bfr[NT];
+#pragma unroll
+                for (int i = 0; i < MT; i++)
+                    af[i] = *reinterpret_cast<const bf16x8 *>(&S[(16 * i + (lane & 15)) * 128 + pc * 8]);
+#pragma unroll
+                for (int jj = 0; jj < NT; jj++)
+                    bfr[jj] = *reinterpret_cast<const bf16x8 *>(&S[(BT + 16 * (we * NT + jj) + (lane & 15)) * 128 + pc * 8]);
+#pragma unroll
+                for (int i = 0; i < MT; i++)
+#pragma unroll
+                    for (int jj = 0; jj < NT; jj++)
+                        acc[i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[jj], acc[i][jj], 0, 0, 0);
+            }
+            if (do_sum) {
+                // 16 lanes per staged x row, one 16-byte chunk each; in shared
+                // mode the workgroup's threads split the rows, in streams mode
+                // each wave sums its own group
+                const int g = gfirst + gstep * q;
+                constexpr int NTH = STREAMS ? 64 : 256;
+                const int tid = STREAMS ? lane : (int)threadIdx.x;
+#pragma unroll
+                for (int c0 = 0; c0 < BT * 16; c0 += NTH) {
+                    const int c = c0 + tid;
+                    const int row = c >> 4;
+                    const uint4 q4 = *reinterpret_cast<const uint4 *>(&S[row * 128 + ((c & 15) ^ (row & 15)) * 8]);
+                    const uint32_t qq[4] = {q4.x, q4.y, q4.z, q4.w};
+                    float v = 0.0f;
+#pragma unroll
+                    for (int k = 0; k < 4; k++) v += bf16f(qq[k] & 0xFFFFu) + bf16f(qq[k] >> 16);
+#pragma unroll
+                    for (int off = 1; off < 16; off <<= 1) v += __shfl_xor(v, off);
+                    const int t = t0 + row;
+                    if ((c & 15) == 0 && t < T) xsum[(size_t)t * G + g] = v * xscale;
+                }
+            }
+        }
+        // no copy may still be writing LDS when the ring is reused or freed
+        __builtin_amdgcn_s_waitcnt(0);
+    }
+
+    if constexpr (STREAMS) {
+        f32x4 *red = reinterpret_cast<f32x4 *>(lds + RINGS * NST * ST);
+        if (wave > 0) {
+#pragma unroll
+            for (int i = 0; i < MT; i++)
+#pragma unroll
+                for (int jj = 0; jj < NT; jj++) red[((wave - 1) * MT * NT + i * NT + jj) * 64 + lane] = acc[i][jj];
+        }
+        __syncthreads();
+        if (wave > 0) return;
+#pragma unroll
+        for (int w = 0; w < 3; w++)
+#pragma unroll
+            for (int i = 0; i < MT; i++)
+#pragma unroll
+                for (int jj = 0; jj < NT; jj++) acc[i][jj] += red[(w * MT * NT + i * NT + jj) * 64 + lane];
+    }
+#pragma unroll
+    for (int jj = 0; jj < NT; jj++) {
+        const int e = e0 + 16 * (we * NT + jj) + (lane & 15);
+        if (e >= E) continue;
+        const float b = bias ? bias[e] : 0.0f;
+#pragma unroll
+        for (int i = 0; i < MT; i++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int t = t0 + 16 * i + (lane >> 4) * 4 + r;
+                if (t < T) logits[(size_t)t * E + e] = acc[i][jj][r] + b;
+            }
+    }
 }
 
 __global__ __launch_bounds__(256) void k_router_f32(const uint16_t *__restrict__ x, const float *__restrict__ wr,
@@ -1009,17 +1221,6 @@ __device__ __forceinline__ bool map_work(int L, int ntiles, int NT, int &tile, i
     return true;
 }
 
-// s_waitcnt immediate (gfx9 encoding): wait until at most `vm` vector-memory
-// operations are outstanding and all LDS operations have completed.
-template <int VM>
-__device__ __forceinline__ void wait_vm_lgkm0() {
-    static_assert(VM >= 0 && VM < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | (0 << 8) | ((VM >> 4) << 14));
-}
-// Workgroup barrier without the compiler's fence (which would drain every
-// outstanding load); the memory clobber keeps LDS accesses on their side.
-__device__ __forceinline__ void raw_barrier() { asm volatile("s_barrier" ::: "memory"); }
-
 // ---- 64-row tiles (prefill): activation ring in LDS, XCD-aware ------------
 //
 // Per wave and group (128 K positions): the gathered activation rows and their
@@ -1029,21 +1230,6 @@ __device__ __forceinline__ void raw_barrier() { asm volatile("s_barrier" ::: "me
 // scales are ordinary loads into a two-slot register ring, also one group
 // ahead. Every group ends with all loads landed (vmcnt 0) and one barrier that
 // publishes the next activation tile to the workgroup.
-__device__ __forceinline__ uint32_t lds_addr(const void *p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
-}
-// Global -> LDS copies (16 or 4 bytes per lane; LDS destination in M0)
-// addressed as a wave-uniform 64-bit base in SGPRs plus a 32-bit per-lane
-// byte offset: advancing through K moves only the scalar base.
-__device__ __forceinline__ void dma16s(const void *sbase, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
-                 : "memory", "m0");
-}
-__device__ __forceinline__ void dma4s(const void *sbase, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
-                 : "memory", "m0");
-}
-
 template <int DF, int MODE, int MI, int NB, int NW, bool ROW_OUTER>
 __global__ __launch_bounds__(64 * NW, 2) void k_gemm_gpf(GemmArgs a) {
     constexpr int BM = 16 * MI, RPW = BM / NW;   // activation rows copied per wave
@@ -1511,27 +1697,45 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ O, co
 // ---------------------------------------------------------------------------
 
 // Expert tiles of 64 for many experts, 32, or 16 when E <= 16 (no idle half tile).
-template <int MT>
+template <int MT, int NW>
 static void launch_router_mt(const uint16_t *x, const uint16_t *wr, const float *bias, float *logits, float *xsum,
                              float xscale, int T, int d, int E, hipStream_t s) {
     const int gx = 8 * ((T + 16 * MT * 8 - 1) / (16 * MT * 8));   // token tiles, padded to a multiple of 8
     if (E > 64)
-        hipLaunchKernelGGL((k_router_bf16<MT, 4>), dim3((E + 63) / 64, gx), dim3(256), 0, s, x, wr, bias, logits, xsum,
-                           xscale, T, d, E);
+        hipLaunchKernelGGL((k_router_bf16<MT, 4, NW>), dim3((E + 63) / 64, gx), dim3(64 * NW), 0, s, x, wr, bias, logits,
+                           xsum, xscale, T, d, E);
     else if (E > 16)
-        hipLaunchKernelGGL((k_router_bf16<MT, 2>), dim3((E + 31) / 32, gx), dim3(256), 0, s, x, wr, bias, logits, xsum,
-                           xscale, T, d, E);
+        hipLaunchKernelGGL((k_router_bf16<MT, 2, NW>), dim3((E + 31) / 32, gx), dim3(64 * NW), 0, s, x, wr, bias, logits,
+                           xsum, xscale, T, d, E);
     else
-        hipLaunchKernelGGL((k_router_bf16<MT, 1>), dim3(1, gx), dim3(256), 0, s, x, wr, bias, logits, xsum, xscale,
-                           T, d, E);
+        hipLaunchKernelGGL((k_router_bf16<MT, 1, NW>), dim3(1, gx), dim3(64 * NW), 0, s, x, wr, bias, logits, xsum,
+                           xscale, T, d, E);
+}
+
+constexpr int kRouterStagedMinT = 256;
+
+template <int BT, int BE, int WE, int NST>
+static void launch_router_lds(const uint16_t *x, const uint16_t *wr, const float *bias, float *logits, float *xsum,
+                              float xscale, int T, int d, int E, hipStream_t s) {
+    const int gx = 8 * ((T + BT * 8 - 1) / (BT * 8));   // token tiles, padded to a multiple of 8
+    hipLaunchKernelGGL((k_router_lds<BT, BE, WE, NST>), dim3((E + BE - 1) / BE, gx), dim3(256), 0, s, x, wr, bias,
+                       logits, xsum, xscale, T, d, E);
 }
 
 hipError_t launch_router_bf16(const uint16_t *x, const uint16_t *wr, const float *bias, float *logits, float *xsum,
                               float xscale, int T, int d, int E, hipStream_t s) {
-    if (T >= 256)
-        launch_router_mt<2>(x, wr, bias, logits, xsum, xscale, T, d, E, s);
-    else
-        launch_router_mt<1>(x, wr, bias, logits, xsum, xscale, T, d, E, s);
+    if (T >= kRouterStagedMinT) {
+        // streams for few experts (LDS: 4 rings of 3 x 8 / 12 KB), a shared
+        // four-way expert split above (3 x 20 KB, 2 x 40 KB)
+        if (E <= 16) launch_router_lds<16, 16, 1, 3>(x, wr, bias, logits, xsum, xscale, T, d, E, s);
+        else if (E <= 32) launch_router_lds<16, 32, 1, 3>(x, wr, bias, logits, xsum, xscale, T, d, E, s);
+        else if (E <= 64) launch_router_lds<16, 64, 4, 3>(x, wr, bias, logits, xsum, xscale, T, d, E, s);
+        else launch_router_lds<32, 128, 4, 2>(x, wr, bias, logits, xsum, xscale, T, d, E, s);
+        return hipGetLastError();
+    }
+    // fewer tokens: fragment-shaped loads straight to registers, four waves
+    // splitting d
+    launch_router_mt<1, 4>(x, wr, bias, logits, xsum, xscale, T, d, E, s);
     return hipGetLastError();
 }
 

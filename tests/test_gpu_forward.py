@@ -66,6 +66,19 @@ def test_forward_tile_shapes(oracle_mod, fmt, T, E, k):
     run_and_check(oracle_mod, small(fmt, T=T, E=E, k=k, d=256, F=384), seed=T + E, tag=f"{fmt} T={T} E={E} k={k}")
 
 
+@pytest.mark.parametrize("T,E,fmt", [(256, 5, "int4_asym_g128"), (300, 16, "int4_sym_g128"),
+                                     (257, 24, "int4_asym_g128"), (700, 48, "int4_sym_g128"),
+                                     (513, 64, "int4_asym_g128"), (300, 100, "int4_sym_g128"),
+                                     (1000, 128, "int4_asym_g128"), (260, 200, "int4_sym_g128"),
+                                     (300, 300, "fp8e4m3_ch")])
+def test_forward_staged_router_tiles(oracle_mod, T, E, fmt):
+    # batches of >= 256 tokens take the router that stages x and router rows
+    # through LDS: expert tiles of 16, 32, 64 or 128 rows (several tiles for
+    # E > 128), ragged T and E, fused row sums of x for the group formats
+    cfg = small(fmt, name=f"router_{T}_{E}_{fmt}", T=T, E=E, k=min(4, E))
+    run_and_check(oracle_mod, cfg, tag=f"staged router T={T} E={E} {fmt}")
+
+
 @pytest.mark.parametrize("fmt", ["int4_asym_g128", "int4_sym_g128", "int3_sym_g128"])
 @pytest.mark.parametrize("S", [0, 1])
 def test_forward_96_row_tiles(oracle_mod, fmt, S):
