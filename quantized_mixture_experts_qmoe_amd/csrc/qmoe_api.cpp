@@ -492,18 +492,12 @@ int qmoe_forward(qmoe_ctx *c, const uint16_t *x, int32_t T, uint16_t *y, qmoe_ro
     // Row sums of x: the prefill GEMMs of the group formats read them; the
     // decode kernel (bm == 16) computes its own while staging rows.
     const bool need_sums = grouped && bm > 16;
-    // small batches: a router grid of 16 x 16 tiles without the row sums
-    const bool small_router = !c->cfg.router_fp32 && T <= kSmallRouteMaxT;
-    // the bf16 router emits the row sums when each of its four waves covers whole 128-wide groups
-    const bool fused_sums = need_sums && !small_router && !c->cfg.router_fp32 && c->d % 512 == 0;
+    // the bf16 router emits the row sums from its staged x tiles
+    const bool fused_sums = need_sums && !c->cfg.router_fp32;
     int rc;
     if (c->cfg.router_fp32)
         rc = timed(c, K_ROUTER, s, [&] {
             return launch_router_f32(x, (const float *)c->router_w, c->router_b, c->logits, T, c->d, c->E, s);
-        });
-    else if (small_router)
-        rc = timed(c, K_ROUTER, s, [&] {
-            return launch_router_small(x, (const uint16_t *)c->router_w, c->router_b, c->logits, T, c->d, c->E, s);
         });
     else
         rc = timed(c, K_ROUTER, s, [&] {

@@ -124,9 +124,6 @@ hipError_t launch_router_bf16(const uint16_t *x, const uint16_t *wr, const float
 hipError_t launch_router_f32(const uint16_t *x, const float *wr, const float *bias, float *logits, int T, int d, int E,
                              hipStream_t s);
 hipError_t launch_topk(const float *logits, int T, int E, int k, int renorm, int32_t *idx, float *w, hipStream_t s);
-// Small batches (T <= kSmallRouteMaxT): bf16 MFMA router without row sums.
-hipError_t launch_router_small(const uint16_t *x, const uint16_t *wr, const float *bias, float *logits, int T, int d,
-                               int E, hipStream_t s);
 // Dispatch: per-chunk histogram, scan + tile list, stable scatter.
 constexpr int kDispatchChunk = 1024;
 // One-workgroup top-k + dispatch for small batches.

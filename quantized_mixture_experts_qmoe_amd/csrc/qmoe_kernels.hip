@@ -84,139 +84,6 @@ __device__ __forceinline__ void dma4s(const void *sbase, uint32_t voff, uint32_t
 // Router
 // ---------------------------------------------------------------------------
 
-// Workgroup = NW waves over one tile of 16*MT tokens x 16*NT experts; the
-// waves split d into NW slices and combine their partial tiles through LDS.
-// Each wave streams its slice one 128-wide group per iteration through a
-// two-slot register ring, the next group's loads issued before the current
-// group's MFMAs. Workgroups of the first expert tile also emit the
-// per-128-group row sums of x (times xscale) that the integer-code expert
-// GEMM uses (xsum may be NULL; needs d % (128 * NW) == 0).
-template <int MT, int NT, int NW>
-__global__ __launch_bounds__(64 * NW) void k_router_bf16(const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr,
-                                                         const float *__restrict__ bias, float *__restrict__ logits,
-                                                         float *__restrict__ xsum, float xscale, int T, int d, int E) {
-    __shared__ f32x4 red[NW - 1][MT * NT][64];
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    // XCD-aware numbering (workgroup L runs on XCD L % 8): the expert tiles of
-    // one token tile are consecutive workgroups of one XCD, so its L2 fetches
-    // the tile's x rows once; the grid's y extent is padded to a multiple of 8
-    const int L = blockIdx.x + blockIdx.y * gridDim.x;
-    const int xcd = L & 7, j = L >> 3;
-    const int et = j % gridDim.x, tt = (j / gridDim.x) * 8 + xcd;
-    const int t0 = tt * 16 * MT;
-    const int e0 = et * 16 * NT;
-    if (t0 >= T) return;
-    // rows past T read the tile's first row and experts past E read the first
-    // expert of the tile; both only feed outputs that are not stored
-    const int kq = (lane >> 4) * 8;
-    const uint16_t *xb = x + (size_t)t0 * d;
-    const uint16_t *wb = wr + (size_t)e0 * d;
-    uint32_t aoff[MT], boff[NT];
-#pragma unroll
-    for (int i = 0; i < MT; i++) {
-        const int r = 16 * i + (lane & 15);
-        aoff[i] = (uint32_t)((t0 + r < T ? r : 0) * d + kq);
-    }
-#pragma unroll
-    for (int i = 0; i < NT; i++) {
-        const int r = 16 * i + (lane & 15);
-        boff[i] = (uint32_t)((e0 + r < E ? r : 0) * d + kq);
-    }
-    f32x4 acc[MT][NT];
-#pragma unroll
-    for (int i = 0; i < MT; i++)
-#pragma unroll
-        for (int j = 0; j < NT; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const bool do_sum = xsum != nullptr && et == 0;
-    const int kw = d / NW, kbeg = wave * kw, kend = kbeg + kw;
-    const int nit = (kw + 127) / 128;
-    // every iteration issues the same loads: k-steps past the slice read its
-    // last step (and are skipped), iterations past the last reread it
-    uint4 av[2][4][MT], bv[2][4][NT];
-    auto load = [&](int it, int slot) {
-        const int k0 = kbeg + 128 * min(it, nit - 1);
-#pragma unroll
-        for (int u = 0; u < 4; u++) {
-            const int kk = min(k0 + 32 * u, kend - 32);
-#pragma unroll
-            for (int i = 0; i < MT; i++) av[slot][u][i] = gload16(xb + aoff[i] + kk);
-#pragma unroll
-            for (int j = 0; j < NT; j++) bv[slot][u][j] = gload16(wb + boff[j] + kk);
-        }
-    };
-    auto compute = [&](int it, int slot) {
-        const int k0 = kbeg + 128 * it;
-        float gs[MT];
-#pragma unroll
-        for (int i = 0; i < MT; i++) gs[i] = 0.0f;
-#pragma unroll
-        for (int u = 0; u < 4; u++) {
-            if (k0 + 32 * u >= kend) continue;   // uniform
-#pragma unroll
-            for (int j = 0; j < NT; j++)
-#pragma unroll
-                for (int i = 0; i < MT; i++)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[slot][u][i]),
-                                                                        __builtin_bit_cast(bf16x8, bv[slot][u][j]),
-                                                                        acc[i][j], 0, 0, 0);
-            if (do_sum) {
-#pragma unroll
-                for (int i = 0; i < MT; i++) {
-                    const uint4 q4 = av[slot][u][i];
-                    const uint32_t q[4] = {q4.x, q4.y, q4.z, q4.w};
-#pragma unroll
-                    for (int c = 0; c < 4; c++) gs[i] += bf16f(q[c] & 0xFFFFu) + bf16f(q[c] >> 16);
-                }
-            }
-        }
-        if (do_sum) {
-#pragma unroll
-            for (int i = 0; i < MT; i++) {
-                float v = gs[i];
-                v += __shfl_xor(v, 16);
-                v += __shfl_xor(v, 32);
-                const int t = t0 + 16 * i + lane;
-                if (lane < 16 && t < T) xsum[(size_t)t * (d / 128) + k0 / 128] = v * xscale;
-            }
-        }
-    };
-    load(0, 0);
-    int it = 0;
-    for (; it + 1 < nit; it += 2) {
-        load(it + 1, 1);
-        compute(it, 0);
-        load(it + 2, 0);
-        compute(it + 1, 1);
-    }
-    if (it < nit) compute(it, 0);
-
-    if (wave > 0) {
-#pragma unroll
-        for (int i = 0; i < MT; i++)
-#pragma unroll
-            for (int j = 0; j < NT; j++) red[wave - 1][i * NT + j][lane] = acc[i][j];
-    }
-    __syncthreads();
-    if (wave != 0) return;
-#pragma unroll
-    for (int i = 0; i < MT; i++)
-#pragma unroll
-        for (int j = 0; j < NT; j++) {
-            f32x4 v = acc[i][j];
-#pragma unroll
-            for (int w = 0; w < NW - 1; w++) v += red[w][i * NT + j][lane];
-            const int e = e0 + 16 * j + (lane & 15);
-            if (e >= E) continue;
-            const float b = bias ? bias[e] : 0.0f;
-#pragma unroll
-            for (int r = 0; r < 4; r++) {
-                const int t = t0 + 16 * i + (lane >> 4) * 4 + r;
-                if (t < T) logits[(size_t)t * E + e] = v[r] + b;
-            }
-        }
-}
-
 // Router for larger batches: a tile of BT tokens x BE experts per workgroup.
 // The x rows and router rows of each 128-wide K group are copied into LDS with
 // asynchronous global -> LDS copies, whole 256-byte row segments per 16 lanes
@@ -392,47 +259,6 @@ __global__ __launch_bounds__(256) void k_router_f32(const uint16_t *__restrict__
     logits[i] = acc + (bias ? bias[e] : 0.0f);
 }
 
-// Small batches (T <= 64): one workgroup per 16 tokens x 16 experts. The four
-// waves split d into quarters and keep up to 16 MFMA k-steps of x and W_r
-// operands in flight straight from memory; partial tiles meet in LDS and are
-// summed in wave order.
-__global__ __launch_bounds__(256) void k_router_small(const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr,
-                                                      const float *__restrict__ bias, float *__restrict__ logits,
-                                                      int T, int d, int E) {
-    constexpr int STEPS = 16;
-    __shared__ float part[4][256];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int t = blockIdx.x * 16 + (lane & 15);
-    const int e = blockIdx.y * 16 + (lane & 15);
-    const bool t_ok = t < T, e_ok = e < E;
-    const int q = d / 4;   // a multiple of 64
-    const uint16_t *xa = x + (size_t)(t_ok ? t : 0) * d + wave * q + (lane >> 4) * 8;
-    const uint16_t *wb = wr + (size_t)(e_ok ? e : 0) * d + wave * q + (lane >> 4) * 8;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < q; k0 += STEPS * 32) {
-        uint4 va[STEPS], vb[STEPS];
-#pragma unroll
-        for (int s = 0; s < STEPS; s++) {
-            const bool in = k0 + s * 32 < q;
-            va[s] = (in && t_ok) ? gload16(xa + k0 + s * 32) : make_uint4(0, 0, 0, 0);
-            vb[s] = (in && e_ok) ? gload16(wb + k0 + s * 32) : make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int s = 0; s < STEPS; s++)
-            if (k0 + s * 32 < q)
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va[s]),
-                                                              __builtin_bit_cast(bf16x8, vb[s]), acc, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; i++) part[wave][(4 * (lane >> 4) + i) * 16 + (lane & 15)] = acc[i];
-    __syncthreads();
-    const int row = threadIdx.x >> 4, col = threadIdx.x & 15;
-    const int tt = blockIdx.x * 16 + row, ee = blockIdx.y * 16 + col;
-    if (tt < T && ee < E) {
-        const float v = ((part[0][threadIdx.x] + part[1][threadIdx.x]) + part[2][threadIdx.x]) + part[3][threadIdx.x];
-        logits[(size_t)tt * E + ee] = v + (bias ? bias[ee] : 0.0f);
-    }
-}
 
 // ---------------------------------------------------------------------------
 // Top-k + softmax weights (gating network)
@@ -1697,23 +1523,6 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ O, co
 // ---------------------------------------------------------------------------
 
 // Expert tiles of 64 for many experts, 32, or 16 when E <= 16 (no idle half tile).
-template <int MT, int NW>
-static void launch_router_mt(const uint16_t *x, const uint16_t *wr, const float *bias, float *logits, float *xsum,
-                             float xscale, int T, int d, int E, hipStream_t s) {
-    const int gx = 8 * ((T + 16 * MT * 8 - 1) / (16 * MT * 8));   // token tiles, padded to a multiple of 8
-    if (E > 64)
-        hipLaunchKernelGGL((k_router_bf16<MT, 4, NW>), dim3((E + 63) / 64, gx), dim3(64 * NW), 0, s, x, wr, bias, logits,
-                           xsum, xscale, T, d, E);
-    else if (E > 16)
-        hipLaunchKernelGGL((k_router_bf16<MT, 2, NW>), dim3((E + 31) / 32, gx), dim3(64 * NW), 0, s, x, wr, bias, logits,
-                           xsum, xscale, T, d, E);
-    else
-        hipLaunchKernelGGL((k_router_bf16<MT, 1, NW>), dim3(1, gx), dim3(64 * NW), 0, s, x, wr, bias, logits, xsum,
-                           xscale, T, d, E);
-}
-
-constexpr int kRouterStagedMinT = 256;
-
 template <int BT, int BE, int WE, int NST>
 static void launch_router_lds(const uint16_t *x, const uint16_t *wr, const float *bias, float *logits, float *xsum,
                               float xscale, int T, int d, int E, hipStream_t s) {
@@ -1724,25 +1533,13 @@ static void launch_router_lds(const uint16_t *x, const uint16_t *wr, const float
 
 hipError_t launch_router_bf16(const uint16_t *x, const uint16_t *wr, const float *bias, float *logits, float *xsum,
                               float xscale, int T, int d, int E, hipStream_t s) {
-    if (T >= kRouterStagedMinT) {
-        // streams for few experts (LDS: 4 rings of 3 x 8 / 12 KB), a shared
-        // four-way expert split above (3 x 20 KB, 2 x 40 KB)
-        if (E <= 16) launch_router_lds<16, 16, 1, 3>(x, wr, bias, logits, xsum, xscale, T, d, E, s);
-        else if (E <= 32) launch_router_lds<16, 32, 1, 3>(x, wr, bias, logits, xsum, xscale, T, d, E, s);
-        else if (E <= 64) launch_router_lds<16, 64, 4, 3>(x, wr, bias, logits, xsum, xscale, T, d, E, s);
-        else launch_router_lds<32, 128, 4, 2>(x, wr, bias, logits, xsum, xscale, T, d, E, s);
-        return hipGetLastError();
-    }
-    // fewer tokens: fragment-shaped loads straight to registers, four waves
-    // splitting d
-    launch_router_mt<1, 4>(x, wr, bias, logits, xsum, xscale, T, d, E, s);
-    return hipGetLastError();
-}
-
-hipError_t launch_router_small(const uint16_t *x, const uint16_t *wr, const float *bias, float *logits, int T, int d,
-                               int E, hipStream_t s) {
-    dim3 grid((T + 15) / 16, (E + 15) / 16);
-    hipLaunchKernelGGL(k_router_small, grid, dim3(256), 0, s, x, wr, bias, logits, T, d, E);
+    // 16 x 16 tiles as four independent streams for small batches and few
+    // experts (LDS: 4 rings of 3 x 8 KB); wider expert tiles for large batches
+    // (4 rings of 3 x 12 KB; shared rings of 3 x 20 KB and 2 x 40 KB)
+    if (T < 256 || E <= 16) launch_router_lds<16, 16, 1, 3>(x, wr, bias, logits, xsum, xscale, T, d, E, s);
+    else if (E <= 32) launch_router_lds<16, 32, 1, 3>(x, wr, bias, logits, xsum, xscale, T, d, E, s);
+    else if (E <= 64) launch_router_lds<16, 64, 4, 3>(x, wr, bias, logits, xsum, xscale, T, d, E, s);
+    else launch_router_lds<32, 128, 4, 2>(x, wr, bias, logits, xsum, xscale, T, d, E, s);
     return hipGetLastError();
 }
 
