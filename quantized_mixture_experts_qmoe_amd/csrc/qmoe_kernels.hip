@@ -1039,9 +1039,9 @@ __global__ __launch_bounds__(256) void k_gemm_dec(GemmArgs a) {
     }
 }
 
-// ---- 64-row tiles (prefill): pipelined, XCD-aware -------------------------
+// ---- prefill tiles: XCD-aware work order -----------------------------------
 //
-// Work items (M-tile of the task list, 256-column N-tile) are numbered in bands
+// Work items (M-tile of the task list, N-tile) are numbered in bands
 // of 4 N-tiles with the M-tile slower inside a band, so concurrently running
 // workgroups share both activation rows and packed weights; the numbering is
 // split into 8 contiguous chunks, one per XCD (workgroup L runs on XCD L % 8),
@@ -1061,13 +1061,14 @@ __device__ __forceinline__ bool map_work(int L, int ntiles, int NT, int &tile, i
     return true;
 }
 
-// ---- 64-row tiles (prefill): activation ring in LDS, XCD-aware ------------
+// ---- prefill tiles (group formats): activation ring in LDS ------------------
 //
-// Per wave and group (128 K positions): the gathered activation rows and their
-// row sums travel as asynchronous global -> LDS copies issued from inline
-// assembly (so the compiler neither waits on them before LDS reads nor counts
-// them), one group ahead in a two-stage ring; the wave's own packed codes and
-// scales are ordinary loads into a two-slot register ring, also one group
+// Tiles of 16*MI rows x 16*NB*NW columns: each of the NW waves owns all the
+// rows and 16*NB columns. Per wave and group (128 K positions): the gathered activation
+// rows and their row sums travel as asynchronous global -> LDS copies issued
+// from inline assembly (so the compiler neither waits on them before LDS reads
+// nor counts them), one group ahead in a two-stage ring; the wave's own packed
+// codes and scales are ordinary loads into a register ring, also one group
 // ahead. Every group ends with all loads landed (vmcnt 0) and one barrier that
 // publishes the next activation tile to the workgroup.
 template <int DF, int MODE, int MI, int NB, int NW, bool ROW_OUTER>
@@ -1645,7 +1646,7 @@ static hipError_t launch_gemm(int df, int bm, int max_tiles, int maxN, const Gem
         return launch_gemm_dec<MODE>(df, dim3((maxN + cols - 1) / cols, max_tiles), a, s);
     }
     dim3 grid(a.n_tiles, max_tiles);
-    // per-channel formats, 64-row tiles
+    // per-channel formats (8-bit codes): 64-row tiles
     if (bm != 64) return hipErrorInvalidValue;
     switch (df) {
     case DF_INT8: hipLaunchKernelGGL((k_gemm_c<DF_INT8, MODE, 4>), grid, dim3(256), 0, s, a); break;
