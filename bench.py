@@ -82,9 +82,11 @@ def measured_traffic(kernel: str, workload: str):
 
 
 def cpu_baseline(inp, n_tokens: int = 0, target_s: float = 15.0):
-    """The fp64 oracle on a token sample of the same layer: 16 tokens are timed
-    first to size the sample for about `target_s` seconds (or `n_tokens` when
-    given); the rate is taken over the second, sized run."""
+    """The fp64 oracle on a token sample of the same layer: 16 and 32 tokens are
+    timed first to separate the per-call cost (the oracle dequantizes each
+    expert it uses on every call) from the per-token cost, which sizes the
+    sample for about `target_s` seconds (or `n_tokens` when given); the rate is
+    taken over the final, sized run."""
     from oracle import oracle as O
     cfg = inp.cfg
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
@@ -93,11 +95,15 @@ def cpu_baseline(inp, n_tokens: int = 0, target_s: float = 15.0):
     rng = np.random.default_rng(123)
     order = rng.permutation(cfg.T).astype(np.int32)
     if not n_tokens:
-        probe = np.sort(order[:min(16, cfg.T)])
-        t0 = time.perf_counter()
-        layer.forward(inp.x, tokens=probe)
-        per_token = (time.perf_counter() - t0) / len(probe)
-        n_tokens = int(min(cfg.T, max(16, target_s / max(per_token, 1e-9))))
+        times = []
+        for n in (16, 32):
+            probe = np.sort(order[:min(n, cfg.T)])
+            t0 = time.perf_counter()
+            layer.forward(inp.x, tokens=probe)
+            times.append(time.perf_counter() - t0)
+        per_token = max((times[1] - times[0]) / 16.0, 1e-9)
+        per_call = max(times[0] - 16 * per_token, 0.0)
+        n_tokens = int(min(cfg.T, max(32, (target_s - per_call) / per_token)))
     toks = np.sort(order[:min(n_tokens, cfg.T)])
     log(f"cpu baseline: oracle forward on {len(toks)} sampled tokens")
     t0 = time.perf_counter()
