@@ -88,7 +88,8 @@ typedef enum {
  *   renormalize  1: weights = softmax over the selected k (they sum to 1);
  *                0: weights = full-softmax probability of each selected expert
  *   max_tokens   largest T a forward may pass; sizes the workspace
- *                (max_tokens <= 2^20 and max_tokens * (top_k + n_shared) <= 2^21)
+ *                (max_tokens <= 2^20, max_tokens * (top_k + n_shared) <= 2^21
+ *                and max_tokens * d_model < 2^31)
  *   device       HIP device ordinal that holds the weights and runs the layer */
 typedef struct {
     int32_t d_model, d_ff, n_experts, top_k, n_shared, d_ff_shared;

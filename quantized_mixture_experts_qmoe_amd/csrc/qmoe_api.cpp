@@ -125,6 +125,10 @@ int validate(const qmoe_config *cfg) {
     if (cfg->max_tokens > (1 << 20) || rows > (1ll << 21))
         return fail(QMOE_EUNSUPPORTED, "max_tokens=%d too large (max_tokens <= 2^20 and max_tokens * (top_k + "
                                        "n_shared) <= 2^21)", cfg->max_tokens);
+    // the prefill GEMM addresses gathered x rows as 32-bit byte offsets from x
+    if ((long long)cfg->max_tokens * cfg->d_model >= (1ll << 31))
+        return fail(QMOE_EUNSUPPORTED, "max_tokens * d_model = %lld: must stay below 2^31",
+                    (long long)cfg->max_tokens * cfg->d_model);
     if (cfg->renormalize != 0 && cfg->renormalize != 1) return fail(QMOE_EINVAL, "renormalize must be 0 or 1");
     if (cfg->router_fp32 != 0 && cfg->router_fp32 != 1) return fail(QMOE_EINVAL, "router_fp32 must be 0 or 1");
     return QMOE_OK;

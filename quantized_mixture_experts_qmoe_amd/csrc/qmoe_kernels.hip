@@ -100,7 +100,8 @@ __device__ __forceinline__ void dma4s(const void *sbase, uint32_t voff, uint32_t
 template <int BT, int BE, int WE, int NST>
 __global__ __launch_bounds__(256) void k_router_lds(const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr,
                                                     const float *__restrict__ bias, float *__restrict__ logits,
-                                                    float *__restrict__ xsum, float xscale, int T, int d, int E) {
+                                                    float *__restrict__ xsum, float xscale, int T, int d, int E,
+                                                    int net) {
     constexpr bool STREAMS = WE == 1;
     static_assert(WE == 1 || WE == 4, "four waves: streams or a four-way expert split");
     constexpr int MT = BT / 16, NT = BE / (16 * WE);
@@ -113,9 +114,13 @@ __global__ __launch_bounds__(256) void k_router_lds(const uint16_t *__restrict__
     __shared__ __attribute__((aligned(1024))) uint8_t lds[RINGS * NST * ST + (STREAMS ? 3 * MT * NT * 1024 : 0)];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int L = blockIdx.x + blockIdx.y * gridDim.x;
+    // one-dimensional grid of net expert tiles x token tiles (padded to a
+    // multiple of 8), numbered XCD-aware: workgroup L runs on XCD L % 8, and
+    // the expert tiles of one token tile are consecutive workgroups of one XCD,
+    // so its L2 fetches the tile's x rows once
+    const int L = blockIdx.x;
     const int xcd = L & 7, j = L >> 3;
-    const int et = j % gridDim.x, tt = (j / gridDim.x) * 8 + xcd;
+    const int et = j % net, tt = (j / net) * 8 + xcd;
     const int t0 = tt * BT;
     const int e0 = et * BE;
     if (t0 >= T) return;
@@ -1105,26 +1110,28 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm_gpf(GemmArgs a) {
     const uint32_t lds0 = lds_addr(lds);
 
     // sources of this lane's ADMA 16-byte activation chunks per group: rows
-    // RPW*w + 4i + lane/16, chunk (lane & 15) ^ (row & 15) (the swizzle)
-    const uint16_t *abase = MODE == 0 ? a.x : a.H;
+    // RPW*w + 4i + lane/16, chunk (lane & 15) ^ (row & 15) (the swizzle), as
+    // 32-bit byte offsets from a base in SGPRs: gathered x rows from x itself
+    // (the host keeps max_tokens * d below 2^31), the tile's contiguous H rows
+    // from its first row
     const int lda = MODE == 0 ? a.d : a.ldh;
+    const int ldr = MODE == 0 ? a.d / 128 : a.ldh / 128;
+    const uint16_t *abase = MODE == 0 ? a.x : a.H + (size_t)tl.row0 * lda;
+    const float *rbase = MODE == 0 ? a.xsum : a.hsum + (size_t)tl.row0 * ldr;
+    // source row of tile row r (rows past the tile read its first row)
+    auto src_row = [&](int r) {
+        const int rr = r < rows ? r : 0;
+        if (MODE == 1) return rr;
+        const int gr = tl.row0 + rr;
+        return gr < a.P ? a.perm[gr] / a.k : (gr - a.P) % a.T;
+    };
     uint32_t aoffb[ADMA];
 #pragma unroll
     for (int i = 0; i < ADMA; i++) {
         const int row = RPW * wave + 4 * i + (lane >> 4);
-        const int gr = tl.row0 + (row < rows ? row : 0);
-        const int src = MODE == 0 ? (gr < a.P ? a.perm[gr] / a.k : (gr - a.P) % a.T) : gr;
-        aoffb[i] = 2u * ((uint32_t)src * (uint32_t)lda + (uint32_t)(((lane & 15) ^ (row & 15)) * 8));
+        aoffb[i] = 2u * ((uint32_t)src_row(row) * (uint32_t)lda + (uint32_t)(((lane & 15) ^ (row & 15)) * 8));
     }
-    const float *rbase = MODE == 0 ? a.xsum : a.hsum;
-    const int ldr = MODE == 0 ? a.d / 128 : a.ldh / 128;
-    uint32_t roffb;
-    {
-        const int row = RPW * wave + (lane < RPW ? lane : 0);
-        const int gr = tl.row0 + (row < rows ? row : 0);
-        const int src = MODE == 0 ? (gr < a.P ? a.perm[gr] / a.k : (gr - a.P) % a.T) : gr;
-        roffb = 4u * (uint32_t)src * (uint32_t)ldr;
-    }
+    const uint32_t roffb = 4u * (uint32_t)src_row(RPW * wave + (lane < RPW ? lane : 0)) * (uint32_t)ldr;
     const uint8_t *codes = MODE == 0 ? ew.c13 : ew.c2;
     const uint16_t *gsc = MODE == 0 ? ew.s13 : ew.s2;
     // a wave whose columns lie past N (last N-tile of a narrower matrix) loads
@@ -1257,12 +1264,7 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm_gpf(GemmArgs a) {
         const int GS = (KB + 31) / 32;
         uint32_t zrow[MI];
 #pragma unroll
-        for (int mi = 0; mi < MI; mi++) {
-            const int row = mi * 16 + (lane & 15);
-            const int gr = tl.row0 + (row < rows ? row : 0);
-            const int src = MODE == 0 ? (gr < a.P ? a.perm[gr] / a.k : (gr - a.P) % a.T) : gr;
-            zrow[mi] = (uint32_t)src * (uint32_t)ldr;
-        }
+        for (int mi = 0; mi < MI; mi++) zrow[mi] = (uint32_t)src_row(mi * 16 + (lane & 15)) * (uint32_t)ldr;
         for (int gs = 0; gs < GS; gs++) {
             bf16x8 bh[NB], bl[NB];
 #pragma unroll
@@ -1534,9 +1536,10 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t *__restrict__ O,
 template <int BT, int BE, int WE, int NST>
 static void launch_router_lds(const uint16_t *x, const uint16_t *wr, const float *bias, float *logits, float *xsum,
                               float xscale, int T, int d, int E, hipStream_t s) {
-    const int gx = 8 * ((T + BT * 8 - 1) / (BT * 8));   // token tiles, padded to a multiple of 8
-    hipLaunchKernelGGL((k_router_lds<BT, BE, WE, NST>), dim3((E + BE - 1) / BE, gx), dim3(256), 0, s, x, wr, bias,
-                       logits, xsum, xscale, T, d, E);
+    const long gx = 8L * ((T + BT * 8 - 1) / (BT * 8));   // token tiles, padded to a multiple of 8
+    const int net = (E + BE - 1) / BE;
+    hipLaunchKernelGGL((k_router_lds<BT, BE, WE, NST>), dim3((unsigned)(gx * net)), dim3(256), 0, s, x, wr, bias,
+                       logits, xsum, xscale, T, d, E, net);
 }
 
 hipError_t launch_router_bf16(const uint16_t *x, const uint16_t *wr, const float *bias, float *logits, float *xsum,

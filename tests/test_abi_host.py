@@ -66,6 +66,7 @@ def base_cfg(**kw):
     (dict(n_experts=128, top_k=65), Q.QMOE_EUNSUPPORTED),
     (dict(max_tokens=(1 << 20) + 1), Q.QMOE_EUNSUPPORTED),
     (dict(max_tokens=(1 << 20), top_k=3), Q.QMOE_EUNSUPPORTED),   # 3 * 2^20 rows
+    (dict(max_tokens=(1 << 19), d_model=4096), Q.QMOE_EUNSUPPORTED),   # x of 2^31 elements
 ])
 def test_pack_rejects_bad_configs(qmoe_lib, kw, rc):
     got, ctx = _pack(base_cfg(**kw))

@@ -159,6 +159,41 @@ def test_zero_tokens_and_limits(oracle_mod):
         layer.forward(to_dev_bf16(make_x(cfg, 9, seed=1)))                              # T > max_tokens
 
 
+def test_forward_at_the_token_limit(oracle_mod):
+    # max_tokens = 2^20 with top-2 (2^21 routed rows, the documented limit):
+    # the largest grids of every kernel; routing and the task list checked on
+    # every token, outputs on sampled tokens
+    from gpu_util import assert_output_close as close
+    cfg = small("int4_sym_g128", name="token_limit", T=1 << 20, d=256, E=8, k=2, F=128)
+    print(f"[case] forward at the token limit {cfg}", flush=True)
+    inp = make_inputs(cfg, seed=20)
+    T = cfg.T
+    layer = QMoE(inp, max_tokens=T)
+    route = QMoE.route_buffers(T, cfg.E, cfg.k)
+    y = layer.forward(to_dev_bf16(inp.x), route=route)
+    torch.cuda.synchronize()
+    idx = route["topk_idx"].cpu().numpy()
+    w = route["topk_w"].cpu().numpy().astype(np.float64)
+    lg = route["logits"].cpu().numpy()
+    counts, offsets, perm, _ = oracle_mod.dispatch(idx, cfg.E)
+    assert np.array_equal(route["counts"].cpu().numpy(), counts)
+    assert np.array_equal(route["offsets"].cpu().numpy(), offsets)
+    assert np.array_equal(route["perm"].cpu().numpy(), perm)
+    assert np.all(np.abs(w.sum(1) - 1.0) <= 1e-5)
+    oracle = oracle_mod.OracleLayer(inp)
+    rng = np.random.default_rng(3)
+    toks = np.sort(np.concatenate([[0, T - 1], rng.choice(np.arange(1, T - 1), 62, replace=False)])).astype(np.int32)
+    ref = oracle.forward(inp.x, tokens=toks)
+    bound = logit_bound(inp.x[toks], inp.w_router, cfg.router_fp32)
+    diff = check_own_routing(ref, lg[toks], idx[toks], w[toks], bound, inp.bias)
+    y_ref = ref["y"].copy()
+    if diff:
+        y_ref[diff] = oracle.forward(inp.x, tokens=toks[diff], given=idx[toks][diff])["y"]
+    close(bf16_tensor_to_f64(y)[toks], y_ref, "token limit (64 sampled tokens)")
+    oracle.close()
+    layer.close()
+
+
 def test_pack_export_matches_oracle_codes(oracle_mod):
     """Library packer and oracle quantizer are independent: codes, scales and
     zeros must agree bit for bit after the device round trip."""
