@@ -629,16 +629,20 @@ __global__ __launch_bounds__(256) void k_xsum(const uint16_t *__restrict__ x, in
     const int t = blockIdx.x * 4 + wave;
     if (t >= T) return;
     const int nchunk = d / 8, G = d / 128;
+    // 16 lanes per 128-wide group; lanes past the row (d % 512 != 0) add
+    // nothing and write nothing
     for (int c0 = 0; c0 < nchunk; c0 += 64) {
         const int c = c0 + lane;
-        const uint4 v = *reinterpret_cast<const uint4 *>(x + (size_t)t * d + c * 8);
+        const bool in = c < nchunk;
+        const uint4 v = *reinterpret_cast<const uint4 *>(x + (size_t)t * d + (in ? c : 0) * 8);
         const uint32_t u[4] = {v.x, v.y, v.z, v.w};
         float s = 0.0f;
 #pragma unroll
         for (int i = 0; i < 4; i++) s += bf16f(u[i] & 0xFFFFu) + bf16f(u[i] >> 16);
+        s = in ? s : 0.0f;
 #pragma unroll
         for (int off = 1; off < 16; off <<= 1) s += __shfl_xor(s, off);
-        if ((lane & 15) == 0) xsum[(size_t)t * G + c / 16] = s * scale;
+        if (in && (lane & 15) == 0) xsum[(size_t)t * G + c / 16] = s * scale;
     }
 }
 

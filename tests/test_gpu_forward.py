@@ -114,6 +114,15 @@ def test_forward_degenerate_shapes(oracle_mod, T, E, k, fmt):
                   output_rounding_allowance=True)
 
 
+@pytest.mark.parametrize("d", [256, 768])
+@pytest.mark.parametrize("fmt", ["int4_asym_g128", "int4_sym_g128"])
+def test_forward_group_format_with_fp32_router(oracle_mod, fmt, d):
+    # an fp32 router leaves the row sums of x to their own kernel (k_xsum),
+    # here with rows of 2 and 6 groups (not a multiple of its 4-group pass)
+    cfg = small(fmt, name=f"fp32router_{fmt}_{d}", d=d, router_fp32=True)
+    run_and_check(oracle_mod, cfg, tag=f"fp32 router {fmt} d={d}")
+
+
 @pytest.mark.parametrize("fmt", ["int3_sym_g128", "int8_sym_ch", "fp8e4m3_ch"])
 def test_forward_shared_experts_and_bias(oracle_mod, fmt):
     cfg = small(fmt, T=257, E=12, k=3, S=2, Fs=384, bias=True)
