@@ -151,11 +151,7 @@ int qmoe_route_topk(qmoe_ctx *ctx, const float *logits, int32_t T, qmoe_route_ou
  *   T       0 <= T <= max_tokens (T = 0 is a no-op)
  *   y       device [T][d] bf16 output (may not alias x)
  *   dbg     NULL, or device buffers that receive this call's routing
- *   stream  hipStream_t (NULL = the null stream)
- * Each weighted expert output w_tj * Expert(x_t) (and each shared output) is
- * held as fp16 of its value * 2^-8 between the down projection and the sum:
- * its magnitude must stay below 2^24 per element (larger values reach y as
- * +-inf, or saturate at 2^24 on top-1 layers without shared experts). */
+ *   stream  hipStream_t (NULL = the null stream) */
 int qmoe_forward(qmoe_ctx *ctx, const uint16_t *x, int32_t T, uint16_t *y, qmoe_route_out *dbg, void *stream);
 
 /* Frees the context and its device memory. NULL is a no-op. The caller must

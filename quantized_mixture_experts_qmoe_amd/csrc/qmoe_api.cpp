@@ -70,8 +70,7 @@ struct qmoe_ctx {
     int32_t *perm = nullptr, *inv = nullptr, *num_tiles = nullptr;
     Tile *tiles = nullptr;
     uint16_t *H = nullptr;
-    uint16_t *O = nullptr;
-    float *xsum = nullptr, *hsum = nullptr;
+    float *O = nullptr, *xsum = nullptr, *hsum = nullptr;
     int ldh = 0;
     size_t tiles_cap = 0;
     std::vector<void *> allocs;
@@ -449,7 +448,7 @@ int qmoe_pack_experts(const qmoe_config *cfg, const float *const *w_gate, const 
     if (!rc) rc = dalloc(c, (void **)&c->num_tiles, 256);
     if (!rc) rc = dalloc(c, (void **)&c->tiles, c->tiles_cap * sizeof(Tile));
     if (!rc) rc = dalloc(c, (void **)&c->H, rows_total * c->ldh * 2);
-    if (!rc) rc = dalloc(c, (void **)&c->O, rows_total * c->d * 2);
+    if (!rc) rc = dalloc(c, (void **)&c->O, rows_total * c->d * 4);
     if (!rc) rc = dalloc(c, (void **)&c->xsum, T * (c->d / 128) * 4);
     if (!rc) rc = dalloc(c, (void **)&c->hsum, rows_total * (c->ldh / 128) * 4);
     if (rc) {
@@ -537,7 +536,6 @@ int qmoe_forward(qmoe_ctx *c, const uint16_t *x, int32_t T, uint16_t *y, qmoe_ro
     a.P = P;
     a.T = T;
     a.E = c->E;
-    a.o_odd = c->k + c->S == 1;
     const int maxN13 = 2 * std::max(c->F, c->Fs);
     rc = timed(c, K_GEMM13, s, [&] { return launch_gemm13(c->df, bm, a, max_tiles, maxN13, s); });
     if (rc) return rc;

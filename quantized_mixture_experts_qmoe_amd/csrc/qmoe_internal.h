@@ -155,7 +155,7 @@ struct GemmArgs {
     const float *xsum;       // [T][d/128] group sums of x
     uint16_t *H;             // [rows][ldh] bf16 intermediate
     float *hsum;             // [rows][ldh/128] group sums of H (bf16-rounded values)
-    uint16_t *O;             // [rows][d] weighted expert outputs, fp16 of v * 2^-8
+    float *O;                // [rows][d] fp32 weighted expert outputs
     int32_t ldh;
     int32_t d;
     int32_t k;               // top-k
@@ -163,13 +163,12 @@ struct GemmArgs {
     int32_t T;
     int32_t E;               // routed experts
     int32_t n_tiles;         // 256-column N-tiles of the widest expert (set by the launcher)
-    int32_t o_odd;           // 1: round O to odd (one contribution per output row)
 };
 // bm: rows per M-tile (16: weight-streaming decode kernel; 64: prefill
 // kernels); max_tiles: grid bound; maxN13: max 2F.
 hipError_t launch_gemm13(int df, int bm, const GemmArgs &a, int max_tiles, int maxN13, hipStream_t s);
 hipError_t launch_gemm2(int df, int bm, const GemmArgs &a, int max_tiles, hipStream_t s);
-hipError_t launch_combine(const uint16_t *O, const int32_t *inv, int T, int d, int k, int P, int n_shared,
+hipError_t launch_combine(const float *O, const int32_t *inv, int T, int d, int k, int P, int n_shared,
                           uint16_t *y, hipStream_t s);
 hipError_t launch_xsum(const uint16_t *x, int T, int d, float scale, float *xsum, hipStream_t s);
 

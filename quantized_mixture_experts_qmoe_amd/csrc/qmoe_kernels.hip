@@ -787,29 +787,6 @@ struct GroupConst {
     static constexpr float ZC = DF == DF_I4SYM ? 136.0f : 128.0f;
 };
 
-// Expert outputs O travel from the down GEMM to the combine as fp16 of
-// v * 2^-8: relative precision 2^-11 (finer than the bf16 H and y around it),
-// range up to 2^24 in magnitude, absolute resolution 2^-16 below 2^-6. Half the
-// bytes of fp32 on the largest write and read of a prefill layer. When every
-// output row has a single contribution (top-1, no shared expert) the combine's
-// bf16 rounding would round the same value a second time, so O is rounded to
-// odd instead of to nearest: with fp16's three bits beyond bf16, round-to-odd
-// followed by round-to-nearest equals one round-to-nearest.
-constexpr float kOScale = 1.0f / 256.0f;
-__device__ __forceinline__ void store_o(uint16_t *p, float v, bool odd) {
-    const float sv = v * kOScale;
-    uint16_t b;
-    if (odd) {
-        // toward zero, then the odd neighbour when inexact (saturates at 65504)
-        const auto h2 = __builtin_amdgcn_cvt_pkrtz(sv, sv);
-        b = __builtin_bit_cast(uint16_t, h2[0]);
-        if ((float)h2[0] != sv) b |= 1u;
-    } else {
-        b = __builtin_bit_cast(uint16_t, (_Float16)sv);
-    }
-    *p = b;
-}
-
 // ---- decode-shaped batches: tiles of at most 16 rows ----------------------
 constexpr int kDecodeBlocksPerWave = 4;
 //
@@ -1042,11 +1019,14 @@ __global__ __launch_bounds__(256) void k_gemm_dec(GemmArgs a) {
 #pragma unroll
             for (int nb = 0; nb < NB; nb++) {
                 const int n = c.n0 + NB * 16 * wave + 16 * nb + (lane & 15);
-                store_o(a.O + (size_t)gr * a.d + n, acc[nb][r] * sn[nb] * wt, a.o_odd);
+                a.O[(size_t)gr * a.d + n] = acc[nb][r] * sn[nb] * wt;
             }
         }
     }
 }
+
+// Expert outputs are written once and read once (by the combine).
+__device__ __forceinline__ void store_o(float *p, float v) { *p = v; }
 
 // ---- prefill tiles: XCD-aware work order -----------------------------------
 //
@@ -1359,7 +1339,7 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm_gpf(GemmArgs a) {
 #pragma unroll
                 for (int nb = 0; nb < NB; nb++) {
                     const int n = n0 + WCOLS * wave + 16 * nb + (lane & 15);
-                    if (wave_on) store_o(a.O + (size_t)gr * a.d + n, acc[mi][nb][r] * wt, a.o_odd);
+                    if (wave_on) store_o(a.O + (size_t)gr * a.d + n, acc[mi][nb][r] * wt);
                 }
             }
     }
@@ -1472,7 +1452,7 @@ __global__ __launch_bounds__(256) void k_gemm_c(GemmArgs a) {
 #pragma unroll
                 for (int nb = 0; nb < 4; nb++) {
                     const int n = c.n0 + 64 * wave + 16 * nb + (lane & 15);
-                    store_o(a.O + (size_t)gr * a.d + n, acc[mi][nb][r] * sn[nb] * wt, a.o_odd);
+                    a.O[(size_t)gr * a.d + n] = acc[mi][nb][r] * sn[nb] * wt;
                 }
             }
     }
@@ -1483,53 +1463,60 @@ __global__ __launch_bounds__(256) void k_gemm_c(GemmArgs a) {
 // ---------------------------------------------------------------------------
 
 // y[t] = sum_j O[inv[t*k+j]] + sum_s O[P + s*T + t], summed in fp32 in slot
-// order, rounded once to bf16. Eight columns per thread (16-byte loads of the
-// fp16 O rows, 16-byte bf16 stores); the rows are loaded eight at a time so
-// that the loads overlap. O is read exactly once: non-temporal loads keep it
-// from displacing cached data.
-__device__ __forceinline__ void load_o8(const uint16_t *p, float (&v)[8]) {
-    const u32x4 q = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        v[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(q[i] & 0xFFFFu));
-        v[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(q[i] >> 16));
+// order, rounded once to bf16. CPT 4-column chunks per thread, 256 columns
+// apart; the rows are loaded eight at a time so that the loads overlap. O is
+// read exactly once: non-temporal loads keep it from displacing cached data.
+constexpr int kCombineCPT = 1;
+constexpr bool kCombineNT = true;
+__device__ __forceinline__ float4 load_o(const float *p) {
+    if (kCombineNT) {
+        const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
+        return make_float4(v[0], v[1], v[2], v[3]);
     }
+    return *reinterpret_cast<const float4 *>(p);
 }
-__global__ __launch_bounds__(256) void k_combine(const uint16_t *__restrict__ O, const int32_t *__restrict__ inv, int T,
+__global__ __launch_bounds__(256) void k_combine(const float *__restrict__ O, const int32_t *__restrict__ inv, int T,
                                                  int d, int k, int P, int n_shared, uint16_t *__restrict__ y) {
+    constexpr int CPT = kCombineCPT;
     const int t = blockIdx.x;
-    const int c8 = blockIdx.y * blockDim.x + threadIdx.x;   // 8-column chunk
-    if (c8 >= d / 8) return;
+    const int d4 = d / 4;
+    const int c0 = blockIdx.y * 256 * CPT + threadIdx.x;
     const int nrows = k + n_shared;
-    float acc[8];
+    float4 acc[CPT];
 #pragma unroll
-    for (int i = 0; i < 8; i++) acc[i] = 0.0f;
+    for (int c = 0; c < CPT; c++) acc[c] = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int j0 = 0; j0 < nrows; j0 += 8) {
-        float v[8][8];
+        float4 v[8][CPT];
 #pragma unroll
         for (int u = 0; u < 8; u++) {
             const int j = j0 + u;
             if (j < nrows) {
                 const size_t row = j < k ? (size_t)inv[(size_t)t * k + j] : (size_t)P + (size_t)(j - k) * T + t;
-                load_o8(O + row * d + c8 * 8, v[u]);
+#pragma unroll
+                for (int c = 0; c < CPT; c++)
+                    if (c0 + 256 * c < d4) v[u][c] = load_o(O + row * d + (c0 + 256 * c) * 4);
             }
         }
 #pragma unroll
         for (int u = 0; u < 8; u++)
             if (j0 + u < nrows)
 #pragma unroll
-                for (int i = 0; i < 8; i++) acc[i] += v[u][i];
+                for (int c = 0; c < CPT; c++) {
+                    acc[c].x += v[u][c].x;
+                    acc[c].y += v[u][c].y;
+                    acc[c].z += v[u][c].z;
+                    acc[c].w += v[u][c].w;
+                }
     }
-    // the stored scale 2^-8 is undone on the fp32 sum (a power of two: the
-    // same result as scaling each term)
 #pragma unroll
-    for (int i = 0; i < 8; i++) acc[i] *= 256.0f;
-    uint4 out;
-    out.x = (uint32_t)to_bf16(acc[0]) | ((uint32_t)to_bf16(acc[1]) << 16);
-    out.y = (uint32_t)to_bf16(acc[2]) | ((uint32_t)to_bf16(acc[3]) << 16);
-    out.z = (uint32_t)to_bf16(acc[4]) | ((uint32_t)to_bf16(acc[5]) << 16);
-    out.w = (uint32_t)to_bf16(acc[6]) | ((uint32_t)to_bf16(acc[7]) << 16);
-    *reinterpret_cast<uint4 *>(y + (size_t)t * d + c8 * 8) = out;
+    for (int c = 0; c < CPT; c++) {
+        const int c4 = c0 + 256 * c;
+        if (c4 >= d4) continue;
+        uint2 out;
+        out.x = (uint32_t)to_bf16(acc[c].x) | ((uint32_t)to_bf16(acc[c].y) << 16);
+        out.y = (uint32_t)to_bf16(acc[c].z) | ((uint32_t)to_bf16(acc[c].w) << 16);
+        *reinterpret_cast<uint2 *>(y + (size_t)t * d + c4 * 4) = out;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1676,12 +1663,10 @@ hipError_t launch_xsum(const uint16_t *x, int T, int d, float scale, float *xsum
     return hipGetLastError();
 }
 
-hipError_t launch_combine(const uint16_t *O, const int32_t *inv, int T, int d, int k, int P, int n_shared,
+hipError_t launch_combine(const float *O, const int32_t *inv, int T, int d, int k, int P, int n_shared,
                           uint16_t *y, hipStream_t s) {
-    // small batches: 64-thread workgroups, so that a few tokens still spread
-    // over the CUs
-    const int nt = T < 1024 ? 64 : 256;
-    hipLaunchKernelGGL(k_combine, dim3(T, (d / 8 + nt - 1) / nt), dim3(nt), 0, s, O, inv, T, d, k, P, n_shared, y);
+    hipLaunchKernelGGL(k_combine, dim3(T, (d / 4 + 256 * kCombineCPT - 1) / (256 * kCombineCPT)), dim3(256), 0, s, O, inv,
+                       T, d, k, P, n_shared, y);
     return hipGetLastError();
 }
 
