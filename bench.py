@@ -141,8 +141,8 @@ def main() -> int:
         print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "launches": 3}))
         return 0
     if args.gpus != 1:
-        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported "
-              f"(the layer is not sharded; see the design notes for how it would shard).", file=sys.stderr)
+        print(f"bench.py: the layer runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              f"(the experts are not sharded across GPUs).", file=sys.stderr)
         return 2
 
     import torch

@@ -49,7 +49,7 @@ extern "C" {
 #define QMOE_EINVAL (-1)       /* bad argument: null pointer, shape, T > max_tokens, ... */
 #define QMOE_EHIP (-2)         /* a HIP runtime call or kernel launch failed */
 #define QMOE_ENOMEM (-3)       /* device or host allocation failed */
-#define QMOE_EUNSUPPORTED (-4) /* valid request outside what this build supports */
+#define QMOE_EUNSUPPORTED (-4) /* valid request outside what the library supports */
 
 typedef struct qmoe_ctx qmoe_ctx; /* opaque; owns all device memory it allocates */
 

@@ -6,7 +6,7 @@
  * Only the test suite, the smoke check and the benchmark's CPU-baseline leg load
  * it. It shares no code with the HIP library: no headers, helpers, tables or
  * constant generators; it is written from the source pages and the readings
- * documented with the design notes.
+ * listed below.
  *
  * Sources (web pages; cited by title and section):
  *  - "Quantized Mixture of Experts (Q-MoE)": section 3 components table
@@ -24,7 +24,7 @@
  *    (expert-centric scheduling: collect tasks, group by expert id, sort by
  *    token id inside each group, grouped GEMM).
  *
- * Readings where the pages are silent (each listed in the design notes):
+ * Readings where the pages are silent:
  *  - selection is on the logits, lowest expert index wins ties; slot order is
  *    descending logit; weights are the softmax over the selected k (equal to
  *    the full softmax renormalised over the selection); renorm = 0 gives the
