@@ -8,7 +8,8 @@ import torch
 
 from quantized_mixture_experts_qmoe_amd import QMoE
 from quantized_mixture_experts_qmoe_amd.inputs import CONFIGS, make_inputs
-from gpu_util import assert_output_close, bf16_tensor_to_f64, check_own_routing, logit_bound, to_dev_bf16
+from gpu_util import (assert_output_close, bf16_bits_to_f32, bf16_tensor_to_f64, check_own_routing, logit_bound,
+                      to_dev_bf16)
 
 pytestmark = pytest.mark.gpu
 
@@ -47,6 +48,27 @@ def test_full_size_layer(oracle_mod, name):
     assert np.array_equal(route["counts"].cpu().numpy(), counts)
     assert np.array_equal(route["offsets"].cpu().numpy(), offsets)
     assert np.array_equal(route["perm"].cpu().numpy(), perm)
+
+    # every token: GPU logits within the fp32 dot-product bound of the fp64
+    # logits, and the GPU's top-k set equal to the exact one wherever the
+    # k-th / (k+1)-th margin exceeds 1e-3 (selection by its definition:
+    # descending logit, ties to the lower index)
+    X = bf16_bits_to_f32(inp.x).astype(np.float64)
+    W = (inp.w_router if cfg.router_fp32 else bf16_bits_to_f32(inp.w_router)).astype(np.float64)
+    L = X @ W.T + (inp.bias.astype(np.float64) if inp.bias is not None else 0.0)
+    bound = logit_bound(inp.x, inp.w_router, cfg.router_fp32)
+    if inp.bias is not None:
+        bound = bound + np.abs(inp.bias.astype(np.float64)) * 2.0 ** -23
+    assert np.all(np.abs(lg.astype(np.float64) - L) <= bound + 1e-30)
+    order = np.argsort(-L, axis=1, kind="stable")
+    kth = np.take_along_axis(L, order[:, cfg.k - 1:cfg.k], axis=1)[:, 0]
+    nxt = np.take_along_axis(L, order[:, cfg.k:cfg.k + 1], axis=1)[:, 0] if cfg.k < cfg.E else np.full(cfg.T, -np.inf)
+    margin = kth - nxt
+    same = np.all(np.sort(order[:, :cfg.k], axis=1) == np.sort(idx, axis=1), axis=1)
+    under = margin <= 1e-3
+    print(f"[routing] all {cfg.T} tokens: {int(under.sum())} under margin 1e-3; "
+          f"set mismatches {int((~same).sum())} (all under the margin)", flush=True)
+    assert np.all(same | under)
 
     # sampled tokens against the oracle
     oracle = O.OracleLayer(inp)
