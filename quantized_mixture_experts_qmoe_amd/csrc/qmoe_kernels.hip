@@ -1249,6 +1249,10 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm_gpf(GemmArgs a) {
         uint32_t zrow[MI];
 #pragma unroll
         for (int mi = 0; mi < MI; mi++) zrow[mi] = (uint32_t)src_row(mi * 16 + (lane & 15)) * (uint32_t)ldr;
+        // the eight row sums a lane needs per row block and K range are
+        // consecutive floats: two 16-byte loads when rows and ranges keep them
+        // aligned (uniform), else eight single loads
+        const bool vec = ldr % 8 == 0 && KB % 8 == 0;
         for (int gs = 0; gs < GS; gs++) {
             bf16x8 bh[NB], bl[NB];
 #pragma unroll
@@ -1258,14 +1262,33 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm_gpf(GemmArgs a) {
                 bl[nb] = __builtin_bit_cast(bf16x8, gload16(q + 512));
             }
             const int g0 = gs * 32 + (lane >> 4) * 8;
+            float rv[MI][8];
+            if (vec) {
+                // past the last group (KB % 32 != 0): the last 8 groups are
+                // read and zeroed
+                const bool gin = g0 < KB;
+                const int gc = gin ? g0 : KB - 8;
+#pragma unroll
+                for (int mi = 0; mi < MI; mi++) {
+                    const uint4 u0 = gload16(rbase + zrow[mi] + gc);
+                    const uint4 u1 = gload16(rbase + zrow[mi] + gc + 4);
+                    const uint32_t uu[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+                    for (int j = 0; j < 8; j++) rv[mi][j] = gin ? __uint_as_float(uu[j]) : 0.0f;
+                }
+            } else {
+#pragma unroll
+                for (int mi = 0; mi < MI; mi++)
+#pragma unroll
+                    for (int j = 0; j < 8; j++) rv[mi][j] = g0 + j < KB ? gload(rbase + zrow[mi] + g0 + j) : 0.0f;
+            }
 #pragma unroll
             for (int mi = 0; mi < MI; mi++) {
                 bf16x8 ah, al;
 #pragma unroll
                 for (int j = 0; j < 8; j++) {
-                    const float v = g0 + j < KB ? gload(rbase + zrow[mi] + g0 + j) : 0.0f;
                     __bf16 h, l;
-                    split_bf16(v, h, l);
+                    split_bf16(rv[mi][j], h, l);
                     ah[j] = h;
                     al[j] = l;
                 }

@@ -114,6 +114,16 @@ def test_forward_degenerate_shapes(oracle_mod, T, E, k, fmt):
                   output_rounding_allowance=True)
 
 
+@pytest.mark.parametrize("d,F", [(3072, 1024), (2048, 1280), (1024, 2048)])
+def test_forward_asym_zero_point_ranges(oracle_mod, d, F):
+    # the zero-point correction reads 8 consecutive row sums per lane as two
+    # 16-byte loads when the group count is a multiple of 8 (d = 3072: 24
+    # groups, the last quarter of the 32-group range zeroed; F = 1024 / 2048:
+    # 8 / 16 groups) and one by one otherwise (F = 1280: 10 groups)
+    cfg = small("int4_asym_g128", name=f"asym_ranges_{d}_{F}", T=256, d=d, E=8, k=2, F=F)
+    run_and_check(oracle_mod, cfg, tag=f"asym zero-point ranges d={d} F={F}")
+
+
 @pytest.mark.parametrize("d", [256, 768])
 @pytest.mark.parametrize("fmt", ["int4_asym_g128", "int4_sym_g128"])
 def test_forward_group_format_with_fp32_router(oracle_mod, fmt, d):
