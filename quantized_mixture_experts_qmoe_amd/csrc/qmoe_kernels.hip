@@ -308,6 +308,19 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
     v += dpp_zero<kDppBcast31, 0xC>(v);
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
+// Sum over each 16-lane row; the total lands in the row's lane 15.
+__device__ __forceinline__ float row16_sum_f32(float v) {
+    v += dpp_zero<kDppShr1, 0xF>(v);
+    v += dpp_zero<kDppShr2, 0xF>(v);
+    v += dpp_zero<kDppShr4, 0xF>(v);
+    v += dpp_zero<kDppShr8, 0xF>(v);
+    return v;
+}
+// SwiGLU gate: silu(g) * u = g / (1 + e^-g) * u with the hardware reciprocal
+// (about 1 ulp of fp32; the product is rounded to bf16 right after)
+__device__ __forceinline__ float silu_mul(float g, float u) {
+    return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
 // Inclusive prefix sum over the wave (lane i: sum of lanes 0..i).
 __device__ __forceinline__ int wave_incl_scan(int v) {
     v += __builtin_amdgcn_update_dpp(0, v, kDppShr1, 0xF, 0xF, true);
@@ -1001,7 +1014,7 @@ __global__ __launch_bounds__(256) void k_gemm_dec(GemmArgs a) {
                 if (row < c.rows) {
                     const float g = acc[2 * pr][r] * sg;
                     const float u = acc[2 * pr + 1][r] * su;
-                    a.H[(size_t)(c.tl.row0 + row) * a.ldh + col] = to_bf16(g / (1.0f + __expf(-g)) * u);
+                    a.H[(size_t)(c.tl.row0 + row) * a.ldh + col] = to_bf16(silu_mul(g, u));
                 }
             }
         }
@@ -1323,7 +1336,7 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm_gpf(GemmArgs a) {
                     const int row = mi * 16 + lrow + r;
                     const float g = acc[mi][2 * pr][r];
                     const float u = acc[mi][2 * pr + 1][r];
-                    const uint16_t hb = to_bf16(g / (1.0f + __expf(-g)) * u);
+                    const uint16_t hb = to_bf16(silu_mul(g, u));
                     hs[mi][r] += bf16f(hb);
                     if (wave_on && row < rows) a.H[(size_t)(tl.row0 + row) * a.ldh + col] = hb;
                 }
@@ -1333,10 +1346,8 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm_gpf(GemmArgs a) {
         for (int mi = 0; mi < MI; mi++)
 #pragma unroll
             for (int r = 0; r < 4; r++) {
-                float v = hs[mi][r];
-#pragma unroll
-                for (int off = 1; off < 16; off <<= 1) v += __shfl_xor(v, off);
-                if ((lane & 15) == 0) red[wave * BM + mi * 16 + lrow + r] = v;
+                const float v = row16_sum_f32(hs[mi][r]);
+                if ((lane & 15) == 15) red[wave * BM + mi * 16 + lrow + r] = v;
             }
         __syncthreads();
         for (int t = threadIdx.x; t < BM * (NW / WPG); t += 64 * NW) {
@@ -1455,7 +1466,7 @@ __global__ __launch_bounds__(256) void k_gemm_c(GemmArgs a) {
                     if (row < c.rows) {
                         const float g = acc[mi][2 * pr][r] * sg;
                         const float u = acc[mi][2 * pr + 1][r] * su;
-                        a.H[(size_t)(c.tl.row0 + row) * a.ldh + col] = to_bf16(g / (1.0f + __expf(-g)) * u);
+                        a.H[(size_t)(c.tl.row0 + row) * a.ldh + col] = to_bf16(silu_mul(g, u));
                     }
                 }
         }
