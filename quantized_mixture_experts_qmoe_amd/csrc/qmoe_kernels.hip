@@ -17,6 +17,7 @@
 //   gemm2       grouped down GEMM; the epilogue applies the mixing weight
 //   combine     y_t = sum_j O[row(t, j)] + sum_s O_shared(t), fp32, bf16 out
 #include <hip/hip_runtime.h>
+#include <type_traits>
 
 #include "qmoe_internal.h"
 
@@ -1342,13 +1343,23 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm_gpf(GemmArgs a) {
                 }
         }
         float *red = reinterpret_cast<float *>(lds);   // [NW][BM]; the last barrier freed the ring
+        // 16-lane row sums, the 4*MI independent chains interleaved step by
+        // step (a DPP read right after the write of its source needs wait states)
+        auto row_step = [&](auto ctrl) {
+#pragma unroll
+            for (int mi = 0; mi < MI; mi++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) hs[mi][r] += dpp_zero<decltype(ctrl)::value, 0xF>(hs[mi][r]);
+        };
+        row_step(std::integral_constant<int, kDppShr1>{});
+        row_step(std::integral_constant<int, kDppShr2>{});
+        row_step(std::integral_constant<int, kDppShr4>{});
+        row_step(std::integral_constant<int, kDppShr8>{});
 #pragma unroll
         for (int mi = 0; mi < MI; mi++)
 #pragma unroll
-            for (int r = 0; r < 4; r++) {
-                const float v = row16_sum_f32(hs[mi][r]);
-                if ((lane & 15) == 15) red[wave * BM + mi * 16 + lrow + r] = v;
-            }
+            for (int r = 0; r < 4; r++)
+                if ((lane & 15) == 15) red[wave * BM + mi * 16 + lrow + r] = hs[mi][r];
         __syncthreads();
         for (int t = threadIdx.x; t < BM * (NW / WPG); t += 64 * NW) {
             const int h = t / BM, row = t % BM;
