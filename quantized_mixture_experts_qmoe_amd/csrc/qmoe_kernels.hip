@@ -252,17 +252,42 @@ __global__ __launch_bounds__(256) void k_router_lds(const uint16_t *__restrict__
     }
 }
 
+__device__ __forceinline__ float wave_sum_f32(float v);   // DPP wave reduction, with the top-k helpers below
+
 __global__ __launch_bounds__(256) void k_router_f32(const uint16_t *__restrict__ x, const float *__restrict__ wr,
                                                     const float *__restrict__ bias, float *__restrict__ logits, int T,
                                                     int d, int E) {
-    const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= (long)T * E) return;
-    const int t = (int)(i / E), e = (int)(i % E);
-    const uint16_t *xr = x + (size_t)t * d;
-    const float *w = wr + (size_t)e * d;
-    float acc = 0.0f;
-    for (int c = 0; c < d; c++) acc = fmaf(bf16f(xr[c]), w[c], acc);
-    logits[i] = acc + (bias ? bias[e] : 0.0f);
+    // one wave per token: lane l takes columns [4l + 256j, 4l + 256j + 4) of x
+    // and of each router row (d % 256 == 0), four experts at a time; the
+    // partial dots are summed across the wave on DPP
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    const uint16_t *xr = x + (size_t)t * d + 4 * lane;
+    for (int e0 = 0; e0 < E; e0 += 4) {
+        float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int c = 0; c < d; c += 256) {
+            const uint2 xv = *reinterpret_cast<const uint2 *>(xr + c);
+            const float x0 = bf16f(xv.x & 0xFFFFu), x1 = bf16f(xv.x >> 16);
+            const float x2 = bf16f(xv.y & 0xFFFFu), x3 = bf16f(xv.y >> 16);
+#pragma unroll
+            for (int u = 0; u < 4; u++) {
+                if (e0 + u < E) {
+                    const float4 w = *reinterpret_cast<const float4 *>(wr + (size_t)(e0 + u) * d + c + 4 * lane);
+                    acc[u] = fmaf(x0, w.x, acc[u]);
+                    acc[u] = fmaf(x1, w.y, acc[u]);
+                    acc[u] = fmaf(x2, w.z, acc[u]);
+                    acc[u] = fmaf(x3, w.w, acc[u]);
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            if (e0 + u >= E) break;
+            const float sum = wave_sum_f32(acc[u]);
+            if (lane == 0) logits[(size_t)t * E + e0 + u] = sum + (bias ? bias[e0 + u] : 0.0f);
+        }
+    }
 }
 
 
@@ -1592,8 +1617,7 @@ hipError_t launch_router_bf16(const uint16_t *x, const uint16_t *wr, const float
 
 hipError_t launch_router_f32(const uint16_t *x, const float *wr, const float *bias, float *logits, int T, int d, int E,
                              hipStream_t s) {
-    const long n = (long)T * E;
-    hipLaunchKernelGGL(k_router_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, x, wr, bias, logits, T, d, E);
+    hipLaunchKernelGGL(k_router_f32, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, x, wr, bias, logits, T, d, E);
     return hipGetLastError();
 }
 
