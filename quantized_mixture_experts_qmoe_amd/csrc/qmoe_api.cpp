@@ -227,11 +227,21 @@ int timed(qmoe_ctx *c, int slot, hipStream_t s, Fn launch) {
     if (on) {
         a = take_event(c);
         b = take_event(c);
-        if (a && b) (void)hipEventRecord(a, s);
+        if (a && b) {
+            (void)hipEventRecord(a, s);
+        } else {   // creation failed: this launch goes untimed
+            if (a) c->pool.push_back(a);
+            if (b) c->pool.push_back(b);
+            a = b = nullptr;
+        }
     }
     hipError_t e = launch();
-    if (e != hipSuccess) return fail(QMOE_EHIP, "launch of %s failed: %s", kKernelNames[slot], hipGetErrorString(e));
-    if (on && a && b) {
+    if (e != hipSuccess) {
+        if (a) c->pool.push_back(a);
+        if (b) c->pool.push_back(b);
+        return fail(QMOE_EHIP, "launch of %s failed: %s", kKernelNames[slot], hipGetErrorString(e));
+    }
+    if (a && b) {
         (void)hipEventRecord(b, s);
         c->recs.push_back({slot, a, b});
     }
@@ -610,16 +620,26 @@ int qmoe_profile_enable(qmoe_ctx *c, int32_t slot_mask) {
 
 int qmoe_profile_read(qmoe_ctx *c, double *total_ms, int64_t *launches) {
     if (!c || !total_ms || !launches) return fail(QMOE_EINVAL, "NULL argument");
-    for (auto &r : c->recs) {
-        if (hipEventSynchronize(r.b) != hipSuccess) return fail(QMOE_EHIP, "hipEventSynchronize failed");
+    size_t done = 0;   // records read so far; their events are back in the pool
+    int rc = QMOE_OK;
+    for (; done < c->recs.size(); done++) {
+        const auto &r = c->recs[done];
         float ms = 0.0f;
-        if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) return fail(QMOE_EHIP, "hipEventElapsedTime failed");
+        if (hipEventSynchronize(r.b) != hipSuccess) {
+            rc = fail(QMOE_EHIP, "hipEventSynchronize failed");
+            break;
+        }
+        if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) {
+            rc = fail(QMOE_EHIP, "hipEventElapsedTime failed");
+            break;
+        }
         c->tot_ms[r.slot] += ms;
         c->launches[r.slot] += 1;
         c->pool.push_back(r.a);
         c->pool.push_back(r.b);
     }
-    c->recs.clear();
+    c->recs.erase(c->recs.begin(), c->recs.begin() + (std::ptrdiff_t)done);
+    if (rc) return rc;
     for (int i = 0; i < QMOE_NUM_KERNELS; i++) {
         total_ms[i] = c->tot_ms[i];
         launches[i] = c->launches[i];
