@@ -75,6 +75,9 @@ typedef enum {
     QMOE_W_FP8E4M3_CH = 4
 } qmoe_wformat;
 
+/* Router weight quantization (config field router_quant). */
+typedef enum { QMOE_RQ_NONE = 0, QMOE_RQ_INT8_CH = 1, QMOE_RQ_FP8E4M3_CH = 2 } qmoe_router_quant;
+
 /* Layer configuration, fixed at pack time.
  *   d_model      input and output width d; multiple of 256
  *   d_ff         routed expert width F; multiple of 128
@@ -85,6 +88,14 @@ typedef enum {
  *   wformat      a qmoe_wformat value
  *   group_size   must be 128 for the group formats (ignored otherwise)
  *   router_fp32  1: router weight is fp32 [E][d]; 0: bf16 [E][d]
+ *   router_quant a qmoe_router_quant value: QMOE_RQ_NONE routes with the
+ *                router weight as given; QMOE_RQ_INT8_CH / QMOE_RQ_FP8E4M3_CH
+ *                quantize it per expert row at pack time with the rules of
+ *                QMOE_W_INT8_SYM_CH / QMOE_W_FP8E4M3_CH above (the weight's
+ *                values, fp32 or bf16, are the quantizer's input), and the
+ *                logits become s_e * (x . q_e) + bias_e (fp32 accumulation).
+ *                Quantized routing is the Q-MoE page's section 4 option and the
+ *                routing-shift concern of the IT Donga DREAM-MoE section.
  *   renormalize  1: weights = softmax over the selected k (they sum to 1);
  *                0: weights = full-softmax probability of each selected expert
  *   max_tokens   largest T a forward may pass; sizes the workspace
@@ -99,6 +110,7 @@ typedef struct {
     int32_t renormalize;
     int32_t max_tokens;
     int32_t device;
+    int32_t router_quant;
 } qmoe_config;
 
 /* Caller-owned device buffers that receive routing results; any may be NULL.

@@ -18,6 +18,8 @@ LIB = os.path.join(HERE, "liboracle.so")
 
 FORMAT_CODES = {"int8_sym_ch": 0, "int4_asym_g128": 1, "int4_sym_g128": 2, "int3_sym_g128": 3,
                 "fp8e4m3_ch": 4}
+# router weight quantization per expert row (0: the weight as given)
+ROUTER_QUANT_CODES = {"none": 0, "int8": 1, "fp8": 2}
 GROUP_FORMATS = ("int4_asym_g128", "int4_sym_g128", "int3_sym_g128")
 
 
@@ -57,7 +59,7 @@ def lib() -> C.CDLL:
         L.orc_dispatch.restype = C.c_int
         L.orc_dispatch.argtypes = [C.c_int, C.c_int, C.c_int, P, P, P, P, P]
         L.orc_layer_create.restype = P
-        L.orc_layer_create.argtypes = [C.c_int] * 10 + [P, P, P, P, P, C.POINTER(C.c_int)]
+        L.orc_layer_create.argtypes = [C.c_int] * 11 + [P, P, P, P, P, C.POINTER(C.c_int)]
         L.orc_layer_free.restype = None
         L.orc_layer_free.argtypes = [P]
         L.orc_layer_codes.restype = C.c_int
@@ -158,7 +160,8 @@ class OracleLayer:
         bias = None if inp.bias is None else np.ascontiguousarray(inp.bias, np.float32)
         err = C.c_int(0)
         self.h = lib().orc_layer_create(cfg.d, cfg.F, cfg.E, cfg.k, cfg.S, cfg.Fs, FORMAT_CODES[cfg.wformat],
-                                        cfg.group, int(cfg.renormalize), int(cfg.router_fp32), _p(wr), _p(bias),
+                                        cfg.group, int(cfg.renormalize), int(cfg.router_fp32),
+                                        ROUTER_QUANT_CODES[cfg.router_quant], _p(wr), _p(bias),
                                         C.cast(wg, C.c_void_p), C.cast(wu, C.c_void_p), C.cast(wd, C.c_void_p),
                                         C.byref(err))
         self._keep = None   # the oracle holds its own codes now

@@ -416,10 +416,14 @@ void orc_layer_free(void *h)
 
 /* Build the oracle's own copy of a layer: quantize every expert matrix with the
  * oracle quantizer. w_router is [E][d] fp32 (router_fp32) or bf16 bit patterns.
+ * router_quant 1 / 2 quantizes the router weight's values per expert row with
+ * the oracle's INT8 / FP8 per-channel quantizer and routes with the dequantized
+ * weight s_e * q_e (Q-MoE page, section 4: quantized routing); 0 routes with
+ * the weight as given.
  * Weight arrays are [F][d] (gate, up) and [d][F] (down), E routed then S shared. */
 void *orc_layer_create(int d, int F, int E, int k, int S, int Fs, int fmt, int group, int renorm, int router_fp32,
-                       const void *w_router, const float *bias, const float *const *wg, const float *const *wu,
-                       const float *const *wd, int *err)
+                       int router_quant, const void *w_router, const float *bias, const float *const *wg,
+                       const float *const *wu, const float *const *wd, int *err)
 {
     orc_layer *L = (orc_layer *)calloc(1, sizeof(orc_layer));
     int rc = 0;
@@ -440,6 +444,28 @@ void *orc_layer_create(int d, int F, int E, int k, int S, int Fs, int fmt, int g
             memcpy(&f, &b, 4);
             L->w_router[i] = f;
         }
+    }
+    if (router_quant == 1 || router_quant == 2) {
+        /* the widened values are floats exactly: quantize them as a [E][d] matrix */
+        orc_matrix r;
+        float *wf = (float *)malloc(sizeof(float) * (size_t)E * d);
+        for (size_t i = 0; i < (size_t)E * d; i++)
+            wf[i] = (float)L->w_router[i];
+        const int rfmt = router_quant == 1 ? ORC_INT8_SYM_CH : ORC_FP8E4M3_CH;
+        rc = quantize_matrix(&r, rfmt, group, E, d, wf);
+        if (rc == 0)
+            rc = orc_dequantize(rfmt, E, d, group, r.q, r.scale, r.zero, L->w_router);
+        free_matrix(&r);
+        free(wf);
+        if (rc != 0) {
+            *err = rc;
+            orc_layer_free(L);
+            return NULL;
+        }
+    } else if (router_quant != 0) {
+        *err = -1;
+        orc_layer_free(L);
+        return NULL;
     }
     if (bias) {
         L->bias = (double *)malloc(sizeof(double) * (size_t)E);

@@ -28,6 +28,7 @@ QMOE_NUM_KERNELS = 10
 
 WFORMAT_CODES = {"int8_sym_ch": 0, "int4_asym_g128": 1, "int4_sym_g128": 2, "int3_sym_g128": 3,
                  "fp8e4m3_ch": 4}
+ROUTER_QUANT_CODES = {"none": 0, "int8": 1, "fp8": 2}
 
 ABI_SYMBOLS = ("qmoe_pack_experts", "qmoe_route_topk", "qmoe_forward", "qmoe_destroy", "qmoe_last_error",
                "qmoe_export_packed", "qmoe_profile_enable", "qmoe_profile_read", "qmoe_kernel_name")
@@ -36,7 +37,7 @@ ABI_SYMBOLS = ("qmoe_pack_experts", "qmoe_route_topk", "qmoe_forward", "qmoe_des
 class QmoeConfig(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("d_model", "d_ff", "n_experts", "top_k", "n_shared", "d_ff_shared",
                                          "wformat", "group_size", "router_fp32", "renormalize", "max_tokens",
-                                         "device")]
+                                         "device", "router_quant")]
 
 
 class QmoeRouteOut(C.Structure):
@@ -131,7 +132,7 @@ def make_config(cfg, max_tokens: int, device: int = 0) -> QmoeConfig:
     return QmoeConfig(d_model=cfg.d, d_ff=cfg.F, n_experts=cfg.E, top_k=cfg.k, n_shared=cfg.S,
                       d_ff_shared=cfg.Fs, wformat=WFORMAT_CODES[cfg.wformat], group_size=cfg.group,
                       router_fp32=int(cfg.router_fp32), renormalize=int(cfg.renormalize),
-                      max_tokens=max_tokens, device=device)
+                      max_tokens=max_tokens, device=device, router_quant=ROUTER_QUANT_CODES[cfg.router_quant])
 
 
 def _ptr_array(arrs: Sequence[np.ndarray]):

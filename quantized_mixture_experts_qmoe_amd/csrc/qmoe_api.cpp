@@ -62,8 +62,10 @@ struct qmoe_ctx {
     std::vector<MatInfo> m13, m2;   // per expert (E + S)
     ExpertW ex0[2] = {};            // routed expert 0, shared expert 0
     int64_t ex_stride[2] = {0, 0};  // byte stride between consecutive experts of each group
-    void *router_w = nullptr;       // bf16 [E][d] or fp32 [E][d]
+    void *router_w = nullptr;       // bf16 [E][d] or fp32 [E][d] (quantized router: the codes' values as bf16)
     float *router_b = nullptr;
+    float *router_s = nullptr;      // quantized router: per-expert scale [E]
+    bool router_bf16 = true;        // the bf16 MFMA router runs (bf16 weights or quantized codes)
     // workspace
     float *logits = nullptr, *wpair = nullptr, *wrow = nullptr;
     int32_t *idx = nullptr, *chunk_counts = nullptr, *chunk_base = nullptr, *counts = nullptr, *offsets = nullptr;
@@ -130,6 +132,8 @@ int validate(const qmoe_config *cfg) {
                     (long long)cfg->max_tokens * cfg->d_model);
     if (cfg->renormalize != 0 && cfg->renormalize != 1) return fail(QMOE_EINVAL, "renormalize must be 0 or 1");
     if (cfg->router_fp32 != 0 && cfg->router_fp32 != 1) return fail(QMOE_EINVAL, "router_fp32 must be 0 or 1");
+    if (cfg->router_quant < QMOE_RQ_NONE || cfg->router_quant > QMOE_RQ_FP8E4M3_CH)
+        return fail(QMOE_EINVAL, "unknown router_quant %d", cfg->router_quant);
     return QMOE_OK;
 }
 
@@ -428,11 +432,35 @@ int qmoe_pack_experts(const qmoe_config *cfg, const float *const *w_gate, const 
         }
     }
 
-    // Router weight and bias.
-    const size_t wr_bytes = (size_t)c->E * c->d * (cfg->router_fp32 ? 4 : 2);
-    if (!rc) rc = dalloc(c, &c->router_w, wr_bytes);
-    if (!rc && hipMemcpy(c->router_w, w_router, wr_bytes, hipMemcpyHostToDevice) != hipSuccess)
-        rc = fail(QMOE_EHIP, "upload of router weight failed");
+    // Router weight (as given, or quantized per expert row) and bias.
+    c->router_bf16 = !cfg->router_fp32 || cfg->router_quant != QMOE_RQ_NONE;
+    if (!rc && cfg->router_quant != QMOE_RQ_NONE) {
+        const size_t n = (size_t)c->E * c->d;
+        std::vector<float> wf(n);
+        for (size_t i = 0; i < n; i++) {
+            if (cfg->router_fp32) {
+                wf[i] = ((const float *)w_router)[i];
+            } else {
+                const uint32_t u = (uint32_t)((const uint16_t *)w_router)[i] << 16;
+                memcpy(&wf[i], &u, 4);
+            }
+        }
+        std::vector<uint16_t> codes;
+        std::vector<float> rs;
+        rc = quantize_router(cfg->router_quant, c->E, c->d, wf.data(), codes, rs);
+        if (rc) rc = fail(rc, "router quantization failed");
+        if (!rc) rc = dalloc(c, &c->router_w, n * 2);
+        if (!rc && hipMemcpy(c->router_w, codes.data(), n * 2, hipMemcpyHostToDevice) != hipSuccess)
+            rc = fail(QMOE_EHIP, "upload of router weight failed");
+        if (!rc) rc = dalloc(c, (void **)&c->router_s, sizeof(float) * c->E);
+        if (!rc && hipMemcpy(c->router_s, rs.data(), sizeof(float) * c->E, hipMemcpyHostToDevice) != hipSuccess)
+            rc = fail(QMOE_EHIP, "upload of router scales failed");
+    } else if (!rc) {
+        const size_t wr_bytes = (size_t)c->E * c->d * (cfg->router_fp32 ? 4 : 2);
+        rc = dalloc(c, &c->router_w, wr_bytes);
+        if (!rc && hipMemcpy(c->router_w, w_router, wr_bytes, hipMemcpyHostToDevice) != hipSuccess)
+            rc = fail(QMOE_EHIP, "upload of router weight failed");
+    }
     if (!rc && router_bias) {
         rc = dalloc(c, (void **)&c->router_b, sizeof(float) * c->E);
         if (!rc && hipMemcpy(c->router_b, router_bias, sizeof(float) * c->E, hipMemcpyHostToDevice) != hipSuccess)
@@ -507,15 +535,15 @@ int qmoe_forward(qmoe_ctx *c, const uint16_t *x, int32_t T, uint16_t *y, qmoe_ro
     // decode kernel (bm == 16) computes its own while staging rows.
     const bool need_sums = grouped && bm > 16;
     // the bf16 router emits the row sums from its staged x tiles
-    const bool fused_sums = need_sums && !c->cfg.router_fp32;
+    const bool fused_sums = need_sums && c->router_bf16;
     int rc;
-    if (c->cfg.router_fp32)
+    if (!c->router_bf16)
         rc = timed(c, K_ROUTER, s, [&] {
             return launch_router_f32(x, (const float *)c->router_w, c->router_b, c->logits, T, c->d, c->E, s);
         });
     else
         rc = timed(c, K_ROUTER, s, [&] {
-            return launch_router_bf16(x, (const uint16_t *)c->router_w, c->router_b, c->logits,
+            return launch_router_bf16(x, (const uint16_t *)c->router_w, c->router_s, c->router_b, c->logits,
                                       fused_sums ? c->xsum : nullptr, zc, T, c->d, c->E, s);
         });
     if (rc) return rc;

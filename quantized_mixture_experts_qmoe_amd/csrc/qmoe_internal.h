@@ -101,6 +101,12 @@ struct CanonMatrix {      // canonical quantized matrix, row-major [N][K]
 // Quantize w[N][K] by the format rules. Returns QMOE_OK or a QMOE_E* code.
 int quantize_matrix(int wformat, int N, int K, const float *w, CanonMatrix &out);
 
+// Router weight w[E][d] quantized per expert row (router_quant: QMOE_RQ_INT8_CH
+// or QMOE_RQ_FP8E4M3_CH, the rules of the per-channel expert formats): the
+// codes' values as bf16 bits (exact) and the fp32 row scales.
+int quantize_router(int router_quant, int E, int d, const float *w, std::vector<uint16_t> &codes_bf16,
+                    std::vector<float> &scale);
+
 // Device layout of a canonical matrix (codes blocks, group scales/zeros as fp16
 // bits, per-channel scales). For W13 the caller passes the interleaved matrix.
 struct PackedMatrix {
@@ -119,8 +125,10 @@ void unlayout_matrix(int wformat, const PackedMatrix &p, CanonMatrix &m);
 // Kernel launchers (qmoe_kernels.hip). All asynchronous on `s`.
 // ---------------------------------------------------------------------------
 // xsum (may be NULL): receives xscale * per-128-group row sums of x.
-hipError_t launch_router_bf16(const uint16_t *x, const uint16_t *wr, const float *bias, float *logits, float *xsum,
-                              float xscale, int T, int d, int E, hipStream_t s);
+// rscale (may be NULL): per-expert scale of a quantized router (logit =
+// rscale[e] * x.wr[e] + bias[e]).
+hipError_t launch_router_bf16(const uint16_t *x, const uint16_t *wr, const float *rscale, const float *bias,
+                              float *logits, float *xsum, float xscale, int T, int d, int E, hipStream_t s);
 hipError_t launch_router_f32(const uint16_t *x, const float *wr, const float *bias, float *logits, int T, int d, int E,
                              hipStream_t s);
 hipError_t launch_topk(const float *logits, int T, int E, int k, int renorm, int32_t *idx, float *w, hipStream_t s);

@@ -100,6 +100,7 @@ __device__ __forceinline__ void dma4s(const void *sbase, uint32_t voff, uint32_t
 // (times xscale) read from the staged tile.
 template <int BT, int BE, int WE, int NST>
 __global__ __launch_bounds__(256) void k_router_lds(const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr,
+                                                    const float *__restrict__ rscale,
                                                     const float *__restrict__ bias, float *__restrict__ logits,
                                                     float *__restrict__ xsum, float xscale, int T, int d, int E,
                                                     int net) {
@@ -242,12 +243,13 @@ __global__ __launch_bounds__(256) void k_router_lds(const uint16_t *__restrict__
         const int e = e0 + 16 * (we * NT + jj) + (lane & 15);
         if (e >= E) continue;
         const float b = bias ? bias[e] : 0.0f;
+        const float sc = rscale ? rscale[e] : 1.0f;
 #pragma unroll
         for (int i = 0; i < MT; i++)
 #pragma unroll
             for (int r = 0; r < 4; r++) {
                 const int t = t0 + 16 * i + (lane >> 4) * 4 + r;
-                if (t < T) logits[(size_t)t * E + e] = acc[i][jj][r] + b;
+                if (t < T) logits[(size_t)t * E + e] = acc[i][jj][r] * sc + b;
             }
     }
 }
@@ -1595,23 +1597,23 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ O, co
 
 // Expert tiles of 64 for many experts, 32, or 16 when E <= 16 (no idle half tile).
 template <int BT, int BE, int WE, int NST>
-static void launch_router_lds(const uint16_t *x, const uint16_t *wr, const float *bias, float *logits, float *xsum,
-                              float xscale, int T, int d, int E, hipStream_t s) {
+static void launch_router_lds(const uint16_t *x, const uint16_t *wr, const float *rscale, const float *bias,
+                              float *logits, float *xsum, float xscale, int T, int d, int E, hipStream_t s) {
     const long gx = 8L * ((T + BT * 8 - 1) / (BT * 8));   // token tiles, padded to a multiple of 8
     const int net = (E + BE - 1) / BE;
-    hipLaunchKernelGGL((k_router_lds<BT, BE, WE, NST>), dim3((unsigned)(gx * net)), dim3(256), 0, s, x, wr, bias,
-                       logits, xsum, xscale, T, d, E, net);
+    hipLaunchKernelGGL((k_router_lds<BT, BE, WE, NST>), dim3((unsigned)(gx * net)), dim3(256), 0, s, x, wr, rscale,
+                       bias, logits, xsum, xscale, T, d, E, net);
 }
 
-hipError_t launch_router_bf16(const uint16_t *x, const uint16_t *wr, const float *bias, float *logits, float *xsum,
-                              float xscale, int T, int d, int E, hipStream_t s) {
+hipError_t launch_router_bf16(const uint16_t *x, const uint16_t *wr, const float *rscale, const float *bias,
+                              float *logits, float *xsum, float xscale, int T, int d, int E, hipStream_t s) {
     // 16 x 16 tiles as four independent streams for small batches and few
     // experts (LDS: 4 rings of 3 x 8 KB); wider expert tiles for large batches
     // (4 rings of 3 x 12 KB; shared rings of 3 x 20 KB and 2 x 40 KB)
-    if (T < 256 || E <= 16) launch_router_lds<16, 16, 1, 3>(x, wr, bias, logits, xsum, xscale, T, d, E, s);
-    else if (E <= 32) launch_router_lds<16, 32, 1, 3>(x, wr, bias, logits, xsum, xscale, T, d, E, s);
-    else if (E <= 64) launch_router_lds<16, 64, 4, 3>(x, wr, bias, logits, xsum, xscale, T, d, E, s);
-    else launch_router_lds<32, 128, 4, 2>(x, wr, bias, logits, xsum, xscale, T, d, E, s);
+    if (T < 256 || E <= 16) launch_router_lds<16, 16, 1, 3>(x, wr, rscale, bias, logits, xsum, xscale, T, d, E, s);
+    else if (E <= 32) launch_router_lds<16, 32, 1, 3>(x, wr, rscale, bias, logits, xsum, xscale, T, d, E, s);
+    else if (E <= 64) launch_router_lds<16, 64, 4, 3>(x, wr, rscale, bias, logits, xsum, xscale, T, d, E, s);
+    else launch_router_lds<32, 128, 4, 2>(x, wr, rscale, bias, logits, xsum, xscale, T, d, E, s);
     return hipGetLastError();
 }
 

@@ -84,7 +84,32 @@ float bf16_value(uint16_t b) {
     return f;
 }
 
+// Value of an OCP e4m3fn code (finite codes only: the saturating encoder never
+// emits NaN): sign, 4 exponent bits with bias 7, 3 mantissa bits; exponent 0
+// holds the subnormal multiples of 2^-9.
+float e4m3_value(uint8_t c) {
+    const int e = (c >> 3) & 15, m = c & 7;
+    const float mag = e == 0 ? ldexpf((float)m, -9) : ldexpf(1.0f + (float)m / 8.0f, e - 7);
+    return (c & 0x80) ? -mag : mag;
+}
+
 }  // namespace
+
+int quantize_router(int router_quant, int E, int d, const float *w, std::vector<uint16_t> &codes_bf16,
+                    std::vector<float> &scale) {
+    const int fmt = router_quant == QMOE_RQ_INT8_CH ? QMOE_W_INT8_SYM_CH : QMOE_W_FP8E4M3_CH;
+    CanonMatrix m;
+    const int rc = quantize_matrix(fmt, E, d, w, m);
+    if (rc != QMOE_OK) return rc;
+    codes_bf16.resize((size_t)E * d);
+    for (size_t i = 0; i < codes_bf16.size(); i++) {
+        // int8 codes and e4m3 values are exact in bf16
+        const float v = fmt == QMOE_W_INT8_SYM_CH ? (float)m.q[i] : e4m3_value((uint8_t)m.q[i]);
+        codes_bf16[i] = bf16_rne_bits(v);
+    }
+    scale = m.scale;   // [E]: one per expert row
+    return QMOE_OK;
+}
 
 int quantize_matrix(int wformat, int N, int K, const float *w, CanonMatrix &out) {
     out.N = N;

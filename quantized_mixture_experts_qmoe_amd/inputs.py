@@ -42,6 +42,7 @@ class LayerConfig:
     S: int = 0        # always-on shared experts
     Fs: int = 0       # d_ff of a shared expert
     router_fp32: bool = False
+    router_quant: str = "none"   # router weight quantized per expert row: "none", "int8" or "fp8"
     bias: bool = False
     renormalize: bool = True
     group: int = 128

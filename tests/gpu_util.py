@@ -66,6 +66,25 @@ def logit_bound(x_bits: np.ndarray, w_router: np.ndarray, router_fp32: bool) -> 
     return gamma * (X @ W.T)
 
 
+def router_weight_and_bound(O, inp):
+    """The router weight the layer routes with (the given one, or its per-row
+    quantization by the oracle's quantizer) in float64, and the GPU logit error
+    bound for it: gamma_d * sum_k |x_k w_k|, plus one rounding of the logit for
+    the scale multiply of a quantized router."""
+    cfg = inp.cfg
+    W = np.asarray(inp.w_router if cfg.router_fp32 else bf16_bits_to_f32(inp.w_router), np.float32)
+    if cfg.router_quant == "none":
+        return W.astype(np.float64), logit_bound(inp.x, inp.w_router, cfg.router_fp32)
+    fmt = {"int8": "int8_sym_ch", "fp8": "fp8e4m3_ch"}[cfg.router_quant]
+    q, s, z = O.quantize(fmt, W)
+    What = O.dequantize(fmt, q, s, z)
+    X = np.abs(bf16_bits_to_f32(inp.x).astype(np.float64))
+    d = X.shape[1]
+    u = 2.0 ** -24
+    gamma = (d + 3) * u / (1 - (d + 3) * u)
+    return What, gamma * (X @ np.abs(What).T)
+
+
 def check_own_routing(ref: dict, logits_gpu: np.ndarray, idx_gpu: np.ndarray, w_gpu: np.ndarray, bound: np.ndarray,
                       bias=None):
     """Router checks against the oracle on the GPU's own logits. Returns the

@@ -59,6 +59,8 @@ def base_cfg(**kw):
     (dict(n_shared=-1), Q.QMOE_EINVAL),
     (dict(n_shared=1, d_ff_shared=0), Q.QMOE_EINVAL),
     (dict(renormalize=2), Q.QMOE_EINVAL),
+    (dict(router_quant=3), Q.QMOE_EINVAL),
+    (dict(router_quant=-1), Q.QMOE_EINVAL),
     (dict(d_model=320), Q.QMOE_EUNSUPPORTED),     # not a multiple of 256
     (dict(d_ff=200), Q.QMOE_EUNSUPPORTED),        # not a multiple of 128
     (dict(wformat=2, group_size=64), Q.QMOE_EUNSUPPORTED),

@@ -7,7 +7,8 @@ import torch
 
 from quantized_mixture_experts_qmoe_amd import QMoE, QmoeError
 from quantized_mixture_experts_qmoe_amd.inputs import CONFIGS, LayerConfig, make_inputs, make_x
-from gpu_util import (assert_output_close, bf16_tensor_to_f64, check_own_routing, logit_bound, to_dev_bf16)
+from gpu_util import (assert_output_close, bf16_tensor_to_f64, check_own_routing, logit_bound,
+                      router_weight_and_bound, to_dev_bf16)
 
 pytestmark = pytest.mark.gpu
 
@@ -28,7 +29,7 @@ def run_and_check(O, cfg, seed=0, x_bits=None, tag="", output_rounding_allowance
     idx_gpu = route["topk_idx"].cpu().numpy()
     w_gpu = route["topk_w"].cpu().numpy()
     lg_gpu = route["logits"].cpu().numpy()
-    bound = logit_bound(inp.x, inp.w_router, cfg.router_fp32)
+    _, bound = router_weight_and_bound(O, inp)
     diff = check_own_routing(ref, lg_gpu, idx_gpu, w_gpu, bound, inp.bias)
     y_ref = ref["y"].copy()
     if diff:
@@ -137,6 +138,18 @@ def test_forward_group_format_with_fp32_router(oracle_mod, fmt, d):
 def test_forward_shared_experts_and_bias(oracle_mod, fmt):
     cfg = small(fmt, T=257, E=12, k=3, S=2, Fs=384, bias=True)
     run_and_check(oracle_mod, cfg, seed=5, tag=f"shared {fmt}")
+
+
+@pytest.mark.parametrize("rq", ["int8", "fp8"])
+@pytest.mark.parametrize("T,E,k,fmt,fp32", [(300, 16, 4, "int4_sym_g128", False), (16, 64, 4, "int4_asym_g128", False),
+                                            (257, 12, 3, "int8_sym_ch", True), (1000, 128, 8, "int4_sym_g128", False)])
+def test_forward_quantized_router(oracle_mod, rq, T, E, k, fmt, fp32):
+    """Router weight quantized per expert row (INT8 / FP8 rules of the
+    per-channel expert formats): the GPU routes on s_e * (x . q_e) + b_e, the
+    oracle on x . (s q)^T + b with its own codes; small, decode-sized and
+    128-expert batches, a bf16 and an fp32 given router weight."""
+    cfg = small(fmt, name=f"rq_{rq}", T=T, E=E, k=k, router_fp32=fp32, router_quant=rq, bias=True)
+    run_and_check(oracle_mod, cfg, seed=T + E, tag=f"router {rq} T={T} E={E} {fmt}")
 
 
 def test_forward_unrenormalised(oracle_mod):
