@@ -85,7 +85,8 @@ typedef enum { QMOE_RQ_NONE = 0, QMOE_RQ_INT8_CH = 1, QMOE_RQ_FP8E4M3_CH = 2 } q
  *   top_k        experts per token k, 1..min(E, 64)
  *   n_shared     always-on shared experts S >= 0 (mixing weight 1, same format)
  *   d_ff_shared  shared expert width (multiple of 128; ignored when S = 0)
- *   wformat      a qmoe_wformat value
+ *   wformat      a qmoe_wformat value (the format of every expert unless
+ *                expert_wformat is given)
  *   group_size   must be 128 for the group formats (ignored otherwise)
  *   router_fp32  1: router weight is fp32 [E][d]; 0: bf16 [E][d]
  *   router_quant a qmoe_router_quant value: QMOE_RQ_NONE routes with the
@@ -98,6 +99,13 @@ typedef enum { QMOE_RQ_NONE = 0, QMOE_RQ_INT8_CH = 1, QMOE_RQ_FP8E4M3_CH = 2 } q
  *                routing-shift concern of the IT Donga DREAM-MoE section.
  *   renormalize  1: weights = softmax over the selected k (they sum to 1);
  *                0: weights = full-softmax probability of each selected expert
+ *   expert_wformat  NULL, or host array [n_experts + n_shared] of qmoe_wformat
+ *                values giving each expert its own format (routed experts
+ *                first, then shared; read during qmoe_pack_experts only); NULL:
+ *                every expert in `wformat`. Per-expert precision is the Q-MoE
+ *                page's expert quantizer (section 3 components table: each
+ *                expert keeps its own precision, e.g. INT8 for frequently
+ *                chosen experts and INT4 for the rest)
  *   max_tokens   largest T a forward may pass; sizes the workspace
  *                (max_tokens <= 2^20, max_tokens * (top_k + n_shared) <= 2^21
  *                and max_tokens * d_model < 2^31)
@@ -111,6 +119,7 @@ typedef struct {
     int32_t max_tokens;
     int32_t device;
     int32_t router_quant;
+    const int32_t *expert_wformat;
 } qmoe_config;
 
 /* Caller-owned device buffers that receive routing results; any may be NULL.

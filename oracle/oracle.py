@@ -59,7 +59,7 @@ def lib() -> C.CDLL:
         L.orc_dispatch.restype = C.c_int
         L.orc_dispatch.argtypes = [C.c_int, C.c_int, C.c_int, P, P, P, P, P]
         L.orc_layer_create.restype = P
-        L.orc_layer_create.argtypes = [C.c_int] * 11 + [P, P, P, P, P, C.POINTER(C.c_int)]
+        L.orc_layer_create.argtypes = [C.c_int] * 11 + [P, P, P, P, P, P, C.POINTER(C.c_int)]
         L.orc_layer_free.restype = None
         L.orc_layer_free.argtypes = [P]
         L.orc_layer_codes.restype = C.c_int
@@ -158,10 +158,12 @@ class OracleLayer:
         wd = arr(*[a.ctypes.data for a in self._keep[2 * n:3 * n]])
         wr = np.ascontiguousarray(inp.w_router)
         bias = None if inp.bias is None else np.ascontiguousarray(inp.bias, np.float32)
+        fmts = None if cfg.expert_formats is None else np.array([FORMAT_CODES[f] for f in cfg.expert_formats],
+                                                                  np.int32)
         err = C.c_int(0)
         self.h = lib().orc_layer_create(cfg.d, cfg.F, cfg.E, cfg.k, cfg.S, cfg.Fs, FORMAT_CODES[cfg.wformat],
                                         cfg.group, int(cfg.renormalize), int(cfg.router_fp32),
-                                        ROUTER_QUANT_CODES[cfg.router_quant], _p(wr), _p(bias),
+                                        ROUTER_QUANT_CODES[cfg.router_quant], _p(fmts), _p(wr), _p(bias),
                                         C.cast(wg, C.c_void_p), C.cast(wu, C.c_void_p), C.cast(wd, C.c_void_p),
                                         C.byref(err))
         self._keep = None   # the oracle holds its own codes now
@@ -180,7 +182,7 @@ class OracleLayer:
         cfg = self.cfg
         f = cfg.F if expert < cfg.E else cfg.Fs
         N, K = (f, cfg.d) if matrix < 2 else (cfg.d, f)
-        G = K // cfg.group if cfg.wformat in GROUP_FORMATS else 1
+        G = K // cfg.group if cfg.expert_format(expert) in GROUP_FORMATS else 1
         q = np.zeros((N, K), np.int8)
         s = np.zeros((N, G), np.float32)
         z = np.zeros((N, G), np.float32)

@@ -419,11 +419,13 @@ void orc_layer_free(void *h)
  * router_quant 1 / 2 quantizes the router weight's values per expert row with
  * the oracle's INT8 / FP8 per-channel quantizer and routes with the dequantized
  * weight s_e * q_e (Q-MoE page, section 4: quantized routing); 0 routes with
- * the weight as given.
+ * the weight as given. fmts (NULL: every expert in fmt) gives each expert its
+ * own format (Q-MoE page, section 3: the expert quantizer keeps a precision
+ * per expert).
  * Weight arrays are [F][d] (gate, up) and [d][F] (down), E routed then S shared. */
 void *orc_layer_create(int d, int F, int E, int k, int S, int Fs, int fmt, int group, int renorm, int router_fp32,
-                       int router_quant, const void *w_router, const float *bias, const float *const *wg,
-                       const float *const *wu, const float *const *wd, int *err)
+                       int router_quant, const int *fmts, const void *w_router, const float *bias,
+                       const float *const *wg, const float *const *wu, const float *const *wd, int *err)
 {
     orc_layer *L = (orc_layer *)calloc(1, sizeof(orc_layer));
     int rc = 0;
@@ -478,9 +480,10 @@ void *orc_layer_create(int d, int F, int E, int k, int S, int Fs, int fmt, int g
     #pragma omp parallel for schedule(dynamic) reduction(min : rc)
     for (int i = 0; i < E + S; i++) {
         int f = i < E ? F : Fs;
-        int r1 = quantize_matrix(&L->gate[i], fmt, group, f, d, wg[i]);
-        int r2 = quantize_matrix(&L->up[i], fmt, group, f, d, wu[i]);
-        int r3 = quantize_matrix(&L->down[i], fmt, group, d, f, wd[i]);
+        int fi = fmts ? fmts[i] : fmt;
+        int r1 = quantize_matrix(&L->gate[i], fi, group, f, d, wg[i]);
+        int r2 = quantize_matrix(&L->up[i], fi, group, f, d, wu[i]);
+        int r3 = quantize_matrix(&L->down[i], fi, group, d, f, wd[i]);
         int r = r1 < r2 ? r1 : r2;
         r = r < r3 ? r : r3;
         if (r < rc) rc = r;

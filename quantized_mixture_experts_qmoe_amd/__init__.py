@@ -37,7 +37,7 @@ ABI_SYMBOLS = ("qmoe_pack_experts", "qmoe_route_topk", "qmoe_forward", "qmoe_des
 class QmoeConfig(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("d_model", "d_ff", "n_experts", "top_k", "n_shared", "d_ff_shared",
                                          "wformat", "group_size", "router_fp32", "renormalize", "max_tokens",
-                                         "device", "router_quant")]
+                                         "device", "router_quant")] + [("expert_wformat", C.c_void_p)]
 
 
 class QmoeRouteOut(C.Structure):
@@ -129,10 +129,15 @@ def _check(rc: int, where: str) -> None:
 
 def make_config(cfg, max_tokens: int, device: int = 0) -> QmoeConfig:
     """QmoeConfig from an ``inputs.LayerConfig``."""
-    return QmoeConfig(d_model=cfg.d, d_ff=cfg.F, n_experts=cfg.E, top_k=cfg.k, n_shared=cfg.S,
-                      d_ff_shared=cfg.Fs, wformat=WFORMAT_CODES[cfg.wformat], group_size=cfg.group,
-                      router_fp32=int(cfg.router_fp32), renormalize=int(cfg.renormalize),
-                      max_tokens=max_tokens, device=device, router_quant=ROUTER_QUANT_CODES[cfg.router_quant])
+    c = QmoeConfig(d_model=cfg.d, d_ff=cfg.F, n_experts=cfg.E, top_k=cfg.k, n_shared=cfg.S,
+                   d_ff_shared=cfg.Fs, wformat=WFORMAT_CODES[cfg.wformat], group_size=cfg.group,
+                   router_fp32=int(cfg.router_fp32), renormalize=int(cfg.renormalize),
+                   max_tokens=max_tokens, device=device, router_quant=ROUTER_QUANT_CODES[cfg.router_quant])
+    if cfg.expert_formats is not None:
+        assert len(cfg.expert_formats) == cfg.E + cfg.S
+        c._formats = np.array([WFORMAT_CODES[f] for f in cfg.expert_formats], np.int32)   # kept alive with c
+        c.expert_wformat = c._formats.ctypes.data
+    return c
 
 
 def _ptr_array(arrs: Sequence[np.ndarray]):
@@ -225,7 +230,7 @@ class QMoE:
         cfg = self.cfg
         f = cfg.F if expert < cfg.E else cfg.Fs
         N, K = (f, cfg.d) if matrix < 2 else (cfg.d, f)
-        G = K // 128 if cfg.wformat in ("int4_asym_g128", "int4_sym_g128", "int3_sym_g128") else 1
+        G = K // 128 if cfg.expert_format(expert) in ("int4_asym_g128", "int4_sym_g128", "int3_sym_g128") else 1
         q = np.zeros((N, K), np.int8)
         s = np.zeros((N, G), np.float32)
         z = np.zeros((N, G), np.float32)

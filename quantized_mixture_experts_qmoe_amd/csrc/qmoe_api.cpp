@@ -53,15 +53,22 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct qmoe_ctx {
     qmoe_config cfg{};
-    int df = 0;
+    int df = 0;                     // device format of every expert (uniform layers)
+    std::vector<int> wfmt;          // per expert: qmoe_wformat
+    bool mixed = false;             // experts in more than one device format
+    bool any_group = false, any_8bit = false;
+    int fmt_mask = 0;               // bit f: some expert uses device format f
+    int32_t *eslot = nullptr;       // per expert: group << 20 | index (mixed layers)
+    float *xsum_asym = nullptr;     // row sums for INT4_ASYM experts when both scales are needed
     int E = 0, S = 0, F = 0, Fs = 0, d = 0, k = 0;
     int maxT = 0;
     // weights
     uint8_t *arena = nullptr;
     size_t arena_bytes = 0;
     std::vector<MatInfo> m13, m2;   // per expert (E + S)
-    ExpertW ex0[2] = {};            // routed expert 0, shared expert 0
-    int64_t ex_stride[2] = {0, 0};  // byte stride between consecutive experts of each group
+    ExpertW ex0[kMaxExpertGroups] = {};        // first expert of each group (see GemmArgs)
+    int64_t ex_stride[kMaxExpertGroups] = {};  // byte stride between consecutive experts of a group
+    int32_t gfmt[kMaxExpertGroups] = {};       // device format of each group
     void *router_w = nullptr;       // bf16 [E][d] or fp32 [E][d] (quantized router: the codes' values as bf16)
     float *router_b = nullptr;
     float *router_s = nullptr;      // quantized router: per-expert scale [E]
@@ -104,6 +111,10 @@ int dalloc(qmoe_ctx *c, void **p, size_t bytes) {
     return QMOE_OK;
 }
 
+// Device formats as a dense index 0..3 (format masks, expert groups).
+int fmt_index(int df) { return df == DF_FP8 ? 3 : df; }
+int fmt_of_index(int fi) { return fi == 3 ? DF_FP8 : fi; }
+
 int validate(const qmoe_config *cfg) {
     if (!cfg) return fail(QMOE_EINVAL, "cfg is NULL");
     if (cfg->d_model <= 0 || cfg->d_ff <= 0 || cfg->n_experts <= 0 || cfg->max_tokens <= 0)
@@ -113,11 +124,19 @@ int validate(const qmoe_config *cfg) {
     if (cfg->n_shared < 0) return fail(QMOE_EINVAL, "n_shared must be >= 0");
     if (cfg->n_shared > 0 && cfg->d_ff_shared <= 0) return fail(QMOE_EINVAL, "d_ff_shared must be positive");
     if (dev_format(cfg->wformat) < 0) return fail(QMOE_EINVAL, "unknown wformat %d", cfg->wformat);
+    if (cfg->expert_wformat && cfg->n_experts > 0 && cfg->n_shared >= 0) {
+        for (int i = 0; i < cfg->n_experts + cfg->n_shared; i++)
+            if (dev_format(cfg->expert_wformat[i]) < 0)
+                return fail(QMOE_EINVAL, "unknown wformat %d for expert %d", cfg->expert_wformat[i], i);
+    }
     if (cfg->d_model % 256 != 0) return fail(QMOE_EUNSUPPORTED, "d_model=%d is not a multiple of 256", cfg->d_model);
     if (cfg->d_ff % 128 != 0) return fail(QMOE_EUNSUPPORTED, "d_ff=%d is not a multiple of 128", cfg->d_ff);
     if (cfg->n_shared > 0 && cfg->d_ff_shared % 128 != 0)
         return fail(QMOE_EUNSUPPORTED, "d_ff_shared=%d is not a multiple of 128", cfg->d_ff_shared);
-    if (is_group_wformat(cfg->wformat) && cfg->group_size != 128)
+    bool group = is_group_wformat(cfg->wformat);
+    if (cfg->expert_wformat && cfg->n_experts > 0 && cfg->n_shared >= 0)
+        for (int i = 0; i < cfg->n_experts + cfg->n_shared; i++) group = group || is_group_wformat(cfg->expert_wformat[i]);
+    if (group && cfg->group_size != 128)
         return fail(QMOE_EUNSUPPORTED, "group_size=%d: only 128 is supported", cfg->group_size);
     if (cfg->n_experts > 1024) return fail(QMOE_EUNSUPPORTED, "n_experts=%d exceeds 1024", cfg->n_experts);
     if (cfg->top_k > 64) return fail(QMOE_EUNSUPPORTED, "top_k=%d exceeds 64", cfg->top_k);
@@ -262,7 +281,7 @@ int rows_per_tile(const qmoe_ctx *c, int T) {
     const long active = std::min<long>(c->E, P);
     const double avg = (double)P / (double)std::max<long>(1, active);
     if (avg <= 16.0) return 16;
-    if (!is_group_wformat(c->cfg.wformat)) return 64;
+    if (c->any_8bit) return 64;   // the per-channel prefill GEMM takes 64-row tiles
     // 96-row tiles convert each packed code for 1.5x more MFMA work, which pays
     // once an expert's rows fill several tiles; below that their ragged tails
     // cost more than the conversions save
@@ -356,6 +375,17 @@ int qmoe_pack_experts(const qmoe_config *cfg, const float *const *w_gate, const 
     c->maxT = cfg->max_tokens;
     c->debug_sync = getenv("QMOE_DEBUG") != nullptr;
 
+    // Per-expert formats: device format groups, one kernel launch per format.
+    c->wfmt.resize(nexp);
+    for (int i = 0; i < nexp; i++) {
+        c->wfmt[i] = cfg->expert_wformat ? cfg->expert_wformat[i] : cfg->wformat;
+        c->fmt_mask |= 1 << fmt_index(dev_format(c->wfmt[i]));
+        c->any_group = c->any_group || is_group_wformat(c->wfmt[i]);
+        c->any_8bit = c->any_8bit || !is_group_wformat(c->wfmt[i]);
+    }
+    c->mixed = (c->fmt_mask & (c->fmt_mask - 1)) != 0;
+    c->df = dev_format(c->wfmt[0]);   // the format of every expert when not mixed
+
     // Quantize and lay out every expert on the host, several experts at a time.
     std::vector<ExpertPack> packs(nexp);
     {
@@ -365,7 +395,7 @@ int qmoe_pack_experts(const qmoe_config *cfg, const float *const *w_gate, const 
             pool.emplace_back([&, tid] {
                 for (int i = tid; i < nexp; i += nthreads) {
                     const int f = i < c->E ? c->F : c->Fs;
-                    pack_one(cfg->wformat, f, c->d, w_gate[i], w_up[i], w_down[i], packs[i]);
+                    pack_one(c->wfmt[i], f, c->d, w_gate[i], w_up[i], w_down[i], packs[i]);
                 }
             });
         for (auto &t : pool) t.join();
@@ -376,10 +406,18 @@ int qmoe_pack_experts(const qmoe_config *cfg, const float *const *w_gate, const 
             return fail(packs[i].rc, "quantization of expert %d failed", i);
         }
 
+    // Arena order: groups of one kind (routed, shared) and one device format,
+    // experts ascending inside a group, so every group is uniformly strided.
+    auto group_of = [&](int i) {
+        return c->mixed ? (i >= c->E ? 4 : 0) + fmt_index(dev_format(c->wfmt[i])) : (i >= c->E ? 1 : 0);
+    };
+    std::vector<int> order(nexp);
+    for (int i = 0; i < nexp; i++) order[i] = i;
+    std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return group_of(x) < group_of(y); });
     size_t cursor = 0;
     c->m13.resize(nexp);
     c->m2.resize(nexp);
-    for (int i = 0; i < nexp; i++) {
+    for (int i : order) {
         const int f = i < c->E ? c->F : c->Fs;
         c->m13[i] = plan_matrix(packs[i].w13, 2 * f, c->d, cursor);
         c->m2[i] = plan_matrix(packs[i].w2, c->d, f, cursor);
@@ -411,15 +449,21 @@ int qmoe_pack_experts(const qmoe_config *cfg, const float *const *w_gate, const 
         w.zc2 = b.zc_off ? (const uint16_t *)(c->arena + b.zc_off) : nullptr;
         w.F = i < c->E ? c->F : c->Fs;
     }
-    // uniform strides of the routed and of the shared experts in the arena
-    for (int grp = 0; grp < 2 && !rc; grp++) {
-        const int first = grp == 0 ? 0 : c->E, count = grp == 0 ? c->E : c->S;
-        if (count == 0) continue;
+    // each group's first expert and uniform stride; the slot table of mixed layers
+    std::vector<int32_t> slot(nexp, 0);
+    for (int grp = 0; grp < kMaxExpertGroups && !rc; grp++) {
+        std::vector<int> mem;
+        for (int i : order)
+            if (group_of(i) == grp) mem.push_back(i);
+        if (mem.empty()) continue;
+        const int first = mem[0], count = (int)mem.size();
         c->ex0[grp] = hexp[first];
-        c->ex_stride[grp] = count > 1 ? (int64_t)(c->m13[first + 1].codes_off - c->m13[first].codes_off) : 0;
-        for (int i = 1; i < count && !rc; i++) {
-            const int64_t off = c->ex_stride[grp] * i;
-            const MatInfo &a0 = c->m13[first], &b0 = c->m2[first], &a = c->m13[first + i], &b = c->m2[first + i];
+        c->gfmt[grp] = dev_format(c->wfmt[first]);
+        c->ex_stride[grp] = count > 1 ? (int64_t)(c->m13[mem[1]].codes_off - c->m13[first].codes_off) : 0;
+        for (int j = 0; j < count; j++) slot[mem[j]] = (grp << 20) | j;
+        for (int j = 1; j < count && !rc; j++) {
+            const int64_t off = c->ex_stride[grp] * j;
+            const MatInfo &a0 = c->m13[first], &b0 = c->m2[first], &a = c->m13[mem[j]], &b = c->m2[mem[j]];
             const size_t z0[10] = {a0.codes_off, a0.gs_off, a0.gz_off, a0.ps_off, a0.zc_off,
                                    b0.codes_off, b0.gs_off, b0.gz_off, b0.ps_off, b0.zc_off};
             const size_t zi[10] = {a.codes_off, a.gs_off, a.gz_off, a.ps_off, a.zc_off,
@@ -428,8 +472,13 @@ int qmoe_pack_experts(const qmoe_config *cfg, const float *const *w_gate, const 
             // for the others offset 0 means "absent"
             for (int f = 0; f < 10; f++)
                 if ((f % 5 && (z0[f] == 0) != (zi[f] == 0)) || ((f % 5 == 0 || z0[f]) && (int64_t)(zi[f] - z0[f]) != off))
-                    rc = fail(QMOE_EHIP, "internal: expert %d is not uniformly strided in the arena", first + i);
+                    rc = fail(QMOE_EHIP, "internal: expert %d is not uniformly strided in the arena", mem[j]);
         }
+    }
+    if (!rc && c->mixed) {
+        rc = dalloc(c, (void **)&c->eslot, sizeof(int32_t) * nexp);
+        if (!rc && hipMemcpy(c->eslot, slot.data(), sizeof(int32_t) * nexp, hipMemcpyHostToDevice) != hipSuccess)
+            rc = fail(QMOE_EHIP, "upload of the expert slot table failed");
     }
 
     // Router weight (as given, or quantized per expert row) and bias.
@@ -488,6 +537,9 @@ int qmoe_pack_experts(const qmoe_config *cfg, const float *const *w_gate, const 
     if (!rc) rc = dalloc(c, (void **)&c->H, rows_total * c->ldh * 2);
     if (!rc) rc = dalloc(c, (void **)&c->O, rows_total * c->d * 4);
     if (!rc) rc = dalloc(c, (void **)&c->xsum, T * (c->d / 128) * 4);
+    // layers mixing INT4_SYM / INT3 (row sums scaled by -136) with INT4_ASYM (-128)
+    if (!rc && ((c->fmt_mask >> fmt_index(DF_I4SYM)) & 1) && ((c->fmt_mask >> fmt_index(DF_I4ASYM)) & 1))
+        rc = dalloc(c, (void **)&c->xsum_asym, T * (c->d / 128) * 4);
     if (!rc) rc = dalloc(c, (void **)&c->hsum, rows_total * (c->ldh / 128) * 4);
     if (rc) {
         free_ctx(c);
@@ -529,8 +581,13 @@ int qmoe_forward(qmoe_ctx *c, const uint16_t *x, int32_t T, uint16_t *y, qmoe_ro
     const int P = T * c->k;
     const int bm = rows_per_tile(c, T);
     const int max_tiles = max_tiles_for(c, T, bm);
-    const bool grouped = is_group_wformat(c->cfg.wformat);
-    const float zc = c->df == DF_I4SYM ? -136.0f : -128.0f;   // row-sum scale of the integer-code GEMM
+    const bool grouped = c->any_group;
+    // row-sum scale of the integer-code GEMM: -136 for INT4_SYM / INT3 (stored
+    // code q + 8), -128 for INT4_ASYM; a layer with both computes the second
+    // set of sums separately
+    const bool sym_present = (c->fmt_mask >> fmt_index(DF_I4SYM)) & 1;
+    const bool asym_present = (c->fmt_mask >> fmt_index(DF_I4ASYM)) & 1;
+    const float zc = sym_present ? -136.0f : -128.0f;
     // Row sums of x: the prefill GEMMs of the group formats read them; the
     // decode kernel (bm == 16) computes its own while staging rows.
     const bool need_sums = grouped && bm > 16;
@@ -553,12 +610,18 @@ int qmoe_forward(qmoe_ctx *c, const uint16_t *x, int32_t T, uint16_t *y, qmoe_ro
         rc = timed(c, K_XSUM, s, [&] { return launch_xsum(x, T, c->d, zc, c->xsum, s); });
         if (rc) return rc;
     }
+    if (need_sums && sym_present && asym_present) {
+        rc = timed(c, K_XSUM, s, [&] { return launch_xsum(x, T, c->d, -128.0f, c->xsum_asym, s); });
+        if (rc) return rc;
+    }
 
     GemmArgs a{};
-    a.ex0[0] = c->ex0[0];
-    a.ex0[1] = c->ex0[1];
-    a.ex_stride[0] = c->ex_stride[0];
-    a.ex_stride[1] = c->ex_stride[1];
+    for (int g = 0; g < kMaxExpertGroups; g++) {
+        a.ex0[g] = c->ex0[g];
+        a.ex_stride[g] = c->ex_stride[g];
+        a.gfmt[g] = c->gfmt[g];
+    }
+    a.eslot = c->eslot;
     a.tiles = c->tiles;
     a.num_tiles = c->num_tiles;
     a.perm = c->perm;
@@ -575,10 +638,21 @@ int qmoe_forward(qmoe_ctx *c, const uint16_t *x, int32_t T, uint16_t *y, qmoe_ro
     a.T = T;
     a.E = c->E;
     const int maxN13 = 2 * std::max(c->F, c->Fs);
-    rc = timed(c, K_GEMM13, s, [&] { return launch_gemm13(c->df, bm, a, max_tiles, maxN13, s); });
-    if (rc) return rc;
-    rc = timed(c, K_GEMM2, s, [&] { return launch_gemm2(c->df, bm, a, max_tiles, s); });
-    if (rc) return rc;
+    // one gate/up launch per device format present, then one down launch per
+    // format (each computes only its own experts' tiles)
+    for (int fi = 0; fi < 4; fi++) {
+        if (!((c->fmt_mask >> fi) & 1)) continue;
+        const int df = fmt_of_index(fi);
+        a.xsum = df == DF_I4ASYM && sym_present ? c->xsum_asym : c->xsum;
+        rc = timed(c, K_GEMM13, s, [&] { return launch_gemm13(df, bm, a, max_tiles, maxN13, s); });
+        if (rc) return rc;
+    }
+    for (int fi = 0; fi < 4; fi++) {
+        if (!((c->fmt_mask >> fi) & 1)) continue;
+        const int df = fmt_of_index(fi);
+        rc = timed(c, K_GEMM2, s, [&] { return launch_gemm2(df, bm, a, max_tiles, s); });
+        if (rc) return rc;
+    }
     rc = timed(c, K_COMBINE, s, [&] { return launch_combine(c->O, c->inv, T, c->d, c->k, P, c->S, y, s); });
     if (rc) return rc;
     if (dbg) {
@@ -614,8 +688,8 @@ int qmoe_export_packed(qmoe_ctx *c, int32_t expert, int32_t matrix, int8_t *code
     CanonMatrix full;
     full.N = m.N;
     full.K = m.K;
-    unlayout_matrix(c->cfg.wformat, p, full);
-    const int G = is_group_wformat(c->cfg.wformat) ? m.K / kBlockK : 1;
+    unlayout_matrix(c->wfmt[expert], p, full);
+    const int G = is_group_wformat(c->wfmt[expert]) ? m.K / kBlockK : 1;
     // W13 rows alternate gate / up in 16-row blocks; select the requested half.
     const int outN = matrix == 2 ? m.N : m.N / 2;
     for (int r = 0; r < outN; r++) {

@@ -149,12 +149,20 @@ hipError_t launch_route_small(const float *logits, int T, int E, int k, int reno
                               int32_t *idx, float *w, int32_t *counts, int32_t *offsets, Tile *tiles,
                               int32_t *num_tiles, int32_t *perm, int32_t *inv, float *wrow, hipStream_t s);
 
+// Experts are laid out in groups of one kind (routed / shared) and one device
+// format, each group uniformly strided in the arena: at most 2 x 4 groups.
+constexpr int kMaxExpertGroups = 8;
+
 struct GemmArgs {
-    // Expert pointers without a table lookup: expert e < E is ex0[0] advanced
-    // by e * ex_stride[0] bytes (routed experts are laid out uniformly in the
-    // arena); shared expert E + i is ex0[1] advanced by i * ex_stride[1].
-    ExpertW ex0[2];
-    int64_t ex_stride[2];
+    // Expert pointers: expert e is group g's first expert advanced by i *
+    // ex_stride[g] bytes. Without a slot table (every expert in one format) g
+    // is 0 for routed and 1 for shared experts and i the index among them, with
+    // no dependent load; with one (per-expert formats), eslot[e] = g << 20 | i.
+    // A launch computes only the experts whose group format gfmt[g] is its own.
+    ExpertW ex0[kMaxExpertGroups];
+    int64_t ex_stride[kMaxExpertGroups];
+    int32_t gfmt[kMaxExpertGroups];
+    const int32_t *eslot;
     const Tile *tiles;
     const int32_t *num_tiles;
     const int32_t *perm;     // task list (pair id per routed row)

@@ -775,11 +775,21 @@ __device__ __forceinline__ bf16x8 codes8_to_bf16<DF_FP8>(uint32_t d0, uint32_t d
 // owns 64 columns = four 16-row packed blocks, so each packed weight is
 // converted by exactly one wave of the workgroup.
 
-// Pointers of expert e from the kernel arguments (no dependent global load).
-__device__ __forceinline__ ExpertW expert_at(const GemmArgs &a, int e) {
-    const int sh = e >= a.E;
-    const ExpertW &b = a.ex0[sh];
-    const int64_t off = a.ex_stride[sh] * (int64_t)(sh ? e - a.E : e);
+// Pointers of expert e from the kernel arguments (a dependent load of its slot
+// only for layers with per-expert formats) and the device format of its group.
+__device__ __forceinline__ ExpertW expert_at(const GemmArgs &a, int e, int &fmt) {
+    int g, i;
+    if (a.eslot) {
+        const int v = a.eslot[e];
+        g = v >> 20;
+        i = v & 0xFFFFF;
+    } else {
+        g = e >= a.E;
+        i = g ? e - a.E : e;
+    }
+    fmt = a.gfmt[g];
+    const ExpertW &b = a.ex0[g];
+    const int64_t off = a.ex_stride[g] * (int64_t)i;
     auto adv = [off](auto *p) { return p ? (decltype(p))((const uint8_t *)p + off) : p; };
     ExpertW w;
     w.c13 = adv(b.c13);
@@ -802,12 +812,14 @@ struct TileCtx {
     int N, K, n0, rows;
 };
 
-template <int MODE>
+template <int DF, int MODE>
 __device__ __forceinline__ bool tile_setup(const GemmArgs &a, TileCtx &c) {
     const int ntiles = *a.num_tiles;   // issued together with the tile load
     c.tl = a.tiles[blockIdx.y];
     if ((int)blockIdx.y >= ntiles) return false;
-    c.ew = expert_at(a, c.tl.e);
+    int fmt;
+    c.ew = expert_at(a, c.tl.e, fmt);
+    if (fmt != DF) return false;   // another launch computes this expert
     c.N = MODE == 0 ? 2 * c.ew.F : a.d;
     c.K = MODE == 0 ? a.d : c.ew.F;
     c.n0 = blockIdx.x * 256;
@@ -866,7 +878,9 @@ __global__ __launch_bounds__(256) void k_gemm_dec(GemmArgs a) {
     const int ntiles = *a.num_tiles;   // issued together with the tile load
     c.tl = a.tiles[blockIdx.y];
     if ((int)blockIdx.y >= ntiles) return;
-    c.ew = expert_at(a, c.tl.e);
+    int fmt;
+    c.ew = expert_at(a, c.tl.e, fmt);
+    if (fmt != DF) return;   // another launch computes this expert
     c.N = MODE == 0 ? 2 * c.ew.F : a.d;
     c.K = MODE == 0 ? a.d : c.ew.F;
     c.n0 = blockIdx.x * WG_COLS;
@@ -1122,7 +1136,9 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm_gpf(GemmArgs a) {
     int tile_id, ntile;
     if (!map_work(blockIdx.x, *a.num_tiles, a.n_tiles, tile_id, ntile)) return;
     const Tile tl = a.tiles[tile_id];
-    const ExpertW ew = expert_at(a, tl.e);
+    int efmt;
+    const ExpertW ew = expert_at(a, tl.e, efmt);
+    if (efmt != DF) return;   // another launch computes this expert
     const int N = MODE == 0 ? 2 * ew.F : a.d;
     const int K = MODE == 0 ? a.d : ew.F;
     const int n0 = ntile * NTILE;
@@ -1426,7 +1442,7 @@ __global__ __launch_bounds__(256) void k_gemm_c(GemmArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t As[BM * PITCH];
 
     TileCtx c;
-    if (!tile_setup<MODE>(a, c)) return;
+    if (!tile_setup<DF, MODE>(a, c)) return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int KB = c.K / 128;
     const int lrow = (lane >> 4) * 4;

@@ -22,7 +22,7 @@ Draw order (fixed, NumPy PCG64 ``default_rng(seed)``):
 from __future__ import annotations
 
 import dataclasses
-from typing import List, Optional
+from typing import List, Optional, Tuple
 
 import numpy as np
 
@@ -43,9 +43,14 @@ class LayerConfig:
     Fs: int = 0       # d_ff of a shared expert
     router_fp32: bool = False
     router_quant: str = "none"   # router weight quantized per expert row: "none", "int8" or "fp8"
+    # per-expert formats (E routed then S shared, each one of WFORMATS); None: all `wformat`
+    expert_formats: Optional[Tuple[str, ...]] = None
     bias: bool = False
     renormalize: bool = True
     group: int = 128
+
+    def expert_format(self, i: int) -> str:
+        return self.wformat if self.expert_formats is None else self.expert_formats[i]
 
     def replace(self, **kw) -> "LayerConfig":
         return dataclasses.replace(self, **kw)

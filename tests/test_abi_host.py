@@ -77,6 +77,17 @@ def test_pack_rejects_bad_configs(qmoe_lib, kw, rc):
     assert Q.qmoe_last_error() != ""
 
 
+@pytest.mark.parametrize("bad", [9, -1])
+def test_pack_rejects_bad_per_expert_format(qmoe_lib, bad):
+    c = base_cfg()
+    fm = np.array([0, 1, 2, 3, 4, 0, 1, 2], np.int32)   # the tiny layer's 8 experts
+    fm[5] = bad
+    c.expert_wformat = fm.ctypes.data
+    got, ctx = _pack(c)
+    assert got == Q.QMOE_EINVAL and not ctx.value
+    assert "expert 5" in Q.qmoe_last_error()
+
+
 def test_pack_rejects_null_weights(qmoe_lib):
     got, ctx = _pack(base_cfg(), weights=False)
     assert got == Q.QMOE_EINVAL and not ctx.value

@@ -32,14 +32,37 @@ def dense_bruteforce(O, layer, inp):
             mask[t, sel] = (p / p.sum())[sel]
     y = np.zeros((T, cfg.d))
     for e in range(cfg.E + cfg.S):
-        Wg = O.dequantize(cfg.wformat, *layer.codes(e, 0), group=cfg.group)
-        Wu = O.dequantize(cfg.wformat, *layer.codes(e, 1), group=cfg.group)
-        Wd = O.dequantize(cfg.wformat, *layer.codes(e, 2), group=cfg.group)
+        fe = cfg.expert_format(e)
+        Wg = O.dequantize(fe, *layer.codes(e, 0), group=cfg.group)
+        Wu = O.dequantize(fe, *layer.codes(e, 1), group=cfg.group)
+        Wd = O.dequantize(fe, *layer.codes(e, 2), group=cfg.group)
         G = X @ Wg.T
         H = G / (1.0 + np.exp(-G)) * (X @ Wu.T)
         out = H @ Wd.T
         y += (mask[:, e:e + 1] if e < cfg.E else 1.0) * out
     return y, L
+
+
+@pytest.mark.parametrize("shared", [0, 2])
+def test_mixed_formats_equal_dense_bruteforce(oracle_mod, shared):
+    """Every expert in its own format (all five among routed and shared
+    experts): the sparse oracle equals the dense brute force, and each
+    expert's codes are the ones its own format's quantizer gives."""
+    O = oracle_mod
+    fm = ("int8_sym_ch", "int4_asym_g128", "int4_sym_g128", "int3_sym_g128", "fp8e4m3_ch", "int4_sym_g128")
+    sh = ("fp8e4m3_ch", "int4_asym_g128")[:shared]
+    cfg = small_cfg("int4_sym_g128", S=shared, Fs=256 if shared else 0, bias=True, expert_formats=fm + sh)
+    inp = make_inputs(cfg, seed=12)
+    layer = O.OracleLayer(inp)
+    for e in range(cfg.E + cfg.S):
+        for m, w in enumerate((inp.w_gate[e], inp.w_up[e], inp.w_down[e])):
+            q, s, z = O.quantize(cfg.expert_format(e), w)
+            q2, s2, z2 = layer.codes(e, m)
+            assert np.array_equal(q, q2) and np.array_equal(s, s2) and np.array_equal(z, z2)
+    out = layer.forward(inp.x)
+    y_ref, L = dense_bruteforce(O, layer, inp)
+    assert np.allclose(out["logits"], L, rtol=1e-13, atol=1e-13)
+    assert np.linalg.norm(out["y"] - y_ref) / np.linalg.norm(y_ref) <= 1e-12
 
 
 @pytest.mark.parametrize("fmt", WFORMATS)
