@@ -46,11 +46,12 @@ def algorithmic_work(cfg):
     return dict(layer=cfg.expert_flops(), gemm_gate_up=fl13, gemm_down=fl2)
 
 
-def packed_bytes_per_expert(cfg, f):
+def packed_bytes_per_expert(cfg, f, fmt=None):
+    fmt = cfg.wformat if fmt is None else fmt
     n = 3 * cfg.d * f
-    if cfg.wformat in ("int4_asym_g128", "int4_sym_g128", "int3_sym_g128"):
+    if fmt in ("int4_asym_g128", "int4_sym_g128", "int3_sym_g128"):
         groups = n // 128
-        return n // 2 + groups * 2 * (2 if cfg.wformat == "int4_asym_g128" else 1)
+        return n // 2 + groups * 2 * (2 if fmt == "int4_asym_g128" else 1)
     return n + 4 * (2 * f + cfg.d)
 
 
@@ -212,10 +213,13 @@ def main() -> int:
     work = algorithmic_work(cfg)
     kernels = {k: {"avg_us": 1e3 * v[0] / max(v[1], 1), "launches": v[1]} for k, v in prof.items() if v[1]}
     ms13, n13 = prof_timed["gemm_gate_up"]
-    k13 = 1e3 * ms13 / n13   # average launch duration (us) over the timed region
+    # per step: a layer with per-expert formats launches each GEMM once per format
+    per_step = max(1, round(n13 / args.steps))
+    k13 = 1e3 * ms13 / args.steps   # the gate/up GEMM's time per step (us) over the timed region
+    kname = "gemm_gate_up" if per_step == 1 else f"gemm_gate_up ({per_step} launches per step, one per format)"
     if not decode:
         achieved = work["gemm_gate_up"] / (k13 * 1e-6) / 1e12
-        roof = {"bound": "mfma", "kernel": "gemm_gate_up", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+        roof = {"bound": "mfma", "kernel": kname, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                 "traffic": measured_traffic("gemm_gate_up", cfg.name), "traffic_unit": "bytes/launch",
                 "per_launch": f"{work['gemm_gate_up']:.4e} FLOP"}
@@ -225,10 +229,10 @@ def main() -> int:
         layer.forward(x, y=y, route=route)
         torch.cuda.synchronize()
         used = np.unique(route["topk_idx"].cpu().numpy())
-        per_exp13 = packed_bytes_per_expert(cfg, cfg.F) * 2 // 3
-        b13 = len(used) * per_exp13 + cfg.T * cfg.d * 2
+        b13 = sum(packed_bytes_per_expert(cfg, cfg.F, cfg.expert_format(int(e))) * 2 // 3 for e in used)
+        b13 += cfg.T * cfg.d * 2
         achieved = b13 / (k13 * 1e-6) / 1e9
-        roof = {"bound": "hbm", "kernel": "gemm_gate_up", "achieved": achieved, "peak": PEAK_HBM_GBS,
+        roof = {"bound": "hbm", "kernel": kname, "achieved": achieved, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
                 "traffic": measured_traffic("gemm_gate_up", cfg.name), "traffic_unit": "bytes/launch",
                 "per_launch": f"{b13} B ({len(used)} distinct experts)"}

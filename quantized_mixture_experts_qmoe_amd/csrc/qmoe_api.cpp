@@ -640,18 +640,22 @@ int qmoe_forward(qmoe_ctx *c, const uint16_t *x, int32_t T, uint16_t *y, qmoe_ro
     const int maxN13 = 2 * std::max(c->F, c->Fs);
     // one gate/up launch per device format present, then one down launch per
     // format (each computes only its own experts' tiles)
+    // (decode tiles of a mixed layer: one launch, each workgroup in its expert's format)
+    const bool one_launch = !c->mixed || bm == 16;
     for (int fi = 0; fi < 4; fi++) {
         if (!((c->fmt_mask >> fi) & 1)) continue;
-        const int df = fmt_of_index(fi);
+        const int df = c->mixed && bm == 16 ? kDfAllFormats : fmt_of_index(fi);
         a.xsum = df == DF_I4ASYM && sym_present ? c->xsum_asym : c->xsum;
         rc = timed(c, K_GEMM13, s, [&] { return launch_gemm13(df, bm, a, max_tiles, maxN13, s); });
         if (rc) return rc;
+        if (one_launch) break;
     }
     for (int fi = 0; fi < 4; fi++) {
         if (!((c->fmt_mask >> fi) & 1)) continue;
-        const int df = fmt_of_index(fi);
+        const int df = c->mixed && bm == 16 ? kDfAllFormats : fmt_of_index(fi);
         rc = timed(c, K_GEMM2, s, [&] { return launch_gemm2(df, bm, a, max_tiles, s); });
         if (rc) return rc;
+        if (one_launch) break;
     }
     rc = timed(c, K_COMBINE, s, [&] { return launch_combine(c->O, c->inv, T, c->d, c->k, P, c->S, y, s); });
     if (rc) return rc;

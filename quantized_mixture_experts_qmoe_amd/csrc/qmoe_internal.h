@@ -181,7 +181,9 @@ struct GemmArgs {
     int32_t n_tiles;         // 256-column N-tiles of the widest expert (set by the launcher)
 };
 // bm: rows per M-tile (16: weight-streaming decode kernel; 64: prefill
-// kernels); max_tiles: grid bound; maxN13: max 2F.
+// kernels); max_tiles: grid bound; maxN13: max 2F. df = kDfAllFormats (decode
+// tiles only): one launch for every expert of a layer with per-expert formats.
+constexpr int kDfAllFormats = -1;
 hipError_t launch_gemm13(int df, int bm, const GemmArgs &a, int max_tiles, int maxN13, hipStream_t s);
 hipError_t launch_gemm2(int df, int bm, const GemmArgs &a, int max_tiles, hipStream_t s);
 hipError_t launch_combine(const float *O, const int32_t *inv, int T, int d, int k, int P, int n_shared,

@@ -842,6 +842,8 @@ struct GroupConst {
 
 // ---- decode-shaped batches: tiles of at most 16 rows ----------------------
 constexpr int kDecodeBlocksPerWave = 4;
+constexpr int kDecKC = 2;                     // K blocks per staged chunk
+constexpr int kDecPitch = kDecKC * 128 + 8;   // bf16 per LDS row: rows 16 bytes apart in the bank space
 //
 // Here the packed weights are the whole cost, so the kernel is built to keep
 // HBM busy. Workgroup = 4 waves over one tile and 256 columns of B's N
@@ -858,34 +860,20 @@ struct DecodeCfg {
     static constexpr int kWords = kGroup ? 1 : 2;   // 16-byte words per lane per block and K block
     static constexpr int kDepth = 1;                // K blocks in flight per wave, beyond the one computed
     static constexpr int kNB = kDecodeBlocksPerWave;
-    static constexpr int kKC = 2;                   // K blocks per staged chunk
+    static constexpr int kKC = kDecKC;
 };
 
+// One decode tile: B columns [c.n0, c.n0 + 256) of the tile's expert against
+// its (at most 16) rows, staged through the calling kernel's LDS.
 template <int DF, int MODE>
-__global__ __launch_bounds__(256) void k_gemm_dec(GemmArgs a) {
+__device__ __forceinline__ void dec_tile(const GemmArgs &a, const TileCtx &c, uint16_t (*As)[16 * kDecPitch],
+                                         float (*Rs)[kDecKC][16]) {
     using CF = DecodeCfg<DF>;
     constexpr int NB = CF::kNB;            // 16-row blocks per wave
     constexpr int KC = CF::kKC;            // K blocks per staged chunk
-    constexpr int WG_COLS = 4 * NB * 16;   // columns of B's N dimension per workgroup
-    static_assert(NB % 2 == 0 && 256 % WG_COLS == 0, "a wave owns whole gate/up pairs; N % 256 == 0 covers the grid");
-    constexpr int PITCH = KC * 128 + 8;    // bf16 per LDS row: rows 16 bytes apart in the bank space
+    constexpr int PITCH = kDecPitch;
     constexpr float ZC = GroupConst<DF>::ZC;
     static_assert(KC % CF::kDepth == 0, "the ring slot must be static inside a chunk");
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][16 * PITCH];
-    __shared__ __attribute__((aligned(16))) float Rs[2][KC][16];
-
-    TileCtx c;
-    const int ntiles = *a.num_tiles;   // issued together with the tile load
-    c.tl = a.tiles[blockIdx.y];
-    if ((int)blockIdx.y >= ntiles) return;
-    int fmt;
-    c.ew = expert_at(a, c.tl.e, fmt);
-    if (fmt != DF) return;   // another launch computes this expert
-    c.N = MODE == 0 ? 2 * c.ew.F : a.d;
-    c.K = MODE == 0 ? a.d : c.ew.F;
-    c.n0 = blockIdx.x * WG_COLS;
-    c.rows = c.tl.row_end - c.tl.row0;
-    if (c.n0 >= c.N) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int KB = c.K / 128;
     const int NC = (KB + KC - 1) / KC;
@@ -1077,6 +1065,56 @@ __global__ __launch_bounds__(256) void k_gemm_dec(GemmArgs a) {
                 a.O[(size_t)gr * a.d + n] = acc[nb][r] * sn[nb] * wt;
             }
         }
+    }
+}
+
+// Sets up a decode tile (row range, expert, B column range); false: nothing to do.
+__device__ __forceinline__ bool dec_setup(const GemmArgs &a, TileCtx &c, int &fmt) {
+    constexpr int WG_COLS = 4 * kDecodeBlocksPerWave * 16;   // columns of B's N dimension per workgroup
+    static_assert(kDecodeBlocksPerWave % 2 == 0 && 256 % WG_COLS == 0,
+                  "a wave owns whole gate/up pairs; N % 256 == 0 covers the grid");
+    const int ntiles = *a.num_tiles;   // issued together with the tile load
+    c.tl = a.tiles[blockIdx.y];
+    if ((int)blockIdx.y >= ntiles) return false;
+    c.ew = expert_at(a, c.tl.e, fmt);
+    return true;
+}
+template <int MODE>
+__device__ __forceinline__ bool dec_cols(const GemmArgs &a, TileCtx &c) {
+    c.N = MODE == 0 ? 2 * c.ew.F : a.d;
+    c.K = MODE == 0 ? a.d : c.ew.F;
+    c.n0 = blockIdx.x * (4 * kDecodeBlocksPerWave * 16);
+    c.rows = c.tl.row_end - c.tl.row0;
+    return c.n0 < c.N;
+}
+
+template <int DF, int MODE>
+__global__ __launch_bounds__(256) void k_gemm_dec(GemmArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][16 * kDecPitch];
+    __shared__ __attribute__((aligned(16))) float Rs[2][kDecKC][16];
+    TileCtx c;
+    int fmt;
+    if (!dec_setup(a, c, fmt) || fmt != DF) return;   // another launch computes another format
+    if (!dec_cols<MODE>(a, c)) return;
+    dec_tile<DF, MODE>(a, c, As, Rs);
+}
+
+// Decode tiles of a layer with per-expert formats: one launch for all of them
+// (one HBM stream instead of one per format), each workgroup running its
+// expert's format.
+template <int MODE>
+__global__ __launch_bounds__(256) void k_gemm_dec_mixed(GemmArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][16 * kDecPitch];
+    __shared__ __attribute__((aligned(16))) float Rs[2][kDecKC][16];
+    TileCtx c;
+    int fmt;
+    if (!dec_setup(a, c, fmt) || !dec_cols<MODE>(a, c)) return;
+    switch (fmt) {
+    case DF_INT8: dec_tile<DF_INT8, MODE>(a, c, As, Rs); break;
+    case DF_I4ASYM: dec_tile<DF_I4ASYM, MODE>(a, c, As, Rs); break;
+    case DF_I4SYM: dec_tile<DF_I4SYM, MODE>(a, c, As, Rs); break;
+    case DF_FP8: dec_tile<DF_FP8, MODE>(a, c, As, Rs); break;
+    default: break;
     }
 }
 
@@ -1695,6 +1733,7 @@ hipError_t launch_dispatch_scatter(const int32_t *idx, const float *w, int P, in
 template <int MODE>
 static hipError_t launch_gemm_dec(int df, dim3 grid, const GemmArgs &a, hipStream_t s) {
     switch (df) {
+    case kDfAllFormats: hipLaunchKernelGGL(k_gemm_dec_mixed<MODE>, grid, dim3(256), 0, s, a); break;
     case DF_INT8: hipLaunchKernelGGL((k_gemm_dec<DF_INT8, MODE>), grid, dim3(256), 0, s, a); break;
     case DF_I4ASYM: hipLaunchKernelGGL((k_gemm_dec<DF_I4ASYM, MODE>), grid, dim3(256), 0, s, a); break;
     case DF_I4SYM: hipLaunchKernelGGL((k_gemm_dec<DF_I4SYM, MODE>), grid, dim3(256), 0, s, a); break;

@@ -80,6 +80,15 @@ CONFIGS = {
                                 wformat="int4_sym_g128"),
     "qwen3_decode_fp8": LayerConfig("qwen3_decode_fp8", T=16, d=2048, E=128, k=8, F=768,
                                     wformat="fp8e4m3_ch"),
+    # per-expert precision: one expert in eight (16 of 128) in INT8, the rest INT4
+    "qwen3_prefill_mixed": LayerConfig("qwen3_prefill_mixed", T=8192, d=2048, E=128, k=8, F=768,
+                                       wformat="int4_sym_g128", bias=True,
+                                       expert_formats=tuple("int8_sym_ch" if e % 8 == 0 else "int4_sym_g128"
+                                                            for e in range(128))),
+    "qwen3_decode_mixed": LayerConfig("qwen3_decode_mixed", T=16, d=2048, E=128, k=8, F=768,
+                                      wformat="int4_sym_g128",
+                                      expert_formats=tuple("int8_sym_ch" if e % 8 == 0 else "int4_sym_g128"
+                                                           for e in range(128))),
 }
 
 

@@ -23,7 +23,7 @@ def sample_tokens(T, n, seed=0):
 
 
 @pytest.mark.parametrize("name", ["tiny", "mixtral_prefill", "qwen3_prefill", "dsv2lite_prefill", "qwen3_decode",
-                                  "qwen3_decode_fp8"])
+                                  "qwen3_decode_fp8", "qwen3_prefill_mixed", "qwen3_decode_mixed"])
 def test_full_size_layer(oracle_mod, name):
     O = oracle_mod
     cfg = CONFIGS[name]
