@@ -156,6 +156,23 @@ typedef struct {
 int qmoe_pack_experts(const qmoe_config *cfg, const float *const *w_gate, const float *const *w_up,
                       const float *const *w_down, const void *w_router, const float *router_bias, qmoe_ctx **out);
 
+/* The expert quantizer on the device: the same layer as qmoe_pack_experts, from
+ * bf16 expert weights that are already in device memory (Q-MoE page, section
+ * 3: the expert quantizer; quantization at load time without a host round
+ * trip). Each expert matrix is quantized by HIP kernels with the rules above
+ * (the bf16 values widen exactly to the fp32 the host quantizer would read), so
+ * the packed arena is byte for byte the one qmoe_pack_experts builds from the
+ * same values. Synchronous: the kernels run on `stream` (a hipStream_t, NULL
+ * for the default stream) and are complete on return.
+ *   w_gate, w_up, w_down  host arrays of E+S DEVICE pointers, each bf16 bit
+ *              patterns row-major [F][d] / [F][d] / [d][F] on cfg->device,
+ *              only read during the call
+ *   w_router, router_bias, out  as for qmoe_pack_experts (host memory)
+ * Errors as for qmoe_pack_experts; QMOE_EHIP if a kernel fails. */
+int qmoe_pack_experts_device(const qmoe_config *cfg, const uint16_t *const *w_gate, const uint16_t *const *w_up,
+                             const uint16_t *const *w_down, const void *w_router, const float *router_bias,
+                             void *stream, qmoe_ctx **out);
+
 /* The gating network's selection and the expert-centric task list, from given
  * logits (Q-MoE page, section 3 "Gating Network"; OmniMoE technical summary
  * 2.2, task collection and grouping). Asynchronous on `stream`.

@@ -30,8 +30,9 @@ WFORMAT_CODES = {"int8_sym_ch": 0, "int4_asym_g128": 1, "int4_sym_g128": 2, "int
                  "fp8e4m3_ch": 4}
 ROUTER_QUANT_CODES = {"none": 0, "int8": 1, "fp8": 2}
 
-ABI_SYMBOLS = ("qmoe_pack_experts", "qmoe_route_topk", "qmoe_forward", "qmoe_destroy", "qmoe_last_error",
-               "qmoe_export_packed", "qmoe_profile_enable", "qmoe_profile_read", "qmoe_kernel_name")
+ABI_SYMBOLS = ("qmoe_pack_experts", "qmoe_pack_experts_device", "qmoe_route_topk", "qmoe_forward", "qmoe_destroy",
+               "qmoe_last_error", "qmoe_export_packed", "qmoe_profile_enable", "qmoe_profile_read",
+               "qmoe_kernel_name")
 
 
 class QmoeConfig(C.Structure):
@@ -64,6 +65,8 @@ def load() -> C.CDLL:
     P = C.c_void_p
     L.qmoe_pack_experts.restype = C.c_int
     L.qmoe_pack_experts.argtypes = [C.POINTER(QmoeConfig), P, P, P, P, P, C.POINTER(P)]
+    L.qmoe_pack_experts_device.restype = C.c_int
+    L.qmoe_pack_experts_device.argtypes = [C.POINTER(QmoeConfig), P, P, P, P, P, P, C.POINTER(P)]
     L.qmoe_route_topk.restype = C.c_int
     L.qmoe_route_topk.argtypes = [P, P, C.c_int32, C.POINTER(QmoeRouteOut), P]
     L.qmoe_forward.restype = C.c_int
@@ -88,6 +91,10 @@ def load() -> C.CDLL:
 
 def qmoe_pack_experts(cfg: QmoeConfig, w_gate, w_up, w_down, w_router, router_bias, out) -> int:
     return load().qmoe_pack_experts(C.byref(cfg), w_gate, w_up, w_down, w_router, router_bias, out)
+
+
+def qmoe_pack_experts_device(cfg: QmoeConfig, w_gate, w_up, w_down, w_router, router_bias, stream, out) -> int:
+    return load().qmoe_pack_experts_device(C.byref(cfg), w_gate, w_up, w_down, w_router, router_bias, stream, out)
 
 
 def qmoe_route_topk(ctx, logits, T: int, out: Optional[QmoeRouteOut], stream) -> int:
@@ -158,12 +165,31 @@ def _dptr(t) -> Optional[int]:
 class QMoE:
     """One packed quantized MoE layer on a GPU (owns a qmoe_ctx)."""
 
-    def __init__(self, inputs, max_tokens: Optional[int] = None, device: int = 0):
+    def __init__(self, inputs, max_tokens: Optional[int] = None, device: int = 0, device_weights=None):
+        """device_weights: None packs the fp32 host weights of `inputs` on the
+        host; (gate, up, down) lists of bf16 CUDA tensors quantizes those on
+        the device instead (qmoe_pack_experts_device)."""
         cfg = inputs.cfg
         self.cfg = cfg
         self.max_tokens = max_tokens if max_tokens is not None else cfg.T
         self.device = device
         c = make_config(cfg, self.max_tokens, device)
+        if device_weights is not None:
+            import torch
+            dg, du, dd = device_weights
+            for t in list(dg) + list(du) + list(dd):
+                assert t.dtype == torch.bfloat16 and t.is_cuda and t.is_contiguous()
+            arr = C.c_void_p * (cfg.E + cfg.S)
+            pg, pu, pd = (arr(*[t.data_ptr() for t in ts]) for ts in (dg, du, dd))
+            wr = np.ascontiguousarray(inputs.w_router)
+            bias = None if inputs.bias is None else np.ascontiguousarray(inputs.bias, np.float32)
+            ctx = C.c_void_p()
+            rc = qmoe_pack_experts_device(c, C.cast(pg, C.c_void_p), C.cast(pu, C.c_void_p), C.cast(pd, C.c_void_p),
+                                          wr.ctypes.data, None if bias is None else bias.ctypes.data,
+                                          _stream_handle(None), C.byref(ctx))
+            _check(rc, "qmoe_pack_experts_device")
+            self.ctx = ctx
+            return
         wg = [np.ascontiguousarray(a, np.float32) for a in inputs.w_gate]
         wu = [np.ascontiguousarray(a, np.float32) for a in inputs.w_up]
         wd = [np.ascontiguousarray(a, np.float32) for a in inputs.w_down]

@@ -37,6 +37,8 @@ def build(verbose: bool = False) -> str:
     objs = []
     steps = [
         ("qmoe_kernels.hip", ["-x", "hip"] + HIP_FLAGS),
+        # the device quantizer: the host quantizer's arithmetic, no contraction
+        ("qmoe_quant.hip", ["-x", "hip"] + HIP_FLAGS + ["-ffp-contract=off"]),
         ("qmoe_api.cpp", HOST_FLAGS),
         # the host quantizer: plain IEEE fp32, no contraction, no fast-math
         ("qmoe_pack.cpp", HOST_FLAGS + ["-ffp-contract=off", "-fno-fast-math"]),

@@ -176,30 +176,40 @@ void pack_one(int wformat, int F, int d, const float *wg, const float *wu, const
     layout_matrix(wformat, dn, out.w2);
 }
 
-MatInfo plan_matrix(const PackedMatrix &p, int N, int K, size_t &cursor) {
+PackSizes sizes_of(const PackedMatrix &p) {
+    PackSizes z;
+    z.codes = p.codes.size();
+    z.gscale = p.gscale.size();
+    z.gzero = p.gzero.size();
+    z.pscale = p.pscale.size();
+    z.zc = p.zc.size();
+    return z;
+}
+
+MatInfo plan_matrix(const PackSizes &p, int N, int K, size_t &cursor) {
     MatInfo m;
     m.N = N;
     m.K = K;
     m.codes_off = cursor;
-    m.codes_bytes = p.codes.size();
+    m.codes_bytes = p.codes;
     cursor = align256(cursor + m.codes_bytes);
-    if (!p.gscale.empty()) {
+    if (p.gscale) {
         m.gs_off = cursor;
-        m.gs_count = p.gscale.size();
-        cursor = align256(cursor + p.gscale.size() * 2);
+        m.gs_count = p.gscale;
+        cursor = align256(cursor + p.gscale * 2);
     }
-    if (!p.gzero.empty()) {
+    if (p.gzero) {
         m.gz_off = cursor;
-        cursor = align256(cursor + p.gzero.size() * 2);
+        cursor = align256(cursor + p.gzero * 2);
     }
-    if (!p.pscale.empty()) {
+    if (p.pscale) {
         m.ps_off = cursor;
-        m.ps_count = p.pscale.size();
-        cursor = align256(cursor + p.pscale.size() * 4);
+        m.ps_count = p.pscale;
+        cursor = align256(cursor + p.pscale * 4);
     }
-    if (!p.zc.empty()) {
+    if (p.zc) {
         m.zc_off = cursor;
-        cursor = align256(cursor + p.zc.size() * 2);
+        cursor = align256(cursor + p.zc * 2);
     }
     return m;
 }
@@ -336,25 +346,36 @@ int copy_route(qmoe_ctx *c, const qmoe_route_out *o, int T, hipStream_t s) {
 
 }  // namespace
 
-extern "C" {
+namespace {
 
-const char *qmoe_last_error(void) { return g_last_error.c_str(); }
+// Where the expert weights come from: host fp32 arrays (host quantizer) or
+// device bf16 arrays (device quantizer).
+struct WeightSource {
+    const float *const *hg = nullptr, *const *hu = nullptr, *const *hd = nullptr;
+    const uint16_t *const *dg = nullptr, *const *du = nullptr, *const *dd = nullptr;
+    hipStream_t stream = nullptr;
+    bool device() const { return dg != nullptr; }
+};
 
-const char *qmoe_kernel_name(int32_t slot) {
-    return (slot >= 0 && slot < QMOE_NUM_KERNELS) ? kKernelNames[slot] : "";
-}
-
-int qmoe_pack_experts(const qmoe_config *cfg, const float *const *w_gate, const float *const *w_up,
-                      const float *const *w_down, const void *w_router, const float *router_bias, qmoe_ctx **out) {
+int pack_layer(const qmoe_config *cfg, const WeightSource &src, const void *w_router, const float *router_bias,
+               qmoe_ctx **out) {
     g_last_error.clear();
     if (!out) return fail(QMOE_EINVAL, "out is NULL");
     *out = nullptr;
     int rc = validate(cfg);
     if (rc) return rc;
-    if (!w_gate || !w_up || !w_down || !w_router) return fail(QMOE_EINVAL, "weight array pointer is NULL");
+    const bool dev = src.device();
+    if ((dev ? (!src.dg || !src.du || !src.dd) : (!src.hg || !src.hu || !src.hd)) || !w_router)
+        return fail(QMOE_EINVAL, "weight array pointer is NULL");
     const int nexp = cfg->n_experts + cfg->n_shared;
-    for (int i = 0; i < nexp; i++)
-        if (!w_gate[i] || !w_up[i] || !w_down[i]) return fail(QMOE_EINVAL, "weights of expert %d are NULL", i);
+    for (int i = 0; i < nexp; i++) {
+        const void *g = dev ? (const void *)src.dg[i] : (const void *)src.hg[i];
+        const void *u = dev ? (const void *)src.du[i] : (const void *)src.hu[i];
+        const void *d = dev ? (const void *)src.dd[i] : (const void *)src.hd[i];
+        if (!g || !u || !d) return fail(QMOE_EINVAL, "weights of expert %d are NULL", i);
+        if (dev && (((uintptr_t)g | (uintptr_t)u | (uintptr_t)d) & 15))
+            return fail(QMOE_EINVAL, "device weights of expert %d are not 16-byte aligned", i);
+    }
 
     int ndev = 0;
     hipError_t he = hipGetDeviceCount(&ndev);
@@ -386,26 +407,6 @@ int qmoe_pack_experts(const qmoe_config *cfg, const float *const *w_gate, const 
     c->mixed = (c->fmt_mask & (c->fmt_mask - 1)) != 0;
     c->df = dev_format(c->wfmt[0]);   // the format of every expert when not mixed
 
-    // Quantize and lay out every expert on the host, several experts at a time.
-    std::vector<ExpertPack> packs(nexp);
-    {
-        const int nthreads = std::max(1, std::min<int>(nexp, (int)std::thread::hardware_concurrency()));
-        std::vector<std::thread> pool;
-        for (int tid = 0; tid < nthreads; tid++)
-            pool.emplace_back([&, tid] {
-                for (int i = tid; i < nexp; i += nthreads) {
-                    const int f = i < c->E ? c->F : c->Fs;
-                    pack_one(c->wfmt[i], f, c->d, w_gate[i], w_up[i], w_down[i], packs[i]);
-                }
-            });
-        for (auto &t : pool) t.join();
-    }
-    for (int i = 0; i < nexp; i++)
-        if (packs[i].rc) {
-            free_ctx(c);
-            return fail(packs[i].rc, "quantization of expert %d failed", i);
-        }
-
     // Arena order: groups of one kind (routed, shared) and one device format,
     // experts ascending inside a group, so every group is uniformly strided.
     auto group_of = [&](int i) {
@@ -414,20 +415,73 @@ int qmoe_pack_experts(const qmoe_config *cfg, const float *const *w_gate, const 
     std::vector<int> order(nexp);
     for (int i = 0; i < nexp; i++) order[i] = i;
     std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return group_of(x) < group_of(y); });
-    size_t cursor = 0;
     c->m13.resize(nexp);
     c->m2.resize(nexp);
-    for (int i : order) {
-        const int f = i < c->E ? c->F : c->Fs;
-        c->m13[i] = plan_matrix(packs[i].w13, 2 * f, c->d, cursor);
-        c->m2[i] = plan_matrix(packs[i].w2, c->d, f, cursor);
-    }
-    c->arena_bytes = cursor;
-    rc = dalloc(c, (void **)&c->arena, c->arena_bytes);
-    for (int i = 0; !rc && i < nexp; i++) {
-        rc = upload_matrix(c, c->m13[i], packs[i].w13);
-        if (!rc) rc = upload_matrix(c, c->m2[i], packs[i].w2);
-        packs[i] = ExpertPack();   // release host copies as we go
+    size_t cursor = 0;
+    if (!dev) {
+        // Quantize and lay out every expert on the host, several experts at a time.
+        std::vector<ExpertPack> packs(nexp);
+        {
+            const int nthreads = std::max(1, std::min<int>(nexp, (int)std::thread::hardware_concurrency()));
+            std::vector<std::thread> pool;
+            for (int tid = 0; tid < nthreads; tid++)
+                pool.emplace_back([&, tid] {
+                    for (int i = tid; i < nexp; i += nthreads) {
+                        const int f = i < c->E ? c->F : c->Fs;
+                        pack_one(c->wfmt[i], f, c->d, src.hg[i], src.hu[i], src.hd[i], packs[i]);
+                    }
+                });
+            for (auto &t : pool) t.join();
+        }
+        for (int i = 0; i < nexp; i++)
+            if (packs[i].rc) {
+                free_ctx(c);
+                return fail(packs[i].rc, "quantization of expert %d failed", i);
+            }
+        for (int i : order) {
+            const int f = i < c->E ? c->F : c->Fs;
+            c->m13[i] = plan_matrix(sizes_of(packs[i].w13), 2 * f, c->d, cursor);
+            c->m2[i] = plan_matrix(sizes_of(packs[i].w2), c->d, f, cursor);
+        }
+        c->arena_bytes = cursor;
+        rc = dalloc(c, (void **)&c->arena, c->arena_bytes);
+        for (int i = 0; !rc && i < nexp; i++) {
+            rc = upload_matrix(c, c->m13[i], packs[i].w13);
+            if (!rc) rc = upload_matrix(c, c->m2[i], packs[i].w2);
+            packs[i] = ExpertPack();   // release host copies as we go
+        }
+    } else {
+        // Quantize and lay out every expert on the device, straight into the
+        // arena (zeroed first: the zero-point operand has padding entries).
+        for (int i : order) {
+            const int f = i < c->E ? c->F : c->Fs;
+            c->m13[i] = plan_matrix(pack_sizes(c->wfmt[i], 2 * f, c->d), 2 * f, c->d, cursor);
+            c->m2[i] = plan_matrix(pack_sizes(c->wfmt[i], c->d, f), c->d, f, cursor);
+        }
+        c->arena_bytes = cursor;
+        rc = dalloc(c, (void **)&c->arena, c->arena_bytes);
+        uint8_t *zero_row = nullptr;
+        const size_t zr_bytes = (size_t)std::max(2 * std::max(c->F, c->Fs), c->d);
+        if (!rc) rc = dalloc(c, (void **)&zero_row, zr_bytes);
+        if (!rc && hipMemsetAsync(c->arena, 0, c->arena_bytes, src.stream) != hipSuccess)
+            rc = fail(QMOE_EHIP, "clearing the weight arena failed");
+        auto quant = [&](int wf, const MatInfo &m, const uint16_t *a, const uint16_t *b) {
+            hipError_t e = launch_quant_matrix(
+                wf, a, b, m.N, m.K, c->arena + m.codes_off, m.gs_off ? (uint16_t *)(c->arena + m.gs_off) : nullptr,
+                m.gz_off ? (uint16_t *)(c->arena + m.gz_off) : nullptr,
+                m.ps_off ? (float *)(c->arena + m.ps_off) : nullptr,
+                m.zc_off ? (uint16_t *)(c->arena + m.zc_off) : nullptr, zero_row, src.stream);
+            return e == hipSuccess ? QMOE_OK : fail(QMOE_EHIP, "quantization kernel launch failed: %s", hipGetErrorString(e));
+        };
+        for (int i = 0; !rc && i < nexp; i++) {
+            rc = quant(c->wfmt[i], c->m13[i], src.dg[i], src.du[i]);
+            if (!rc) rc = quant(c->wfmt[i], c->m2[i], src.dd[i], nullptr);
+            // the row-flag scratch is reused by the next matrix: keep the stream ordered
+        }
+        if (!rc) {
+            const hipError_t e = hipStreamSynchronize(src.stream);
+            if (e != hipSuccess) rc = fail(QMOE_EHIP, "device quantization failed: %s", hipGetErrorString(e));
+        }
     }
     if (rc) {
         free_ctx(c);
@@ -547,6 +601,38 @@ int qmoe_pack_experts(const qmoe_config *cfg, const float *const *w_gate, const 
     }
     *out = c;
     return QMOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *qmoe_last_error(void) { return g_last_error.c_str(); }
+
+const char *qmoe_kernel_name(int32_t slot) {
+    return (slot >= 0 && slot < QMOE_NUM_KERNELS) ? kKernelNames[slot] : "";
+}
+
+int qmoe_pack_experts(const qmoe_config *cfg, const float *const *w_gate, const float *const *w_up,
+                      const float *const *w_down, const void *w_router, const float *router_bias, qmoe_ctx **out) {
+    WeightSource src;
+    src.hg = w_gate;
+    src.hu = w_up;
+    src.hd = w_down;
+    if (!w_gate || !w_up || !w_down) return fail(QMOE_EINVAL, "weight array pointer is NULL");
+    return pack_layer(cfg, src, w_router, router_bias, out);
+}
+
+int qmoe_pack_experts_device(const qmoe_config *cfg, const uint16_t *const *w_gate, const uint16_t *const *w_up,
+                             const uint16_t *const *w_down, const void *w_router, const float *router_bias,
+                             void *stream, qmoe_ctx **out) {
+    if (!w_gate || !w_up || !w_down) return fail(QMOE_EINVAL, "weight array pointer is NULL");
+    WeightSource src;
+    src.dg = w_gate;
+    src.du = w_up;
+    src.dd = w_down;
+    src.stream = (hipStream_t)stream;
+    return pack_layer(cfg, src, w_router, router_bias, out);
 }
 
 void qmoe_destroy(qmoe_ctx *ctx) {

@@ -121,6 +121,20 @@ void interleave_gate_up(const CanonMatrix &gate, const CanonMatrix &up, CanonMat
 // Inverse of layout_matrix (for export): fills codes/scales/zeros of m (N, K preset).
 void unlayout_matrix(int wformat, const PackedMatrix &p, CanonMatrix &m);
 
+// Element counts of a packed matrix (what layout_matrix produces), without packing.
+struct PackSizes {
+    size_t codes = 0, gscale = 0, gzero = 0, pscale = 0, zc = 0;
+};
+PackSizes pack_sizes(int wformat, int N, int K);
+
+// On-device quantizer (qmoe_quant.hip): matrix [N][K] of bf16 values at `a`
+// (for W13: gate at `a`, up at `b`, interleaved by 16-row blocks; otherwise b
+// is NULL) into the packed arrays at their arena addresses. zero_row: N bytes
+// of scratch (per-channel formats). The zc array must be zeroed beforehand.
+hipError_t launch_quant_matrix(int wformat, const uint16_t *a, const uint16_t *b, int N, int K, uint8_t *codes,
+                               uint16_t *gscale, uint16_t *gzero, float *pscale, uint16_t *zc, uint8_t *zero_row,
+                               hipStream_t s);
+
 // ---------------------------------------------------------------------------
 // Kernel launchers (qmoe_kernels.hip). All asynchronous on `s`.
 // ---------------------------------------------------------------------------

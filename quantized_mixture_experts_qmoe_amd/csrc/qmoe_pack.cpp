@@ -269,6 +269,23 @@ void layout_matrix(int wformat, const CanonMatrix &m, PackedMatrix &out) {
     }
 }
 
+PackSizes pack_sizes(int wformat, int N, int K) {
+    const int df = dev_format(wformat);
+    const size_t NB = (size_t)N / kBlockRows, KB = (size_t)K / kBlockK;
+    PackSizes z;
+    z.codes = NB * KB * (size_t)block_bytes(df);
+    if (is_group_wformat(wformat)) {
+        z.gscale = NB * KB * kBlockRows;
+        if (df == DF_I4ASYM) {
+            z.gzero = z.gscale;
+            z.zc = NB * ((KB + 31) / 32) * 1024;
+        }
+    } else {
+        z.pscale = (size_t)N;
+    }
+    return z;
+}
+
 void unlayout_matrix(int wformat, const PackedMatrix &p, CanonMatrix &m) {
     const int df = dev_format(wformat);
     const int bb = block_bytes(df);

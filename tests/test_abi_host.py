@@ -88,6 +88,18 @@ def test_pack_rejects_bad_per_expert_format(qmoe_lib, bad):
     assert "expert 5" in Q.qmoe_last_error()
 
 
+def test_device_pack_rejects_bad_pointers(qmoe_lib):
+    c = base_cfg()
+    ctx = C.c_void_p()
+    wr = np.zeros((c.n_experts, c.d_model), np.float32)
+    assert Q.qmoe_pack_experts_device(c, None, None, None, wr.ctypes.data, None, None, C.byref(ctx)) == Q.QMOE_EINVAL
+    n = c.n_experts + c.n_shared
+    odd = (C.c_void_p * n)(*([8] * n))   # not 16-byte aligned (checked before any device access)
+    p = C.cast(odd, C.c_void_p)
+    assert Q.qmoe_pack_experts_device(c, p, p, p, wr.ctypes.data, None, None, C.byref(ctx)) == Q.QMOE_EINVAL
+    assert "aligned" in Q.qmoe_last_error() and not ctx.value
+
+
 def test_pack_rejects_null_weights(qmoe_lib):
     got, ctx = _pack(base_cfg(), weights=False)
     assert got == Q.QMOE_EINVAL and not ctx.value
