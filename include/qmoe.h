@@ -208,6 +208,58 @@ const char *qmoe_last_error(void);
  *   zeros   host, same shape as scales (0 except INT4_ASYM), or NULL */
 int qmoe_export_packed(qmoe_ctx *ctx, int32_t expert, int32_t matrix, int8_t *codes, float *scales, float *zeros);
 
+/* ---- Atomic experts --------------------------------------------------------
+ * The OmniMoE page's routed branch (technical summary 2.1-2.2): N = n_rows x
+ * n_cols vector experts E_i(x) = silu(x . w_in_i) * w_out_i whose parameters
+ * are two global matrices W (rows w_in_i) and V (rows w_out_i), chosen by a
+ * Cartesian product router: row logits x . R_r^T and column logits x . R_c^T
+ * (fp32 accumulation); expert i = a * n_cols + b scores l_r[a] + l_c[b] (fp32);
+ * the top-k scores win (ties to the lower i) and the weights are the softmax
+ * over the k selected scores; y_t = sum_j w_tj E_{i_tj}(x_t), rounded once to
+ * bf16. The always-on dense MLP of that page is the shared-expert path of
+ * qmoe_forward. All matrices are bf16 bit patterns, row-major [rows][d_model].
+ *   d_model   multiple of 512, at most 8192
+ *   n_rows, n_cols  1..1024 each (N = n_rows * n_cols experts)
+ *   top_k     1..min(8, N)
+ *   max_tokens  1..2^20 with max_tokens * top_k <= 2^21 */
+typedef struct qmoe_atomic_ctx qmoe_atomic_ctx;
+typedef struct {
+    int32_t d_model, n_rows, n_cols, top_k, max_tokens, device;
+} qmoe_atomic_config;
+
+/* Caller-owned device buffers that receive the routing of a forward; any may
+ * be NULL: logits_rows [T][n_rows], logits_cols [T][n_cols] fp32, topk_idx
+ * [T][k] int32 (flat expert index, best first), topk_w [T][k] fp32. */
+typedef struct {
+    float *logits_rows, *logits_cols;
+    int32_t *topk_idx;
+    float *topk_w;
+} qmoe_atomic_route_out;
+
+/* Uploads W, V [N][d] and R_r [n_rows][d], R_c [n_cols][d] (host bf16 arrays,
+ * only read during the call) to cfg->device and sizes a workspace for
+ * cfg->max_tokens. Synchronous. */
+int qmoe_atomic_create(const qmoe_atomic_config *cfg, const uint16_t *w_in, const uint16_t *w_out,
+                       const uint16_t *router_rows, const uint16_t *router_cols, qmoe_atomic_ctx **out);
+
+/* Schedules of qmoe_atomic_forward (OmniMoE technical summary 2.2):
+ *   EXPERT_CENTRIC  routing decisions flattened into a task list, grouped by
+ *                   contiguous ranges of expert ids and by token inside a group
+ *                   (the dispatch of qmoe_forward), each group's tasks computed
+ *                   together so its W and V rows are fetched once for them
+ *   TOKEN_CENTRIC   each token gathers its own k experts' rows (the baseline
+ *                   the page replaces; kept for comparison) */
+#define QMOE_SCHEDULE_EXPERT_CENTRIC 0
+#define QMOE_SCHEDULE_TOKEN_CENTRIC 1
+
+/* y [T][d] bf16 (device) from x [T][d] bf16 (device), asynchronous on `stream`;
+ * T = 0 is a no-op, T > max_tokens is QMOE_EINVAL. */
+int qmoe_atomic_forward(qmoe_atomic_ctx *ctx, const uint16_t *x, int32_t T, uint16_t *y, int32_t schedule,
+                        qmoe_atomic_route_out *dbg, void *stream);
+
+/* Releases what qmoe_atomic_create allocated; NULL is a no-op. */
+void qmoe_atomic_destroy(qmoe_atomic_ctx *ctx);
+
 /* Kernel timing with HIP events recorded on the launch stream around every
  * kernel of qmoe_forward / qmoe_route_topk (for measurement).
  *   qmoe_profile_enable   slot_mask != 0 starts recording the kernel slots

@@ -31,14 +31,24 @@ WFORMAT_CODES = {"int8_sym_ch": 0, "int4_asym_g128": 1, "int4_sym_g128": 2, "int
 ROUTER_QUANT_CODES = {"none": 0, "int8": 1, "fp8": 2}
 
 ABI_SYMBOLS = ("qmoe_pack_experts", "qmoe_pack_experts_device", "qmoe_route_topk", "qmoe_forward", "qmoe_destroy",
-               "qmoe_last_error", "qmoe_export_packed", "qmoe_profile_enable", "qmoe_profile_read",
-               "qmoe_kernel_name")
+               "qmoe_last_error", "qmoe_export_packed", "qmoe_atomic_create", "qmoe_atomic_forward",
+               "qmoe_atomic_destroy", "qmoe_profile_enable", "qmoe_profile_read", "qmoe_kernel_name")
+QMOE_SCHEDULE_EXPERT_CENTRIC = 0
+QMOE_SCHEDULE_TOKEN_CENTRIC = 1
 
 
 class QmoeConfig(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("d_model", "d_ff", "n_experts", "top_k", "n_shared", "d_ff_shared",
                                          "wformat", "group_size", "router_fp32", "renormalize", "max_tokens",
                                          "device", "router_quant")] + [("expert_wformat", C.c_void_p)]
+
+
+class QmoeAtomicConfig(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in ("d_model", "n_rows", "n_cols", "top_k", "max_tokens", "device")]
+
+
+class QmoeAtomicRouteOut(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("logits_rows", "logits_cols", "topk_idx", "topk_w")]
 
 
 class QmoeRouteOut(C.Structure):
@@ -67,6 +77,12 @@ def load() -> C.CDLL:
     L.qmoe_pack_experts.argtypes = [C.POINTER(QmoeConfig), P, P, P, P, P, C.POINTER(P)]
     L.qmoe_pack_experts_device.restype = C.c_int
     L.qmoe_pack_experts_device.argtypes = [C.POINTER(QmoeConfig), P, P, P, P, P, P, C.POINTER(P)]
+    L.qmoe_atomic_create.restype = C.c_int
+    L.qmoe_atomic_create.argtypes = [C.POINTER(QmoeAtomicConfig), P, P, P, P, C.POINTER(P)]
+    L.qmoe_atomic_forward.restype = C.c_int
+    L.qmoe_atomic_forward.argtypes = [P, P, C.c_int32, P, C.c_int32, C.POINTER(QmoeAtomicRouteOut), P]
+    L.qmoe_atomic_destroy.restype = None
+    L.qmoe_atomic_destroy.argtypes = [P]
     L.qmoe_route_topk.restype = C.c_int
     L.qmoe_route_topk.argtypes = [P, P, C.c_int32, C.POINTER(QmoeRouteOut), P]
     L.qmoe_forward.restype = C.c_int
@@ -95,6 +111,18 @@ def qmoe_pack_experts(cfg: QmoeConfig, w_gate, w_up, w_down, w_router, router_bi
 
 def qmoe_pack_experts_device(cfg: QmoeConfig, w_gate, w_up, w_down, w_router, router_bias, stream, out) -> int:
     return load().qmoe_pack_experts_device(C.byref(cfg), w_gate, w_up, w_down, w_router, router_bias, stream, out)
+
+
+def qmoe_atomic_create(cfg: QmoeAtomicConfig, w_in, w_out, router_rows, router_cols, out) -> int:
+    return load().qmoe_atomic_create(C.byref(cfg), w_in, w_out, router_rows, router_cols, out)
+
+
+def qmoe_atomic_forward(ctx, x, T: int, y, schedule: int, dbg: Optional[QmoeAtomicRouteOut], stream) -> int:
+    return load().qmoe_atomic_forward(ctx, x, T, y, schedule, C.byref(dbg) if dbg is not None else None, stream)
+
+
+def qmoe_atomic_destroy(ctx) -> None:
+    load().qmoe_atomic_destroy(ctx)
 
 
 def qmoe_route_topk(ctx, logits, T: int, out: Optional[QmoeRouteOut], stream) -> int:
@@ -283,3 +311,45 @@ class QMoE:
         n = np.zeros(QMOE_NUM_KERNELS, np.int64)
         _check(qmoe_profile_read(self.ctx, ms.ctypes.data, n.ctypes.data), "qmoe_profile_read")
         return {qmoe_kernel_name(i): (float(ms[i]), int(n[i])) for i in range(QMOE_NUM_KERNELS)}
+
+
+class AtomicLayer:
+    """An atomic-expert layer (qmoe_atomic_ctx) from host bf16 bit-pattern arrays:
+    w_in, w_out [N][d], router_rows [n_rows][d], router_cols [n_cols][d]."""
+
+    def __init__(self, w_in, w_out, router_rows, router_cols, top_k: int, max_tokens: int, device: int = 0):
+        arrs = [np.ascontiguousarray(a, np.uint16) for a in (w_in, w_out, router_rows, router_cols)]
+        self.d = arrs[0].shape[1]
+        self.n_rows, self.n_cols, self.k = arrs[2].shape[0], arrs[3].shape[0], top_k
+        cfg = QmoeAtomicConfig(d_model=self.d, n_rows=self.n_rows, n_cols=self.n_cols, top_k=top_k,
+                               max_tokens=max_tokens, device=device)
+        ctx = C.c_void_p()
+        _check(qmoe_atomic_create(cfg, *[a.ctypes.data for a in arrs], C.byref(ctx)), "qmoe_atomic_create")
+        self.ctx = ctx
+
+    def close(self) -> None:
+        if getattr(self, "ctx", None):
+            qmoe_atomic_destroy(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def forward(self, x, y=None, schedule: int = QMOE_SCHEDULE_EXPERT_CENTRIC, route=None, stream=None):
+        """x: [T][d] bf16 CUDA tensor -> y; route: optional dict of CUDA tensors
+        logits_rows, logits_cols, topk_idx, topk_w to fill."""
+        import torch
+        assert x.dtype == torch.bfloat16 and x.is_cuda and x.is_contiguous()
+        if y is None:
+            y = torch.empty_like(x)
+        dbg = None
+        if route is not None:
+            dbg = QmoeAtomicRouteOut(*[_dptr(route.get(n)) for n in ("logits_rows", "logits_cols", "topk_idx",
+                                                                      "topk_w")])
+        rc = qmoe_atomic_forward(self.ctx, x.data_ptr(), x.shape[0], y.data_ptr(), schedule, dbg,
+                                 _stream_handle(stream))
+        _check(rc, "qmoe_atomic_forward")
+        return y

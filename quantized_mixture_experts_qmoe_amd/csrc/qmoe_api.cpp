@@ -839,4 +839,166 @@ int qmoe_profile_read(qmoe_ctx *c, double *total_ms, int64_t *launches) {
     return QMOE_OK;
 }
 
+// ---- Atomic experts ---------------------------------------------------------
+
+struct qmoe_atomic_ctx {
+    qmoe_atomic_config cfg{};
+    int N = 0, B = 1, NG = 1, P = 0, max_tiles = 0;
+    uint16_t *W = nullptr, *V = nullptr, *Rr = nullptr, *Rc = nullptr;
+    float *lr = nullptr, *lc = nullptr, *w = nullptr, *wrow = nullptr, *O = nullptr;
+    int32_t *idx = nullptr, *gidx = nullptr, *chunk_counts = nullptr, *chunk_base = nullptr, *counts = nullptr;
+    int32_t *offsets = nullptr, *perm = nullptr, *inv = nullptr, *num_tiles = nullptr;
+    Tile *tiles = nullptr;
+    std::vector<void *> allocs;
+};
+
+namespace {
+
+constexpr int kAtomicRows = 64;   // task rows per expert-centric tile
+
+void atomic_free(qmoe_atomic_ctx *c) {
+    if (!c) return;
+    for (void *p : c->allocs) (void)hipFree(p);
+    delete c;
+}
+
+int atomic_alloc(qmoe_atomic_ctx *c, void **p, size_t bytes) {
+    *p = nullptr;
+    if (getenv("QMOE_TEST_FAIL_ALLOC")) return fail(QMOE_ENOMEM, "allocation failure injected (QMOE_TEST_FAIL_ALLOC)");
+    const hipError_t e = hipMalloc(p, std::max<size_t>(bytes, 4));
+    if (e != hipSuccess) {
+        *p = nullptr;
+        return fail(QMOE_ENOMEM, "hipMalloc(%zu) failed: %s", bytes, hipGetErrorString(e));
+    }
+    c->allocs.push_back(*p);
+    return QMOE_OK;
+}
+
+int atomic_validate(const qmoe_atomic_config *cfg) {
+    if (!cfg) return fail(QMOE_EINVAL, "cfg is NULL");
+    if (cfg->d_model <= 0 || cfg->n_rows <= 0 || cfg->n_cols <= 0 || cfg->max_tokens <= 0)
+        return fail(QMOE_EINVAL, "d_model, n_rows, n_cols and max_tokens must be positive");
+    const long long N = (long long)cfg->n_rows * cfg->n_cols;
+    if (cfg->top_k < 1 || cfg->top_k > N) return fail(QMOE_EINVAL, "top_k=%d must be in [1, N=%lld]", cfg->top_k, N);
+    if (cfg->d_model % 512 != 0 || cfg->d_model > 8192)
+        return fail(QMOE_EUNSUPPORTED, "d_model=%d: must be a multiple of 512 and at most 8192", cfg->d_model);
+    if (cfg->n_rows > 1024 || cfg->n_cols > 1024)
+        return fail(QMOE_EUNSUPPORTED, "n_rows=%d, n_cols=%d: at most 1024 each", cfg->n_rows, cfg->n_cols);
+    if (cfg->top_k > 8) return fail(QMOE_EUNSUPPORTED, "top_k=%d exceeds 8", cfg->top_k);
+    if (cfg->max_tokens > (1 << 20) || (long long)cfg->max_tokens * cfg->top_k > (1ll << 21))
+        return fail(QMOE_EUNSUPPORTED, "max_tokens=%d too large (<= 2^20 and max_tokens * top_k <= 2^21)",
+                    cfg->max_tokens);
+    return QMOE_OK;
+}
+
+}  // namespace
+
+int qmoe_atomic_create(const qmoe_atomic_config *cfg, const uint16_t *w_in, const uint16_t *w_out,
+                       const uint16_t *router_rows, const uint16_t *router_cols, qmoe_atomic_ctx **out) {
+    g_last_error.clear();
+    if (!out) return fail(QMOE_EINVAL, "out is NULL");
+    *out = nullptr;
+    int rc = atomic_validate(cfg);
+    if (rc) return rc;
+    if (!w_in || !w_out || !router_rows || !router_cols) return fail(QMOE_EINVAL, "weight pointer is NULL");
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || ndev == 0) return fail(QMOE_EHIP, "no HIP device available");
+    if (cfg->device < 0 || cfg->device >= ndev) return fail(QMOE_EINVAL, "device %d out of range", cfg->device);
+    if (hipSetDevice(cfg->device) != hipSuccess) return fail(QMOE_EHIP, "hipSetDevice failed");
+    qmoe_atomic_ctx *c = new qmoe_atomic_ctx();
+    c->cfg = *cfg;
+    const size_t d = (size_t)cfg->d_model;
+    c->N = cfg->n_rows * cfg->n_cols;
+    c->B = (c->N + 1023) / 1024;          // experts per dispatch group: at most 1024 groups
+    c->NG = (c->N + c->B - 1) / c->B;
+    c->P = cfg->max_tokens * cfg->top_k;
+    c->max_tiles = (c->P + kAtomicRows - 1) / kAtomicRows + std::min(c->NG, c->P);
+    auto up = [&](uint16_t **dst, const uint16_t *src, size_t n) {
+        int r = atomic_alloc(c, (void **)dst, n * 2);
+        if (!r && hipMemcpy(*dst, src, n * 2, hipMemcpyHostToDevice) != hipSuccess)
+            r = fail(QMOE_EHIP, "upload of atomic-expert weights failed");
+        return r;
+    };
+    rc = up(&c->W, w_in, (size_t)c->N * d);
+    if (!rc) rc = up(&c->V, w_out, (size_t)c->N * d);
+    if (!rc) rc = up(&c->Rr, router_rows, (size_t)cfg->n_rows * d);
+    if (!rc) rc = up(&c->Rc, router_cols, (size_t)cfg->n_cols * d);
+    const size_t T = (size_t)cfg->max_tokens, P = (size_t)c->P;
+    const size_t nchunks = (P + kDispatchChunk - 1) / kDispatchChunk;
+    if (!rc) rc = atomic_alloc(c, (void **)&c->lr, T * cfg->n_rows * 4);
+    if (!rc) rc = atomic_alloc(c, (void **)&c->lc, T * cfg->n_cols * 4);
+    if (!rc) rc = atomic_alloc(c, (void **)&c->idx, P * 4);
+    if (!rc) rc = atomic_alloc(c, (void **)&c->gidx, P * 4);
+    if (!rc) rc = atomic_alloc(c, (void **)&c->w, P * 4);
+    if (!rc) rc = atomic_alloc(c, (void **)&c->wrow, P * 4);
+    if (!rc) rc = atomic_alloc(c, (void **)&c->perm, P * 4);
+    if (!rc) rc = atomic_alloc(c, (void **)&c->inv, P * 4);
+    if (!rc) rc = atomic_alloc(c, (void **)&c->chunk_counts, nchunks * c->NG * 4);
+    if (!rc) rc = atomic_alloc(c, (void **)&c->chunk_base, nchunks * c->NG * 4);
+    if (!rc) rc = atomic_alloc(c, (void **)&c->counts, (size_t)c->NG * 4);
+    if (!rc) rc = atomic_alloc(c, (void **)&c->offsets, ((size_t)c->NG + 1) * 4);
+    if (!rc) rc = atomic_alloc(c, (void **)&c->num_tiles, 256);
+    if (!rc) rc = atomic_alloc(c, (void **)&c->tiles, ((size_t)c->max_tiles + 16) * sizeof(Tile));
+    if (!rc) rc = atomic_alloc(c, (void **)&c->O, P * d * 4);
+    if (rc) {
+        atomic_free(c);
+        return rc;
+    }
+    *out = c;
+    return QMOE_OK;
+}
+
+int qmoe_atomic_forward(qmoe_atomic_ctx *c, const uint16_t *x, int32_t T, uint16_t *y, int32_t schedule,
+                        qmoe_atomic_route_out *dbg, void *stream) {
+    g_last_error.clear();
+    if (!c) return fail(QMOE_EINVAL, "ctx is NULL");
+    if (T < 0 || T > c->cfg.max_tokens) return fail(QMOE_EINVAL, "T=%d outside [0, max_tokens=%d]", T, c->cfg.max_tokens);
+    if (schedule != QMOE_SCHEDULE_EXPERT_CENTRIC && schedule != QMOE_SCHEDULE_TOKEN_CENTRIC)
+        return fail(QMOE_EINVAL, "unknown schedule %d", schedule);
+    if (T == 0) return QMOE_OK;
+    if (!x || !y) return fail(QMOE_EINVAL, "x or y is NULL");
+    if ((const void *)x == (const void *)y) return fail(QMOE_EINVAL, "y may not alias x");
+    if (hipSetDevice(c->cfg.device) != hipSuccess) return fail(QMOE_EHIP, "hipSetDevice failed");
+    hipStream_t s = (hipStream_t)stream;
+    const int d = c->cfg.d_model, k = c->cfg.top_k, Nr = c->cfg.n_rows, Nc = c->cfg.n_cols, P = T * k;
+    auto ok = [](hipError_t e, const char *what) {
+        return e == hipSuccess ? QMOE_OK : fail(QMOE_EHIP, "%s failed: %s", what, hipGetErrorString(e));
+    };
+    int rc = ok(launch_router_bf16(x, c->Rr, nullptr, nullptr, c->lr, nullptr, 0.0f, T, d, Nr, s), "row router");
+    if (!rc) rc = ok(launch_router_bf16(x, c->Rc, nullptr, nullptr, c->lc, nullptr, 0.0f, T, d, Nc, s), "column router");
+    if (!rc) rc = ok(launch_cart_topk(c->lr, c->lc, T, Nr, Nc, k, c->B, c->idx, c->w, c->gidx, s), "cartesian top-k");
+    if (!rc && schedule == QMOE_SCHEDULE_TOKEN_CENTRIC) {
+        rc = ok(launch_atomic_token(x, c->W, c->V, c->idx, c->w, T, d, k, y, s), "token-centric experts");
+    } else if (!rc) {
+        const int nchunks = (P + kDispatchChunk - 1) / kDispatchChunk;
+        rc = ok(launch_dispatch_count(c->gidx, P, c->NG, c->chunk_counts, s), "dispatch count");
+        if (!rc)
+            rc = ok(launch_dispatch_scan(c->chunk_counts, nchunks, c->NG, P, T, 0, kAtomicRows, c->chunk_base,
+                                         c->counts, c->offsets, c->tiles, c->num_tiles, s),
+                    "dispatch scan");
+        if (!rc)
+            rc = ok(launch_dispatch_scatter(c->gidx, c->w, P, c->NG, c->chunk_base, c->perm, c->inv, c->wrow, s),
+                    "dispatch scatter");
+        const int max_tiles = (P + kAtomicRows - 1) / kAtomicRows + std::min(c->NG, P);
+        if (!rc)
+            rc = ok(launch_atomic_tiles(x, c->W, c->V, c->tiles, c->num_tiles, max_tiles, c->perm, c->idx, c->wrow, d,
+                                        k, c->O, s),
+                    "expert-centric experts");
+        if (!rc) rc = ok(launch_combine(c->O, c->inv, T, d, k, P, 0, y, s), "combine");
+    }
+    if (!rc && dbg) {
+        if (dbg->logits_rows) rc = copy_out(dbg->logits_rows, c->lr, (size_t)T * Nr * 4, s);
+        if (!rc && dbg->logits_cols) rc = copy_out(dbg->logits_cols, c->lc, (size_t)T * Nc * 4, s);
+        if (!rc && dbg->topk_idx) rc = copy_out(dbg->topk_idx, c->idx, (size_t)P * 4, s);
+        if (!rc && dbg->topk_w) rc = copy_out(dbg->topk_w, c->w, (size_t)P * 4, s);
+    }
+    return rc;
+}
+
+void qmoe_atomic_destroy(qmoe_atomic_ctx *c) {
+    if (!c) return;
+    (void)hipSetDevice(c->cfg.device);
+    atomic_free(c);
+}
+
 }  // extern "C"

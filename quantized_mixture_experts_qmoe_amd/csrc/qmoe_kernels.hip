@@ -1646,6 +1646,174 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ O, co
 }
 
 // ---------------------------------------------------------------------------
+// Atomic experts (OmniMoE technical summary 2.1, 2.2): N = N_r x N_c vector
+// experts E_i(x) = silu(x . w_in_i) w_out_i held in two global bf16 matrices
+// W, V [N][d], chosen by a Cartesian product router.
+// ---------------------------------------------------------------------------
+
+// Indices of the kk largest of v[0..n) (ties to the lower index), one
+// wavefront: lane j < kk returns the j-th, the other lanes -1.
+template <int EPL>
+__device__ __forceinline__ int wave_topk_index(const float *__restrict__ v, int n, int kk, int lane) {
+    uint64_t key[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; i++) {
+        const int e = lane + 64 * i;
+        key[i] = e < n ? select_key(v[e], e) : 0ull;
+    }
+    int mine = -1;
+    for (int j = 0; j < kk; j++) {
+        uint64_t best = key[0];
+#pragma unroll
+        for (int i = 1; i < EPL; i++) best = key[i] > best ? key[i] : best;
+        const int be = key_expert(wave_max_u64(best));
+#pragma unroll
+        for (int i = 0; i < EPL; i++)
+            if (be == lane + 64 * i) key[i] = 0ull;
+        if (lane == j) mine = be;
+    }
+    return mine;
+}
+
+// Cartesian product routing, one wavefront per token: score(a, b) = l_r[a] +
+// l_c[b] (fp32). The top-k of the N_r x N_c scores lies among the top-min(k,
+// N_r) rows x top-min(k, N_c) columns (a pair outside them has k better pairs
+// in its own column or row), so k rounds over those <= 64 candidates select it;
+// ties go to the lower flat index a * N_c + b. Weights: softmax over the k
+// selected scores. Also writes each task's dispatch key, its expert's group of
+// B consecutive expert ids.
+template <int EPL>
+__global__ __launch_bounds__(256) void k_cart_topk(const float *__restrict__ lr, const float *__restrict__ lc, int T,
+                                                   int Nr, int Nc, int k, int B, int32_t *__restrict__ idx,
+                                                   float *__restrict__ w, int32_t *__restrict__ gidx) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    const float *lrt = lr + (size_t)t * Nr, *lct = lc + (size_t)t * Nc;
+    const int kr = min(k, Nr), kc = min(k, Nc);
+    const int ra = wave_topk_index<EPL>(lrt, Nr, kr, lane);
+    const int cb = wave_topk_index<EPL>(lct, Nc, kc, lane);
+    const int a = __shfl(ra, lane / kc), b = __shfl(cb, lane % kc);
+    uint64_t key = 0ull;
+    if (lane < kr * kc) key = select_key(lrt[a] + lct[b], a * Nc + b);
+    uint64_t mine = 0ull, first = 0ull;
+    for (int j = 0; j < k; j++) {
+        const uint64_t wb = wave_max_u64(key);
+        if (key == wb) key = 0ull;   // keys are distinct: their low words are distinct indices
+        if (lane == j) mine = wb;
+        if (j == 0) first = wb;
+    }
+    const float ex = lane < k ? expf(key_value(mine) - key_value(first)) : 0.0f;
+    const float denom = wave_sum_f32(ex);
+    if (lane < k) {
+        const int e = key_expert(mine);
+        idx[(size_t)t * k + lane] = e;
+        w[(size_t)t * k + lane] = ex / denom;
+        gidx[(size_t)t * k + lane] = e / B;
+    }
+}
+
+// Expert-centric: one tile of task rows of one expert-id group per workgroup,
+// a row per wavefront at a time: h = silu(x_t . w_in_e) * (mixing weight),
+// O[row] = h * w_out_e in fp32 (the combine adds a token's k rows). The rows of
+// a tile share their group's W and V rows through the cache.
+__global__ __launch_bounds__(256) void k_atomic_tile(const uint16_t *__restrict__ x, const uint16_t *__restrict__ W,
+                                                     const uint16_t *__restrict__ V, const Tile *__restrict__ tiles,
+                                                     const int32_t *__restrict__ num_tiles,
+                                                     const int32_t *__restrict__ perm, const int32_t *__restrict__ idx,
+                                                     const float *__restrict__ wrow, int d, int k, float *__restrict__ O) {
+    if ((int)blockIdx.x >= *num_tiles) return;
+    const Tile tl = tiles[blockIdx.x];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int row = tl.row0 + wave; row < tl.row_end; row += 4) {
+        const int pair = perm[row];
+        const int t = pair / k, e = idx[pair];
+        const uint16_t *xr = x + (size_t)t * d, *wi = W + (size_t)e * d, *wo = V + (size_t)e * d;
+        float acc = 0.0f;
+        for (int c = lane * 8; c < d; c += 512) {
+            const uint4 xv = gload16(xr + c), wv = gload16(wi + c);
+            const uint32_t xu[4] = {xv.x, xv.y, xv.z, xv.w}, wu[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+            for (int h = 0; h < 4; h++) {
+                acc = fmaf(bf16f(xu[h] & 0xFFFFu), bf16f(wu[h] & 0xFFFFu), acc);
+                acc = fmaf(bf16f(xu[h] >> 16), bf16f(wu[h] >> 16), acc);
+            }
+        }
+        const float g = silu_mul(wave_sum_f32(acc), wrow[row]);
+        float *orow = O + (size_t)row * d;
+        for (int c = lane * 8; c < d; c += 512) {
+            const uint4 vv = gload16(wo + c);
+            const uint32_t vu[4] = {vv.x, vv.y, vv.z, vv.w};
+            float4 lo, hi;
+            lo.x = g * bf16f(vu[0] & 0xFFFFu); lo.y = g * bf16f(vu[0] >> 16);
+            lo.z = g * bf16f(vu[1] & 0xFFFFu); lo.w = g * bf16f(vu[1] >> 16);
+            hi.x = g * bf16f(vu[2] & 0xFFFFu); hi.y = g * bf16f(vu[2] >> 16);
+            hi.z = g * bf16f(vu[3] & 0xFFFFu); hi.w = g * bf16f(vu[3] >> 16);
+            *reinterpret_cast<float4 *>(orow + c) = lo;
+            *reinterpret_cast<float4 *>(orow + c + 4) = hi;
+        }
+    }
+}
+
+// Token-centric (the scheduling the OmniMoE page replaces, kept as the
+// ablation): one wavefront per token gathers its k experts' W and V rows one
+// after another and accumulates y_t in registers (d <= 8192).
+__global__ __launch_bounds__(256) void k_atomic_token(const uint16_t *__restrict__ x, const uint16_t *__restrict__ W,
+                                                      const uint16_t *__restrict__ V, const int32_t *__restrict__ idx,
+                                                      const float *__restrict__ w, int T, int d, int k,
+                                                      uint16_t *__restrict__ y) {
+    constexpr int MAXC = 16;   // 512-column chunks per row
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    const int nch = d / 512;
+    const uint16_t *xr = x + (size_t)t * d;
+    float acc[MAXC][8];
+#pragma unroll
+    for (int c = 0; c < MAXC; c++)
+#pragma unroll
+        for (int q = 0; q < 8; q++) acc[c][q] = 0.0f;
+    for (int j = 0; j < k; j++) {
+        const int e = idx[(size_t)t * k + j];
+        const uint16_t *wi = W + (size_t)e * d, *wo = V + (size_t)e * d;
+        float dot = 0.0f;
+#pragma unroll
+        for (int c = 0; c < MAXC; c++) {
+            if (c >= nch) break;
+            const uint4 xv = gload16(xr + c * 512 + lane * 8), wv = gload16(wi + c * 512 + lane * 8);
+            const uint32_t xu[4] = {xv.x, xv.y, xv.z, xv.w}, wu[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+            for (int h = 0; h < 4; h++) {
+                dot = fmaf(bf16f(xu[h] & 0xFFFFu), bf16f(wu[h] & 0xFFFFu), dot);
+                dot = fmaf(bf16f(xu[h] >> 16), bf16f(wu[h] >> 16), dot);
+            }
+        }
+        const float g = silu_mul(wave_sum_f32(dot), w[(size_t)t * k + j]);
+#pragma unroll
+        for (int c = 0; c < MAXC; c++) {
+            if (c >= nch) break;
+            const uint4 vv = gload16(wo + c * 512 + lane * 8);
+            const uint32_t vu[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+            for (int h = 0; h < 4; h++) {
+                acc[c][2 * h] += g * bf16f(vu[h] & 0xFFFFu);
+                acc[c][2 * h + 1] += g * bf16f(vu[h] >> 16);
+            }
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < MAXC; c++) {
+        if (c >= nch) break;
+        uint4 out;
+        out.x = (uint32_t)to_bf16(acc[c][0]) | ((uint32_t)to_bf16(acc[c][1]) << 16);
+        out.y = (uint32_t)to_bf16(acc[c][2]) | ((uint32_t)to_bf16(acc[c][3]) << 16);
+        out.z = (uint32_t)to_bf16(acc[c][4]) | ((uint32_t)to_bf16(acc[c][5]) << 16);
+        out.w = (uint32_t)to_bf16(acc[c][6]) | ((uint32_t)to_bf16(acc[c][7]) << 16);
+        *reinterpret_cast<uint4 *>(y + (size_t)t * d + c * 512 + lane * 8) = out;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
 
@@ -1793,6 +1961,30 @@ hipError_t launch_combine(const float *O, const int32_t *inv, int T, int d, int 
                           uint16_t *y, hipStream_t s) {
     hipLaunchKernelGGL(k_combine, dim3(T, (d / 4 + 256 * kCombineCPT - 1) / (256 * kCombineCPT)), dim3(256), 0, s, O, inv,
                        T, d, k, P, n_shared, y);
+    return hipGetLastError();
+}
+
+hipError_t launch_cart_topk(const float *lr, const float *lc, int T, int Nr, int Nc, int k, int B, int32_t *idx,
+                            float *w, int32_t *gidx, hipStream_t s) {
+    const dim3 grid((T + 3) / 4);
+    const int n = Nr > Nc ? Nr : Nc;
+    if (n <= 64) hipLaunchKernelGGL(k_cart_topk<1>, grid, dim3(256), 0, s, lr, lc, T, Nr, Nc, k, B, idx, w, gidx);
+    else if (n <= 256) hipLaunchKernelGGL(k_cart_topk<4>, grid, dim3(256), 0, s, lr, lc, T, Nr, Nc, k, B, idx, w, gidx);
+    else hipLaunchKernelGGL(k_cart_topk<16>, grid, dim3(256), 0, s, lr, lc, T, Nr, Nc, k, B, idx, w, gidx);
+    return hipGetLastError();
+}
+
+hipError_t launch_atomic_tiles(const uint16_t *x, const uint16_t *W, const uint16_t *V, const Tile *tiles,
+                               const int32_t *num_tiles, int max_tiles, const int32_t *perm, const int32_t *idx,
+                               const float *wrow, int d, int k, float *O, hipStream_t s) {
+    hipLaunchKernelGGL(k_atomic_tile, dim3(max_tiles), dim3(256), 0, s, x, W, V, tiles, num_tiles, perm, idx, wrow, d,
+                       k, O);
+    return hipGetLastError();
+}
+
+hipError_t launch_atomic_token(const uint16_t *x, const uint16_t *W, const uint16_t *V, const int32_t *idx,
+                               const float *w, int T, int d, int k, uint16_t *y, hipStream_t s) {
+    hipLaunchKernelGGL(k_atomic_token, dim3((T + 3) / 4), dim3(256), 0, s, x, W, V, idx, w, T, d, k, y);
     return hipGetLastError();
 }
 

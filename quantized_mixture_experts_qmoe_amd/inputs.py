@@ -179,3 +179,28 @@ def make_logits(T: int, E: int, seed: int, kind: str = "normal", k: int = 2) -> 
         a[:, :n] += np.float32(100.0)
         return a
     raise ValueError(kind)
+
+
+@dataclasses.dataclass
+class AtomicInputs:
+    """Seeded synthetic atomic-expert layer (OmniMoE shapes): bf16 bit patterns."""
+    router_rows: np.ndarray   # [n_rows][d]
+    router_cols: np.ndarray   # [n_cols][d]
+    w_in: np.ndarray          # [N][d]
+    w_out: np.ndarray         # [N][d]
+    x: np.ndarray             # [T][d]
+
+
+def make_atomic_inputs(T: int, d: int, n_rows: int, n_cols: int, seed: int = 0) -> AtomicInputs:
+    """Draw order: R_r, R_c, W, V ~ N(0, 0.02), then x ~ N(0, 1); all rounded to bf16."""
+    rng = np.random.default_rng(seed)
+    n = n_rows * n_cols
+
+    def draw(shape, std):
+        return f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32) * np.float32(std))
+    rr = draw((n_rows, d), 0.02)
+    rc = draw((n_cols, d), 0.02)
+    w_in = draw((n, d), 0.02)
+    w_out = draw((n, d), 0.02)
+    x = draw((T, d), 1.0)
+    return AtomicInputs(rr, rc, w_in, w_out, x)
