@@ -245,8 +245,9 @@ int qmoe_atomic_create(const qmoe_atomic_config *cfg, const uint16_t *w_in, cons
 /* Schedules of qmoe_atomic_forward (OmniMoE technical summary 2.2):
  *   EXPERT_CENTRIC  routing decisions flattened into a task list, grouped by
  *                   contiguous ranges of expert ids and by token inside a group
- *                   (the dispatch of qmoe_forward), each group's tasks computed
- *                   together so its W and V rows are fetched once for them
+ *                   (the dispatch of qmoe_forward); the tasks run in that
+ *                   order, so the tasks of one group, computed side by side,
+ *                   share its W and V rows through the cache
  *   TOKEN_CENTRIC   each token gathers its own k experts' rows (the baseline
  *                   the page replaces; kept for comparison) */
 #define QMOE_SCHEDULE_EXPERT_CENTRIC 0

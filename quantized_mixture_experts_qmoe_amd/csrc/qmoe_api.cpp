@@ -844,8 +844,8 @@ int qmoe_profile_read(qmoe_ctx *c, double *total_ms, int64_t *launches) {
 struct qmoe_atomic_ctx {
     qmoe_atomic_config cfg{};
     int N = 0, B = 1, NG = 1, P = 0, max_tiles = 0;
-    uint16_t *W = nullptr, *V = nullptr, *Rr = nullptr, *Rc = nullptr;
-    float *lr = nullptr, *lc = nullptr, *w = nullptr, *wrow = nullptr, *O = nullptr;
+    uint16_t *W = nullptr, *V = nullptr, *R = nullptr;   // R: router rows, then router columns [Nr + Nc][d]
+    float *logits = nullptr, *w = nullptr, *wrow = nullptr, *O = nullptr;   // logits [T][Nr + Nc]
     int32_t *idx = nullptr, *gidx = nullptr, *chunk_counts = nullptr, *chunk_base = nullptr, *counts = nullptr;
     int32_t *offsets = nullptr, *perm = nullptr, *inv = nullptr, *num_tiles = nullptr;
     Tile *tiles = nullptr;
@@ -854,7 +854,9 @@ struct qmoe_atomic_ctx {
 
 namespace {
 
-constexpr int kAtomicRows = 64;   // task rows per expert-centric tile
+// The dispatch scan also emits a tile list (rows per tile below); the
+// expert-centric kernel walks the sorted rows directly and does not read it.
+constexpr int kAtomicRows = 64;
 
 void atomic_free(qmoe_atomic_ctx *c) {
     if (!c) return;
@@ -913,20 +915,23 @@ int qmoe_atomic_create(const qmoe_atomic_config *cfg, const uint16_t *w_in, cons
     c->NG = (c->N + c->B - 1) / c->B;
     c->P = cfg->max_tokens * cfg->top_k;
     c->max_tiles = (c->P + kAtomicRows - 1) / kAtomicRows + std::min(c->NG, c->P);
-    auto up = [&](uint16_t **dst, const uint16_t *src, size_t n) {
-        int r = atomic_alloc(c, (void **)dst, n * 2);
-        if (!r && hipMemcpy(*dst, src, n * 2, hipMemcpyHostToDevice) != hipSuccess)
-            r = fail(QMOE_EHIP, "upload of atomic-expert weights failed");
-        return r;
+    auto up = [&](uint16_t *dst, const uint16_t *src, size_t n) {
+        return hipMemcpy(dst, src, n * 2, hipMemcpyHostToDevice) == hipSuccess
+                   ? QMOE_OK
+                   : fail(QMOE_EHIP, "upload of atomic-expert weights failed");
     };
-    rc = up(&c->W, w_in, (size_t)c->N * d);
-    if (!rc) rc = up(&c->V, w_out, (size_t)c->N * d);
-    if (!rc) rc = up(&c->Rr, router_rows, (size_t)cfg->n_rows * d);
-    if (!rc) rc = up(&c->Rc, router_cols, (size_t)cfg->n_cols * d);
+    const size_t nr = (size_t)cfg->n_rows, nc = (size_t)cfg->n_cols;
+    rc = atomic_alloc(c, (void **)&c->W, (size_t)c->N * d * 2);
+    if (!rc) rc = up(c->W, w_in, (size_t)c->N * d);
+    if (!rc) rc = atomic_alloc(c, (void **)&c->V, (size_t)c->N * d * 2);
+    if (!rc) rc = up(c->V, w_out, (size_t)c->N * d);
+    // one router matrix, so that one pass over x yields both logit sets
+    if (!rc) rc = atomic_alloc(c, (void **)&c->R, (nr + nc) * d * 2);
+    if (!rc) rc = up(c->R, router_rows, nr * d);
+    if (!rc) rc = up(c->R + nr * d, router_cols, nc * d);
     const size_t T = (size_t)cfg->max_tokens, P = (size_t)c->P;
     const size_t nchunks = (P + kDispatchChunk - 1) / kDispatchChunk;
-    if (!rc) rc = atomic_alloc(c, (void **)&c->lr, T * cfg->n_rows * 4);
-    if (!rc) rc = atomic_alloc(c, (void **)&c->lc, T * cfg->n_cols * 4);
+    if (!rc) rc = atomic_alloc(c, (void **)&c->logits, T * (nr + nc) * 4);
     if (!rc) rc = atomic_alloc(c, (void **)&c->idx, P * 4);
     if (!rc) rc = atomic_alloc(c, (void **)&c->gidx, P * 4);
     if (!rc) rc = atomic_alloc(c, (void **)&c->w, P * 4);
@@ -964,9 +969,8 @@ int qmoe_atomic_forward(qmoe_atomic_ctx *c, const uint16_t *x, int32_t T, uint16
     auto ok = [](hipError_t e, const char *what) {
         return e == hipSuccess ? QMOE_OK : fail(QMOE_EHIP, "%s failed: %s", what, hipGetErrorString(e));
     };
-    int rc = ok(launch_router_bf16(x, c->Rr, nullptr, nullptr, c->lr, nullptr, 0.0f, T, d, Nr, s), "row router");
-    if (!rc) rc = ok(launch_router_bf16(x, c->Rc, nullptr, nullptr, c->lc, nullptr, 0.0f, T, d, Nc, s), "column router");
-    if (!rc) rc = ok(launch_cart_topk(c->lr, c->lc, T, Nr, Nc, k, c->B, c->idx, c->w, c->gidx, s), "cartesian top-k");
+    int rc = ok(launch_router_bf16(x, c->R, nullptr, nullptr, c->logits, nullptr, 0.0f, T, d, Nr + Nc, s), "router");
+    if (!rc) rc = ok(launch_cart_topk(c->logits, T, Nr, Nc, k, c->B, c->idx, c->w, c->gidx, s), "cartesian top-k");
     if (!rc && schedule == QMOE_SCHEDULE_TOKEN_CENTRIC) {
         rc = ok(launch_atomic_token(x, c->W, c->V, c->idx, c->w, T, d, k, y, s), "token-centric experts");
     } else if (!rc) {
@@ -979,16 +983,20 @@ int qmoe_atomic_forward(qmoe_atomic_ctx *c, const uint16_t *x, int32_t T, uint16
         if (!rc)
             rc = ok(launch_dispatch_scatter(c->gidx, c->w, P, c->NG, c->chunk_base, c->perm, c->inv, c->wrow, s),
                     "dispatch scatter");
-        const int max_tiles = (P + kAtomicRows - 1) / kAtomicRows + std::min(c->NG, P);
         if (!rc)
-            rc = ok(launch_atomic_tiles(x, c->W, c->V, c->tiles, c->num_tiles, max_tiles, c->perm, c->idx, c->wrow, d,
-                                        k, c->O, s),
+            rc = ok(launch_atomic_rows(x, c->W, c->V, c->perm, c->idx, c->wrow, P, d, k, c->O, s),
                     "expert-centric experts");
         if (!rc) rc = ok(launch_combine(c->O, c->inv, T, d, k, P, 0, y, s), "combine");
     }
     if (!rc && dbg) {
-        if (dbg->logits_rows) rc = copy_out(dbg->logits_rows, c->lr, (size_t)T * Nr * 4, s);
-        if (!rc && dbg->logits_cols) rc = copy_out(dbg->logits_cols, c->lc, (size_t)T * Nc * 4, s);
+        const size_t ld = (size_t)(Nr + Nc) * 4;
+        auto copy_cols = [&](float *dst, const float *src, int n) {
+            const hipError_t e = hipMemcpy2DAsync(dst, (size_t)n * 4, src, ld, (size_t)n * 4, (size_t)T,
+                                                  hipMemcpyDeviceToDevice, s);
+            return e == hipSuccess ? QMOE_OK : fail(QMOE_EHIP, "logit copy failed: %s", hipGetErrorString(e));
+        };
+        if (dbg->logits_rows) rc = copy_cols(dbg->logits_rows, c->logits, Nr);
+        if (!rc && dbg->logits_cols) rc = copy_cols(dbg->logits_cols, c->logits + Nr, Nc);
         if (!rc && dbg->topk_idx) rc = copy_out(dbg->topk_idx, c->idx, (size_t)P * 4, s);
         if (!rc && dbg->topk_w) rc = copy_out(dbg->topk_w, c->w, (size_t)P * 4, s);
     }

@@ -204,16 +204,15 @@ hipError_t launch_combine(const float *O, const int32_t *inv, int T, int d, int 
                           uint16_t *y, hipStream_t s);
 hipError_t launch_xsum(const uint16_t *x, int T, int d, float scale, float *xsum, hipStream_t s);
 
-// Atomic experts: Cartesian top-k over row logits lr [T][Nr] and column logits
-// lc [T][Nc] (k <= 8; Nr, Nc <= 1024), writing idx / w [T][k] and the dispatch
-// key idx / B; the expert-centric tiles (task rows of the dispatch) into O
-// [rows][d] fp32; the token-centric ablation straight into y [T][d] bf16
-// (d <= 8192).
-hipError_t launch_cart_topk(const float *lr, const float *lc, int T, int Nr, int Nc, int k, int B, int32_t *idx,
-                            float *w, int32_t *gidx, hipStream_t s);
-hipError_t launch_atomic_tiles(const uint16_t *x, const uint16_t *W, const uint16_t *V, const Tile *tiles,
-                               const int32_t *num_tiles, int max_tiles, const int32_t *perm, const int32_t *idx,
-                               const float *wrow, int d, int k, float *O, hipStream_t s);
+// Atomic experts: Cartesian top-k over logits [T][Nr + Nc] (each token's row
+// logits, then its column logits; k <= 8; Nr, Nc <= 1024), writing idx / w
+// [T][k] and the dispatch key idx / B; the expert-centric kernel (the task rows
+// of the dispatch, one wavefront each) into O [rows][d] fp32; the token-centric
+// ablation straight into y [T][d] bf16 (d = 512 * n, n <= 16).
+hipError_t launch_cart_topk(const float *logits, int T, int Nr, int Nc, int k, int B, int32_t *idx, float *w,
+                            int32_t *gidx, hipStream_t s);
+hipError_t launch_atomic_rows(const uint16_t *x, const uint16_t *W, const uint16_t *V, const int32_t *perm,
+                              const int32_t *idx, const float *wrow, int P, int d, int k, float *O, hipStream_t s);
 hipError_t launch_atomic_token(const uint16_t *x, const uint16_t *W, const uint16_t *V, const int32_t *idx,
                                const float *w, int T, int d, int k, uint16_t *y, hipStream_t s);
 

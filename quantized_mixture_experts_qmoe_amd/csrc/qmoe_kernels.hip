@@ -1683,13 +1683,14 @@ __device__ __forceinline__ int wave_topk_index(const float *__restrict__ v, int 
 // selected scores. Also writes each task's dispatch key, its expert's group of
 // B consecutive expert ids.
 template <int EPL>
-__global__ __launch_bounds__(256) void k_cart_topk(const float *__restrict__ lr, const float *__restrict__ lc, int T,
-                                                   int Nr, int Nc, int k, int B, int32_t *__restrict__ idx,
-                                                   float *__restrict__ w, int32_t *__restrict__ gidx) {
+__global__ __launch_bounds__(256) void k_cart_topk(const float *__restrict__ logits, int T, int Nr, int Nc, int k,
+                                                   int B, int32_t *__restrict__ idx, float *__restrict__ w,
+                                                   int32_t *__restrict__ gidx) {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
-    const float *lrt = lr + (size_t)t * Nr, *lct = lc + (size_t)t * Nc;
+    // a token's row logits and then its column logits, one row of Nr + Nc
+    const float *lrt = logits + (size_t)t * (Nr + Nc), *lct = lrt + Nr;
     const int kr = min(k, Nr), kc = min(k, Nc);
     const int ra = wave_topk_index<EPL>(lrt, Nr, kr, lane);
     const int cb = wave_topk_index<EPL>(lct, Nc, kc, lane);
@@ -1713,103 +1714,171 @@ __global__ __launch_bounds__(256) void k_cart_topk(const float *__restrict__ lr,
     }
 }
 
-// Expert-centric: one tile of task rows of one expert-id group per workgroup,
-// a row per wavefront at a time: h = silu(x_t . w_in_e) * (mixing weight),
-// O[row] = h * w_out_e in fp32 (the combine adds a token's k rows). The rows of
-// a tile share their group's W and V rows through the cache.
-__global__ __launch_bounds__(256) void k_atomic_tile(const uint16_t *__restrict__ x, const uint16_t *__restrict__ W,
-                                                     const uint16_t *__restrict__ V, const Tile *__restrict__ tiles,
-                                                     const int32_t *__restrict__ num_tiles,
-                                                     const int32_t *__restrict__ perm, const int32_t *__restrict__ idx,
-                                                     const float *__restrict__ wrow, int d, int k, float *__restrict__ O) {
-    if ((int)blockIdx.x >= *num_tiles) return;
-    const Tile tl = tiles[blockIdx.x];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int row = tl.row0 + wave; row < tl.row_end; row += 4) {
-        const int pair = perm[row];
-        const int t = pair / k, e = idx[pair];
-        const uint16_t *xr = x + (size_t)t * d, *wi = W + (size_t)e * d, *wo = V + (size_t)e * d;
-        float acc = 0.0f;
-        for (int c = lane * 8; c < d; c += 512) {
-            const uint4 xv = gload16(xr + c), wv = gload16(wi + c);
-            const uint32_t xu[4] = {xv.x, xv.y, xv.z, xv.w}, wu[4] = {wv.x, wv.y, wv.z, wv.w};
+// dot of eight bf16 pairs (one 16-byte chunk of each operand) into acc
+__device__ __forceinline__ float dot8_bf16(uint4 a, uint4 b, float acc) {
+    const uint32_t au[4] = {a.x, a.y, a.z, a.w}, bu[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
-            for (int h = 0; h < 4; h++) {
-                acc = fmaf(bf16f(xu[h] & 0xFFFFu), bf16f(wu[h] & 0xFFFFu), acc);
-                acc = fmaf(bf16f(xu[h] >> 16), bf16f(wu[h] >> 16), acc);
-            }
+    for (int h = 0; h < 4; h++) {
+        acc = fmaf(bf16f(au[h] & 0xFFFFu), bf16f(bu[h] & 0xFFFFu), acc);
+        acc = fmaf(bf16f(au[h] >> 16), bf16f(bu[h] >> 16), acc);
+    }
+    return acc;
+}
+// p[0..8) = g * (eight bf16 of v), fp32
+__device__ __forceinline__ void store_scaled8(float *p, float g, uint4 v) {
+    float4 lo, hi;
+    lo.x = g * bf16f(v.x & 0xFFFFu); lo.y = g * bf16f(v.x >> 16);
+    lo.z = g * bf16f(v.y & 0xFFFFu); lo.w = g * bf16f(v.y >> 16);
+    hi.x = g * bf16f(v.z & 0xFFFFu); hi.y = g * bf16f(v.z >> 16);
+    hi.z = g * bf16f(v.w & 0xFFFFu); hi.w = g * bf16f(v.w >> 16);
+    *reinterpret_cast<float4 *>(p) = lo;
+    *reinterpret_cast<float4 *>(p + 4) = hi;
+}
+
+// Expert-centric: the task rows in expert-group order (groups of B
+// consecutive expert ids, tokens ascending inside a group), one wavefront per
+// row: h = silu(x_t . w_in_e) * (mixing weight), O[row] = h * w_out_e in fp32
+// (the combine adds a token's k rows). Neighbouring wavefronts hold the rows of
+// one group, so W and V rows that several tasks share come through the cache.
+// d = 512 * NCH; each lane owns 16-byte chunk `lane` of every 512-wide column
+// chunk. The row's x, w_in and w_out loads are issued together (up to eight
+// chunks at a time), one memory round trip per row for d <= 4096.
+template <int NCH>
+__global__ __launch_bounds__(256) void k_atomic_rows(const uint16_t *__restrict__ x, const uint16_t *__restrict__ W,
+                                                     const uint16_t *__restrict__ V, const int32_t *__restrict__ perm,
+                                                     const int32_t *__restrict__ idx, const float *__restrict__ wrow,
+                                                     int P, int k, float *__restrict__ O) {
+    constexpr int d = NCH * 512, CB = NCH < 8 ? NCH : 8;
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= P) return;   // uniform per wave
+    const int pair = perm[row];
+    const int t = pair / k, e = idx[pair];
+    const float wt = wrow[row];
+    const uint16_t *xr = x + (size_t)t * d + lane * 8, *wi = W + (size_t)e * d + lane * 8;
+    const uint16_t *wo = V + (size_t)e * d + lane * 8;
+    float *orow = O + (size_t)row * d + lane * 8;
+    if constexpr (NCH == CB) {
+        uint4 xv[NCH], wv[NCH], vv[NCH];
+#pragma unroll
+        for (int c = 0; c < NCH; c++) {
+            xv[c] = gload16(xr + c * 512);
+            wv[c] = gload16(wi + c * 512);
         }
-        const float g = silu_mul(wave_sum_f32(acc), wrow[row]);
-        float *orow = O + (size_t)row * d;
-        for (int c = lane * 8; c < d; c += 512) {
-            const uint4 vv = gload16(wo + c);
-            const uint32_t vu[4] = {vv.x, vv.y, vv.z, vv.w};
-            float4 lo, hi;
-            lo.x = g * bf16f(vu[0] & 0xFFFFu); lo.y = g * bf16f(vu[0] >> 16);
-            lo.z = g * bf16f(vu[1] & 0xFFFFu); lo.w = g * bf16f(vu[1] >> 16);
-            hi.x = g * bf16f(vu[2] & 0xFFFFu); hi.y = g * bf16f(vu[2] >> 16);
-            hi.z = g * bf16f(vu[3] & 0xFFFFu); hi.w = g * bf16f(vu[3] >> 16);
-            *reinterpret_cast<float4 *>(orow + c) = lo;
-            *reinterpret_cast<float4 *>(orow + c + 4) = hi;
+#pragma unroll
+        for (int c = 0; c < NCH; c++) vv[c] = gload16(wo + c * 512);
+        float dot = 0.0f;
+#pragma unroll
+        for (int c = 0; c < NCH; c++) dot = dot8_bf16(xv[c], wv[c], dot);
+        const float g = silu_mul(wave_sum_f32(dot), wt);
+#pragma unroll
+        for (int c = 0; c < NCH; c++) store_scaled8(orow + c * 512, g, vv[c]);
+    } else {
+        float dot = 0.0f;
+#pragma unroll
+        for (int c0 = 0; c0 < NCH; c0 += CB) {
+            uint4 xv[CB], wv[CB];
+#pragma unroll
+            for (int c = 0; c < CB; c++)
+                if (c0 + c < NCH) {
+                    xv[c] = gload16(xr + (c0 + c) * 512);
+                    wv[c] = gload16(wi + (c0 + c) * 512);
+                }
+#pragma unroll
+            for (int c = 0; c < CB; c++)
+                if (c0 + c < NCH) dot = dot8_bf16(xv[c], wv[c], dot);
+        }
+        const float g = silu_mul(wave_sum_f32(dot), wt);
+#pragma unroll
+        for (int c0 = 0; c0 < NCH; c0 += CB) {
+            uint4 vv[CB];
+#pragma unroll
+            for (int c = 0; c < CB; c++)
+                if (c0 + c < NCH) vv[c] = gload16(wo + (c0 + c) * 512);
+#pragma unroll
+            for (int c = 0; c < CB; c++)
+                if (c0 + c < NCH) store_scaled8(orow + (c0 + c) * 512, g, vv[c]);
         }
     }
 }
 
 // Token-centric (the scheduling the OmniMoE page replaces, kept as the
-// ablation): one wavefront per token gathers its k experts' W and V rows one
-// after another and accumulates y_t in registers (d <= 8192).
+// ablation): one wavefront per token takes its k experts in slot order and
+// accumulates y_t in registers. Each expert's w_in and w_out rows are loaded
+// together; for d <= 2048 the next expert's rows are loaded while the current
+// one is computed (two register slots).
+template <int NCH>
 __global__ __launch_bounds__(256) void k_atomic_token(const uint16_t *__restrict__ x, const uint16_t *__restrict__ W,
                                                       const uint16_t *__restrict__ V, const int32_t *__restrict__ idx,
-                                                      const float *__restrict__ w, int T, int d, int k,
+                                                      const float *__restrict__ w, int T, int k,
                                                       uint16_t *__restrict__ y) {
-    constexpr int MAXC = 16;   // 512-column chunks per row
+    constexpr int d = NCH * 512;
+    constexpr bool kAhead = NCH <= 4;
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= T) return;
-    const int nch = d / 512;
-    const uint16_t *xr = x + (size_t)t * d;
-    float acc[MAXC][8];
+    if (t >= T) return;   // uniform per wave
+    // lane j < k holds slot j's expert and weight (k <= 8)
+    const int my_e = lane < k ? idx[(size_t)t * k + lane] : 0;
+    const float my_w = lane < k ? w[(size_t)t * k + lane] : 0.0f;
+    const uint16_t *xr = x + (size_t)t * d + lane * 8;
+    uint4 xv[NCH];
 #pragma unroll
-    for (int c = 0; c < MAXC; c++)
+    for (int c = 0; c < NCH; c++) xv[c] = gload16(xr + c * 512);
+    float acc[NCH][8];
+#pragma unroll
+    for (int c = 0; c < NCH; c++)
 #pragma unroll
         for (int q = 0; q < 8; q++) acc[c][q] = 0.0f;
-    for (int j = 0; j < k; j++) {
-        const int e = idx[(size_t)t * k + j];
-        const uint16_t *wi = W + (size_t)e * d, *wo = V + (size_t)e * d;
+    auto load = [&](int j, uint4 (&wv)[NCH], uint4 (&vv)[NCH]) {
+        const int e = __builtin_amdgcn_readlane(my_e, j);
+        const uint16_t *wi = W + (size_t)e * d + lane * 8, *wo = V + (size_t)e * d + lane * 8;
+#pragma unroll
+        for (int c = 0; c < NCH; c++) {
+            wv[c] = gload16(wi + c * 512);
+            vv[c] = gload16(wo + c * 512);
+        }
+    };
+    auto expert = [&](int j, const uint4 (&wv)[NCH], const uint4 (&vv)[NCH]) {
         float dot = 0.0f;
 #pragma unroll
-        for (int c = 0; c < MAXC; c++) {
-            if (c >= nch) break;
-            const uint4 xv = gload16(xr + c * 512 + lane * 8), wv = gload16(wi + c * 512 + lane * 8);
-            const uint32_t xu[4] = {xv.x, xv.y, xv.z, xv.w}, wu[4] = {wv.x, wv.y, wv.z, wv.w};
+        for (int c = 0; c < NCH; c++) dot = dot8_bf16(xv[c], wv[c], dot);
+        const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_w), j));
+        const float g = silu_mul(wave_sum_f32(dot), wj);
 #pragma unroll
-            for (int h = 0; h < 4; h++) {
-                dot = fmaf(bf16f(xu[h] & 0xFFFFu), bf16f(wu[h] & 0xFFFFu), dot);
-                dot = fmaf(bf16f(xu[h] >> 16), bf16f(wu[h] >> 16), dot);
-            }
-        }
-        const float g = silu_mul(wave_sum_f32(dot), w[(size_t)t * k + j]);
-#pragma unroll
-        for (int c = 0; c < MAXC; c++) {
-            if (c >= nch) break;
-            const uint4 vv = gload16(wo + c * 512 + lane * 8);
-            const uint32_t vu[4] = {vv.x, vv.y, vv.z, vv.w};
+        for (int c = 0; c < NCH; c++) {
+            const uint32_t vu[4] = {vv[c].x, vv[c].y, vv[c].z, vv[c].w};
 #pragma unroll
             for (int h = 0; h < 4; h++) {
                 acc[c][2 * h] += g * bf16f(vu[h] & 0xFFFFu);
                 acc[c][2 * h + 1] += g * bf16f(vu[h] >> 16);
             }
         }
-    }
+    };
+    if constexpr (kAhead) {
+        uint4 wv[2][NCH], vv[2][NCH];
+        load(0, wv[0], vv[0]);
 #pragma unroll
-    for (int c = 0; c < MAXC; c++) {
-        if (c >= nch) break;
+        for (int j = 0; j < 8; j++) {   // k <= 8; unrolled so the slots are static
+            if (j >= k) break;
+            if (j + 1 < k) load(j + 1, wv[(j + 1) & 1], vv[(j + 1) & 1]);
+            expert(j, wv[j & 1], vv[j & 1]);
+        }
+    } else {
+        for (int j = 0; j < k; j++) {
+            uint4 wv[NCH], vv[NCH];
+            load(j, wv, vv);
+            expert(j, wv, vv);
+        }
+    }
+    uint16_t *yr = y + (size_t)t * d + lane * 8;
+#pragma unroll
+    for (int c = 0; c < NCH; c++) {
         uint4 out;
         out.x = (uint32_t)to_bf16(acc[c][0]) | ((uint32_t)to_bf16(acc[c][1]) << 16);
         out.y = (uint32_t)to_bf16(acc[c][2]) | ((uint32_t)to_bf16(acc[c][3]) << 16);
         out.z = (uint32_t)to_bf16(acc[c][4]) | ((uint32_t)to_bf16(acc[c][5]) << 16);
         out.w = (uint32_t)to_bf16(acc[c][6]) | ((uint32_t)to_bf16(acc[c][7]) << 16);
-        *reinterpret_cast<uint4 *>(y + (size_t)t * d + c * 512 + lane * 8) = out;
+        *reinterpret_cast<uint4 *>(yr + c * 512) = out;
     }
 }
 
@@ -1964,28 +2033,45 @@ hipError_t launch_combine(const float *O, const int32_t *inv, int T, int d, int 
     return hipGetLastError();
 }
 
-hipError_t launch_cart_topk(const float *lr, const float *lc, int T, int Nr, int Nc, int k, int B, int32_t *idx,
-                            float *w, int32_t *gidx, hipStream_t s) {
+hipError_t launch_cart_topk(const float *logits, int T, int Nr, int Nc, int k, int B, int32_t *idx, float *w,
+                            int32_t *gidx, hipStream_t s) {
     const dim3 grid((T + 3) / 4);
     const int n = Nr > Nc ? Nr : Nc;
-    if (n <= 64) hipLaunchKernelGGL(k_cart_topk<1>, grid, dim3(256), 0, s, lr, lc, T, Nr, Nc, k, B, idx, w, gidx);
-    else if (n <= 256) hipLaunchKernelGGL(k_cart_topk<4>, grid, dim3(256), 0, s, lr, lc, T, Nr, Nc, k, B, idx, w, gidx);
-    else hipLaunchKernelGGL(k_cart_topk<16>, grid, dim3(256), 0, s, lr, lc, T, Nr, Nc, k, B, idx, w, gidx);
+    if (n <= 64) hipLaunchKernelGGL(k_cart_topk<1>, grid, dim3(256), 0, s, logits, T, Nr, Nc, k, B, idx, w, gidx);
+    else if (n <= 256) hipLaunchKernelGGL(k_cart_topk<4>, grid, dim3(256), 0, s, logits, T, Nr, Nc, k, B, idx, w, gidx);
+    else hipLaunchKernelGGL(k_cart_topk<16>, grid, dim3(256), 0, s, logits, T, Nr, Nc, k, B, idx, w, gidx);
     return hipGetLastError();
 }
 
-hipError_t launch_atomic_tiles(const uint16_t *x, const uint16_t *W, const uint16_t *V, const Tile *tiles,
-                               const int32_t *num_tiles, int max_tiles, const int32_t *perm, const int32_t *idx,
-                               const float *wrow, int d, int k, float *O, hipStream_t s) {
-    hipLaunchKernelGGL(k_atomic_tile, dim3(max_tiles), dim3(256), 0, s, x, W, V, tiles, num_tiles, perm, idx, wrow, d,
-                       k, O);
+// d = 512 * NCH with 1 <= NCH <= 16 (checked by the caller)
+#define QMOE_NCH_CASES(F) \
+    F(1) F(2) F(3) F(4) F(5) F(6) F(7) F(8) F(9) F(10) F(11) F(12) F(13) F(14) F(15) F(16)
+
+hipError_t launch_atomic_rows(const uint16_t *x, const uint16_t *W, const uint16_t *V, const int32_t *perm,
+                              const int32_t *idx, const float *wrow, int P, int d, int k, float *O, hipStream_t s) {
+    const dim3 grid((P + 3) / 4);
+    switch (d / 512) {
+#define QMOE_ROWS_CASE(n) \
+    case n: hipLaunchKernelGGL(k_atomic_rows<n>, grid, dim3(256), 0, s, x, W, V, perm, idx, wrow, P, k, O); break;
+        QMOE_NCH_CASES(QMOE_ROWS_CASE)
+#undef QMOE_ROWS_CASE
+    default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_atomic_token(const uint16_t *x, const uint16_t *W, const uint16_t *V, const int32_t *idx,
                                const float *w, int T, int d, int k, uint16_t *y, hipStream_t s) {
-    hipLaunchKernelGGL(k_atomic_token, dim3((T + 3) / 4), dim3(256), 0, s, x, W, V, idx, w, T, d, k, y);
+    const dim3 grid((T + 3) / 4);
+    switch (d / 512) {
+#define QMOE_TOKEN_CASE(n) \
+    case n: hipLaunchKernelGGL(k_atomic_token<n>, grid, dim3(256), 0, s, x, W, V, idx, w, T, k, y); break;
+        QMOE_NCH_CASES(QMOE_TOKEN_CASE)
+#undef QMOE_TOKEN_CASE
+    default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
+#undef QMOE_NCH_CASES
 
 }  // namespace qmoe

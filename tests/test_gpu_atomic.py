@@ -83,7 +83,18 @@ def test_atomic_schedules_timed(nr, nc):
         e1.record()
         e1.synchronize()
         res.setdefault(name, []).append(e0.elapsed_time(e1) / 10 * 1e3)
+    # algorithmic bytes of the expert kernels: x, y, and every selected
+    # expert's w_in and w_out rows once; the expert-centric kernel also writes
+    # the fp32 task rows that the combine reads back
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    layer.forward(x, y=y, schedule=SCHEDULES["token"], route={"topk_idx": idx})
+    torch.cuda.synchronize()
     layer.close()
+    uniq = int(torch.unique(idx).numel())
+    xy, rows_w = 2 * T * d * 2, uniq * 2 * d * 2
+    print(f"[atomic] {nr}x{nc} grid: {uniq} distinct experts selected; algorithmic MB: "
+          f"token kernel {(xy + rows_w) / 1e6:.1f}, expert-row kernel {(T * d * 2 + rows_w + T * k * d * 4) / 1e6:.1f}, "
+          f"combine {(T * k * d * 4 + T * d * 2) / 1e6:.1f}", flush=True)
     for name, v in res.items():
         us = min(v)
         print(f"[atomic] {nr}x{nc} grid, {name}-centric: {us:.1f} us per forward, {T / us:.2f} M tokens/s",
