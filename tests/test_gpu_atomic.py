@@ -23,7 +23,10 @@ SCHEDULES = {"expert": QMOE_SCHEDULE_EXPERT_CENTRIC, "token": QMOE_SCHEDULE_TOKE
 
 @pytest.mark.parametrize("schedule", ["expert", "token"])
 @pytest.mark.parametrize("T,d,nr,nc,k", [(300, 512, 64, 64, 8), (1, 512, 1, 50, 4), (64, 1024, 17, 130, 8),
-                                         (1000, 512, 1024, 2, 3), (257, 512, 8, 8, 1), (40, 2048, 300, 300, 8)])
+                                         (1000, 512, 1024, 2, 3), (257, 512, 8, 8, 1), (40, 2048, 300, 300, 8),
+                                         # wider rows: the token kernel without the look-ahead slot (d > 2048),
+                                         # the row kernel in batches of eight chunks with a tail (d > 4096)
+                                         (50, 3072, 16, 16, 2), (37, 4608, 12, 12, 5), (20, 8192, 3, 40, 8)])
 def test_atomic_layer(schedule, T, d, nr, nc, k):
     print(f"[case] atomic {schedule} T={T} d={d} grid={nr}x{nc} k={k}", flush=True)
     inp = make_atomic_inputs(T, d, nr, nc, seed=T + nr + nc)
