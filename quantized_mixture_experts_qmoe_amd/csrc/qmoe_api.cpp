@@ -911,7 +911,9 @@ int qmoe_atomic_create(const qmoe_atomic_config *cfg, const uint16_t *w_in, cons
     c->cfg = *cfg;
     const size_t d = (size_t)cfg->d_model;
     c->N = cfg->n_rows * cfg->n_cols;
-    c->B = (c->N + 1023) / 1024;          // experts per dispatch group: at most 1024 groups
+    // experts per dispatch group: at most 256 groups, which keeps the one-
+    // workgroup scan of the dispatch short (four threads per group)
+    c->B = (c->N + 255) / 256;
     c->NG = (c->N + c->B - 1) / c->B;
     c->P = cfg->max_tokens * cfg->top_k;
     c->max_tiles = (c->P + kAtomicRows - 1) / kAtomicRows + std::min(c->NG, c->P);
