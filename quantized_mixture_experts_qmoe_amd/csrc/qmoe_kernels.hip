@@ -374,8 +374,56 @@ __device__ __forceinline__ float key_value(uint64_t key) {
 }
 __device__ __forceinline__ int key_expert(uint64_t key) { return (int)~(uint32_t)key; }
 
-// Top-k of one token by one wavefront: k rounds of a wave-wide key maximum;
-// lane j ends holding slot j. Weights: softmax over the k selected logits
+// The same order on the value alone: an order-preserving 32-bit image of a
+// finite fp32 value (+0.0 and -0.0 equal); every image is above 0, which marks
+// an empty or taken entry.
+__device__ __forceinline__ uint32_t ord_u32(float v) {
+    const uint32_t u = __float_as_uint(v + 0.0f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float ord_value(uint32_t u) {
+    return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+}
+// lanes without a source read 0, which is below every image (the step then
+// keeps the lane's own value); this form lets the shift fold into the max
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t max_step32(uint32_t v) {
+    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, true);
+    return o > v ? o : v;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max_step32<kDppShr1, 0xF>(v);
+    v = max_step32<kDppShr2, 0xF>(v);
+    v = max_step32<kDppShr4, 0xF>(v);
+    v = max_step32<kDppShr8, 0xF>(v);
+    v = max_step32<kDppBcast15, 0xA>(v);
+    v = max_step32<kDppBcast31, 0xC>(v);
+    return __builtin_amdgcn_readlane(v, 63);
+}
+// One selection round over entries hv[i] of index lane + 64 i: the largest
+// value, ties to the lowest index (the first entry slot i with a match, then
+// its lowest lane, from ballots). Takes the winner out (sets it to 0) and
+// returns its index (wave-uniform); vmax receives its value image.
+template <int EPL>
+__device__ __forceinline__ int wave_take_max(uint32_t (&hv)[EPL], int lane, uint32_t &vmax) {
+    uint32_t m = hv[0];
+#pragma unroll
+    for (int i = 1; i < EPL; i++) m = hv[i] > m ? hv[i] : m;
+    vmax = wave_max_u32(m);
+    int win = -1;
+#pragma unroll
+    for (int i = 0; i < EPL; i++) {
+        const unsigned long long hit = __ballot(hv[i] == vmax);
+        if (win < 0 && hit) win = 64 * i + __ffsll(hit) - 1;
+    }
+#pragma unroll
+    for (int i = 0; i < EPL; i++)
+        if (lane + 64 * i == win) hv[i] = 0u;
+    return win;
+}
+
+// Top-k of one token by one wavefront: k selection rounds (largest logit,
+// ties to the lower expert index); lane j ends holding slot j. Weights: softmax over the k selected logits
 // (renorm) or the full-softmax probabilities of the selected. Writes
 // idx_out[0..k) and w_out[0..k); returns this lane's expert (slot = lane) or -1
 // for lanes >= k.
@@ -383,28 +431,26 @@ template <int EPL>
 __device__ __forceinline__ int topk_token(const float *__restrict__ lt, int E, int k, int renorm, int lane,
                                           int32_t *__restrict__ idx_out, float *__restrict__ w_out) {
     float v[EPL];
-    uint64_t key[EPL];
+    uint32_t hv[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; i++) {
         const int e = lane + 64 * i;
         v[i] = e < E ? lt[e] : 0.0f;
-        key[i] = e < E ? select_key(v[i], e) : 0ull;
+        hv[i] = e < E ? ord_u32(v[i]) : 0u;
     }
-    uint64_t mine = 0, first = 0;
+    int my_e = -1;
+    uint32_t my_h = 0u, first_h = 0u;
     for (int j = 0; j < k; j++) {
-        uint64_t best = key[0];
-#pragma unroll
-        for (int i = 1; i < EPL; i++) best = key[i] > best ? key[i] : best;
-        const uint64_t wbest = wave_max_u64(best);
-        const int be = key_expert(wbest);
-#pragma unroll
-        for (int i = 0; i < EPL; i++)
-            if (be == lane + 64 * i) key[i] = 0ull;
-        if (lane == j) mine = wbest;
-        if (j == 0) first = wbest;
+        uint32_t vm;
+        const int e = wave_take_max<EPL>(hv, lane, vm);
+        if (lane == j) {
+            my_e = e;
+            my_h = vm;
+        }
+        if (j == 0) first_h = vm;
     }
-    const float vmax = key_value(first);
-    const float ex = lane < k ? expf(key_value(mine) - vmax) : 0.0f;
+    const float vmax = ord_value(first_h);
+    const float ex = lane < k ? expf(ord_value(my_h) - vmax) : 0.0f;
     float part;
     if (renorm) {
         part = ex;
@@ -416,7 +462,6 @@ __device__ __forceinline__ int topk_token(const float *__restrict__ lt, int E, i
     }
     const float denom = wave_sum_f32(part);
     if (lane < k) {
-        const int my_e = key_expert(mine);
         idx_out[lane] = my_e;
         w_out[lane] = ex / denom;
         return my_e;
@@ -1655,22 +1700,17 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ O, co
 // wavefront: lane j < kk returns the j-th, the other lanes -1.
 template <int EPL>
 __device__ __forceinline__ int wave_topk_index(const float *__restrict__ v, int n, int kk, int lane) {
-    uint64_t key[EPL];
+    uint32_t hv[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; i++) {
         const int e = lane + 64 * i;
-        key[i] = e < n ? select_key(v[e], e) : 0ull;
+        hv[i] = e < n ? ord_u32(v[e]) : 0u;
     }
     int mine = -1;
     for (int j = 0; j < kk; j++) {
-        uint64_t best = key[0];
-#pragma unroll
-        for (int i = 1; i < EPL; i++) best = key[i] > best ? key[i] : best;
-        const int be = key_expert(wave_max_u64(best));
-#pragma unroll
-        for (int i = 0; i < EPL; i++)
-            if (be == lane + 64 * i) key[i] = 0ull;
-        if (lane == j) mine = be;
+        uint32_t vm;
+        const int e = wave_take_max<EPL>(hv, lane, vm);
+        if (lane == j) mine = e;
     }
     return mine;
 }
