@@ -301,32 +301,12 @@ __global__ __launch_bounds__(256) void k_router_f32(const uint16_t *__restrict__
 // row-15 and row-31 broadcasts): each step is a VALU op, not an LDS round trip.
 // After the six steps lane 63 holds the result.
 template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ uint32_t dpp_keep(uint32_t v) {   // lanes without a source keep their own value
-    return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROW_MASK, 0xF, false);
-}
-template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ float dpp_zero(float v) {         // lanes without a source read 0
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF, true));
-}
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ uint64_t max_step(uint64_t key) {
-    const uint64_t o = ((uint64_t)dpp_keep<CTRL, ROW_MASK>((uint32_t)(key >> 32)) << 32) | dpp_keep<CTRL, ROW_MASK>((uint32_t)key);
-    return o > key ? o : key;
 }
 constexpr int kDppShr1 = 0x111, kDppShr2 = 0x112, kDppShr4 = 0x114, kDppShr8 = 0x118;
 constexpr int kDppBcast15 = 0x142, kDppBcast31 = 0x143;
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t key) {
-    key = max_step<kDppShr1, 0xF>(key);
-    key = max_step<kDppShr2, 0xF>(key);
-    key = max_step<kDppShr4, 0xF>(key);
-    key = max_step<kDppShr8, 0xF>(key);
-    key = max_step<kDppBcast15, 0xA>(key);
-    key = max_step<kDppBcast31, 0xC>(key);
-    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)key, 63);
-    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(key >> 32), 63);
-    return ((uint64_t)hi << 32) | lo;
-}
 __device__ __forceinline__ float wave_sum_f32(float v) {
     v += dpp_zero<kDppShr1, 0xF>(v);
     v += dpp_zero<kDppShr2, 0xF>(v);
@@ -360,23 +340,9 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
     return v;
 }
 
-// Selection key of (logit, expert): larger logit first, then lower index. The
-// logit is mapped to an order-preserving unsigned integer (+0.0 and -0.0 made
-// equal first); the low word holds ~index. 0 means "no candidate".
-__device__ __forceinline__ uint64_t select_key(float v, int e) {
-    uint32_t u = __float_as_uint(v + 0.0f);
-    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return ((uint64_t)u << 32) | (uint32_t)~(uint32_t)e;
-}
-__device__ __forceinline__ float key_value(uint64_t key) {
-    const uint32_t u = (uint32_t)(key >> 32);
-    return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
-}
-__device__ __forceinline__ int key_expert(uint64_t key) { return (int)~(uint32_t)key; }
-
-// The same order on the value alone: an order-preserving 32-bit image of a
-// finite fp32 value (+0.0 and -0.0 equal); every image is above 0, which marks
-// an empty or taken entry.
+// Selection order: larger logit first, ties to the lower index. Values are
+// compared as an order-preserving 32-bit image of the finite fp32 value (+0.0
+// and -0.0 equal); every image is above 0, which marks an empty or taken entry.
 __device__ __forceinline__ uint32_t ord_u32(float v) {
     const uint32_t u = __float_as_uint(v + 0.0f);
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
@@ -1735,19 +1701,28 @@ __global__ __launch_bounds__(256) void k_cart_topk(const float *__restrict__ log
     const int ra = wave_topk_index<EPL>(lrt, Nr, kr, lane);
     const int cb = wave_topk_index<EPL>(lct, Nc, kc, lane);
     const int a = __shfl(ra, lane / kc), b = __shfl(cb, lane % kc);
-    uint64_t key = 0ull;
-    if (lane < kr * kc) key = select_key(lrt[a] + lct[b], a * Nc + b);
-    uint64_t mine = 0ull, first = 0ull;
+    const bool cand = lane < kr * kc;
+    // candidate pairs are not in index order across lanes: each round takes
+    // the largest score, then among the lanes holding it the lowest flat index
+    // (the largest complement)
+    uint32_t h = 0u;
+    if (cand) h = ord_u32(lrt[a] + lct[b]);
+    const uint32_t nflat = ~(uint32_t)(a * Nc + b);
+    uint32_t mine_h = 0u, mine_n = 0u, first_h = 0u;
     for (int j = 0; j < k; j++) {
-        const uint64_t wb = wave_max_u64(key);
-        if (key == wb) key = 0ull;   // keys are distinct: their low words are distinct indices
-        if (lane == j) mine = wb;
-        if (j == 0) first = wb;
+        const uint32_t vm = wave_max_u32(h);
+        const uint32_t nw = wave_max_u32(h == vm ? nflat : 0u);
+        if (h == vm && nflat == nw) h = 0u;   // the winner: pairs have distinct flat indices
+        if (lane == j) {
+            mine_h = vm;
+            mine_n = nw;
+        }
+        if (j == 0) first_h = vm;
     }
-    const float ex = lane < k ? expf(key_value(mine) - key_value(first)) : 0.0f;
+    const float ex = lane < k ? expf(ord_value(mine_h) - ord_value(first_h)) : 0.0f;
     const float denom = wave_sum_f32(ex);
     if (lane < k) {
-        const int e = key_expert(mine);
+        const int e = (int)~mine_n;
         idx[(size_t)t * k + lane] = e;
         w[(size_t)t * k + lane] = ex / denom;
         gidx[(size_t)t * k + lane] = e / B;
