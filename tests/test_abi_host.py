@@ -114,3 +114,41 @@ def test_null_context_calls(qmoe_lib):
     assert Q.qmoe_profile_enable(None, 1) == Q.QMOE_EINVAL
     assert [Q.qmoe_kernel_name(i) for i in range(Q.QMOE_NUM_KERNELS)][0] == "router"
     assert Q.qmoe_kernel_name(99) == ""
+
+
+def _atomic_cfg(**kw):
+    base = dict(d_model=512, n_rows=4, n_cols=4, top_k=2, max_tokens=16, device=0)
+    base.update(kw)
+    return Q.QmoeAtomicConfig(**base)
+
+
+@pytest.mark.parametrize("kw,rc", [
+    (dict(d_model=0), Q.QMOE_EINVAL),
+    (dict(n_rows=0), Q.QMOE_EINVAL),
+    (dict(max_tokens=0), Q.QMOE_EINVAL),
+    (dict(top_k=0), Q.QMOE_EINVAL),
+    (dict(top_k=17), Q.QMOE_EINVAL),                               # k > N = 16
+    (dict(d_model=768), Q.QMOE_EUNSUPPORTED),                      # not a multiple of 512
+    (dict(d_model=8704), Q.QMOE_EUNSUPPORTED),                     # above 8192
+    (dict(n_rows=1025), Q.QMOE_EUNSUPPORTED),
+    (dict(n_rows=8, n_cols=8, top_k=9), Q.QMOE_EUNSUPPORTED),      # k > 8
+    (dict(max_tokens=(1 << 20) + 1), Q.QMOE_EUNSUPPORTED),
+    (dict(max_tokens=1 << 19, top_k=8), Q.QMOE_EUNSUPPORTED),      # 2^22 task rows
+])
+def test_atomic_create_rejects_bad_configs(qmoe_lib, kw, rc):
+    """The atomic-expert limits of include/qmoe.h, checked before any device
+    call (the weight arrays are never read)."""
+    ctx = C.c_void_p()
+    w = np.zeros(16, np.uint16)
+    p = w.ctypes.data
+    assert Q.qmoe_atomic_create(_atomic_cfg(**kw), p, p, p, p, C.byref(ctx)) == rc
+    assert not ctx.value and Q.qmoe_last_error() != ""
+
+
+def test_atomic_null_arguments(qmoe_lib):
+    ctx = C.c_void_p()
+    assert Q.qmoe_atomic_create(_atomic_cfg(), None, None, None, None, C.byref(ctx)) == Q.QMOE_EINVAL
+    assert "NULL" in Q.qmoe_last_error() and not ctx.value
+    assert Q.qmoe_atomic_forward(None, None, 4, None, Q.QMOE_SCHEDULE_TOKEN_CENTRIC, None, None) == Q.QMOE_EINVAL
+    assert "ctx" in Q.qmoe_last_error()
+    Q.qmoe_atomic_destroy(None)   # no-op
