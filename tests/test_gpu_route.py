@@ -24,6 +24,8 @@ CASES = [  # (T, E, k, kind)
     # one-workgroup path at its limits (T <= 64, E <= 256), the decode shape,
     # and a small batch with too many experts for it
     (64, 256, 8, "equal"), (64, 256, 64, "grid"), (16, 128, 8, "normal"), (40, 300, 8, "grid"),
+    # sixteen entries per lane (E above 512), with heavy ties
+    (300, 1000, 8, "grid"), (100, 1024, 64, "equal"), (257, 1024, 2, "hot"),
 ]
 
 
