@@ -192,6 +192,21 @@ int qmoe_route_topk(qmoe_ctx *ctx, const float *logits, int32_t T, qmoe_route_ou
  *   stream  hipStream_t (NULL = the null stream) */
 int qmoe_forward(qmoe_ctx *ctx, const uint16_t *x, int32_t T, uint16_t *y, qmoe_route_out *dbg, void *stream);
 
+/* qmoe_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc). Same
+ * arguments, kernels and results as qmoe_forward, but the forward's workspace
+ * (logits, routing tables, task list, H, O, row sums) lives in the library's
+ * static per-device scratch array instead of the context's workspace, and the
+ * call allocates nothing (no hipMalloc/hipFree, no events: the context's
+ * kernel timing is not recorded by this call). The array holds 32 MiB per
+ * device for the life of the process; a T whose workspace does not fit
+ * returns QMOE_EUNSUPPORTED (at d_model = 2048, top-8, d_ff = 768 about 400
+ * tokens fit; at d_model = 4096, top-2, d_ff = 14336 about 350). Every call on
+ * one device shares that device's array: calls that overlap on a device (any
+ * context, any stream) race and must be serialised by the caller. Nothing in
+ * the array needs clearing between calls. */
+int qmoe_forward_static(qmoe_ctx *ctx, const uint16_t *x, int32_t T, uint16_t *y, qmoe_route_out *dbg, void *stream);
+
 /* Frees the context and its device memory. NULL is a no-op. The caller must
  * have synchronised every stream that used the context. */
 void qmoe_destroy(qmoe_ctx *ctx);

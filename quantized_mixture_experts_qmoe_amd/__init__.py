@@ -30,7 +30,8 @@ WFORMAT_CODES = {"int8_sym_ch": 0, "int4_asym_g128": 1, "int4_sym_g128": 2, "int
                  "fp8e4m3_ch": 4}
 ROUTER_QUANT_CODES = {"none": 0, "int8": 1, "fp8": 2}
 
-ABI_SYMBOLS = ("qmoe_pack_experts", "qmoe_pack_experts_device", "qmoe_route_topk", "qmoe_forward", "qmoe_destroy",
+ABI_SYMBOLS = ("qmoe_pack_experts", "qmoe_pack_experts_device", "qmoe_route_topk", "qmoe_forward",
+               "qmoe_forward_static", "qmoe_destroy",
                "qmoe_last_error", "qmoe_export_packed", "qmoe_atomic_create", "qmoe_atomic_forward",
                "qmoe_atomic_destroy", "qmoe_profile_enable", "qmoe_profile_read", "qmoe_kernel_name")
 QMOE_SCHEDULE_EXPERT_CENTRIC = 0
@@ -87,6 +88,8 @@ def load() -> C.CDLL:
     L.qmoe_route_topk.argtypes = [P, P, C.c_int32, C.POINTER(QmoeRouteOut), P]
     L.qmoe_forward.restype = C.c_int
     L.qmoe_forward.argtypes = [P, P, C.c_int32, P, C.POINTER(QmoeRouteOut), P]
+    L.qmoe_forward_static.restype = C.c_int
+    L.qmoe_forward_static.argtypes = [P, P, C.c_int32, P, C.POINTER(QmoeRouteOut), P]
     L.qmoe_destroy.restype = None
     L.qmoe_destroy.argtypes = [P]
     L.qmoe_last_error.restype = C.c_char_p
@@ -131,6 +134,10 @@ def qmoe_route_topk(ctx, logits, T: int, out: Optional[QmoeRouteOut], stream) ->
 
 def qmoe_forward(ctx, x, T: int, y, dbg: Optional[QmoeRouteOut], stream) -> int:
     return load().qmoe_forward(ctx, x, T, y, C.byref(dbg) if dbg is not None else None, stream)
+
+
+def qmoe_forward_static(ctx, x, T: int, y, dbg: Optional[QmoeRouteOut], stream) -> int:
+    return load().qmoe_forward_static(ctx, x, T, y, C.byref(dbg) if dbg is not None else None, stream)
 
 
 def qmoe_destroy(ctx) -> None:

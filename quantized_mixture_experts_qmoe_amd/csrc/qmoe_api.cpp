@@ -51,6 +51,18 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 }  // namespace
 
+// Device buffers one forward works in, carved out of a single region: the
+// context's own allocation (sized for max_tokens at pack time) or, for
+// qmoe_forward_static, the library's static per-device scratch array.
+struct QmoeWorkspace {
+    float *logits = nullptr, *wpair = nullptr, *wrow = nullptr;
+    int32_t *idx = nullptr, *chunk_counts = nullptr, *chunk_base = nullptr, *counts = nullptr, *offsets = nullptr;
+    int32_t *perm = nullptr, *inv = nullptr, *num_tiles = nullptr;
+    Tile *tiles = nullptr;
+    uint16_t *H = nullptr;
+    float *O = nullptr, *xsum = nullptr, *xsum_asym = nullptr, *hsum = nullptr;
+};
+
 struct qmoe_ctx {
     qmoe_config cfg{};
     int df = 0;                     // device format of every expert (uniform layers)
@@ -59,7 +71,6 @@ struct qmoe_ctx {
     bool any_group = false, any_8bit = false;
     int fmt_mask = 0;               // bit f: some expert uses device format f
     int32_t *eslot = nullptr;       // per expert: group << 20 | index (mixed layers)
-    float *xsum_asym = nullptr;     // row sums for INT4_ASYM experts when both scales are needed
     int E = 0, S = 0, F = 0, Fs = 0, d = 0, k = 0;
     int maxT = 0;
     // weights
@@ -73,15 +84,9 @@ struct qmoe_ctx {
     float *router_b = nullptr;
     float *router_s = nullptr;      // quantized router: per-expert scale [E]
     bool router_bf16 = true;        // the bf16 MFMA router runs (bf16 weights or quantized codes)
-    // workspace
-    float *logits = nullptr, *wpair = nullptr, *wrow = nullptr;
-    int32_t *idx = nullptr, *chunk_counts = nullptr, *chunk_base = nullptr, *counts = nullptr, *offsets = nullptr;
-    int32_t *perm = nullptr, *inv = nullptr, *num_tiles = nullptr;
-    Tile *tiles = nullptr;
-    uint16_t *H = nullptr;
-    float *O = nullptr, *xsum = nullptr, *hsum = nullptr;
+    // workspace for max_tokens
+    QmoeWorkspace ws;
     int ldh = 0;
-    size_t tiles_cap = 0;
     std::vector<void *> allocs;
     // profiling
     uint32_t prof = 0;   // bit i: time kernel slot i
@@ -253,10 +258,12 @@ hipEvent_t take_event(qmoe_ctx *c) {
 }
 
 // Runs `launch` (returning hipError_t) with optional event timing around it.
+// prof: the kernel slots to time on this call (c->prof, or 0 where the call
+// may create no events).
 template <typename Fn>
-int timed(qmoe_ctx *c, int slot, hipStream_t s, Fn launch) {
+int timed(qmoe_ctx *c, uint32_t prof, int slot, hipStream_t s, Fn launch) {
     hipEvent_t a = nullptr, b = nullptr;
-    const bool on = (c->prof >> slot) & 1u;
+    const bool on = (prof >> slot) & 1u;
     if (on) {
         a = take_event(c);
         b = take_event(c);
@@ -304,26 +311,67 @@ int max_tiles_for(const qmoe_ctx *c, int T, int bm) {
     return (int)((P + bm - 1) / bm + std::min<long>(c->E, P) + (long)c->S * ((T + bm - 1) / bm));
 }
 
+// Carves the workspace of a forward over up to T tokens out of `base` (NULL:
+// only measures) and returns its size in bytes. Every buffer starts on a
+// 256-byte boundary. Nothing in it needs clearing: each forward writes every
+// entry it later reads.
+size_t carve_workspace(const qmoe_ctx *c, size_t T, uint8_t *base, QmoeWorkspace &w) {
+    const size_t P = T * c->k;
+    const size_t nchunks = (P + kDispatchChunk - 1) / kDispatchChunk;
+    const size_t rows_total = P + (size_t)c->S * T;
+    // 16-row tiles give the most tiles of any tile height
+    const size_t tiles_cap = (size_t)max_tiles_for(c, (int)T, 16) + 16;
+    const bool both_sums = ((c->fmt_mask >> fmt_index(DF_I4SYM)) & 1) && ((c->fmt_mask >> fmt_index(DF_I4ASYM)) & 1);
+    size_t cur = 0;
+    auto take = [&](auto *&ptr, size_t bytes) {
+        ptr = base ? reinterpret_cast<std::remove_reference_t<decltype(ptr)>>(base + cur) : nullptr;
+        cur = align256(cur + std::max<size_t>(bytes, 4));
+    };
+    take(w.logits, T * c->E * 4);
+    take(w.wpair, P * 4);
+    take(w.wrow, P * 4);
+    take(w.idx, P * 4);
+    take(w.chunk_counts, nchunks * c->E * 4);
+    take(w.chunk_base, nchunks * c->E * 4);
+    take(w.counts, (size_t)c->E * 4);
+    take(w.offsets, (size_t)(c->E + 1) * 4);
+    take(w.perm, P * 4);
+    take(w.inv, P * 4);
+    take(w.num_tiles, 4);
+    take(w.tiles, tiles_cap * sizeof(Tile));
+    take(w.H, rows_total * c->ldh * 2);
+    take(w.O, rows_total * c->d * 4);
+    take(w.xsum, T * (c->d / 128) * 4);
+    // layers mixing INT4_SYM / INT3 (row sums scaled by -136) with INT4_ASYM (-128)
+    if (both_sums) take(w.xsum_asym, T * (c->d / 128) * 4);
+    else w.xsum_asym = nullptr;
+    take(w.hsum, rows_total * (c->ldh / 128) * 4);
+    return cur;
+}
+
 // Top-k + dispatch shared by route_topk and forward.
-int run_route(qmoe_ctx *c, const float *logits, int T, int bm, int n_shared, hipStream_t s) {
+int run_route(qmoe_ctx *c, const QmoeWorkspace &w, uint32_t prof, const float *logits, int T, int bm, int n_shared,
+              hipStream_t s) {
     const int P = T * c->k;
     if (T <= kSmallRouteMaxT && c->E <= kSmallRouteMaxE)
-        return timed(c, K_TOPKD, s, [&] {
-            return launch_route_small(logits, T, c->E, c->k, c->cfg.renormalize, n_shared, bm, c->idx, c->wpair,
-                                      c->counts, c->offsets, c->tiles, c->num_tiles, c->perm, c->inv, c->wrow, s);
+        return timed(c, prof, K_TOPKD, s, [&] {
+            return launch_route_small(logits, T, c->E, c->k, c->cfg.renormalize, n_shared, bm, w.idx, w.wpair,
+                                      w.counts, w.offsets, w.tiles, w.num_tiles, w.perm, w.inv, w.wrow, s);
         });
     const int nchunks = (P + kDispatchChunk - 1) / kDispatchChunk;
-    int rc = timed(c, K_TOPK, s, [&] { return launch_topk(logits, T, c->E, c->k, c->cfg.renormalize, c->idx, c->wpair, s); });
+    int rc = timed(c, prof, K_TOPK, s,
+                   [&] { return launch_topk(logits, T, c->E, c->k, c->cfg.renormalize, w.idx, w.wpair, s); });
     if (rc) return rc;
-    rc = timed(c, K_DCOUNT, s, [&] { return launch_dispatch_count(c->idx, P, c->E, c->chunk_counts, s); });
+    rc = timed(c, prof, K_DCOUNT, s, [&] { return launch_dispatch_count(w.idx, P, c->E, w.chunk_counts, s); });
     if (rc) return rc;
-    rc = timed(c, K_DSCAN, s, [&] {
-        return launch_dispatch_scan(c->chunk_counts, nchunks, c->E, P, T, n_shared, bm, c->chunk_base, c->counts,
-                                    c->offsets, c->tiles, c->num_tiles, s);
+    rc = timed(c, prof, K_DSCAN, s, [&] {
+        return launch_dispatch_scan(w.chunk_counts, nchunks, c->E, P, T, n_shared, bm, w.chunk_base, w.counts,
+                                    w.offsets, w.tiles, w.num_tiles, s);
     });
     if (rc) return rc;
-    return timed(c, K_DSCATTER, s,
-                 [&] { return launch_dispatch_scatter(c->idx, c->wpair, P, c->E, c->chunk_base, c->perm, c->inv, c->wrow, s); });
+    return timed(c, prof, K_DSCATTER, s, [&] {
+        return launch_dispatch_scatter(w.idx, w.wpair, P, c->E, w.chunk_base, w.perm, w.inv, w.wrow, s);
+    });
 }
 
 int copy_out(void *dst, const void *src, size_t bytes, hipStream_t s) {
@@ -333,14 +381,14 @@ int copy_out(void *dst, const void *src, size_t bytes, hipStream_t s) {
     return QMOE_OK;
 }
 
-int copy_route(qmoe_ctx *c, const qmoe_route_out *o, int T, hipStream_t s) {
+int copy_route(const qmoe_ctx *c, const QmoeWorkspace &w, const qmoe_route_out *o, int T, hipStream_t s) {
     if (!o) return QMOE_OK;
     const size_t P = (size_t)T * c->k;
-    int rc = copy_out(o->topk_idx, c->idx, P * 4, s);
-    if (!rc) rc = copy_out(o->topk_w, c->wpair, P * 4, s);
-    if (!rc) rc = copy_out(o->counts, c->counts, (size_t)c->E * 4, s);
-    if (!rc) rc = copy_out(o->offsets, c->offsets, (size_t)(c->E + 1) * 4, s);
-    if (!rc) rc = copy_out(o->perm, c->perm, P * 4, s);
+    int rc = copy_out(o->topk_idx, w.idx, P * 4, s);
+    if (!rc) rc = copy_out(o->topk_w, w.wpair, P * 4, s);
+    if (!rc) rc = copy_out(o->counts, w.counts, (size_t)c->E * 4, s);
+    if (!rc) rc = copy_out(o->offsets, w.offsets, (size_t)(c->E + 1) * 4, s);
+    if (!rc) rc = copy_out(o->perm, w.perm, P * 4, s);
     return rc;
 }
 
@@ -570,31 +618,13 @@ int pack_layer(const qmoe_config *cfg, const WeightSource &src, const void *w_ro
             rc = fail(QMOE_EHIP, "upload of router bias failed");
     }
 
-    // Workspace sized for max_tokens.
-    const size_t T = (size_t)c->maxT, P = T * c->k;
-    const size_t nchunks = (P + kDispatchChunk - 1) / kDispatchChunk;
-    const size_t rows_total = P + (size_t)c->S * T;
+    // Workspace sized for max_tokens: one allocation, carved.
     c->ldh = std::max(c->F, c->Fs);
-    c->tiles_cap = (size_t)max_tiles_for(c, c->maxT, 16) + 16;
-    if (!rc) rc = dalloc(c, (void **)&c->logits, T * c->E * 4);
-    if (!rc) rc = dalloc(c, (void **)&c->wpair, P * 4);
-    if (!rc) rc = dalloc(c, (void **)&c->wrow, P * 4);
-    if (!rc) rc = dalloc(c, (void **)&c->idx, P * 4);
-    if (!rc) rc = dalloc(c, (void **)&c->chunk_counts, nchunks * c->E * 4);
-    if (!rc) rc = dalloc(c, (void **)&c->chunk_base, nchunks * c->E * 4);
-    if (!rc) rc = dalloc(c, (void **)&c->counts, (size_t)c->E * 4);
-    if (!rc) rc = dalloc(c, (void **)&c->offsets, (size_t)(c->E + 1) * 4);
-    if (!rc) rc = dalloc(c, (void **)&c->perm, P * 4);
-    if (!rc) rc = dalloc(c, (void **)&c->inv, P * 4);
-    if (!rc) rc = dalloc(c, (void **)&c->num_tiles, 256);
-    if (!rc) rc = dalloc(c, (void **)&c->tiles, c->tiles_cap * sizeof(Tile));
-    if (!rc) rc = dalloc(c, (void **)&c->H, rows_total * c->ldh * 2);
-    if (!rc) rc = dalloc(c, (void **)&c->O, rows_total * c->d * 4);
-    if (!rc) rc = dalloc(c, (void **)&c->xsum, T * (c->d / 128) * 4);
-    // layers mixing INT4_SYM / INT3 (row sums scaled by -136) with INT4_ASYM (-128)
-    if (!rc && ((c->fmt_mask >> fmt_index(DF_I4SYM)) & 1) && ((c->fmt_mask >> fmt_index(DF_I4ASYM)) & 1))
-        rc = dalloc(c, (void **)&c->xsum_asym, T * (c->d / 128) * 4);
-    if (!rc) rc = dalloc(c, (void **)&c->hsum, rows_total * (c->ldh / 128) * 4);
+    if (!rc) {
+        uint8_t *wsb = nullptr;
+        rc = dalloc(c, (void **)&wsb, carve_workspace(c, (size_t)c->maxT, nullptr, c->ws));
+        if (!rc) carve_workspace(c, (size_t)c->maxT, wsb, c->ws);
+    }
     if (rc) {
         free_ctx(c);
         return rc;
@@ -649,21 +679,28 @@ int qmoe_route_topk(qmoe_ctx *c, const float *logits, int32_t T, qmoe_route_out 
     if (!logits) return fail(QMOE_EINVAL, "logits is NULL");
     hipStream_t s = (hipStream_t)stream;
     if (hipSetDevice(c->cfg.device) != hipSuccess) return fail(QMOE_EHIP, "hipSetDevice failed");
-    int rc = run_route(c, logits, T, 128, 0, s);
+    int rc = run_route(c, c->ws, c->prof, logits, T, 128, 0, s);
     if (rc) return rc;
-    return copy_route(c, out, T, s);
+    return copy_route(c, c->ws, out, T, s);
 }
 
-int qmoe_forward(qmoe_ctx *c, const uint16_t *x, int32_t T, uint16_t *y, qmoe_route_out *dbg, void *stream) {
-    g_last_error.clear();
+}  // extern "C"
+
+namespace {
+
+int check_forward_args(const qmoe_ctx *c, const uint16_t *x, int32_t T, const uint16_t *y) {
     if (!c) return fail(QMOE_EINVAL, "ctx is NULL");
     if (T < 0 || T > c->maxT) return fail(QMOE_EINVAL, "T=%d outside [0, max_tokens=%d]", T, c->maxT);
     if (T == 0) return QMOE_OK;
     if (!x || !y) return fail(QMOE_EINVAL, "x or y is NULL");
     if ((const void *)x == (const void *)y) return fail(QMOE_EINVAL, "y may not alias x");
-    hipStream_t s = (hipStream_t)stream;
-    if (hipSetDevice(c->cfg.device) != hipSuccess) return fail(QMOE_EHIP, "hipSetDevice failed");
+    return QMOE_OK;
+}
 
+// The forward's launches (router -> top-k/dispatch -> row sums -> grouped
+// gate/up -> grouped down -> combine) on the workspace w.
+int run_forward(qmoe_ctx *c, const QmoeWorkspace &w, uint32_t prof, const uint16_t *x, int32_t T, uint16_t *y,
+                qmoe_route_out *dbg, hipStream_t s) {
     const int P = T * c->k;
     const int bm = rows_per_tile(c, T);
     const int max_tiles = max_tiles_for(c, T, bm);
@@ -681,23 +718,23 @@ int qmoe_forward(qmoe_ctx *c, const uint16_t *x, int32_t T, uint16_t *y, qmoe_ro
     const bool fused_sums = need_sums && c->router_bf16;
     int rc;
     if (!c->router_bf16)
-        rc = timed(c, K_ROUTER, s, [&] {
-            return launch_router_f32(x, (const float *)c->router_w, c->router_b, c->logits, T, c->d, c->E, s);
+        rc = timed(c, prof, K_ROUTER, s, [&] {
+            return launch_router_f32(x, (const float *)c->router_w, c->router_b, w.logits, T, c->d, c->E, s);
         });
     else
-        rc = timed(c, K_ROUTER, s, [&] {
-            return launch_router_bf16(x, (const uint16_t *)c->router_w, c->router_s, c->router_b, c->logits,
-                                      fused_sums ? c->xsum : nullptr, zc, T, c->d, c->E, s);
+        rc = timed(c, prof, K_ROUTER, s, [&] {
+            return launch_router_bf16(x, (const uint16_t *)c->router_w, c->router_s, c->router_b, w.logits,
+                                      fused_sums ? w.xsum : nullptr, zc, T, c->d, c->E, s);
         });
     if (rc) return rc;
-    rc = run_route(c, c->logits, T, bm, c->S, s);
+    rc = run_route(c, w, prof, w.logits, T, bm, c->S, s);
     if (rc) return rc;
     if (need_sums && !fused_sums) {
-        rc = timed(c, K_XSUM, s, [&] { return launch_xsum(x, T, c->d, zc, c->xsum, s); });
+        rc = timed(c, prof, K_XSUM, s, [&] { return launch_xsum(x, T, c->d, zc, w.xsum, s); });
         if (rc) return rc;
     }
     if (need_sums && sym_present && asym_present) {
-        rc = timed(c, K_XSUM, s, [&] { return launch_xsum(x, T, c->d, -128.0f, c->xsum_asym, s); });
+        rc = timed(c, prof, K_XSUM, s, [&] { return launch_xsum(x, T, c->d, -128.0f, w.xsum_asym, s); });
         if (rc) return rc;
     }
 
@@ -708,15 +745,15 @@ int qmoe_forward(qmoe_ctx *c, const uint16_t *x, int32_t T, uint16_t *y, qmoe_ro
         a.gfmt[g] = c->gfmt[g];
     }
     a.eslot = c->eslot;
-    a.tiles = c->tiles;
-    a.num_tiles = c->num_tiles;
-    a.perm = c->perm;
-    a.wrow = c->wrow;
+    a.tiles = w.tiles;
+    a.num_tiles = w.num_tiles;
+    a.perm = w.perm;
+    a.wrow = w.wrow;
     a.x = x;
-    a.xsum = c->xsum;
-    a.H = c->H;
-    a.hsum = c->hsum;
-    a.O = c->O;
+    a.xsum = w.xsum;
+    a.H = w.H;
+    a.hsum = w.hsum;
+    a.O = w.O;
     a.ldh = c->ldh;
     a.d = c->d;
     a.k = c->k;
@@ -731,25 +768,55 @@ int qmoe_forward(qmoe_ctx *c, const uint16_t *x, int32_t T, uint16_t *y, qmoe_ro
     for (int fi = 0; fi < 4; fi++) {
         if (!((c->fmt_mask >> fi) & 1)) continue;
         const int df = c->mixed && bm == 16 ? kDfAllFormats : fmt_of_index(fi);
-        a.xsum = df == DF_I4ASYM && sym_present ? c->xsum_asym : c->xsum;
-        rc = timed(c, K_GEMM13, s, [&] { return launch_gemm13(df, bm, a, max_tiles, maxN13, s); });
+        a.xsum = df == DF_I4ASYM && sym_present ? w.xsum_asym : w.xsum;
+        rc = timed(c, prof, K_GEMM13, s, [&] { return launch_gemm13(df, bm, a, max_tiles, maxN13, s); });
         if (rc) return rc;
         if (one_launch) break;
     }
     for (int fi = 0; fi < 4; fi++) {
         if (!((c->fmt_mask >> fi) & 1)) continue;
         const int df = c->mixed && bm == 16 ? kDfAllFormats : fmt_of_index(fi);
-        rc = timed(c, K_GEMM2, s, [&] { return launch_gemm2(df, bm, a, max_tiles, s); });
+        rc = timed(c, prof, K_GEMM2, s, [&] { return launch_gemm2(df, bm, a, max_tiles, s); });
         if (rc) return rc;
         if (one_launch) break;
     }
-    rc = timed(c, K_COMBINE, s, [&] { return launch_combine(c->O, c->inv, T, c->d, c->k, P, c->S, y, s); });
+    rc = timed(c, prof, K_COMBINE, s, [&] { return launch_combine(w.O, w.inv, T, c->d, c->k, P, c->S, y, s); });
     if (rc) return rc;
     if (dbg) {
-        rc = copy_out(dbg->logits, c->logits, (size_t)T * c->E * 4, s);
-        if (!rc) rc = copy_route(c, dbg, T, s);
+        rc = copy_out(dbg->logits, w.logits, (size_t)T * c->E * 4, s);
+        if (!rc) rc = copy_route(c, w, dbg, T, s);
     }
     return rc;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qmoe_forward(qmoe_ctx *c, const uint16_t *x, int32_t T, uint16_t *y, qmoe_route_out *dbg, void *stream) {
+    g_last_error.clear();
+    int rc = check_forward_args(c, x, T, y);
+    if (rc || T == 0) return rc;
+    if (hipSetDevice(c->cfg.device) != hipSuccess) return fail(QMOE_EHIP, "hipSetDevice failed");
+    return run_forward(c, c->ws, c->prof, x, T, y, dbg, (hipStream_t)stream);
+}
+
+int qmoe_forward_static(qmoe_ctx *c, const uint16_t *x, int32_t T, uint16_t *y, qmoe_route_out *dbg, void *stream) {
+    g_last_error.clear();
+    int rc = check_forward_args(c, x, T, y);
+    if (rc || T == 0) return rc;
+    if (hipSetDevice(c->cfg.device) != hipSuccess) return fail(QMOE_EHIP, "hipSetDevice failed");
+    QmoeWorkspace w;
+    const size_t need = carve_workspace(c, (size_t)T, nullptr, w);
+    if (need > kStaticScratchBytes)
+        return fail(QMOE_EUNSUPPORTED, "T=%d needs %zu bytes of workspace; the static scratch holds %zu", T, need,
+                    kStaticScratchBytes);
+    void *base = nullptr;
+    const hipError_t e = static_scratch(&base);
+    if (e != hipSuccess) return fail(QMOE_EHIP, "static scratch address: %s", hipGetErrorString(e));
+    carve_workspace(c, (size_t)T, static_cast<uint8_t *>(base), w);
+    // no profiling events here: the call creates nothing
+    return run_forward(c, w, 0u, x, T, y, dbg, (hipStream_t)stream);
 }
 
 int qmoe_export_packed(qmoe_ctx *c, int32_t expert, int32_t matrix, int8_t *codes, float *scales, float *zeros) {

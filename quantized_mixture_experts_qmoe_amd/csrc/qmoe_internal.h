@@ -204,6 +204,12 @@ hipError_t launch_combine(const float *O, const int32_t *inv, int T, int d, int 
                           uint16_t *y, hipStream_t s);
 hipError_t launch_xsum(const uint16_t *x, int T, int d, float scale, float *xsum, hipStream_t s);
 
+// Static per-device scratch (qmoe_forward_static): a file-scope device array of
+// kStaticScratchBytes in qmoe_kernels.hip. static_scratch() returns its
+// address on the current device (looked up once per device, then cached).
+constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
+hipError_t static_scratch(void **ptr);
+
 // Atomic experts: Cartesian top-k over logits [T][Nr + Nc] (each token's row
 // logits, then its column logits; k <= 8; Nr, Nc <= 1024), writing idx / w
 // [T][k] and the dispatch key idx / B; the expert-centric kernel (the task rows

@@ -17,6 +17,7 @@
 //   gemm2       grouped down GEMM; the epilogue applies the mixing weight
 //   combine     y_t = sum_j O[row(t, j)] + sum_s O_shared(t), fp32, bf16 out
 #include <hip/hip_runtime.h>
+#include <mutex>
 #include <type_traits>
 
 #include "qmoe_internal.h"
@@ -1895,6 +1896,35 @@ __global__ __launch_bounds__(256) void k_atomic_token(const uint16_t *__restrict
         out.w = (uint32_t)to_bf16(acc[c][6]) | ((uint32_t)to_bf16(acc[c][7]) << 16);
         *reinterpret_cast<uint4 *>(yr + c * 512) = out;
     }
+}
+
+// ---------------------------------------------------------------------------
+// Static scratch for the allocation-free forward
+// ---------------------------------------------------------------------------
+
+// Workspace of qmoe_forward_static. Each device holds its own copy for the
+// life of the process. In host code `scratch` names a host-side stand-in, not
+// device memory: its device address comes from hipGetSymbolAddress, looked up
+// once per device with that device current.
+static __device__ __attribute__((aligned(256))) uint8_t scratch[kStaticScratchBytes];
+
+hipError_t static_scratch(void **ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
 }
 
 // ---------------------------------------------------------------------------
