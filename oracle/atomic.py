@@ -13,7 +13,11 @@ Plain fp64 NumPy, written from the definitions:
 """
 import numpy as np
 
-from quantized_mixture_experts_qmoe_amd.inputs import bf16_bits_to_f32
+
+def bf16_bits_to_f32(b) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) widened exactly to float32: the pattern
+    is the upper half of the float32 pattern."""
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
 def scores(lr: np.ndarray, lc: np.ndarray, dtype=np.float64) -> np.ndarray:

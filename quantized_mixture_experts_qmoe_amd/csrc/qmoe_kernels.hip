@@ -1663,32 +1663,20 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ O, co
 // W, V [N][d], chosen by a Cartesian product router.
 // ---------------------------------------------------------------------------
 
-// Indices of the kk largest of v[0..n) (ties to the lower index), one
-// wavefront: lane j < kk returns the j-th, the other lanes -1.
-template <int EPL>
-__device__ __forceinline__ int wave_topk_index(const float *__restrict__ v, int n, int kk, int lane) {
-    uint32_t hv[EPL];
-#pragma unroll
-    for (int i = 0; i < EPL; i++) {
-        const int e = lane + 64 * i;
-        hv[i] = e < n ? ord_u32(v[e]) : 0u;
-    }
-    int mine = -1;
-    for (int j = 0; j < kk; j++) {
-        uint32_t vm;
-        const int e = wave_take_max<EPL>(hv, lane, vm);
-        if (lane == j) mine = e;
-    }
-    return mine;
-}
-
 // Cartesian product routing, one wavefront per token: score(a, b) = l_r[a] +
-// l_c[b] (fp32). The top-k of the N_r x N_c scores lies among the top-min(k,
-// N_r) rows x top-min(k, N_c) columns (a pair outside them has k better pairs
-// in its own column or row), so k rounds over those <= 64 candidates select it;
-// ties go to the lower flat index a * N_c + b. Weights: softmax over the k
-// selected scores. Also writes each task's dispatch key, its expert's group of
-// B consecutive expert ids.
+// l_c[b] in fp32, expert a * N_c + b; the k best scores win, ties to the lower
+// flat index; weights: softmax over the k selected scores. Also writes each
+// task's dispatch key (its expert's group of B consecutive expert ids).
+//
+// fp32 addition is monotone in each operand, so every pair outside the best
+// min(k, N_r) rows R x best min(k, N_c) columns C scores at most the k-th best
+// score s_k among the <= 64 pairs of R x C (k pairs of R x C dominate it in its
+// own column or row). The k rounds over R x C are therefore exact unless an
+// outside pair rounds to exactly s_k and has a lower flat index than a selected
+// pair of score s_k. That needs an outside row a with l_r[a] + max l_c >= s_k
+// or an outside column b with max l_r + l_c[b] >= s_k; only then (exact ties,
+// rare) are the slots of score s_k refilled with the tied pairs of lowest flat
+// index, found row by row in ascending order.
 template <int EPL>
 __global__ __launch_bounds__(256) void k_cart_topk(const float *__restrict__ logits, int T, int Nr, int Nc, int k,
                                                    int B, int32_t *__restrict__ idx, float *__restrict__ w,
@@ -1699,8 +1687,28 @@ __global__ __launch_bounds__(256) void k_cart_topk(const float *__restrict__ log
     // a token's row logits and then its column logits, one row of Nr + Nc
     const float *lrt = logits + (size_t)t * (Nr + Nc), *lct = lrt + Nr;
     const int kr = min(k, Nr), kc = min(k, Nc);
-    const int ra = wave_topk_index<EPL>(lrt, Nr, kr, lane);
-    const int cb = wave_topk_index<EPL>(lct, Nc, kc, lane);
+    // best rows and columns; taken entries' images become 0
+    float vr[EPL], vc[EPL];
+    uint32_t hr[EPL], hc[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; i++) {
+        const int a = lane + 64 * i;
+        vr[i] = a < Nr ? lrt[a] : 0.0f;
+        hr[i] = a < Nr ? ord_u32(vr[i]) : 0u;
+        vc[i] = a < Nc ? lct[a] : 0.0f;
+        hc[i] = a < Nc ? ord_u32(vc[i]) : 0u;
+    }
+    int ra = -1, cb = -1;
+    for (int j = 0; j < kr; j++) {
+        uint32_t vm;
+        const int e = wave_take_max<EPL>(hr, lane, vm);
+        if (lane == j) ra = e;
+    }
+    for (int j = 0; j < kc; j++) {
+        uint32_t vm;
+        const int e = wave_take_max<EPL>(hc, lane, vm);
+        if (lane == j) cb = e;
+    }
     const int a = __shfl(ra, lane / kc), b = __shfl(cb, lane % kc);
     const bool cand = lane < kr * kc;
     // candidate pairs are not in index order across lanes: each round takes
@@ -1709,7 +1717,7 @@ __global__ __launch_bounds__(256) void k_cart_topk(const float *__restrict__ log
     uint32_t h = 0u;
     if (cand) h = ord_u32(lrt[a] + lct[b]);
     const uint32_t nflat = ~(uint32_t)(a * Nc + b);
-    uint32_t mine_h = 0u, mine_n = 0u, first_h = 0u;
+    uint32_t mine_h = 0u, mine_n = 0u, first_h = 0u, sk = 0u;
     for (int j = 0; j < k; j++) {
         const uint32_t vm = wave_max_u32(h);
         const uint32_t nw = wave_max_u32(h == vm ? nflat : 0u);
@@ -1719,6 +1727,48 @@ __global__ __launch_bounds__(256) void k_cart_topk(const float *__restrict__ log
             mine_n = nw;
         }
         if (j == 0) first_h = vm;
+        sk = vm;
+    }
+    // can a pair outside R x C reach s_k? (only by an exact tie)
+    const float lrmax = lrt[__shfl(ra, 0)], lcmax = lct[__shfl(cb, 0)];
+    bool reach = false;
+#pragma unroll
+    for (int i = 0; i < EPL; i++) {
+        const int e = lane + 64 * i;
+        reach = reach || (e < Nr && hr[i] != 0u && ord_u32(vr[i] + lcmax) >= sk);
+        reach = reach || (e < Nc && hc[i] != 0u && ord_u32(lrmax + vc[i]) >= sk);
+    }
+    if (__ballot(reach) != 0ull) {   // wave-uniform
+        // slots [keep, k) hold score s_k: refill them with the tied pairs of
+        // lowest flat index over every row that can reach s_k (the taken rows
+        // and the outside rows that passed), rows ascending, columns ascending
+        const int keep = __popcll(__ballot(lane < k && mine_h > sk));
+        const int m = k - keep;
+        int got = 0;
+#pragma unroll
+        for (int i = 0; i < EPL; i++) {
+            const int e = lane + 64 * i;
+            const bool rel = e < Nr && (hr[i] == 0u || ord_u32(vr[i] + lcmax) >= sk);
+            unsigned long long rm = __ballot(rel);
+            while (rm != 0ull && got < m) {
+                const int row = 64 * i + __ffsll(rm) - 1;
+                rm &= rm - 1ull;
+                const float lrow = lrt[row];
+                for (int c0 = 0; c0 < Nc && got < m; c0 += 64) {
+                    const int col = c0 + lane;
+                    unsigned long long tm = __ballot(col < Nc && ord_u32(lrow + lct[col < Nc ? col : 0]) == sk);
+                    while (tm != 0ull && got < m) {
+                        const int cc = c0 + __ffsll(tm) - 1;
+                        tm &= tm - 1ull;
+                        if (lane == keep + got) {
+                            mine_h = sk;
+                            mine_n = ~(uint32_t)(row * Nc + cc);
+                        }
+                        got++;
+                    }
+                }
+            }
+        }
     }
     const float ex = lane < k ? expf(ord_value(mine_h) - ord_value(first_h)) : 0.0f;
     const float denom = wave_sum_f32(ex);

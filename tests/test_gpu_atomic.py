@@ -64,6 +64,55 @@ def test_atomic_layer(schedule, T, d, nr, nc, k):
     assert_output_close(bf16_tensor_to_f64(y), y_ref, f"atomic {schedule}", own >= 0.75 * MAX_ABS_RMS)
 
 
+@pytest.mark.parametrize("schedule", ["expert", "token"])
+def test_cartesian_topk_exact_rounding_ties(schedule):
+    """Scores that round to the same fp32 value although their row logits
+    differ: the selection must still follow the definition (equal scores go to
+    the lower flat index), also where the tied pair lies outside the best k
+    rows or columns. Token t routes on one-hot x (position t % 8), so its
+    logits are router entries exactly: row logits 1 + j/128 (half of them fall
+    on a rounding tie at 2^17, where the fp32 spacing is 1/64) and column
+    logits 2^17 + 1024 c. The first token is the smallest case: rows 1.0 and
+    1.0078125, one column 2^17, k = 1, both scores 131073: expert 0 wins."""
+    d, T = 512, 64
+    rng = np.random.default_rng(5)
+
+    def bits(a):
+        return (np.asarray(a, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+    for nr, nc, k in [(2, 1, 1), (40, 24, 8), (64, 64, 8), (13, 100, 5), (100, 3, 7)]:
+        rr = np.zeros((nr, d), np.float32)
+        rc = np.zeros((nc, d), np.float32)
+        for p in range(8):
+            rr[:, p] = 1.0 + rng.permutation(128)[:nr] / 128.0 if nr > 2 else [1.0, 1.0078125]
+            rc[:, p] = 131072.0 + 1024.0 * rng.integers(0, 4, nc)
+        x = np.zeros((T, d), np.float32)
+        x[np.arange(T), np.arange(T) % 8] = 1.0
+        w_in = make_atomic_inputs(1, d, nr, nc, seed=9).w_in
+        w_out = make_atomic_inputs(1, d, nr, nc, seed=10).w_out
+        print(f"[case] cartesian ties {schedule} grid={nr}x{nc} k={k}", flush=True)
+        layer = AtomicLayer(w_in, w_out, bits(rr), bits(rc), top_k=k, max_tokens=T)
+        route = dict(logits_rows=torch.empty((T, nr), dtype=torch.float32, device="cuda"),
+                     logits_cols=torch.empty((T, nc), dtype=torch.float32, device="cuda"),
+                     topk_idx=torch.empty((T, k), dtype=torch.int32, device="cuda"),
+                     topk_w=torch.empty((T, k), dtype=torch.float32, device="cuda"))
+        layer.forward(to_dev_bf16(bits(x)), schedule=SCHEDULES[schedule], route=route)
+        torch.cuda.synchronize()
+        layer.close()
+        lr, lc = route["logits_rows"].cpu().numpy(), route["logits_cols"].cpu().numpy()
+        assert np.array_equal(lr, rr[:, np.arange(T) % 8].T) and np.array_equal(lc, rc[:, np.arange(T) % 8].T)
+        s32 = A.scores(lr, lc, np.float32)
+        g_idx, g_w, _ = A.topk(s32, k)
+        idx = route["topk_idx"].cpu().numpy()
+        assert np.array_equal(idx, g_idx), (nr, nc, k)
+        assert np.allclose(route["topk_w"].cpu().numpy(), g_w, rtol=0, atol=1e-6)
+        if nr == 2:
+            assert np.all(idx[:, 0] == 0)
+        # the case exercises ties at the k-th score that cross the best rows
+        n_tie = int(sum(np.sum(s32[t] == s32[t, g_idx[t, -1]]) > 1 for t in range(T)))
+        print(f"[routing] tokens with a tie at the k-th score: {n_tie} of {T}", flush=True)
+
+
 @pytest.mark.parametrize("nr,nc", [(256, 256), (64, 64)])
 def test_atomic_schedules_timed(nr, nc):
     """Atomic experts of width 2048, top-8, 8192 tokens, on a 256 x 256 grid
