@@ -197,6 +197,54 @@ def _dptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+def check_tensor(name: str, t, shape, dtype, require_cuda: bool = True) -> None:
+    """Raises ValueError unless t is a contiguous tensor of exactly this shape
+    and dtype (on a GPU when require_cuda): the library reads and writes
+    through raw pointers and cannot see a buffer's extent."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if require_cuda and not t.is_cuda:
+        raise ValueError(f"{name}: must be a CUDA (HIP) tensor")
+
+
+def check_forward_args(cfg, max_tokens: int, x, y=None, route=None, require_cuda: bool = True) -> int:
+    """Shapes of a layer forward's tensors against the layer: x [T][d] bf16
+    with T <= max_tokens, y like x, the route buffers (logits [T][E] fp32,
+    topk_idx / topk_w [T][k], counts [E], offsets [E+1], perm [T*k]). Returns T."""
+    import torch
+    if x.dim() != 2:
+        raise ValueError(f"x: expected a 2-D [T][d_model] tensor, got shape {tuple(x.shape)}")
+    T = x.shape[0]
+    if T > max_tokens:
+        raise ValueError(f"x: T={T} exceeds max_tokens={max_tokens}")
+    check_tensor("x", x, (T, cfg.d), torch.bfloat16, require_cuda)
+    if y is not None:
+        check_tensor("y", y, (T, cfg.d), torch.bfloat16, require_cuda)
+        if y.device != x.device:
+            raise ValueError("y: must be on x's device")
+    if route is not None:
+        check_route(cfg, T, route, require_cuda)
+    return T
+
+
+def check_route(cfg, T: int, route, require_cuda: bool = True) -> None:
+    """Route buffers of T tokens: logits [T][E] fp32, topk_idx / topk_w [T][k],
+    counts [E], offsets [E+1], perm [T*k] (any may be missing or None)."""
+    import torch
+    want = dict(logits=((T, cfg.E), torch.float32), topk_idx=((T, cfg.k), torch.int32),
+                topk_w=((T, cfg.k), torch.float32), counts=((cfg.E,), torch.int32),
+                offsets=((cfg.E + 1,), torch.int32), perm=((T * cfg.k,), torch.int32))
+    for n, t in route.items():
+        if n not in want:
+            raise ValueError(f"route: unknown buffer {n}")
+        if t is not None:
+            check_tensor(f"route[{n}]", t, *want[n], require_cuda)
+
+
 class QMoE:
     """One packed quantized MoE layer on a GPU (owns a qmoe_ctx)."""
 
@@ -272,8 +320,7 @@ class QMoE:
     def forward(self, x, y=None, route=None, stream=None):
         """x: [T][d] bf16 CUDA tensor -> y [T][d] bf16 (allocated if None)."""
         import torch
-        assert x.dtype == torch.bfloat16 and x.is_cuda and x.is_contiguous()
-        T = x.shape[0]
+        T = check_forward_args(self.cfg, self.max_tokens, x, y, route)
         if y is None:
             y = torch.empty_like(x)
         rs = self._route_struct(route)
@@ -283,7 +330,16 @@ class QMoE:
 
     def route_topk(self, logits, route, stream=None):
         """logits: [T][E] fp32 CUDA tensor; fills the route buffers."""
+        import torch
+        if logits.dim() != 2:
+            raise ValueError(f"logits: expected [T][E], got shape {tuple(logits.shape)}")
         T = logits.shape[0]
+        if T > self.max_tokens:
+            raise ValueError(f"logits: T={T} exceeds max_tokens={self.max_tokens}")
+        check_tensor("logits", logits, (T, self.cfg.E), torch.float32)
+        if route is not None:
+            # the logits member is not written by route_topk
+            check_route(self.cfg, T, {n: t for n, t in route.items() if n != "logits"})
         rc = qmoe_route_topk(self.ctx, logits.data_ptr(), T, self._route_struct(route), _stream_handle(stream))
         _check(rc, "qmoe_route_topk")
 
@@ -330,6 +386,7 @@ class AtomicLayer:
         self.n_rows, self.n_cols, self.k = arrs[2].shape[0], arrs[3].shape[0], top_k
         cfg = QmoeAtomicConfig(d_model=self.d, n_rows=self.n_rows, n_cols=self.n_cols, top_k=top_k,
                                max_tokens=max_tokens, device=device)
+        self.max_tokens = max_tokens
         ctx = C.c_void_p()
         _check(qmoe_atomic_create(cfg, *[a.ctypes.data for a in arrs], C.byref(ctx)), "qmoe_atomic_create")
         self.ctx = ctx
@@ -349,7 +406,7 @@ class AtomicLayer:
         """x: [T][d] bf16 CUDA tensor -> y; route: optional dict of CUDA tensors
         logits_rows, logits_cols, topk_idx, topk_w to fill."""
         import torch
-        assert x.dtype == torch.bfloat16 and x.is_cuda and x.is_contiguous()
+        self.check_args(x, y, route)
         if y is None:
             y = torch.empty_like(x)
         dbg = None
@@ -360,3 +417,26 @@ class AtomicLayer:
                                  _stream_handle(stream))
         _check(rc, "qmoe_atomic_forward")
         return y
+
+    def check_args(self, x, y=None, route=None, require_cuda: bool = True) -> int:
+        """x [T][d] bf16 with T <= max_tokens, y like x, route buffers
+        logits_rows [T][n_rows], logits_cols [T][n_cols] fp32, topk_idx [T][k]
+        int32, topk_w [T][k] fp32. Raises ValueError; returns T."""
+        import torch
+        if x.dim() != 2:
+            raise ValueError(f"x: expected a 2-D [T][d_model] tensor, got shape {tuple(x.shape)}")
+        T = x.shape[0]
+        if T > self.max_tokens:
+            raise ValueError(f"x: T={T} exceeds max_tokens={self.max_tokens}")
+        check_tensor("x", x, (T, self.d), torch.bfloat16, require_cuda)
+        if y is not None:
+            check_tensor("y", y, (T, self.d), torch.bfloat16, require_cuda)
+        if route is not None:
+            want = dict(logits_rows=((T, self.n_rows), torch.float32), logits_cols=((T, self.n_cols), torch.float32),
+                        topk_idx=((T, self.k), torch.int32), topk_w=((T, self.k), torch.float32))
+            for n, t in route.items():
+                if n not in want:
+                    raise ValueError(f"route: unknown buffer {n}")
+                if t is not None:
+                    check_tensor(f"route[{n}]", t, *want[n], require_cuda)
+        return T

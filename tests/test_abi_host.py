@@ -152,3 +152,47 @@ def test_atomic_null_arguments(qmoe_lib):
     assert Q.qmoe_atomic_forward(None, None, 4, None, Q.QMOE_SCHEDULE_TOKEN_CENTRIC, None, None) == Q.QMOE_EINVAL
     assert "ctx" in Q.qmoe_last_error()
     Q.qmoe_atomic_destroy(None)   # no-op
+
+
+def test_binding_rejects_mismatched_tensors():
+    """The binding checks every tensor against the layer before a pointer
+    reaches the C ABI (which cannot see a buffer's extent)."""
+    import torch
+    from quantized_mixture_experts_qmoe_amd import AtomicLayer, check_forward_args, check_route
+    from quantized_mixture_experts_qmoe_amd.inputs import CONFIGS
+    cfg = CONFIGS["qwen3_decode"]
+    T = 16
+    bf = torch.bfloat16
+
+    def ok(**kw):
+        return check_forward_args(cfg, 32, require_cuda=False, **kw)
+
+    x = torch.zeros((T, cfg.d), dtype=bf)
+    assert ok(x=x, y=torch.zeros_like(x)) == T
+    bad = [dict(x=torch.zeros((T, cfg.d + 8), dtype=bf)),                      # wrong width
+           dict(x=torch.zeros((T * cfg.d,), dtype=bf)),                          # not 2-D
+           dict(x=torch.zeros((33, cfg.d), dtype=bf)),                           # T > max_tokens
+           dict(x=torch.zeros((T, cfg.d), dtype=torch.float32)),                 # dtype
+           dict(x=torch.zeros((cfg.d, T), dtype=bf).t()),                        # not contiguous
+           dict(x=x, y=torch.zeros((T - 1, cfg.d), dtype=bf)),                   # y too small
+           dict(x=x, route=dict(logits=torch.zeros((T, cfg.E - 1)))),            # route shapes
+           dict(x=x, route=dict(topk_idx=torch.zeros((T, cfg.k), dtype=torch.int64))),
+           dict(x=x, route=dict(perm=torch.zeros((T * cfg.k - 1,), dtype=torch.int32))),
+           dict(x=x, route=dict(offsets=torch.zeros((cfg.E,), dtype=torch.int32))),
+           dict(x=x, route=dict(bogus=torch.zeros(1)))]
+    for kw in bad:
+        with pytest.raises(ValueError):
+            ok(**kw)
+    with pytest.raises(ValueError):                                              # CPU tensor, GPU required
+        check_forward_args(cfg, 32, x)
+    check_route(cfg, T, dict(counts=torch.zeros((cfg.E,), dtype=torch.int32)), require_cuda=False)
+
+    layer = AtomicLayer.__new__(AtomicLayer)   # shapes only: no context is created
+    layer.d, layer.n_rows, layer.n_cols, layer.k, layer.max_tokens = 512, 4, 6, 3, 10
+    xa = torch.zeros((5, 512), dtype=bf)
+    assert layer.check_args(xa, route=dict(logits_rows=torch.zeros((5, 4))), require_cuda=False) == 5
+    for args in [(torch.zeros((5, 256), dtype=bf),), (torch.zeros((11, 512), dtype=bf),),
+                 (xa, torch.zeros((5, 511), dtype=bf)), (xa, None, dict(logits_cols=torch.zeros((5, 4)))),
+                 (xa, None, dict(topk_idx=torch.zeros((5, 3), dtype=torch.float32)))]:
+        with pytest.raises(ValueError):
+            layer.check_args(*args, require_cuda=False)

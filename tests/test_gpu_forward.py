@@ -193,8 +193,13 @@ def test_zero_tokens_and_limits(oracle_mod):
     layer = QMoE(inp, max_tokens=8)
     y = torch.empty((0, cfg.d), dtype=torch.bfloat16, device="cuda")
     layer.forward(torch.empty((0, cfg.d), dtype=torch.bfloat16, device="cuda"), y=y)   # no-op
-    with pytest.raises(QmoeError):
-        layer.forward(to_dev_bf16(make_x(cfg, 9, seed=1)))                              # T > max_tokens
+    x9 = to_dev_bf16(make_x(cfg, 9, seed=1))
+    with pytest.raises(ValueError):                                                      # T > max_tokens
+        layer.forward(x9)
+    # the C ABI's own check behind the binding's
+    import quantized_mixture_experts_qmoe_amd as Q
+    y9 = torch.empty_like(x9)
+    assert Q.qmoe_forward(layer.ctx, x9.data_ptr(), 9, y9.data_ptr(), None, None) == Q.QMOE_EINVAL
 
 
 def test_forward_at_the_token_limit(oracle_mod):
