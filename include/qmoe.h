@@ -293,6 +293,19 @@ int qmoe_profile_enable(qmoe_ctx *ctx, int32_t slot_mask);
 int qmoe_profile_read(qmoe_ctx *ctx, double *total_ms, int64_t *launches);
 const char *qmoe_kernel_name(int32_t slot);
 
+/* Shader clock probe (for measurement): launches one wavefront on `stream`
+ * that, until duration_ticks of the device's constant-rate real-time counter
+ * have passed (hipDeviceAttributeWallClockRate kHz; a bounded wait, so it
+ * always ends), writes up to max_samples pairs (shader-cycle counter,
+ * real-time counter) about period_ticks apart to samples (device memory,
+ * uint64 [max_samples][2]; entries past the last sample are left as they
+ * were). Launched on a second stream beside a timed region, the ratio of
+ * cycle and tick differences over a window, times the real-time rate, is the
+ * shader clock during that window. *wall_khz (host) receives the real-time
+ * counter's rate in kHz. Asynchronous; runs on the current device. */
+int qmoe_clock_probe(void *stream, int64_t duration_ticks, int64_t period_ticks, int32_t max_samples,
+                     uint64_t *samples, int64_t *wall_khz);
+
 #ifdef __cplusplus
 }
 #endif

@@ -33,7 +33,8 @@ ROUTER_QUANT_CODES = {"none": 0, "int8": 1, "fp8": 2}
 ABI_SYMBOLS = ("qmoe_pack_experts", "qmoe_pack_experts_device", "qmoe_route_topk", "qmoe_forward",
                "qmoe_forward_static", "qmoe_destroy",
                "qmoe_last_error", "qmoe_export_packed", "qmoe_atomic_create", "qmoe_atomic_forward",
-               "qmoe_atomic_destroy", "qmoe_profile_enable", "qmoe_profile_read", "qmoe_kernel_name")
+               "qmoe_atomic_destroy", "qmoe_profile_enable", "qmoe_profile_read", "qmoe_kernel_name",
+               "qmoe_clock_probe")
 QMOE_SCHEDULE_EXPERT_CENTRIC = 0
 QMOE_SCHEDULE_TOKEN_CENTRIC = 1
 
@@ -102,6 +103,8 @@ def load() -> C.CDLL:
     L.qmoe_profile_read.argtypes = [P, P, P]
     L.qmoe_kernel_name.restype = C.c_char_p
     L.qmoe_kernel_name.argtypes = [C.c_int32]
+    L.qmoe_clock_probe.restype = C.c_int
+    L.qmoe_clock_probe.argtypes = [P, C.c_int64, C.c_int64, C.c_int32, P, P]
     _lib = L
     return L
 
@@ -162,6 +165,10 @@ def qmoe_profile_read(ctx, total_ms, launches) -> int:
 
 def qmoe_kernel_name(slot: int) -> str:
     return load().qmoe_kernel_name(slot).decode()
+
+
+def qmoe_clock_probe(stream, duration_ticks: int, period_ticks: int, max_samples: int, samples, wall_khz) -> int:
+    return load().qmoe_clock_probe(stream, duration_ticks, period_ticks, max_samples, samples, wall_khz)
 
 
 def _check(rc: int, where: str) -> None:

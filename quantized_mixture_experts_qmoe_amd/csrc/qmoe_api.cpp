@@ -906,6 +906,20 @@ int qmoe_profile_read(qmoe_ctx *c, double *total_ms, int64_t *launches) {
     return QMOE_OK;
 }
 
+int qmoe_clock_probe(void *stream, int64_t duration_ticks, int64_t period_ticks, int32_t max_samples,
+                     uint64_t *samples, int64_t *wall_khz) {
+    if (!samples || !wall_khz || duration_ticks <= 0 || period_ticks <= 0 || max_samples < 1)
+        return fail(QMOE_EINVAL, "clock probe: bad arguments");
+    int dev = 0, khz = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess)
+        return fail(QMOE_EHIP, "clock probe: wall clock rate unavailable");
+    *wall_khz = khz;
+    const hipError_t e = launch_clock_probe(reinterpret_cast<unsigned long long *>(samples),
+                                            (unsigned long long)duration_ticks, (unsigned long long)period_ticks,
+                                            max_samples, (hipStream_t)stream);
+    return e == hipSuccess ? QMOE_OK : fail(QMOE_EHIP, "clock probe launch failed: %s", hipGetErrorString(e));
+}
+
 // ---- Atomic experts ---------------------------------------------------------
 
 struct qmoe_atomic_ctx {

@@ -204,6 +204,10 @@ hipError_t launch_combine(const float *O, const int32_t *inv, int T, int d, int 
                           uint16_t *y, hipStream_t s);
 hipError_t launch_xsum(const uint16_t *x, int T, int d, float scale, float *xsum, hipStream_t s);
 
+// Shader clock probe: one wave sampling (shader cycles, real-time ticks) pairs.
+hipError_t launch_clock_probe(unsigned long long *out, unsigned long long duration, unsigned long long period,
+                              int max_samples, hipStream_t s);
+
 // Static per-device scratch (qmoe_forward_static): a file-scope device array of
 // kStaticScratchBytes in qmoe_kernels.hip. static_scratch() returns its
 // address on the current device (looked up once per device, then cached).

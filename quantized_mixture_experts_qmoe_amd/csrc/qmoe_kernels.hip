@@ -1949,6 +1949,42 @@ __global__ __launch_bounds__(256) void k_atomic_token(const uint16_t *__restrict
 }
 
 // ---------------------------------------------------------------------------
+// Shader clock probe (measurement)
+// ---------------------------------------------------------------------------
+
+// One wave that samples the shader-cycle counter (s_memtime) and the
+// constant-rate real-time counter (s_memrealtime) every ~`period` real-time
+// ticks until `duration` ticks have passed (a bounded wait on the wall clock:
+// it always ends), writing (cycles, ticks) pairs to out[2 i], out[2 i + 1] for
+// i < max_samples. Run beside other work on another stream, the cycle/tick
+// ratio over a window gives the shader clock during that window.
+__global__ __launch_bounds__(64) void k_clock_probe(unsigned long long *out, unsigned long long duration,
+                                                    unsigned long long period, int max_samples) {
+    if (threadIdx.x != 0) return;
+    const unsigned long long r0 = __builtin_amdgcn_s_memrealtime();
+    unsigned long long next = r0;
+    int i = 0;
+    for (;;) {
+        const unsigned long long c = __builtin_amdgcn_s_memtime();
+        const unsigned long long r = __builtin_amdgcn_s_memrealtime();
+        if (r >= next && i < max_samples) {
+            out[2 * i] = c;
+            out[2 * i + 1] = r;
+            i++;
+            next = r + period;
+        }
+        if (r - r0 >= duration || i >= max_samples) break;
+        __builtin_amdgcn_s_sleep(8);
+    }
+}
+
+hipError_t launch_clock_probe(unsigned long long *out, unsigned long long duration, unsigned long long period,
+                              int max_samples, hipStream_t s) {
+    hipLaunchKernelGGL(k_clock_probe, dim3(1), dim3(64), 0, s, out, duration, period, max_samples);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Static scratch for the allocation-free forward
 // ---------------------------------------------------------------------------
 
