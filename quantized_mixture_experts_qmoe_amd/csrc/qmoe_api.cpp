@@ -317,7 +317,9 @@ int max_tiles_for(const qmoe_ctx *c, int T, int bm) {
 // entry it later reads.
 size_t carve_workspace(const qmoe_ctx *c, size_t T, uint8_t *base, QmoeWorkspace &w) {
     const size_t P = T * c->k;
-    const size_t nchunks = (P + kDispatchChunk - 1) / kDispatchChunk;
+    // dispatch chunks: kDispatchChunk tasks, or one router token tile
+    const size_t nchunks = std::max((P + kDispatchChunk - 1) / kDispatchChunk,
+                                    (T + kMinRouterTile - 1) / kMinRouterTile);
     const size_t rows_total = P + (size_t)c->S * T;
     // 16-row tiles give the most tiles of any tile height
     const size_t tiles_cap = (size_t)max_tiles_for(c, (int)T, 16) + 16;
@@ -349,28 +351,34 @@ size_t carve_workspace(const qmoe_ctx *c, size_t T, uint8_t *base, QmoeWorkspace
     return cur;
 }
 
-// Top-k + dispatch shared by route_topk and forward.
+// Top-k + dispatch shared by route_topk and forward. fused_chunk > 0: the
+// router's epilogue already selected the top k and wrote the per-expert counts
+// of chunks of fused_chunk tasks; only the scan and the scatter remain.
 int run_route(qmoe_ctx *c, const QmoeWorkspace &w, uint32_t prof, const float *logits, int T, int bm, int n_shared,
-              hipStream_t s) {
+              int fused_chunk, hipStream_t s) {
     const int P = T * c->k;
-    if (T <= kSmallRouteMaxT && c->E <= kSmallRouteMaxE)
+    if (!fused_chunk && T <= kSmallRouteMaxT && c->E <= kSmallRouteMaxE)
         return timed(c, prof, K_TOPKD, s, [&] {
             return launch_route_small(logits, T, c->E, c->k, c->cfg.renormalize, n_shared, bm, w.idx, w.wpair,
                                       w.counts, w.offsets, w.tiles, w.num_tiles, w.perm, w.inv, w.wrow, s);
         });
-    const int nchunks = (P + kDispatchChunk - 1) / kDispatchChunk;
-    int rc = timed(c, prof, K_TOPK, s,
+    int rc = QMOE_OK;
+    const int chunk = fused_chunk ? fused_chunk : kDispatchChunk;
+    const int nchunks = (P + chunk - 1) / chunk;
+    if (!fused_chunk) {
+        rc = timed(c, prof, K_TOPK, s,
                    [&] { return launch_topk(logits, T, c->E, c->k, c->cfg.renormalize, w.idx, w.wpair, s); });
-    if (rc) return rc;
-    rc = timed(c, prof, K_DCOUNT, s, [&] { return launch_dispatch_count(w.idx, P, c->E, w.chunk_counts, s); });
-    if (rc) return rc;
+        if (rc) return rc;
+        rc = timed(c, prof, K_DCOUNT, s, [&] { return launch_dispatch_count(w.idx, P, c->E, w.chunk_counts, s); });
+        if (rc) return rc;
+    }
     rc = timed(c, prof, K_DSCAN, s, [&] {
         return launch_dispatch_scan(w.chunk_counts, nchunks, c->E, P, T, n_shared, bm, w.chunk_base, w.counts,
                                     w.offsets, w.tiles, w.num_tiles, s);
     });
     if (rc) return rc;
     return timed(c, prof, K_DSCATTER, s, [&] {
-        return launch_dispatch_scatter(w.idx, w.wpair, P, c->E, w.chunk_base, w.perm, w.inv, w.wrow, s);
+        return launch_dispatch_scatter(w.idx, w.wpair, P, c->E, chunk, w.chunk_base, w.perm, w.inv, w.wrow, s);
     });
 }
 
@@ -679,7 +687,7 @@ int qmoe_route_topk(qmoe_ctx *c, const float *logits, int32_t T, qmoe_route_out 
     if (!logits) return fail(QMOE_EINVAL, "logits is NULL");
     hipStream_t s = (hipStream_t)stream;
     if (hipSetDevice(c->cfg.device) != hipSuccess) return fail(QMOE_EHIP, "hipSetDevice failed");
-    int rc = run_route(c, c->ws, c->prof, logits, T, 128, 0, s);
+    int rc = run_route(c, c->ws, c->prof, logits, T, 128, 0, 0, s);
     if (rc) return rc;
     return copy_route(c, c->ws, out, T, s);
 }
@@ -717,17 +725,27 @@ int run_forward(qmoe_ctx *c, const QmoeWorkspace &w, uint32_t prof, const uint16
     // the bf16 router emits the row sums from its staged x tiles
     const bool fused_sums = need_sums && c->router_bf16;
     int rc;
+    // the gating network runs in the router's epilogue where one router
+    // workgroup holds every expert of its tokens (larger batches; the small
+    // ones take the one-workgroup top-k + dispatch)
+    int fused_chunk = 0;
+    const bool try_fuse = c->router_bf16 && T > kSmallRouteMaxT && router_fuses(T, c->E, c->k);
+    RouteFuse rf{w.idx, w.wpair, w.chunk_counts, c->k, c->cfg.renormalize};
+    // logits are written only when the caller asks for them (or the top-k runs separately)
+    float *lg = (dbg && dbg->logits) || !try_fuse ? w.logits : nullptr;
     if (!c->router_bf16)
         rc = timed(c, prof, K_ROUTER, s, [&] {
             return launch_router_f32(x, (const float *)c->router_w, c->router_b, w.logits, T, c->d, c->E, s);
         });
     else
         rc = timed(c, prof, K_ROUTER, s, [&] {
-            return launch_router_bf16(x, (const uint16_t *)c->router_w, c->router_s, c->router_b, w.logits,
-                                      fused_sums ? w.xsum : nullptr, zc, T, c->d, c->E, s);
+            return launch_router_bf16(x, (const uint16_t *)c->router_w, c->router_s, c->router_b, lg,
+                                      fused_sums ? w.xsum : nullptr, zc, T, c->d, c->E, try_fuse ? &rf : nullptr,
+                                      &fused_chunk, s);
         });
     if (rc) return rc;
-    rc = run_route(c, w, prof, w.logits, T, bm, c->S, s);
+    if (try_fuse && !fused_chunk) return fail(QMOE_EHIP, "internal: the router's gating epilogue did not run");
+    rc = run_route(c, w, prof, w.logits, T, bm, c->S, fused_chunk, s);
     if (rc) return rc;
     if (need_sums && !fused_sums) {
         rc = timed(c, prof, K_XSUM, s, [&] { return launch_xsum(x, T, c->d, zc, w.xsum, s); });
@@ -1052,7 +1070,8 @@ int qmoe_atomic_forward(qmoe_atomic_ctx *c, const uint16_t *x, int32_t T, uint16
     auto ok = [](hipError_t e, const char *what) {
         return e == hipSuccess ? QMOE_OK : fail(QMOE_EHIP, "%s failed: %s", what, hipGetErrorString(e));
     };
-    int rc = ok(launch_router_bf16(x, c->R, nullptr, nullptr, c->logits, nullptr, 0.0f, T, d, Nr + Nc, s), "router");
+    int rc = ok(launch_router_bf16(x, c->R, nullptr, nullptr, c->logits, nullptr, 0.0f, T, d, Nr + Nc, nullptr,
+                                   nullptr, s), "router");
     if (!rc) rc = ok(launch_cart_topk(c->logits, T, Nr, Nc, k, c->B, c->idx, c->w, c->gidx, s), "cartesian top-k");
     if (!rc && schedule == QMOE_SCHEDULE_TOKEN_CENTRIC) {
         rc = ok(launch_atomic_token(x, c->W, c->V, c->idx, c->w, T, d, k, y, s), "token-centric experts");
@@ -1064,7 +1083,8 @@ int qmoe_atomic_forward(qmoe_atomic_ctx *c, const uint16_t *x, int32_t T, uint16
                                          c->counts, c->offsets, c->tiles, c->num_tiles, s),
                     "dispatch scan");
         if (!rc)
-            rc = ok(launch_dispatch_scatter(c->gidx, c->w, P, c->NG, c->chunk_base, c->perm, c->inv, c->wrow, s),
+            rc = ok(launch_dispatch_scatter(c->gidx, c->w, P, c->NG, kDispatchChunk, c->chunk_base, c->perm, c->inv,
+                                            c->wrow, s),
                     "dispatch scatter");
         if (!rc)
             rc = ok(launch_atomic_rows(x, c->W, c->V, c->perm, c->idx, c->wrow, P, d, k, c->O, s),

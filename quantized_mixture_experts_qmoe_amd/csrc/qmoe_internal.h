@@ -141,13 +141,31 @@ hipError_t launch_quant_matrix(int wformat, const uint16_t *a, const uint16_t *b
 // xsum (may be NULL): receives xscale * per-128-group row sums of x.
 // rscale (may be NULL): per-expert scale of a quantized router (logit =
 // rscale[e] * x.wr[e] + bias[e]).
+// rf (may be NULL): the gating network's outputs when it runs fused in the
+// router's epilogue (possible where one router workgroup holds every expert of
+// its tokens, k <= 16): top-k indices and weights and the per-expert task
+// counts of each token tile (one dispatch chunk of BT * k tasks). *chunk (may
+// be NULL when rf is) receives BT * k when the fused epilogue ran, else 0.
+// logits may be NULL when it runs.
+struct RouteFuse {
+    int32_t *idx;           // [T][k] selected experts
+    float *w;               // [T][k] mixing weights
+    int32_t *chunk_counts;  // [token tiles][E] tasks per expert of each tile
+    int32_t k, renorm;
+};
 hipError_t launch_router_bf16(const uint16_t *x, const uint16_t *wr, const float *rscale, const float *bias,
-                              float *logits, float *xsum, float xscale, int T, int d, int E, hipStream_t s);
+                              float *logits, float *xsum, float xscale, int T, int d, int E, const RouteFuse *rf,
+                              int *chunk, hipStream_t s);
+// Whether launch_router_bf16 runs the fused gating epilogue for this shape.
+bool router_fuses(int T, int E, int k);
 hipError_t launch_router_f32(const uint16_t *x, const float *wr, const float *bias, float *logits, int T, int d, int E,
                              hipStream_t s);
 hipError_t launch_topk(const float *logits, int T, int E, int k, int renorm, int32_t *idx, float *w, hipStream_t s);
-// Dispatch: per-chunk histogram, scan + tile list, stable scatter.
+// Dispatch: per-chunk histogram, scan + tile list, stable scatter. The
+// histogram kernel's chunk is kDispatchChunk tasks; the fused router's is one
+// token tile (BT * k tasks, BT >= 16).
 constexpr int kDispatchChunk = 1024;
+constexpr int kMinRouterTile = 16;
 // One-workgroup top-k + dispatch for small batches.
 constexpr int kSmallRouteMaxT = 64;
 constexpr int kSmallRouteMaxE = 256;
@@ -156,8 +174,9 @@ hipError_t launch_dispatch_scan(const int32_t *chunk_counts, int nchunks, int E,
                                 int32_t *chunk_base, int32_t *counts, int32_t *offsets, Tile *tiles,
                                 int32_t *num_tiles, hipStream_t s);
 // Also writes wrow[row] = w[pair of row] (the mixing weight in row order).
-hipError_t launch_dispatch_scatter(const int32_t *idx, const float *w, int P, int E, const int32_t *chunk_base,
-                                   int32_t *perm, int32_t *inv, float *wrow, hipStream_t s);
+// chunk: tasks per chunk of the counts the scan consumed.
+hipError_t launch_dispatch_scatter(const int32_t *idx, const float *w, int P, int E, int chunk,
+                                   const int32_t *chunk_base, int32_t *perm, int32_t *inv, float *wrow, hipStream_t s);
 // Top-k and the whole dispatch in one workgroup (T <= kSmallRouteMaxT, E <= kSmallRouteMaxE).
 hipError_t launch_route_small(const float *logits, int T, int E, int k, int renorm, int n_shared, int bm,
                               int32_t *idx, float *w, int32_t *counts, int32_t *offsets, Tile *tiles,

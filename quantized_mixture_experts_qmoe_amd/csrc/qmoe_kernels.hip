@@ -86,6 +86,14 @@ __device__ __forceinline__ void dma4s(const void *sbase, uint32_t voff, uint32_t
 // Router
 // ---------------------------------------------------------------------------
 
+// Selection helpers used by the router's fused epilogue (defined with the
+// gating network below).
+__device__ __forceinline__ uint32_t ord_u32(float v);
+__device__ __forceinline__ float ord_value(uint32_t u);
+template <int EPL16>
+__device__ __forceinline__ void topk_row16(const float *__restrict__ lt, int E, int k, int renorm, int lane,
+                                           int &my_e, float &my_w);
+
 // Router for larger batches: a tile of BT tokens x BE experts per workgroup.
 // The x rows and router rows of each 128-wide K group are copied into LDS with
 // asynchronous global -> LDS copies, whole 256-byte row segments per 16 lanes
@@ -99,12 +107,19 @@ __device__ __forceinline__ void dma4s(const void *sbase, uint32_t voff, uint32_t
 //     tiles are added through LDS at the end.
 // Workgroups of the first expert tile also emit the per-group row sums of x
 // (times xscale) read from the staged tile.
-template <int BT, int BE, int WE, int NST>
+// FUSE (one expert tile holds all E experts, k <= 16): the gating network runs
+// in the epilogue on the tile's logits staged in LDS (Q-MoE page, section 3:
+// the gating network's top-k; weights: softmax over the selection): each
+// 16-lane row of a wave selects one token's top k (DPP row maxima, ties to
+// the lower expert index) and writes idx, w; the workgroup then writes the
+// tile's per-expert task counts (its BT*k tasks are one dispatch chunk).
+// Logits go to memory only when `logits` is given.
+template <int BT, int BE, int WE, int NST, bool FUSE>
 __global__ __launch_bounds__(256) void k_router_lds(const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr,
                                                     const float *__restrict__ rscale,
                                                     const float *__restrict__ bias, float *__restrict__ logits,
                                                     float *__restrict__ xsum, float xscale, int T, int d, int E,
-                                                    int net) {
+                                                    int net, RouteFuse rf) {
     constexpr bool STREAMS = WE == 1;
     static_assert(WE == 1 || WE == 4, "four waves: streams or a four-way expert split");
     constexpr int MT = BT / 16, NT = BE / (16 * WE);
@@ -238,10 +253,22 @@ __global__ __launch_bounds__(256) void k_router_lds(const uint16_t *__restrict__
             for (int i = 0; i < MT; i++)
 #pragma unroll
                 for (int jj = 0; jj < NT; jj++) acc[i][jj] += red[(w * MT * NT + i * NT + jj) * 64 + lane];
+    } else if constexpr (FUSE) {
+        __syncthreads();   // every wave's copies have landed: the ring is free
+    }
+    // staged logits of the tile (FUSE): [BT][LP] fp32 over the free ring, then
+    // the per-expert task counts
+    constexpr int LP = BE + 1;
+    float *Ls = reinterpret_cast<float *>(lds);
+    int *cnt = reinterpret_cast<int *>(lds + BT * LP * 4);
+    static_assert(!FUSE || BT * LP * 4 + BE * 4 <= RINGS * NST * ST, "the logit tile fits in the ring");
+    if constexpr (FUSE) {
+        for (int e = STREAMS ? lane : (int)threadIdx.x; e < BE; e += STREAMS ? 64 : 256) cnt[e] = 0;
     }
 #pragma unroll
     for (int jj = 0; jj < NT; jj++) {
-        const int e = e0 + 16 * (we * NT + jj) + (lane & 15);
+        const int el = 16 * (we * NT + jj) + (lane & 15);
+        const int e = e0 + el;
         if (e >= E) continue;
         const float b = bias ? bias[e] : 0.0f;
         const float sc = rscale ? rscale[e] : 1.0f;
@@ -249,9 +276,33 @@ __global__ __launch_bounds__(256) void k_router_lds(const uint16_t *__restrict__
         for (int i = 0; i < MT; i++)
 #pragma unroll
             for (int r = 0; r < 4; r++) {
-                const int t = t0 + 16 * i + (lane >> 4) * 4 + r;
-                if (t < T) logits[(size_t)t * E + e] = acc[i][jj][r] * sc + b;
+                const int tr = 16 * i + (lane >> 4) * 4 + r;
+                const float lv = acc[i][jj][r] * sc + b;
+                if (FUSE) Ls[tr * LP + el] = lv;
+                if (logits && t0 + tr < T) logits[(size_t)(t0 + tr) * E + e] = lv;
             }
+    }
+    if constexpr (FUSE) {
+        // (streams mode: one wave left, whose LDS accesses stay in order)
+        if constexpr (!STREAMS) __syncthreads();
+        // 16-lane rows over the tile's tokens: row g of wave w is row 4w + g
+        constexpr int NROWS = STREAMS ? 4 : 16;
+        const int row0 = (STREAMS ? 0 : 4 * wave) + (lane >> 4);
+        for (int tr = row0; tr < BT; tr += NROWS) {
+            const int t = t0 + tr;
+            int my_e;
+            float my_w;
+            topk_row16<BE / 16>(Ls + tr * LP, E, rf.k, rf.renorm, lane, my_e, my_w);
+            if (t < T && (lane & 15) < rf.k) {
+                rf.idx[(size_t)t * rf.k + (lane & 15)] = my_e;
+                rf.w[(size_t)t * rf.k + (lane & 15)] = my_w;
+                atomicAdd(&cnt[my_e], 1);
+            }
+        }
+        if constexpr (!STREAMS) __syncthreads();
+        const int tt = t0 / BT;
+        for (int e = STREAMS ? lane : (int)threadIdx.x; e < E; e += STREAMS ? 64 : 256)
+            rf.chunk_counts[(size_t)tt * E + e] = cnt[e];
     }
 }
 
@@ -436,6 +487,80 @@ __device__ __forceinline__ int topk_token(const float *__restrict__ lt, int E, i
     return -1;
 }
 
+// Row maximum over a 16-lane row, in every lane of the row: four rotate-and-max
+// steps (DPP row_ror 1, 2, 4, 8).
+constexpr int kDppRor1 = 0x121, kDppRor2 = 0x122, kDppRor4 = 0x124, kDppRor8 = 0x128;
+template <int CTRL>
+__device__ __forceinline__ uint32_t ror_max(uint32_t v) {
+    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+    return o > v ? o : v;
+}
+template <int CTRL>
+__device__ __forceinline__ float ror_add(float v) {
+    return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Top-k of one token by one 16-lane row (the router's fused epilogue): entry e
+// of lt[0..E) is held by lane e % 16 of the row (EPL16 entries per lane); k <=
+// 16 selection rounds (largest logit, ties to the lower expert index); lane
+// j < k of the row ends holding slot j's expert and weight (softmax over the k
+// selected, or the full-softmax probability when renorm = 0).
+template <int EPL16>
+__device__ __forceinline__ void topk_row16(const float *__restrict__ lt, int E, int k, int renorm, int lane,
+                                           int &my_e, float &my_w) {
+    const int l16 = lane & 15, rshift = lane & 48;
+    float v[EPL16];
+    uint32_t hv[EPL16];
+#pragma unroll
+    for (int i = 0; i < EPL16; i++) {
+        const int e = l16 + 16 * i;
+        v[i] = e < E ? lt[e] : 0.0f;
+        hv[i] = e < E ? ord_u32(v[i]) : 0u;
+    }
+    my_e = -1;
+    uint32_t my_h = 0u, first_h = 0u;
+    for (int j = 0; j < k; j++) {
+        uint32_t m = hv[0];
+#pragma unroll
+        for (int i = 1; i < EPL16; i++) m = hv[i] > m ? hv[i] : m;
+        m = ror_max<kDppRor1>(m);
+        m = ror_max<kDppRor2>(m);
+        m = ror_max<kDppRor4>(m);
+        m = ror_max<kDppRor8>(m);
+        // the first entry slot holding the maximum, then its lowest lane
+        int win = -1;
+#pragma unroll
+        for (int i = 0; i < EPL16; i++) {
+            const uint32_t bits = (uint32_t)(__ballot(hv[i] == m) >> rshift) & 0xFFFFu;
+            if (win < 0 && bits) win = 16 * i + __builtin_ctz(bits);
+        }
+#pragma unroll
+        for (int i = 0; i < EPL16; i++)
+            if (l16 + 16 * i == win) hv[i] = 0u;
+        if (l16 == j) {
+            my_e = win;
+            my_h = m;
+        }
+        if (j == 0) first_h = m;
+    }
+    const float vmax = ord_value(first_h);
+    const float ex = l16 < k ? expf(ord_value(my_h) - vmax) : 0.0f;
+    float part;
+    if (renorm) {
+        part = ex;
+    } else {
+        part = 0.0f;
+#pragma unroll
+        for (int i = 0; i < EPL16; i++)
+            if (l16 + 16 * i < E) part += expf(v[i] - vmax);
+    }
+    part = ror_add<kDppRor1>(part);
+    part = ror_add<kDppRor2>(part);
+    part = ror_add<kDppRor4>(part);
+    part = ror_add<kDppRor8>(part);
+    my_w = ex / part;
+}
+
 template <int EPL>
 __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, int T, int E, int k, int renorm,
                                               int32_t *__restrict__ idx, float *__restrict__ w) {
@@ -498,8 +623,18 @@ __global__ __launch_bounds__(1024) void k_dispatch_scan(const int32_t *__restric
     const int tid = threadIdx.x, e = tid / G, g = tid % G;
     const bool live = e < E;
     const int b0 = (int)((long)nchunks * g / G), b1 = (int)((long)nchunks * (g + 1) / G);
+    // ranges of up to kScanRegs chunks are loaded all at once into registers
+    // (every load in flight together; reused for the chunk bases below)
+    constexpr int kScanRegs = 32;
+    const bool in_regs = b1 - b0 <= kScanRegs;
+    int cv[kScanRegs];
     int s = 0;
-    if (live) {
+    if (in_regs) {
+#pragma unroll
+        for (int i = 0; i < kScanRegs; i++) cv[i] = (live && b0 + i < b1) ? cc[(size_t)(b0 + i) * E + e] : 0;
+#pragma unroll
+        for (int i = 0; i < kScanRegs; i++) s += cv[i];
+    } else if (live) {
         int b = b0;
         for (; b + 4 <= b1; b += 4) {
             const int v0 = cc[(size_t)b * E + e], v1 = cc[(size_t)(b + 1) * E + e];
@@ -520,7 +655,15 @@ __global__ __launch_bounds__(1024) void k_dispatch_scan(const int32_t *__restric
         offsets[e] = first_row;
         for (int m = 0; m < cnt; m += bm) tiles[tile_base + m / bm] = Tile{e, first_row + m, first_row + cnt, 0};
     }
-    if (live) {
+    if (live && in_regs) {
+        int run = first_row;
+#pragma unroll
+        for (int i = 0; i < kScanRegs; i++)
+            if (b0 + i < b1) {
+                chunk_base[(size_t)(b0 + i) * E + e] = run;
+                run += cv[i];
+            }
+    } else if (live) {
         int run = first_row;
         for (int b = b0; b < b1; b++) {
             chunk_base[(size_t)b * E + e] = run;
@@ -537,10 +680,12 @@ __global__ __launch_bounds__(1024) void k_dispatch_scan(const int32_t *__restric
     }
 }
 
-// Stable scatter: ranks inside a chunk follow pair order. Each round takes 256
-// consecutive pairs; ranks inside a wave come from per-expert 64-bit lane masks.
+// Stable scatter: ranks inside a chunk (`chunk` consecutive pairs) follow pair
+// order. Each round takes 256 consecutive pairs; ranks inside a wave come from
+// per-expert 64-bit lane masks.
 __global__ __launch_bounds__(256) void k_dispatch_scatter(const int32_t *__restrict__ idx, const float *__restrict__ w,
-                                                          int P, int E, const int32_t *__restrict__ chunk_base,
+                                                          int P, int E, int chunk,
+                                                          const int32_t *__restrict__ chunk_base,
                                                           int32_t *__restrict__ perm, int32_t *__restrict__ inv,
                                                           float *__restrict__ wrow) {
     extern __shared__ unsigned long long smem64[];
@@ -552,9 +697,10 @@ __global__ __launch_bounds__(256) void k_dispatch_scatter(const int32_t *__restr
         masks[e] = masks[E + e] = masks[2 * E + e] = masks[3 * E + e] = 0ull;
     }
     __syncthreads();
-    for (int round = 0; round < kDispatchChunk / 256; round++) {
-        const int p = blockIdx.x * kDispatchChunk + round * 256 + threadIdx.x;
-        const bool valid = p < P;
+    const int c0 = blockIdx.x * chunk;
+    for (int r0 = 0; r0 < chunk; r0 += 256) {
+        const int p = c0 + r0 + threadIdx.x;
+        const bool valid = r0 + (int)threadIdx.x < chunk && p < P;
         const int e = valid ? idx[p] : 0;
         const float wp = valid ? w[p] : 0.0f;
         if (valid) atomicOr(&masks[wave * E + e], 1ull << lane);
@@ -2018,24 +2164,41 @@ hipError_t static_scratch(void **ptr) {
 // ---------------------------------------------------------------------------
 
 // Expert tiles of 64 for many experts, 32, or 16 when E <= 16 (no idle half tile).
+// rf != NULL: the gating epilogue runs in the router when one expert tile
+// holds every expert (and k <= 16); *chunk receives the tasks per dispatch
+// chunk it used (BT * k), or 0 when it did not run.
 template <int BT, int BE, int WE, int NST>
 static void launch_router_lds(const uint16_t *x, const uint16_t *wr, const float *rscale, const float *bias,
-                              float *logits, float *xsum, float xscale, int T, int d, int E, hipStream_t s) {
+                              float *logits, float *xsum, float xscale, int T, int d, int E, const RouteFuse *rf,
+                              int *chunk, hipStream_t s) {
     const long gx = 8L * ((T + BT * 8 - 1) / (BT * 8));   // token tiles, padded to a multiple of 8
     const int net = (E + BE - 1) / BE;
-    hipLaunchKernelGGL((k_router_lds<BT, BE, WE, NST>), dim3((unsigned)(gx * net)), dim3(256), 0, s, x, wr, rscale,
-                       bias, logits, xsum, xscale, T, d, E, net);
+    if (rf && net == 1 && rf->k <= 16) {
+        *chunk = BT * rf->k;
+        hipLaunchKernelGGL((k_router_lds<BT, BE, WE, NST, true>), dim3((unsigned)gx), dim3(256), 0, s, x, wr, rscale,
+                           bias, logits, xsum, xscale, T, d, E, net, *rf);
+        return;
+    }
+    if (chunk) *chunk = 0;
+    hipLaunchKernelGGL((k_router_lds<BT, BE, WE, NST, false>), dim3((unsigned)(gx * net)), dim3(256), 0, s, x, wr,
+                       rscale, bias, logits, xsum, xscale, T, d, E, net, RouteFuse{});
 }
 
+// The expert tile width launch_router_bf16 picks, and whether the gating
+// epilogue fuses for that shape (one expert tile covers every expert, k <= 16).
+static int router_tile_experts(int T, int E) { return (T < 256 || E <= 16) ? 16 : E <= 32 ? 32 : E <= 64 ? 64 : 128; }
+bool router_fuses(int T, int E, int k) { return E <= router_tile_experts(T, E) && k <= 16; }
+
 hipError_t launch_router_bf16(const uint16_t *x, const uint16_t *wr, const float *rscale, const float *bias,
-                              float *logits, float *xsum, float xscale, int T, int d, int E, hipStream_t s) {
+                              float *logits, float *xsum, float xscale, int T, int d, int E, const RouteFuse *rf,
+                              int *chunk, hipStream_t s) {
     // 16 x 16 tiles as four independent streams for small batches and few
     // experts (LDS: 4 rings of 3 x 8 KB); wider expert tiles for large batches
     // (4 rings of 3 x 12 KB; shared rings of 3 x 20 KB and 2 x 40 KB)
-    if (T < 256 || E <= 16) launch_router_lds<16, 16, 1, 3>(x, wr, rscale, bias, logits, xsum, xscale, T, d, E, s);
-    else if (E <= 32) launch_router_lds<16, 32, 1, 3>(x, wr, rscale, bias, logits, xsum, xscale, T, d, E, s);
-    else if (E <= 64) launch_router_lds<16, 64, 4, 3>(x, wr, rscale, bias, logits, xsum, xscale, T, d, E, s);
-    else launch_router_lds<32, 128, 4, 2>(x, wr, rscale, bias, logits, xsum, xscale, T, d, E, s);
+    if (T < 256 || E <= 16) launch_router_lds<16, 16, 1, 3>(x, wr, rscale, bias, logits, xsum, xscale, T, d, E, rf, chunk, s);
+    else if (E <= 32) launch_router_lds<16, 32, 1, 3>(x, wr, rscale, bias, logits, xsum, xscale, T, d, E, rf, chunk, s);
+    else if (E <= 64) launch_router_lds<16, 64, 4, 3>(x, wr, rscale, bias, logits, xsum, xscale, T, d, E, rf, chunk, s);
+    else launch_router_lds<32, 128, 4, 2>(x, wr, rscale, bias, logits, xsum, xscale, T, d, E, rf, chunk, s);
     return hipGetLastError();
 }
 
@@ -2090,11 +2253,12 @@ hipError_t launch_dispatch_scan(const int32_t *chunk_counts, int nchunks, int E,
     return hipGetLastError();
 }
 
-hipError_t launch_dispatch_scatter(const int32_t *idx, const float *w, int P, int E, const int32_t *chunk_base,
-                                   int32_t *perm, int32_t *inv, float *wrow, hipStream_t s) {
-    const int nchunks = (P + kDispatchChunk - 1) / kDispatchChunk;
+hipError_t launch_dispatch_scatter(const int32_t *idx, const float *w, int P, int E, int chunk,
+                                   const int32_t *chunk_base, int32_t *perm, int32_t *inv, float *wrow, hipStream_t s) {
+    const int nchunks = (P + chunk - 1) / chunk;
     const size_t lds = (size_t)E * (4 * sizeof(unsigned long long) + sizeof(int));
-    hipLaunchKernelGGL(k_dispatch_scatter, dim3(nchunks), dim3(256), lds, s, idx, w, P, E, chunk_base, perm, inv, wrow);
+    hipLaunchKernelGGL(k_dispatch_scatter, dim3(nchunks), dim3(256), lds, s, idx, w, P, E, chunk, chunk_base, perm,
+                       inv, wrow);
     return hipGetLastError();
 }
 
