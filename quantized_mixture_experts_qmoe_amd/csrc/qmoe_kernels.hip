@@ -1322,12 +1322,15 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm_gpf(GemmArgs a) {
     constexpr int ST_A = 0, ST_R = BM * 256, ST_BYTES = ST_R + BM * 4;
     constexpr int WCOLS = 16 * NB;                // B columns per wave
     constexpr int NTILE = WCOLS * NW;             // B columns per workgroup
-    // Row-block-outer order keeps one row block of chain partials live instead
-    // of all of them; its B ring has one slot, refilled once the group's codes
-    // are converted. Row-block-inner order double-buffers the ring.
-    constexpr int RS = ROW_OUTER ? 1 : 2;
+    // Two activation stages, the next group's copies issued early in each
+    // group, and two B register slots. Row-block-outer order
+    // (accumulators in scale units, see group()) loads B two groups ahead,
+    // each slot refilled once its codes are converted; row-block-inner order
+    // loads it one group ahead at the start of the group.
+    constexpr int RS = 2;
+    constexpr int NST = 2;
     constexpr float ZC = GroupConst<DF>::ZC;
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * ST_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[NST * ST_BYTES];
 
     int tile_id, ntile;
     if (!map_work(blockIdx.x, *a.num_tiles, a.n_tiles, tile_id, ntile)) return;
@@ -1371,14 +1374,17 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm_gpf(GemmArgs a) {
     const uint32_t roffb = 4u * (uint32_t)src_row(RPW * wave + (lane < RPW ? lane : 0)) * (uint32_t)ldr;
     const uint8_t *codes = MODE == 0 ? ew.c13 : ew.c2;
     const uint16_t *gsc = MODE == 0 ? ew.s13 : ew.s2;
-    // a wave whose columns lie past N (last N-tile of a narrower matrix) loads
-    // blocks 0.. instead to keep its load count, and computes nothing
-    const bool wave_on = n0 + WCOLS * wave < N;
-    const int ib0 = wave_on ? n0 / 16 + NB * wave : 0;
+    // N (2F or d) is a multiple of 256 = NTILE: every wave of a tile with
+    // n0 < N owns columns below N
+    static_assert(NTILE == 256, "tiles of 256 columns");
+    const int ib0 = n0 / 16 + NB * wave;
 
     // the copies' per-lane byte offsets are constant through K; only the
     // scalar bases advance with the group index
-    auto issue = [&](int kb, int st) {
+    auto issue = [&](int kb, int st) __attribute__((always_inline)) {
+        // wave-uniform by construction; readfirstlane keeps them in SGPRs
+        kb = __builtin_amdgcn_readfirstlane(kb);
+        st = __builtin_amdgcn_readfirstlane(st);
         const uint32_t sb = lds0 + st * ST_BYTES;
         const uint16_t *as = abase + kb * 128;
 #pragma unroll
@@ -1391,7 +1397,7 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm_gpf(GemmArgs a) {
     uint32_t sring[RS][NB];
     const int spair2 = (lane & 15) & ~1;
     const uint32_t hsel = (lane & 1) * 16;
-    auto load_b = [&](int kb, int slot) {
+    auto load_b = [&](int kb, int slot) __attribute__((always_inline)) {
 #pragma unroll
         for (int nb = 0; nb < NB; nb++) {
             const size_t blk = (size_t)(ib0 + nb) * KB + kb;
@@ -1407,56 +1413,105 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm_gpf(GemmArgs a) {
 #pragma unroll
         for (int nb = 0; nb < NB; nb++) acc[mi][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
     const NibbleConst nc = nibble_const();
+    // scale of the previous group per column block (accumulators in scale units)
+    float s_prev[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++) s_prev[nb] = 1.0f;
 
     // one group: this wave's codes and scales, then the group's MFMAs
-    auto group = [&](int st, int slot, int next_kb) {
+    auto group = [&](int st, int slot, int next_kb, int copy_kb, int copy_st) __attribute__((always_inline)) {
         const uint8_t *S = lds + st * ST_BYTES;
-        bf16x8 bq[NB][4];
-        float sc[NB];
-#pragma unroll
-        for (int nb = 0; nb < NB; nb++) {
-            const uint4 raw = bring[slot][nb];
-            bq[nb][0] = nibbles_to_bf16_128(raw.x, nc);
-            bq[nb][1] = nibbles_to_bf16_128(raw.y, nc);
-            bq[nb][2] = nibbles_to_bf16_128(raw.z, nc);
-            bq[nb][3] = nibbles_to_bf16_128(raw.w, nc);
-            sc[nb] = half_bits_to_f32((uint16_t)(sring[slot][nb] >> hsel));
-        }
-        if constexpr (RS == 1) load_b(next_kb, 0);
         const uint16_t *Ab = reinterpret_cast<const uint16_t *>(S + ST_A);
         const float *Rb = reinterpret_cast<const float *>(S + ST_R);
-        if (!wave_on) return;
+        bf16x8 bq[NB][4];
+        float sc[NB];
+        // A fragment of row block mi, k-step s (XOR-swizzled chunks)
+        auto afrag = [&](int mi, int s) __attribute__((always_inline)) {
+            const int pc = (s * 4 + (lane >> 4)) ^ (lane & 15);
+            return *reinterpret_cast<const bf16x8 *>(&Ab[(mi * 16 + (lane & 15)) * 128 + pc * 8]);
+        };
         if constexpr (ROW_OUTER) {
-            // row block outer: NB chains per row block, each 4 MFMAs deep
+            // Accumulators in units of the current group's scale: per column,
+            // X = X * (s_prev / s_cur) + nrs, then the group's MFMAs add the
+            // integer-code products straight into X (nrs = -ZC * row sum folds
+            // in the code offset, as a chain's start value would); the tile
+            // ends with X * s_last. With no chain partials live, the codes are
+            // converted half a group (two k-steps) at a time, each half right
+            // before its MFMAs, and the A fragments stream one k-step ahead
+            // through a two-slot ring (each LDS read in flight behind four
+            // MFMAs). Once the first half's codes are converted the next
+            // group's activation copies are issued; once the second half's are,
+            // the slot is refilled for two groups ahead.
+            float r[NB];
 #pragma unroll
-            for (int mi = 0; mi < MI; mi++) {
-                bf16x8 af[4];
+            for (int nb = 0; nb < NB; nb++) {
+                const float sc_cur = half_bits_to_f32((uint16_t)(sring[slot][nb] >> hsel));
+                r[nb] = s_prev[nb] * __builtin_amdgcn_rcpf(sc_cur);
+                s_prev[nb] = sc_cur;
+            }
+            bf16x8 afr[2];
+            afr[0] = afrag(0, 0);
 #pragma unroll
-                for (int s = 0; s < 4; s++) {
-                    const int pc = (s * 4 + (lane >> 4)) ^ (lane & 15);
-                    af[s] = *reinterpret_cast<const bf16x8 *>(&Ab[(mi * 16 + (lane & 15)) * 128 + pc * 8]);
+            for (int h = 0; h < 2; h++) {
+                bf16x8 bh[NB][2];
+#pragma unroll
+                for (int nb = 0; nb < NB; nb++) {
+                    bh[nb][0] = nibbles_to_bf16_128(h == 0 ? bring[slot][nb].x : bring[slot][nb].z, nc);
+                    bh[nb][1] = nibbles_to_bf16_128(h == 0 ? bring[slot][nb].y : bring[slot][nb].w, nc);
                 }
-                const f32x4 c0 = *reinterpret_cast<const f32x4 *>(&Rb[mi * 16 + lrow]);
-                f32x4 p[NB];
+                // (after the conversion, which is where the compiler waits for
+                // this slot's loads: the copies and loads issued here are not
+                // caught by that wait)
+                // the converted operands (and the scale ratios) as inputs of an
+                // empty volatile asm: the copies and loads below cannot move
+                // above the conversion, and with it the compiler's waits for
+                // this slot's loads
 #pragma unroll
-                for (int s = 0; s < 4; s++)
+                for (int nb = 0; nb < NB; nb++)
+                    asm volatile("" ::"v"(bh[nb][0]), "v"(bh[nb][1]), "v"(r[nb]));
+                if (h == 0) issue(copy_kb, copy_st);
+                else load_b(next_kb, slot);
 #pragma unroll
-                    for (int nb = 0; nb < NB; nb++)
-                        p[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s], bq[nb][s], s == 0 ? c0 : p[nb], 0, 0, 0);
+                for (int mi = 0; mi < MI; mi++) {
+                    if (h == 0) {
+                        const f32x4 nrs = *reinterpret_cast<const f32x4 *>(&Rb[mi * 16 + lrow]);
 #pragma unroll
-                for (int nb = 0; nb < NB; nb++) acc[mi][nb] += sc[nb] * p[nb];
+                        for (int nb = 0; nb < NB; nb++) acc[mi][nb] = acc[mi][nb] * r[nb] + nrs;
+                    }
+#pragma unroll
+                    for (int ss = 0; ss < 2; ss++) {
+                        const int q = (h * MI + mi) * 2 + ss;   // fragment sequence number
+                        // next fragment: (mi, s+1), then (mi+1, 2h), then (0, 2) after half 0
+                        if (ss == 0) afr[(q + 1) & 1] = afrag(mi, 2 * h + 1);
+                        else if (mi + 1 < MI) afr[(q + 1) & 1] = afrag(mi + 1, 2 * h);
+                        else if (h == 0) afr[(q + 1) & 1] = afrag(0, 2);
+                        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                        for (int nb = 0; nb < NB; nb++)
+                            acc[mi][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[q & 1], bh[nb][ss], acc[mi][nb], 0, 0, 0);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
             }
         } else {
+#pragma unroll
+            for (int nb = 0; nb < NB; nb++) {
+                const uint4 raw = bring[slot][nb];
+                bq[nb][0] = nibbles_to_bf16_128(raw.x, nc);
+                bq[nb][1] = nibbles_to_bf16_128(raw.y, nc);
+                bq[nb][2] = nibbles_to_bf16_128(raw.z, nc);
+                bq[nb][3] = nibbles_to_bf16_128(raw.w, nc);
+                sc[nb] = half_bits_to_f32((uint16_t)(sring[slot][nb] >> hsel));
+            }
             // k-step outer: the MI*NB MFMA chains of the group advance together,
             // so consecutive MFMAs of a chain are MI*NB instructions apart, and
             // the scale FMAs at the end read chains that finished long before
             f32x4 p[MI][NB];
 #pragma unroll
             for (int s = 0; s < 4; s++) {
-                const int pc = (s * 4 + (lane >> 4)) ^ (lane & 15);
 #pragma unroll
                 for (int mi = 0; mi < MI; mi++) {
-                    const bf16x8 af = *reinterpret_cast<const bf16x8 *>(&Ab[(mi * 16 + (lane & 15)) * 128 + pc * 8]);
+                    const bf16x8 af = afrag(mi, s);
                     const f32x4 c0 = s == 0 ? *reinterpret_cast<const f32x4 *>(&Rb[mi * 16 + lrow]) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int nb = 0; nb < NB; nb++)
@@ -1470,30 +1525,62 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm_gpf(GemmArgs a) {
         }
     };
 
-    // two stages, B one group ahead in registers; every group ends with all
-    // copies landed (vmcnt 0), so the compiler's own waits are already met
-    load_b(0, 0);
-    issue(0, 0);
-    wait_vm_lgkm0<0>();
-    raw_barrier();
-    auto step = [&](int kb, int st, int slot) {
-        const int nk = min(kb + 1, last);
-        if constexpr (RS == 2) load_b(nk, slot ^ 1);
-        issue(nk, st ^ 1);
-        group(st, slot, nk);
+    if constexpr (ROW_OUTER) {
+        // B two groups ahead, activations one group ahead. The compiler counts
+        // only the B loads (the copies are inline assembly), so before it
+        // reads a slot it waits for everything issued before the other slot's
+        // loads, the next group's copies included: both operands are in hand
+        // at the start of the group they feed, as the barrier requires anyway.
+        issue(0, 0);
+        load_b(0, 0);
+        load_b(min(1, last), 1);
+        wait_vm_lgkm0<2 * NB>();
+        raw_barrier();
+        auto step = [&](int kb, int st, int slot) __attribute__((always_inline)) {
+            group(st, slot, min(kb + 2, last), min(kb + 1, last), st ^ 1);
+            // the next group's copies landed; this group's B loads (for two
+            // groups ahead) may still be in flight
+            wait_vm_lgkm0<2 * NB>();
+            raw_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        int kb = 0;
+        for (; kb + 1 < KB; kb += 2) {
+            step(kb, 0, 0);
+            step(kb + 1, 1, 1);
+        }
+        if (kb < KB) step(kb, 0, 0);
+        // back from scale units
+#pragma unroll
+        for (int mi = 0; mi < MI; mi++)
+#pragma unroll
+            for (int nb = 0; nb < NB; nb++) acc[mi][nb] *= s_prev[nb];
+    } else {
+        // two stages, B one group ahead in registers; every group ends with all
+        // copies landed (vmcnt 0), so the compiler's own waits are already met
+        load_b(0, 0);
+        issue(0, 0);
         wait_vm_lgkm0<0>();
         raw_barrier();
-    };
-    int kb = 0;
-    for (; kb + 1 < KB; kb += 2) {
-        step(kb, 0, 0);
-        step(kb + 1, 1, RS - 1);
+        auto step = [&](int kb, int st, int slot) __attribute__((always_inline)) {
+            const int nk = min(kb + 1, last);
+            load_b(nk, slot ^ 1);
+            issue(nk, st ^ 1);
+            group(st, slot, nk, 0, 0);
+            wait_vm_lgkm0<0>();
+            raw_barrier();
+        };
+        int kb = 0;
+        for (; kb + 1 < KB; kb += 2) {
+            step(kb, 0, 0);
+            step(kb + 1, 1, 1);
+        }
+        if (kb < KB) step(kb, 0, 0);
     }
-    if (kb < KB) step(kb, 0, 0);
     __builtin_amdgcn_s_waitcnt(0);
     raw_barrier();
 
-    if (DF == DF_I4ASYM && wave_on) {
+    if (DF == DF_I4ASYM) {
         // zero points: acc[m][n] += sum_g (s_ng z_ng / 128) * nrs_mg, one MFMA
         // contraction over the group index with bf16 hi/lo splits of both sides
         // (hi*hi + hi*lo + lo*hi; relative error ~2^-16 of the correction)
@@ -1578,7 +1665,7 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm_gpf(GemmArgs a) {
                     const float u = acc[mi][2 * pr + 1][r];
                     const uint16_t hb = to_bf16(silu_mul(g, u));
                     hs[mi][r] += bf16f(hb);
-                    if (wave_on && row < rows) a.H[(size_t)(tl.row0 + row) * a.ldh + col] = hb;
+                    if (row < rows) a.H[(size_t)(tl.row0 + row) * a.ldh + col] = hb;
                 }
         }
         float *red = reinterpret_cast<float *>(lds);   // [NW][BM]; the last barrier freed the ring
@@ -1623,7 +1710,7 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm_gpf(GemmArgs a) {
 #pragma unroll
                 for (int nb = 0; nb < NB; nb++) {
                     const int n = n0 + WCOLS * wave + 16 * nb + (lane & 15);
-                    if (wave_on) store_o(a.O + (size_t)gr * a.d + n, acc[mi][nb][r] * wt);
+                    store_o(a.O + (size_t)gr * a.d + n, acc[mi][nb][r] * wt);
                 }
             }
     }
