@@ -212,6 +212,8 @@ struct GemmArgs {
     int32_t T;
     int32_t E;               // routed experts
     int32_t n_tiles;         // 256-column N-tiles of the widest expert (set by the launcher)
+    int32_t nsub;            // prefill: consecutive N-tiles per workgroup (set by the launcher)
+    int32_t n_groups;        // prefill: ceil(n_tiles / nsub)
 };
 // bm: rows per M-tile (16: weight-streaming decode kernel; 64: prefill
 // kernels); max_tiles: grid bound; maxN13: max 2F. df = kDfAllFormats (decode

@@ -17,6 +17,8 @@
 //   gemm2       grouped down GEMM; the epilogue applies the mixing weight
 //   combine     y_t = sum_j O[row(t, j)] + sum_s O_shared(t), fp32, bf16 out
 #include <hip/hip_runtime.h>
+#include <algorithm>
+#include <cstdlib>
 #include <mutex>
 #include <type_traits>
 
@@ -1303,15 +1305,20 @@ __device__ __forceinline__ bool map_work(int L, int ntiles, int NT, int &tile, i
 
 // ---- prefill tiles (group formats): activation ring in LDS ------------------
 //
-// Tiles of 16*MI rows x 16*NB*NW columns: each of the NW waves owns all the
-// rows and 16*NB columns. Per wave and group (128 K positions): the gathered activation
-// rows and their row sums travel as asynchronous global -> LDS copies issued
-// from inline assembly (so the compiler neither waits on them before LDS reads
-// nor counts them), one group ahead in a two-stage ring; the wave's own packed
-// codes and scales are ordinary loads into a register ring, also one group
-// ahead. Every group ends with all loads landed (vmcnt 0) and one barrier that
-// publishes the next activation tile to the workgroup.
-template <int DF, int MODE, int MI, int NB, int NW, bool ROW_OUTER>
+// Tiles of 16*MI rows x 256 columns: each of the NW waves owns all the rows
+// and 16*NB columns. A workgroup computes nsub such tiles side by side (the
+// same rows, consecutive 256-column ranges), running one load pipeline through
+// all of them, so the fixed start and drain of a tile is paid once per
+// workgroup rather than once per tile: the next tile's first operands are in
+// flight while the previous one's results are stored. Per wave and group (128
+// K positions): the gathered activation rows and their row sums travel as
+// asynchronous global -> LDS copies issued from inline assembly (so the
+// compiler neither waits on them before LDS reads nor counts them), one group
+// ahead in a two-stage ring; the wave's own packed codes and scales are
+// ordinary loads into a two-slot register ring, two groups ahead. Every group
+// ends with the next group's copies landed and one barrier that publishes them
+// to the workgroup.
+template <int DF, int MODE, int MI, int NB, int NW, bool MULTI>
 __global__ __launch_bounds__(64 * NW, 2) void k_gemm_gpf(GemmArgs a) {
     constexpr int BM = 16 * MI, RPW = BM / NW;   // activation rows copied per wave
     static_assert(RPW % 4 == 0 && RPW <= 64, "each wave copies whole 4-row slabs");
@@ -1321,31 +1328,36 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm_gpf(GemmArgs a) {
     // the activation tile and its row sums.
     constexpr int ST_A = 0, ST_R = BM * 256, ST_BYTES = ST_R + BM * 4;
     constexpr int WCOLS = 16 * NB;                // B columns per wave
-    constexpr int NTILE = WCOLS * NW;             // B columns per workgroup
-    // Two activation stages, the next group's copies issued early in each
-    // group, and two B register slots. Row-block-outer order
-    // (accumulators in scale units, see group()) loads B two groups ahead,
-    // each slot refilled once its codes are converted; row-block-inner order
-    // loads it one group ahead at the start of the group.
-    constexpr int RS = 2;
-    constexpr int NST = 2;
+    constexpr int NTILE = WCOLS * NW;             // B columns per tile
+    // N (2F or d) is a multiple of 256 = NTILE: every wave of a tile with
+    // n0 < N owns columns below N
+    static_assert(NTILE == 256, "tiles of 256 columns");
+    constexpr int RS = 2;                         // B register slots
+    constexpr int NST = 2;                        // activation stages
+    // apart from the ring (which holds the next tile's first activations
+    // while a tile ends): gate/up, the per-row H sums of each wave, [NW][BM]
+    // floats; down, the rows' mixing weights, [BM] floats
+    constexpr int RED = NST * ST_BYTES;
     constexpr float ZC = GroupConst<DF>::ZC;
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[NST * ST_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[RED + (MODE == 0 ? NW * BM : BM) * 4];
 
-    int tile_id, ntile;
-    if (!map_work(blockIdx.x, *a.num_tiles, a.n_tiles, tile_id, ntile)) return;
+    int tile_id, ngrp;
+    if (!map_work(blockIdx.x, *a.num_tiles, a.n_groups, tile_id, ngrp)) return;
     const Tile tl = a.tiles[tile_id];
     int efmt;
     const ExpertW ew = expert_at(a, tl.e, efmt);
     if (efmt != DF) return;   // another launch computes this expert
     const int N = MODE == 0 ? 2 * ew.F : a.d;
     const int K = MODE == 0 ? a.d : ew.F;
-    const int n0 = ntile * NTILE;
-    if (n0 >= N) return;
+    const int nt0 = ngrp * a.nsub;                // first 256-column tile
+    if (nt0 * NTILE >= N) return;
+    // (one tile per workgroup: nothing is carried past the last group)
+    const int nsub = MULTI ? min(a.nsub, N / NTILE - nt0) : 1;
+    const int KB = K / 128;
+    const int V = nsub * KB;                      // groups through all the tiles
     const int rows = tl.row_end - tl.row0;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform, kept in an SGPR
-    const int KB = K / 128;
     const int lrow = (lane >> 4) * 4;
     const uint32_t lds0 = lds_addr(lds);
 
@@ -1358,29 +1370,30 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm_gpf(GemmArgs a) {
     const int ldr = MODE == 0 ? a.d / 128 : a.ldh / 128;
     const uint16_t *abase = MODE == 0 ? a.x : a.H + (size_t)tl.row0 * lda;
     const float *rbase = MODE == 0 ? a.xsum : a.hsum + (size_t)tl.row0 * ldr;
-    // source row of tile row r (rows past the tile read its first row)
-    auto src_row = [&](int r) {
-        const int rr = r < rows ? r : 0;
+    // source row of tile row r (rows past the tile read its first row), the
+    // tile's nr rows starting at row0
+    auto src_row = [&](int r, int row0, int nr) {
+        const int rr = r < nr ? r : 0;
         if (MODE == 1) return rr;
-        const int gr = tl.row0 + rr;
+        const int gr = row0 + rr;
         return gr < a.P ? a.perm[gr] / a.k : (gr - a.P) % a.T;
     };
     uint32_t aoffb[ADMA];
 #pragma unroll
     for (int i = 0; i < ADMA; i++) {
         const int row = RPW * wave + 4 * i + (lane >> 4);
-        aoffb[i] = 2u * ((uint32_t)src_row(row) * (uint32_t)lda + (uint32_t)(((lane & 15) ^ (row & 15)) * 8));
+        aoffb[i] = 2u * ((uint32_t)src_row(row, tl.row0, rows) * (uint32_t)lda + (uint32_t)(((lane & 15) ^ (row & 15)) * 8));
     }
-    const uint32_t roffb = 4u * (uint32_t)src_row(RPW * wave + (lane < RPW ? lane : 0)) * (uint32_t)ldr;
+    const uint32_t roffb = 4u * (uint32_t)src_row(RPW * wave + (lane < RPW ? lane : 0), tl.row0, rows) * (uint32_t)ldr;
     const uint8_t *codes = MODE == 0 ? ew.c13 : ew.c2;
     const uint16_t *gsc = MODE == 0 ? ew.s13 : ew.s2;
-    // N (2F or d) is a multiple of 256 = NTILE: every wave of a tile with
-    // n0 < N owns columns below N
-    static_assert(NTILE == 256, "tiles of 256 columns");
-    const int ib0 = n0 / 16 + NB * wave;
+    // this wave's first 16-column block in the first tile
+    const int ib0 = nt0 * (NTILE / 16) + NB * wave;
+    const int last = V - 1;
 
-    // the copies' per-lane byte offsets are constant through K; only the
-    // scalar bases advance with the group index
+    // Pipeline position v = j * KB + kb is group kb of tile j. The copies'
+    // per-lane byte offsets are constant through K; only the scalar bases
+    // advance with the group index.
     auto issue = [&](int kb, int st) __attribute__((always_inline)) {
         // wave-uniform by construction; readfirstlane keeps them in SGPRs
         kb = __builtin_amdgcn_readfirstlane(kb);
@@ -1397,323 +1410,321 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm_gpf(GemmArgs a) {
     uint32_t sring[RS][NB];
     const int spair2 = (lane & 15) & ~1;
     const uint32_t hsel = (lane & 1) * 16;
-    auto load_b = [&](int kb, int slot) __attribute__((always_inline)) {
+    auto load_b = [&](int j, int kb, int slot) __attribute__((always_inline)) {
+        j = __builtin_amdgcn_readfirstlane(j);
+        kb = __builtin_amdgcn_readfirstlane(kb);
 #pragma unroll
         for (int nb = 0; nb < NB; nb++) {
-            const size_t blk = (size_t)(ib0 + nb) * KB + kb;
+            const size_t blk = (size_t)(ib0 + (NTILE / 16) * j + nb) * KB + kb;
             bring[slot][nb] = gload16(codes + blk * 1024 + lane * 16);
             sring[slot][nb] = gload(reinterpret_cast<const uint32_t *>(gsc + blk * 16 + spair2));
         }
     };
-    const int last = KB - 1;
 
     f32x4 acc[MI][NB];
-#pragma unroll
-    for (int mi = 0; mi < MI; mi++)
-#pragma unroll
-        for (int nb = 0; nb < NB; nb++) acc[mi][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const NibbleConst nc = nibble_const();
     // scale of the previous group per column block (accumulators in scale units)
     float s_prev[NB];
+    auto reset = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int nb = 0; nb < NB; nb++) s_prev[nb] = 1.0f;
+        for (int mi = 0; mi < MI; mi++)
+#pragma unroll
+            for (int nb = 0; nb < NB; nb++) acc[mi][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int nb = 0; nb < NB; nb++) s_prev[nb] = 1.0f;
+    };
+    reset();
+    const NibbleConst nc = nibble_const();
 
-    // one group: this wave's codes and scales, then the group's MFMAs
-    auto group = [&](int st, int slot, int next_kb, int copy_kb, int copy_st) __attribute__((always_inline)) {
+    // One group: this wave's codes and scales, then the group's MFMAs.
+    // Accumulators in units of the current group's scale: per column,
+    // X = X * (s_prev / s_cur) + nrs, then the group's MFMAs add the
+    // integer-code products straight into X (nrs = -ZC * row sum folds in the
+    // code offset, as a chain's start value would); the tile ends with
+    // X * s_last. With no chain partials live, the codes are converted half a
+    // group (two k-steps) at a time, each half right before its MFMAs, and the
+    // A fragments stream one k-step ahead through a two-slot ring (each LDS
+    // read in flight behind four MFMAs). Once the first half's codes are
+    // converted the next group's activation copies are issued; once the second
+    // half's are, the slot is refilled for two groups ahead.
+    auto group = [&](int st, int slot, int next_j, int next_kb, int copy_kb, int copy_st) __attribute__((always_inline)) {
         const uint8_t *S = lds + st * ST_BYTES;
         const uint16_t *Ab = reinterpret_cast<const uint16_t *>(S + ST_A);
         const float *Rb = reinterpret_cast<const float *>(S + ST_R);
-        bf16x8 bq[NB][4];
-        float sc[NB];
         // A fragment of row block mi, k-step s (XOR-swizzled chunks)
         auto afrag = [&](int mi, int s) __attribute__((always_inline)) {
             const int pc = (s * 4 + (lane >> 4)) ^ (lane & 15);
             return *reinterpret_cast<const bf16x8 *>(&Ab[(mi * 16 + (lane & 15)) * 128 + pc * 8]);
         };
-        if constexpr (ROW_OUTER) {
-            // Accumulators in units of the current group's scale: per column,
-            // X = X * (s_prev / s_cur) + nrs, then the group's MFMAs add the
-            // integer-code products straight into X (nrs = -ZC * row sum folds
-            // in the code offset, as a chain's start value would); the tile
-            // ends with X * s_last. With no chain partials live, the codes are
-            // converted half a group (two k-steps) at a time, each half right
-            // before its MFMAs, and the A fragments stream one k-step ahead
-            // through a two-slot ring (each LDS read in flight behind four
-            // MFMAs). Once the first half's codes are converted the next
-            // group's activation copies are issued; once the second half's are,
-            // the slot is refilled for two groups ahead.
-            float r[NB];
+        float r[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; nb++) {
+            const float sc_cur = half_bits_to_f32((uint16_t)(sring[slot][nb] >> hsel));
+            r[nb] = s_prev[nb] * __builtin_amdgcn_rcpf(sc_cur);
+            s_prev[nb] = sc_cur;
+        }
+        bf16x8 afr[2];
+        afr[0] = afrag(0, 0);
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            bf16x8 bh[NB][2];
 #pragma unroll
             for (int nb = 0; nb < NB; nb++) {
-                const float sc_cur = half_bits_to_f32((uint16_t)(sring[slot][nb] >> hsel));
-                r[nb] = s_prev[nb] * __builtin_amdgcn_rcpf(sc_cur);
-                s_prev[nb] = sc_cur;
+                bh[nb][0] = nibbles_to_bf16_128(h == 0 ? bring[slot][nb].x : bring[slot][nb].z, nc);
+                bh[nb][1] = nibbles_to_bf16_128(h == 0 ? bring[slot][nb].y : bring[slot][nb].w, nc);
             }
-            bf16x8 afr[2];
-            afr[0] = afrag(0, 0);
+            // The converted operands (and the scale ratios) as inputs of an
+            // empty volatile asm: the copies and loads below cannot move above
+            // the conversion, which is where the compiler waits for this
+            // slot's loads, so that wait does not catch them.
 #pragma unroll
-            for (int h = 0; h < 2; h++) {
-                bf16x8 bh[NB][2];
+            for (int nb = 0; nb < NB; nb++)
+                asm volatile("" ::"v"(bh[nb][0]), "v"(bh[nb][1]), "v"(r[nb]));
+            if (h == 0) issue(copy_kb, copy_st);
+            else load_b(next_j, next_kb, slot);
 #pragma unroll
-                for (int nb = 0; nb < NB; nb++) {
-                    bh[nb][0] = nibbles_to_bf16_128(h == 0 ? bring[slot][nb].x : bring[slot][nb].z, nc);
-                    bh[nb][1] = nibbles_to_bf16_128(h == 0 ? bring[slot][nb].y : bring[slot][nb].w, nc);
+            for (int mi = 0; mi < MI; mi++) {
+                if (h == 0) {
+                    const f32x4 nrs = *reinterpret_cast<const f32x4 *>(&Rb[mi * 16 + lrow]);
+#pragma unroll
+                    for (int nb = 0; nb < NB; nb++) acc[mi][nb] = acc[mi][nb] * r[nb] + nrs;
                 }
-                // (after the conversion, which is where the compiler waits for
-                // this slot's loads: the copies and loads issued here are not
-                // caught by that wait)
-                // the converted operands (and the scale ratios) as inputs of an
-                // empty volatile asm: the copies and loads below cannot move
-                // above the conversion, and with it the compiler's waits for
-                // this slot's loads
 #pragma unroll
-                for (int nb = 0; nb < NB; nb++)
-                    asm volatile("" ::"v"(bh[nb][0]), "v"(bh[nb][1]), "v"(r[nb]));
-                if (h == 0) issue(copy_kb, copy_st);
-                else load_b(next_kb, slot);
-#pragma unroll
-                for (int mi = 0; mi < MI; mi++) {
-                    if (h == 0) {
-                        const f32x4 nrs = *reinterpret_cast<const f32x4 *>(&Rb[mi * 16 + lrow]);
-#pragma unroll
-                        for (int nb = 0; nb < NB; nb++) acc[mi][nb] = acc[mi][nb] * r[nb] + nrs;
-                    }
-#pragma unroll
-                    for (int ss = 0; ss < 2; ss++) {
-                        const int q = (h * MI + mi) * 2 + ss;   // fragment sequence number
-                        // next fragment: (mi, s+1), then (mi+1, 2h), then (0, 2) after half 0
-                        if (ss == 0) afr[(q + 1) & 1] = afrag(mi, 2 * h + 1);
-                        else if (mi + 1 < MI) afr[(q + 1) & 1] = afrag(mi + 1, 2 * h);
-                        else if (h == 0) afr[(q + 1) & 1] = afrag(0, 2);
-                        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                        for (int nb = 0; nb < NB; nb++)
-                            acc[mi][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[q & 1], bh[nb][ss], acc[mi][nb], 0, 0, 0);
-                        __builtin_amdgcn_sched_barrier(0);
-                    }
-                }
-            }
-        } else {
-#pragma unroll
-            for (int nb = 0; nb < NB; nb++) {
-                const uint4 raw = bring[slot][nb];
-                bq[nb][0] = nibbles_to_bf16_128(raw.x, nc);
-                bq[nb][1] = nibbles_to_bf16_128(raw.y, nc);
-                bq[nb][2] = nibbles_to_bf16_128(raw.z, nc);
-                bq[nb][3] = nibbles_to_bf16_128(raw.w, nc);
-                sc[nb] = half_bits_to_f32((uint16_t)(sring[slot][nb] >> hsel));
-            }
-            // k-step outer: the MI*NB MFMA chains of the group advance together,
-            // so consecutive MFMAs of a chain are MI*NB instructions apart, and
-            // the scale FMAs at the end read chains that finished long before
-            f32x4 p[MI][NB];
-#pragma unroll
-            for (int s = 0; s < 4; s++) {
-#pragma unroll
-                for (int mi = 0; mi < MI; mi++) {
-                    const bf16x8 af = afrag(mi, s);
-                    const f32x4 c0 = s == 0 ? *reinterpret_cast<const f32x4 *>(&Rb[mi * 16 + lrow]) : f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int ss = 0; ss < 2; ss++) {
+                    const int q = (h * MI + mi) * 2 + ss;   // fragment sequence number
+                    // next fragment: (mi, s+1), then (mi+1, 2h), then (0, 2) after half 0
+                    if (ss == 0) afr[(q + 1) & 1] = afrag(mi, 2 * h + 1);
+                    else if (mi + 1 < MI) afr[(q + 1) & 1] = afrag(mi + 1, 2 * h);
+                    else if (h == 0) afr[(q + 1) & 1] = afrag(0, 2);
+                    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                     for (int nb = 0; nb < NB; nb++)
-                        p[mi][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bq[nb][s], s == 0 ? c0 : p[mi][nb], 0, 0, 0);
+                        acc[mi][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[q & 1], bh[nb][ss], acc[mi][nb], 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
-#pragma unroll
-            for (int mi = 0; mi < MI; mi++)
-#pragma unroll
-                for (int nb = 0; nb < NB; nb++) acc[mi][nb] += sc[nb] * p[mi][nb];
         }
     };
-
-    if constexpr (ROW_OUTER) {
-        // B two groups ahead, activations one group ahead. The compiler counts
-        // only the B loads (the copies are inline assembly), so before it
-        // reads a slot it waits for everything issued before the other slot's
-        // loads, the next group's copies included: both operands are in hand
-        // at the start of the group they feed, as the barrier requires anyway.
-        issue(0, 0);
-        load_b(0, 0);
-        load_b(min(1, last), 1);
+    // tile and group of pipeline position t, from tile j starting at vs
+    auto locate = [&](int t, int j, int vs, int &jt, int &kb) __attribute__((always_inline)) {
+        jt = j;
+        kb = t - vs;
+        if (MULTI)
+            while (kb >= KB) {
+                kb -= KB;
+                ++jt;
+            }
+    };
+    // group v of tile j (which starts at vs); afterwards group v+1's copies
+    // have landed (group v+2's B loads may still be in flight) and the
+    // barrier has published them
+    auto step = [&](int v, int st, int slot, int j, int vs) __attribute__((always_inline)) {
+        int nj, nkb, cj, ckb;
+        locate(min(v + 2, last), j, vs, nj, nkb);
+        locate(min(v + 1, last), j, vs, cj, ckb);
+        group(st, slot, nj, nkb, ckb, st ^ 1);
         wait_vm_lgkm0<2 * NB>();
         raw_barrier();
-        auto step = [&](int kb, int st, int slot) __attribute__((always_inline)) {
-            group(st, slot, min(kb + 2, last), min(kb + 1, last), st ^ 1);
-            // the next group's copies landed; this group's B loads (for two
-            // groups ahead) may still be in flight
-            wait_vm_lgkm0<2 * NB>();
-            raw_barrier();
-            __builtin_amdgcn_sched_barrier(0);
-        };
-        int kb = 0;
-        for (; kb + 1 < KB; kb += 2) {
-            step(kb, 0, 0);
-            step(kb + 1, 1, 1);
-        }
-        if (kb < KB) step(kb, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // Results of tile j (its columns start at 256 * (nt0 + j)).
+    auto finish = [&](int j) __attribute__((always_inline)) {
+        const int n0 = (nt0 + j) * NTILE;
+        const int ibj = ib0 + (NTILE / 16) * j;
+        // the tile's rows and the output pitches as opaque values here: the
+        // row addresses and bounds below are computed per tile, not hoisted
+        // out of the loop into registers live through every group
+        int row0 = tl.row0, nrows = rows, ld_out = MODE == 0 ? a.ldh : a.d, lrow = (lane >> 4) * 4;
+        asm volatile("" : "+s"(row0), "+s"(nrows), "+s"(ld_out), "+v"(lrow));
         // back from scale units
 #pragma unroll
         for (int mi = 0; mi < MI; mi++)
 #pragma unroll
             for (int nb = 0; nb < NB; nb++) acc[mi][nb] *= s_prev[nb];
-    } else {
-        // two stages, B one group ahead in registers; every group ends with all
-        // copies landed (vmcnt 0), so the compiler's own waits are already met
-        load_b(0, 0);
-        issue(0, 0);
-        wait_vm_lgkm0<0>();
-        raw_barrier();
-        auto step = [&](int kb, int st, int slot) __attribute__((always_inline)) {
-            const int nk = min(kb + 1, last);
-            load_b(nk, slot ^ 1);
-            issue(nk, st ^ 1);
-            group(st, slot, nk, 0, 0);
-            wait_vm_lgkm0<0>();
-            raw_barrier();
-        };
-        int kb = 0;
-        for (; kb + 1 < KB; kb += 2) {
-            step(kb, 0, 0);
-            step(kb + 1, 1, 1);
-        }
-        if (kb < KB) step(kb, 0, 0);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    raw_barrier();
 
-    if (DF == DF_I4ASYM) {
-        // zero points: acc[m][n] += sum_g (s_ng z_ng / 128) * nrs_mg, one MFMA
-        // contraction over the group index with bf16 hi/lo splits of both sides
-        // (hi*hi + hi*lo + lo*hi; relative error ~2^-16 of the correction)
-        const uint16_t *zcp = MODE == 0 ? ew.zc13 : ew.zc2;
-        const int GS = (KB + 31) / 32;
-        uint32_t zrow[MI];
+        if (DF == DF_I4ASYM) {
+            // zero points: acc[m][n] += sum_g (s_ng z_ng / 128) * nrs_mg, one MFMA
+            // contraction over the group index with bf16 hi/lo splits of both sides
+            // (hi*hi + hi*lo + lo*hi; relative error ~2^-16 of the correction)
+            const uint16_t *zcp = MODE == 0 ? ew.zc13 : ew.zc2;
+            const int GS = (KB + 31) / 32;
+            uint32_t zrow[MI];
 #pragma unroll
-        for (int mi = 0; mi < MI; mi++) zrow[mi] = (uint32_t)src_row(mi * 16 + (lane & 15)) * (uint32_t)ldr;
-        // the eight row sums a lane needs per row block and K range are
-        // consecutive floats: two 16-byte loads when rows and ranges keep them
-        // aligned (uniform), else eight single loads
-        const bool vec = ldr % 8 == 0 && KB % 8 == 0;
-        for (int gs = 0; gs < GS; gs++) {
-            bf16x8 bh[NB], bl[NB];
+            for (int mi = 0; mi < MI; mi++) zrow[mi] = (uint32_t)src_row(mi * 16 + (lane & 15), row0, nrows) * (uint32_t)ldr;
+            // the eight row sums a lane needs per row block and K range are
+            // consecutive floats: two 16-byte loads when rows and ranges keep them
+            // aligned (uniform), else eight single loads
+            const bool vec = ldr % 8 == 0 && KB % 8 == 0;
+            for (int gs = 0; gs < GS; gs++) {
+                bf16x8 bh[NB], bl[NB];
 #pragma unroll
-            for (int nb = 0; nb < NB; nb++) {
-                const uint16_t *q = zcp + ((size_t)(ib0 + nb) * GS + gs) * 1024 + lane * 8;
-                bh[nb] = __builtin_bit_cast(bf16x8, gload16(q));
-                bl[nb] = __builtin_bit_cast(bf16x8, gload16(q + 512));
-            }
-            const int g0 = gs * 32 + (lane >> 4) * 8;
-            float rv[MI][8];
-            if (vec) {
-                // past the last group (KB % 32 != 0): the last 8 groups are
-                // read and zeroed
-                const bool gin = g0 < KB;
-                const int gc = gin ? g0 : KB - 8;
+                for (int nb = 0; nb < NB; nb++) {
+                    const uint16_t *q = zcp + ((size_t)(ibj + nb) * GS + gs) * 1024 + lane * 8;
+                    bh[nb] = __builtin_bit_cast(bf16x8, gload16(q));
+                    bl[nb] = __builtin_bit_cast(bf16x8, gload16(q + 512));
+                }
+                const int g0 = gs * 32 + (lane >> 4) * 8;
+                float rv[MI][8];
+                if (vec) {
+                    // past the last group (KB % 32 != 0): the last 8 groups are
+                    // read and zeroed
+                    const bool gin = g0 < KB;
+                    const int gc = gin ? g0 : KB - 8;
+#pragma unroll
+                    for (int mi = 0; mi < MI; mi++) {
+                        const uint4 u0 = gload16(rbase + zrow[mi] + gc);
+                        const uint4 u1 = gload16(rbase + zrow[mi] + gc + 4);
+                        const uint32_t uu[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+                        for (int jj = 0; jj < 8; jj++) rv[mi][jj] = gin ? __uint_as_float(uu[jj]) : 0.0f;
+                    }
+                } else {
+#pragma unroll
+                    for (int mi = 0; mi < MI; mi++)
+#pragma unroll
+                        for (int jj = 0; jj < 8; jj++) rv[mi][jj] = g0 + jj < KB ? gload(rbase + zrow[mi] + g0 + jj) : 0.0f;
+                }
 #pragma unroll
                 for (int mi = 0; mi < MI; mi++) {
-                    const uint4 u0 = gload16(rbase + zrow[mi] + gc);
-                    const uint4 u1 = gload16(rbase + zrow[mi] + gc + 4);
-                    const uint32_t uu[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+                    bf16x8 ah, al;
 #pragma unroll
-                    for (int j = 0; j < 8; j++) rv[mi][j] = gin ? __uint_as_float(uu[j]) : 0.0f;
+                    for (int jj = 0; jj < 8; jj++) {
+                        __bf16 hh, ll;
+                        split_bf16(rv[mi][jj], hh, ll);
+                        ah[jj] = hh;
+                        al[jj] = ll;
+                    }
+#pragma unroll
+                    for (int nb = 0; nb < NB; nb++) {
+                        acc[mi][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh[nb], acc[mi][nb], 0, 0, 0);
+                        acc[mi][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl[nb], acc[mi][nb], 0, 0, 0);
+                        acc[mi][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh[nb], acc[mi][nb], 0, 0, 0);
+                    }
                 }
-            } else {
+            }
+        }
+
+        if (MODE == 0) {
+            // H = silu(gate) * up; the tile's columns are two groups of 128 H
+            // columns, whose per-row sums (of the bf16 values) feed the down
+            // GEMM's zero-offset term
+            constexpr int WPG = 16 / NB;   // waves per 128-wide H group
+            static_assert(NB % 2 == 0 && NW % WPG == 0, "a tile covers whole 128-wide H groups");
+            float hs[MI][4];
+#pragma unroll
+            for (int mi = 0; mi < MI; mi++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) hs[mi][r] = 0.0f;
+            // the tile's H rows: a uniform base and 32-bit per-lane offsets
+            uint8_t *Hb = reinterpret_cast<uint8_t *>(a.H + (size_t)row0 * ld_out);
+#pragma unroll
+            for (int pr = 0; pr < NB / 2; pr++) {
+                const int col = ((ibj + 2 * pr) >> 1) * 16 + (lane & 15);
 #pragma unroll
                 for (int mi = 0; mi < MI; mi++)
 #pragma unroll
-                    for (int j = 0; j < 8; j++) rv[mi][j] = g0 + j < KB ? gload(rbase + zrow[mi] + g0 + j) : 0.0f;
+                    for (int r = 0; r < 4; r++) {
+                        const int row = mi * 16 + lrow + r;
+                        const float g = acc[mi][2 * pr][r];
+                        const float u = acc[mi][2 * pr + 1][r];
+                        const uint16_t hb = to_bf16(silu_mul(g, u));
+                        hs[mi][r] += bf16f(hb);
+                        if (row < nrows) *reinterpret_cast<uint16_t *>(Hb + 2u * (uint32_t)(row * ld_out + col)) = hb;
+                    }
             }
+            float *red = reinterpret_cast<float *>(lds + RED);
+            // 16-lane row sums, the 4*MI independent chains interleaved step by
+            // step (a DPP read right after the write of its source needs wait states)
+            auto row_step = [&](auto ctrl) {
 #pragma unroll
-            for (int mi = 0; mi < MI; mi++) {
-                bf16x8 ah, al;
+                for (int mi = 0; mi < MI; mi++)
 #pragma unroll
-                for (int j = 0; j < 8; j++) {
-                    __bf16 h, l;
-                    split_bf16(rv[mi][j], h, l);
-                    ah[j] = h;
-                    al[j] = l;
-                }
-#pragma unroll
-                for (int nb = 0; nb < NB; nb++) {
-                    acc[mi][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh[nb], acc[mi][nb], 0, 0, 0);
-                    acc[mi][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl[nb], acc[mi][nb], 0, 0, 0);
-                    acc[mi][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh[nb], acc[mi][nb], 0, 0, 0);
-                }
-            }
-        }
-    }
-
-    if (MODE == 0) {
-        // H = silu(gate) * up; the workgroup's columns are NTILE/256 groups of
-        // 128 H columns, whose per-row sums (of the bf16 values) feed the down
-        // GEMM's zero-offset term
-        constexpr int WPG = 16 / NB;   // waves per 128-wide H group
-        static_assert(NB % 2 == 0 && NW % WPG == 0, "a workgroup covers whole 128-wide H groups");
-        float hs[MI][4];
-#pragma unroll
-        for (int mi = 0; mi < MI; mi++)
-#pragma unroll
-            for (int r = 0; r < 4; r++) hs[mi][r] = 0.0f;
-#pragma unroll
-        for (int pr = 0; pr < NB / 2; pr++) {
-            const int col = ((ib0 + 2 * pr) >> 1) * 16 + (lane & 15);
+                    for (int r = 0; r < 4; r++) hs[mi][r] += dpp_zero<decltype(ctrl)::value, 0xF>(hs[mi][r]);
+            };
+            row_step(std::integral_constant<int, kDppShr1>{});
+            row_step(std::integral_constant<int, kDppShr2>{});
+            row_step(std::integral_constant<int, kDppShr4>{});
+            row_step(std::integral_constant<int, kDppShr8>{});
 #pragma unroll
             for (int mi = 0; mi < MI; mi++)
+#pragma unroll
+                for (int r = 0; r < 4; r++)
+                    if ((lane & 15) == 15) red[wave * BM + mi * 16 + lrow + r] = hs[mi][r];
+            // LDS writes done, then the barrier (no wait for the B loads in
+            // flight); the group barriers that follow order these reads
+            // before the next tile's writes
+            wait_vm_lgkm0<63>();
+            raw_barrier();
+            for (int t = threadIdx.x; t < BM * (NW / WPG); t += 64 * NW) {
+                const int h = t / BM, row = t % BM;
+                const int grp = n0 / 256 + h;   // 128-wide H group
+                if (row < nrows && grp < ew.F / 128) {
+                    const float *rr = red + WPG * h * BM + row;
+                    float v = 0.0f;
+#pragma unroll
+                    for (int w = 0; w < WPG; w++) v += rr[w * BM];
+                    a.hsum[(size_t)(row0 + row) * (a.ldh / 128) + grp] = -ZC * v;
+                }
+            }
+        } else {
+            // the tile's O rows: a uniform base and 32-bit per-lane offsets
+            uint8_t *Ob = reinterpret_cast<uint8_t *>(a.O + (size_t)row0 * ld_out);
+            const float *wts = reinterpret_cast<const float *>(lds + RED);
+#pragma unroll
+            for (int mi = 0; mi < MI; mi++) {
+                const f32x4 wt = *reinterpret_cast<const f32x4 *>(&wts[mi * 16 + lrow]);
 #pragma unroll
                 for (int r = 0; r < 4; r++) {
                     const int row = mi * 16 + lrow + r;
-                    const float g = acc[mi][2 * pr][r];
-                    const float u = acc[mi][2 * pr + 1][r];
-                    const uint16_t hb = to_bf16(silu_mul(g, u));
-                    hs[mi][r] += bf16f(hb);
-                    if (row < rows) a.H[(size_t)(tl.row0 + row) * a.ldh + col] = hb;
-                }
-        }
-        float *red = reinterpret_cast<float *>(lds);   // [NW][BM]; the last barrier freed the ring
-        // 16-lane row sums, the 4*MI independent chains interleaved step by
-        // step (a DPP read right after the write of its source needs wait states)
-        auto row_step = [&](auto ctrl) {
+                    if (row >= nrows) continue;
 #pragma unroll
-            for (int mi = 0; mi < MI; mi++)
-#pragma unroll
-                for (int r = 0; r < 4; r++) hs[mi][r] += dpp_zero<decltype(ctrl)::value, 0xF>(hs[mi][r]);
-        };
-        row_step(std::integral_constant<int, kDppShr1>{});
-        row_step(std::integral_constant<int, kDppShr2>{});
-        row_step(std::integral_constant<int, kDppShr4>{});
-        row_step(std::integral_constant<int, kDppShr8>{});
-#pragma unroll
-        for (int mi = 0; mi < MI; mi++)
-#pragma unroll
-            for (int r = 0; r < 4; r++)
-                if ((lane & 15) == 15) red[wave * BM + mi * 16 + lrow + r] = hs[mi][r];
-        __syncthreads();
-        for (int t = threadIdx.x; t < BM * (NW / WPG); t += 64 * NW) {
-            const int h = t / BM, row = t % BM;
-            const int grp = n0 / 256 + h;   // 128-wide H group
-            if (row < rows && grp < ew.F / 128) {
-                const float *rr = red + WPG * h * BM + row;
-                float v = 0.0f;
-#pragma unroll
-                for (int w = 0; w < WPG; w++) v += rr[w * BM];
-                a.hsum[(size_t)(tl.row0 + row) * (a.ldh / 128) + grp] = -ZC * v;
-            }
-        }
-    } else {
-#pragma unroll
-        for (int mi = 0; mi < MI; mi++)
-#pragma unroll
-            for (int r = 0; r < 4; r++) {
-                const int row = mi * 16 + lrow + r;
-                if (row >= rows) continue;
-                const int gr = tl.row0 + row;
-                const float wt = gr < a.P ? a.wrow[gr] : 1.0f;
-#pragma unroll
-                for (int nb = 0; nb < NB; nb++) {
-                    const int n = n0 + WCOLS * wave + 16 * nb + (lane & 15);
-                    store_o(a.O + (size_t)gr * a.d + n, acc[mi][nb][r] * wt);
+                    for (int nb = 0; nb < NB; nb++) {
+                        const int n = n0 + WCOLS * wave + 16 * nb + (lane & 15);
+                        store_o(reinterpret_cast<float *>(Ob + 4u * (uint32_t)(row * ld_out + n)), acc[mi][nb][r] * wt[r]);
+                    }
                 }
             }
+        }
+    };
+
+    // The compiler counts only the B loads (the copies are inline assembly),
+    // so before it reads a slot it waits for everything issued before the
+    // other slot's loads, the next group's copies included: both operands are
+    // in hand at the start of the group they feed, as the barrier requires
+    // anyway.
+    if (MODE == 1 && threadIdx.x < BM) {
+        // mixing weight per row (1 for shared-expert rows and rows past the tile)
+        const int gr = tl.row0 + threadIdx.x;
+        reinterpret_cast<float *>(lds + RED)[threadIdx.x] = threadIdx.x < rows && gr < a.P ? a.wrow[gr] : 1.0f;
     }
+    issue(0, 0);
+    load_b(0, 0, 0);
+    {
+        int j1, kb1;
+        locate(min(1, last), 0, 0, j1, kb1);
+        load_b(j1, kb1, 1);
+    }
+    wait_vm_lgkm0<2 * NB>();
+    raw_barrier();
+    // Group v reads stage and slot v & 1; a tile's groups run in pairs (one
+    // lone group first when it starts at an odd v, one last when it ends
+    // before a pair is complete).
+    int v = 0, j = 0, vend = KB;
+    for (;;) {
+        const int vs = vend - KB;
+        if (v & 1) step(v++, 1, 1, j, vs);
+        for (; v + 1 < vend; v += 2) {
+            step(v, 0, 0, j, vs);
+            step(v + 1, 1, 1, j, vs);
+        }
+        if (v < vend) step(v++, 0, 0, j, vs);
+        finish(j);
+        if (++j == nsub) break;
+        vend += KB;
+        reset();
+    }
+    // no copy into LDS may be in flight when the workgroup ends
+    __builtin_amdgcn_s_waitcnt(0);
 }
 
 // Per-channel formats (int8, e4m3): codes convert exactly to bf16 and the
@@ -2362,21 +2373,63 @@ static hipError_t launch_gemm_dec(int df, dim3 grid, const GemmArgs &a, hipStrea
     return hipGetLastError();
 }
 
+// Consecutive 256-column tiles per prefill workgroup: with short K (the down
+// projection of narrow experts) a tile spends a large part of its time on
+// filling and draining its load pipeline, which one pipeline through several
+// tiles pays once. Fewer, longer workgroups also quantize worse onto the
+// machine's 512 workgroup slots (two per CU): a workgroup takes up to
+// kGemmGroupTarget / KB tiles, as long as the launch keeps at least
+// kGemmMinWorkgroups workgroups (six rounds of the slots). The environment
+// variable QMOE_PREFILL_TILES_PER_WG = n >= 1 sets the count instead (capped
+// at the tiles there are; for tuning and tests).
+#ifndef QMOE_GEMM_GROUP_TARGET
+#define QMOE_GEMM_GROUP_TARGET 12
+#endif
+constexpr int kGemmGroupTarget = QMOE_GEMM_GROUP_TARGET;
+constexpr long kGemmMinWorkgroups = 6 * 512;
+
+static int gemm_nsub(int df, int bm, int KB, int n_tiles, int max_tiles) {
+    // the 96-row INT4-asym variant has no registers to spare for the
+    // operands in flight while a tile's zero-point correction runs
+    if (df == DF_I4ASYM && bm == 96) return 1;
+    if (const char *env = std::getenv("QMOE_PREFILL_TILES_PER_WG")) {
+        const int n = std::atoi(env);
+        if (n >= 1) return std::min(n, n_tiles);
+    }
+    int nsub = std::min(n_tiles, std::max(1, (kGemmGroupTarget + KB - 1) / KB));
+    while (nsub > 1 && (long)max_tiles * ((n_tiles + nsub - 1) / nsub) < kGemmMinWorkgroups) nsub--;
+    return nsub;
+}
+
+template <int DF, int MODE, int MI>
+static void launch_gpf(bool multi, dim3 grid, const GemmArgs &a, hipStream_t s) {
+    if constexpr (DF == DF_I4ASYM && MI == 6) {
+        hipLaunchKernelGGL((k_gemm_gpf<DF, MODE, MI, 4, 4, false>), grid, dim3(256), 0, s, a);
+    } else {
+        if (multi) hipLaunchKernelGGL((k_gemm_gpf<DF, MODE, MI, 4, 4, true>), grid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((k_gemm_gpf<DF, MODE, MI, 4, 4, false>), grid, dim3(256), 0, s, a);
+    }
+}
+
 template <int MODE>
 static hipError_t launch_gemm(int df, int bm, int max_tiles, int maxN, const GemmArgs &a0, hipStream_t s) {
     GemmArgs a = a0;
     a.n_tiles = (maxN + 255) / 256;
     if ((bm == 64 || bm == 96) && (df == DF_I4SYM || df == DF_I4ASYM)) {
         // prefill tiles: bm rows x 256 columns, 4 waves of bm x 64, two stages,
-        // two workgroups per CU (<= 256 VGPRs; 33 KB / 50 KB LDS each)
-        const long total = (long)max_tiles * a.n_tiles;
+        // two workgroups per CU (<= 256 VGPRs; 34 KB / 52 KB LDS each); K of
+        // the down projection taken as the widest expert's
+        a.nsub = gemm_nsub(df, bm, (MODE == 0 ? a.d : a.ldh) / 128, a.n_tiles, max_tiles);
+        a.n_groups = (a.n_tiles + a.nsub - 1) / a.nsub;
+        const long total = (long)max_tiles * a.n_groups;
         dim3 grid((unsigned)(8 * ((total + 7) / 8)));
+        const bool multi = a.nsub > 1;
         if (bm == 64) {
-            if (df == DF_I4SYM) hipLaunchKernelGGL((k_gemm_gpf<DF_I4SYM, MODE, 4, 4, 4, false>), grid, dim3(256), 0, s, a);
-            else hipLaunchKernelGGL((k_gemm_gpf<DF_I4ASYM, MODE, 4, 4, 4, false>), grid, dim3(256), 0, s, a);
+            if (df == DF_I4SYM) launch_gpf<DF_I4SYM, MODE, 4>(multi, grid, a, s);
+            else launch_gpf<DF_I4ASYM, MODE, 4>(multi, grid, a, s);
         } else {
-            if (df == DF_I4SYM) hipLaunchKernelGGL((k_gemm_gpf<DF_I4SYM, MODE, 6, 4, 4, true>), grid, dim3(256), 0, s, a);
-            else hipLaunchKernelGGL((k_gemm_gpf<DF_I4ASYM, MODE, 6, 4, 4, true>), grid, dim3(256), 0, s, a);
+            if (df == DF_I4SYM) launch_gpf<DF_I4SYM, MODE, 6>(multi, grid, a, s);
+            else launch_gpf<DF_I4ASYM, MODE, 6>(multi, grid, a, s);
         }
         return hipGetLastError();
     }

@@ -101,7 +101,7 @@ def test_forward_expert_relabelling_invariance(cfg):
         route = QMoE.route_buffers(T, cfg.E, cfg.k)
         y = layer.forward(x, route=route)
         torch.cuda.synchronize()
-        out.append((y.cpu().numpy().view(np.uint16), route["logits"].cpu().numpy(),
+        out.append((y.view(torch.int16).cpu().numpy().view(np.uint16), route["logits"].cpu().numpy(),
                     route["topk_idx"].cpu().numpy(), route["topk_w"].cpu().numpy()))
         del layer
     (ya, la, ia, wa), (yb, lb, ib, wb) = out
