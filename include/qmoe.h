@@ -244,11 +244,16 @@ typedef struct {
 
 /* Caller-owned device buffers that receive the routing of a forward; any may
  * be NULL: logits_rows [T][n_rows], logits_cols [T][n_cols] fp32, topk_idx
- * [T][k] int32 (flat expert index, best first), topk_w [T][k] fp32. */
+ * [T][k] int32 (flat expert index, best first), topk_w [T][k] fp32; perm
+ * [T*k] int32, written by the expert-centric schedule only: its task list,
+ * perm[row] = t*k + j, rows grouped by expert group (group of flat index i:
+ * i / ceil(N/256), groups in ascending order) and tokens ascending inside a
+ * group. */
 typedef struct {
     float *logits_rows, *logits_cols;
     int32_t *topk_idx;
     float *topk_w;
+    int32_t *perm;
 } qmoe_atomic_route_out;
 
 /* Uploads W, V [N][d] and R_r [n_rows][d], R_c [n_cols][d] (host bf16 arrays,

@@ -50,7 +50,7 @@ class QmoeAtomicConfig(C.Structure):
 
 
 class QmoeAtomicRouteOut(C.Structure):
-    _fields_ = [(n, C.c_void_p) for n in ("logits_rows", "logits_cols", "topk_idx", "topk_w")]
+    _fields_ = [(n, C.c_void_p) for n in ("logits_rows", "logits_cols", "topk_idx", "topk_w", "perm")]
 
 
 class QmoeRouteOut(C.Structure):
@@ -411,7 +411,8 @@ class AtomicLayer:
 
     def forward(self, x, y=None, schedule: int = QMOE_SCHEDULE_EXPERT_CENTRIC, route=None, stream=None):
         """x: [T][d] bf16 CUDA tensor -> y; route: optional dict of CUDA tensors
-        logits_rows, logits_cols, topk_idx, topk_w to fill."""
+        logits_rows, logits_cols, topk_idx, topk_w, perm (expert-centric task
+        list) to fill."""
         import torch
         self.check_args(x, y, route)
         if y is None:
@@ -419,7 +420,7 @@ class AtomicLayer:
         dbg = None
         if route is not None:
             dbg = QmoeAtomicRouteOut(*[_dptr(route.get(n)) for n in ("logits_rows", "logits_cols", "topk_idx",
-                                                                      "topk_w")])
+                                                                      "topk_w", "perm")])
         rc = qmoe_atomic_forward(self.ctx, x.data_ptr(), x.shape[0], y.data_ptr(), schedule, dbg,
                                  _stream_handle(stream))
         _check(rc, "qmoe_atomic_forward")
@@ -428,7 +429,7 @@ class AtomicLayer:
     def check_args(self, x, y=None, route=None, require_cuda: bool = True) -> int:
         """x [T][d] bf16 with T <= max_tokens, y like x, route buffers
         logits_rows [T][n_rows], logits_cols [T][n_cols] fp32, topk_idx [T][k]
-        int32, topk_w [T][k] fp32. Raises ValueError; returns T."""
+        int32, topk_w [T][k] fp32, perm [T*k] int32. Raises ValueError; returns T."""
         import torch
         if x.dim() != 2:
             raise ValueError(f"x: expected a 2-D [T][d_model] tensor, got shape {tuple(x.shape)}")
@@ -440,7 +441,8 @@ class AtomicLayer:
             check_tensor("y", y, (T, self.d), torch.bfloat16, require_cuda)
         if route is not None:
             want = dict(logits_rows=((T, self.n_rows), torch.float32), logits_cols=((T, self.n_cols), torch.float32),
-                        topk_idx=((T, self.k), torch.int32), topk_w=((T, self.k), torch.float32))
+                        topk_idx=((T, self.k), torch.int32), topk_w=((T, self.k), torch.float32),
+                        perm=((T * self.k,), torch.int32))
             for n, t in route.items():
                 if n not in want:
                     raise ValueError(f"route: unknown buffer {n}")

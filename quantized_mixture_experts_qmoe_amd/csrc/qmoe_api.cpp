@@ -1102,6 +1102,8 @@ int qmoe_atomic_forward(qmoe_atomic_ctx *c, const uint16_t *x, int32_t T, uint16
         if (!rc && dbg->logits_cols) rc = copy_cols(dbg->logits_cols, c->logits + Nr, Nc);
         if (!rc && dbg->topk_idx) rc = copy_out(dbg->topk_idx, c->idx, (size_t)P * 4, s);
         if (!rc && dbg->topk_w) rc = copy_out(dbg->topk_w, c->w, (size_t)P * 4, s);
+        if (!rc && dbg->perm && schedule == QMOE_SCHEDULE_EXPERT_CENTRIC)
+            rc = copy_out(dbg->perm, c->perm, (size_t)P * 4, s);
     }
     return rc;
 }

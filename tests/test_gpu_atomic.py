@@ -64,6 +64,30 @@ def test_atomic_layer(schedule, T, d, nr, nc, k):
     assert_output_close(bf16_tensor_to_f64(y), y_ref, f"atomic {schedule}", own >= 0.75 * MAX_ABS_RMS)
 
 
+@pytest.mark.parametrize("T,nr,nc,k", [(300, 64, 64, 8), (1000, 1024, 2, 3), (40, 300, 300, 8), (257, 8, 8, 1),
+                                       (1, 1, 50, 4)])
+def test_atomic_task_list_is_the_stable_sort(oracle_mod, T, nr, nc, k):
+    """The expert-centric task list, bit for bit: the stable sort of the
+    (token, slot) tasks by expert group (ceil(N/256) consecutive flat indices
+    per group), tokens ascending inside a group (OmniMoE page, technical
+    summary 2.2: routing decisions flattened and grouped by expert), computed
+    by the oracle's dispatch on the GPU's own selection."""
+    d = 512
+    print(f"[case] atomic task list T={T} grid={nr}x{nc} k={k}", flush=True)
+    inp = make_atomic_inputs(T, d, nr, nc, seed=3 * T + nr)
+    layer = AtomicLayer(inp.w_in, inp.w_out, inp.router_rows, inp.router_cols, top_k=k, max_tokens=T)
+    route = dict(topk_idx=torch.empty((T, k), dtype=torch.int32, device="cuda"),
+                 perm=torch.full((T * k,), -1, dtype=torch.int32, device="cuda"))
+    layer.forward(to_dev_bf16(inp.x), schedule=QMOE_SCHEDULE_EXPERT_CENTRIC, route=route)
+    torch.cuda.synchronize()
+    idx, perm = route["topk_idx"].cpu().numpy(), route["perm"].cpu().numpy()
+    layer.close()
+    N = nr * nc
+    B = (N + 255) // 256
+    counts, offsets, ref_perm, _ = oracle_mod.dispatch(idx // B, (N + B - 1) // B)
+    assert np.array_equal(perm, ref_perm)
+
+
 @pytest.mark.parametrize("schedule", ["expert", "token"])
 def test_cartesian_topk_exact_rounding_ties(schedule):
     """Scores that round to the same fp32 value although their row logits
