@@ -609,20 +609,23 @@ __device__ int block_exclusive_scan_1024(int v, int *wsum) {
 }
 
 // One workgroup of 1024 threads; G = 1024 / next_pow2(E) threads per expert
-// (thread e * G + g), each owning a contiguous range of chunks. One exclusive
-// scan of the range sums in (expert, range) order gives every range's first
-// row directly -- the expert's offset plus the rows of its earlier ranges --
-// and the experts' offsets and counts with it; a second scan places the tiles.
+// (thread g * next_pow2(E) + e, so that neighbouring threads read neighbouring
+// experts of one chunk: the chunk counts are [chunk][E]), each owning a
+// contiguous range of chunks. One exclusive scan of the range sums in
+// (expert, range) order, through LDS, gives every range's first row directly
+// -- the expert's offset plus the rows of its earlier ranges -- and the
+// experts' offsets and counts with it; a second scan places the tiles.
 __global__ __launch_bounds__(1024) void k_dispatch_scan(const int32_t *__restrict__ cc, int nchunks, int E, int P,
                                                         int T, int n_shared, int bm, int32_t *__restrict__ chunk_base,
                                                         int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
                                                         Tile *__restrict__ tiles, int32_t *__restrict__ num_tiles) {
     __shared__ int wsum[32];
     __shared__ int ebase[1025];
+    __shared__ int xs[1024];
     int E2 = 1;
     while (E2 < E) E2 <<= 1;
     const int G = 1024 / E2;
-    const int tid = threadIdx.x, e = tid / G, g = tid % G;
+    const int tid = threadIdx.x, e = tid % E2, g = tid / E2;
     const bool live = e < E;
     const int b0 = (int)((long)nchunks * g / G), b1 = (int)((long)nchunks * (g + 1) / G);
     // ranges of up to kScanRegs chunks are loaded all at once into registers
@@ -645,7 +648,14 @@ __global__ __launch_bounds__(1024) void k_dispatch_scan(const int32_t *__restric
         }
         for (; b < b1; b++) s += cc[(size_t)b * E + e];
     }
-    const int first_row = block_exclusive_scan_1024(s, wsum);
+    // the range sums in (expert, range) order
+    xs[e * G + g] = s;
+    __syncthreads();
+    const int v = xs[tid];
+    const int vx = block_exclusive_scan_1024(v, wsum);   // ends with a barrier: every xs read is done
+    xs[tid] = vx;
+    __syncthreads();
+    const int first_row = xs[e * G + g];
     if (live && g == 0) ebase[e] = first_row;
     if (tid == 0) ebase[E] = P;
     __syncthreads();
