@@ -96,6 +96,20 @@ template <int EPL16>
 __device__ __forceinline__ void topk_row16(const float *__restrict__ lt, int E, int k, int renorm, int lane,
                                            int &my_e, float &my_w);
 
+// Sum over each 16-lane row of a wave, in the row's last lane (DPP row
+// shifts: no LDS round trip, unlike a lane shuffle).
+__device__ __forceinline__ float row16_sum_last(float v) {
+    auto step = [](float x, auto ctrl) {
+        return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                                         decltype(ctrl)::value, 0xF, 0xF, true));
+    };
+    v = step(v, std::integral_constant<int, 0x111>{});   // row_shr:1
+    v = step(v, std::integral_constant<int, 0x112>{});   // row_shr:2
+    v = step(v, std::integral_constant<int, 0x114>{});   // row_shr:4
+    v = step(v, std::integral_constant<int, 0x118>{});   // row_shr:8
+    return v;
+}
+
 // Router for larger batches: a tile of BT tokens x BE experts per workgroup.
 // The x rows and router rows of each 128-wide K group are copied into LDS with
 // asynchronous global -> LDS copies, whole 256-byte row segments per 16 lanes
@@ -228,10 +242,10 @@ __global__ __launch_bounds__(256) void k_router_lds(const uint16_t *__restrict__
                     float v = 0.0f;
 #pragma unroll
                     for (int k = 0; k < 4; k++) v += bf16f(qq[k] & 0xFFFFu) + bf16f(qq[k] >> 16);
-#pragma unroll
-                    for (int off = 1; off < 16; off <<= 1) v += __shfl_xor(v, off);
+                    // the 16 chunks of a row are one 16-lane DPP row (c & 15 = lane & 15)
+                    v = row16_sum_last(v);
                     const int t = t0 + row;
-                    if ((c & 15) == 0 && t < T) xsum[(size_t)t * G + g] = v * xscale;
+                    if ((c & 15) == 15 && t < T) xsum[(size_t)t * G + g] = v * xscale;
                 }
             }
         }
