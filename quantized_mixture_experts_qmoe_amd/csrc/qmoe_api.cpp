@@ -68,7 +68,7 @@ struct qmoe_ctx {
     int df = 0;                     // device format of every expert (uniform layers)
     std::vector<int> wfmt;          // per expert: qmoe_wformat
     bool mixed = false;             // experts in more than one device format
-    bool any_group = false, any_8bit = false;
+    bool any_group = false, any_8bit = false, any_fp8 = false;
     int fmt_mask = 0;               // bit f: some expert uses device format f
     int32_t *eslot = nullptr;       // per expert: group << 20 | index (mixed layers)
     int E = 0, S = 0, F = 0, Fs = 0, d = 0, k = 0;
@@ -298,7 +298,7 @@ int rows_per_tile(const qmoe_ctx *c, int T) {
     const long active = std::min<long>(c->E, P);
     const double avg = (double)P / (double)std::max<long>(1, active);
     if (avg <= 16.0) return 16;
-    if (c->any_8bit) return 64;   // the per-channel prefill GEMM takes 64-row tiles
+    if (c->any_fp8) return 64;   // the e4m3 prefill GEMM takes 64-row tiles (96 would spill)
     // 96-row tiles convert each packed code for 1.5x more MFMA work, which pays
     // once an expert's rows fill several tiles; below that their ragged tails
     // cost more than the conversions save
@@ -459,6 +459,7 @@ int pack_layer(const qmoe_config *cfg, const WeightSource &src, const void *w_ro
         c->fmt_mask |= 1 << fmt_index(dev_format(c->wfmt[i]));
         c->any_group = c->any_group || is_group_wformat(c->wfmt[i]);
         c->any_8bit = c->any_8bit || !is_group_wformat(c->wfmt[i]);
+        c->any_fp8 = c->any_fp8 || c->wfmt[i] == QMOE_W_FP8E4M3_CH;
     }
     c->mixed = (c->fmt_mask & (c->fmt_mask - 1)) != 0;
     c->df = dev_format(c->wfmt[0]);   // the format of every expert when not mixed

@@ -996,21 +996,6 @@ struct TileCtx {
     int N, K, n0, rows;
 };
 
-template <int DF, int MODE>
-__device__ __forceinline__ bool tile_setup(const GemmArgs &a, TileCtx &c) {
-    const int ntiles = *a.num_tiles;   // issued together with the tile load
-    c.tl = a.tiles[blockIdx.y];
-    if ((int)blockIdx.y >= ntiles) return false;
-    int fmt;
-    c.ew = expert_at(a, c.tl.e, fmt);
-    if (fmt != DF) return false;   // another launch computes this expert
-    c.N = MODE == 0 ? 2 * c.ew.F : a.d;
-    c.K = MODE == 0 ? a.d : c.ew.F;
-    c.n0 = blockIdx.x * 256;
-    c.rows = c.tl.row_end - c.tl.row0;
-    return c.n0 < c.N;
-}
-
 // Group formats: the MFMA consumes exact integer codes (128 + u as bf16).
 // Per 128-wide group g and output (m, n):
 //   sum_k a_mk (u_nk - z_ng) = sum_k a_mk (128 + u_nk) - (128 + z_ng) * rowsum_mg
@@ -1327,7 +1312,7 @@ __device__ __forceinline__ bool map_work(int L, int ntiles, int NT, int &tile, i
     return true;
 }
 
-// ---- prefill tiles (group formats): activation ring in LDS ------------------
+// ---- prefill tiles: activation ring in LDS ------------------------------------
 //
 // Tiles of 16*MI rows x 256 columns: each of the NW waves owns all the rows
 // and 16*NB columns. A workgroup computes nsub such tiles side by side (the
@@ -1350,7 +1335,12 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm_gpf(GemmArgs a) {
     // Packed codes and scales go straight to registers (each wave owns its B
     // blocks, so nothing would be shared through LDS); the two stages hold only
     // the activation tile and its row sums.
-    constexpr int ST_A = 0, ST_R = BM * 256, ST_BYTES = ST_R + BM * 4;
+    // Group formats (4-bit codes, fp16 scale per 128-group) or per-channel
+    // 8-bit codes (INT8, e4m3; the column scale multiplies the finished
+    // accumulator, no row sums needed)
+    constexpr bool GRP = DF == DF_I4SYM || DF == DF_I4ASYM;
+    constexpr int BW = GRP ? 1 : 2;               // 16-byte code words per lane, block and group
+    constexpr int ST_A = 0, ST_R = BM * 256, ST_BYTES = ST_R + (GRP ? BM * 4 : 0);
     constexpr int WCOLS = 16 * NB;                // B columns per wave
     constexpr int NTILE = WCOLS * NW;             // B columns per tile
     // N (2F or d) is a multiple of 256 = NTILE: every wave of a tile with
@@ -1426,11 +1416,11 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm_gpf(GemmArgs a) {
         const uint16_t *as = abase + kb * 128;
 #pragma unroll
         for (int i = 0; i < ADMA; i++) dma16s(as, aoffb[i], sb + ST_A + (RPW * wave + 4 * i) * 256);
-        if (lane < RPW) dma4s(rbase + kb, roffb, sb + ST_R + wave * RPW * 4);
+        if (GRP && lane < RPW) dma4s(rbase + kb, roffb, sb + ST_R + wave * RPW * 4);
     };
     // B register ring: codes, and the dword holding this lane's fp16 scale and
     // its neighbour's
-    uint4 bring[RS][NB];
+    uint4 bring[RS][NB][BW];
     uint32_t sring[RS][NB];
     const int spair2 = (lane & 15) & ~1;
     const uint32_t hsel = (lane & 1) * 16;
@@ -1440,8 +1430,13 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm_gpf(GemmArgs a) {
 #pragma unroll
         for (int nb = 0; nb < NB; nb++) {
             const size_t blk = (size_t)(ib0 + (NTILE / 16) * j + nb) * KB + kb;
-            bring[slot][nb] = gload16(codes + blk * 1024 + lane * 16);
-            sring[slot][nb] = gload(reinterpret_cast<const uint32_t *>(gsc + blk * 16 + spair2));
+            if constexpr (GRP) {
+                bring[slot][nb][0] = gload16(codes + blk * 1024 + lane * 16);
+                sring[slot][nb] = gload(reinterpret_cast<const uint32_t *>(gsc + blk * 16 + spair2));
+            } else {
+                bring[slot][nb][0] = gload16(codes + blk * 2048 + lane * 32);
+                bring[slot][nb][1] = gload16(codes + blk * 2048 + lane * 32 + 16);
+            }
         }
     };
 
@@ -1482,9 +1477,13 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm_gpf(GemmArgs a) {
         float r[NB];
 #pragma unroll
         for (int nb = 0; nb < NB; nb++) {
-            const float sc_cur = half_bits_to_f32((uint16_t)(sring[slot][nb] >> hsel));
-            r[nb] = s_prev[nb] * __builtin_amdgcn_rcpf(sc_cur);
-            s_prev[nb] = sc_cur;
+            if constexpr (GRP) {
+                const float sc_cur = half_bits_to_f32((uint16_t)(sring[slot][nb] >> hsel));
+                r[nb] = s_prev[nb] * __builtin_amdgcn_rcpf(sc_cur);
+                s_prev[nb] = sc_cur;
+            } else {
+                r[nb] = 1.0f;
+            }
         }
         bf16x8 afr[2];
         afr[0] = afrag(0, 0);
@@ -1493,8 +1492,15 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm_gpf(GemmArgs a) {
             bf16x8 bh[NB][2];
 #pragma unroll
             for (int nb = 0; nb < NB; nb++) {
-                bh[nb][0] = nibbles_to_bf16_128(h == 0 ? bring[slot][nb].x : bring[slot][nb].z, nc);
-                bh[nb][1] = nibbles_to_bf16_128(h == 0 ? bring[slot][nb].y : bring[slot][nb].w, nc);
+                if constexpr (GRP) {
+                    bh[nb][0] = nibbles_to_bf16_128(h == 0 ? bring[slot][nb][0].x : bring[slot][nb][0].z, nc);
+                    bh[nb][1] = nibbles_to_bf16_128(h == 0 ? bring[slot][nb][0].y : bring[slot][nb][0].w, nc);
+                } else {
+                    // k-steps 2h and 2h+1: the low and high half of word h
+                    const uint4 q = bring[slot][nb][h];
+                    bh[nb][0] = codes8_to_bf16<DF>(q.x, q.y);
+                    bh[nb][1] = codes8_to_bf16<DF>(q.z, q.w);
+                }
             }
             // The converted operands (and the scale ratios) as inputs of an
             // empty volatile asm: the copies and loads below cannot move above
@@ -1507,7 +1513,7 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm_gpf(GemmArgs a) {
             else load_b(next_j, next_kb, slot);
 #pragma unroll
             for (int mi = 0; mi < MI; mi++) {
-                if (h == 0) {
+                if (GRP && h == 0) {
                     const f32x4 nrs = *reinterpret_cast<const f32x4 *>(&Rb[mi * 16 + lrow]);
 #pragma unroll
                     for (int nb = 0; nb < NB; nb++) acc[mi][nb] = acc[mi][nb] * r[nb] + nrs;
@@ -1560,11 +1566,23 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm_gpf(GemmArgs a) {
         // out of the loop into registers live through every group
         int row0 = tl.row0, nrows = rows, ld_out = MODE == 0 ? a.ldh : a.d, lrow = (lane >> 4) * 4;
         asm volatile("" : "+s"(row0), "+s"(nrows), "+s"(ld_out), "+v"(lrow));
-        // back from scale units
+        if constexpr (GRP) {
+            // back from scale units
 #pragma unroll
-        for (int mi = 0; mi < MI; mi++)
+            for (int mi = 0; mi < MI; mi++)
 #pragma unroll
-            for (int nb = 0; nb < NB; nb++) acc[mi][nb] *= s_prev[nb];
+                for (int nb = 0; nb < NB; nb++) acc[mi][nb] *= s_prev[nb];
+        } else {
+            // per-channel scales of the tile's columns (W13: interleaved gate /
+            // up blocks, as the codes)
+            const float *ps = MODE == 0 ? ew.p13 : ew.p2;
+#pragma unroll
+            for (int nb = 0; nb < NB; nb++) {
+                const float cs = ps[(ibj + nb) * 16 + (lane & 15)];
+#pragma unroll
+                for (int mi = 0; mi < MI; mi++) acc[mi][nb] *= cs;
+            }
+        }
 
         if (DF == DF_I4ASYM) {
             // zero points: acc[m][n] += sum_g (s_ng z_ng / 128) * nrs_mg, one MFMA
@@ -1656,38 +1674,41 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm_gpf(GemmArgs a) {
                         if (row < nrows) *reinterpret_cast<uint16_t *>(Hb + 2u * (uint32_t)(row * ld_out + col)) = hb;
                     }
             }
-            float *red = reinterpret_cast<float *>(lds + RED);
-            // 16-lane row sums, the 4*MI independent chains interleaved step by
-            // step (a DPP read right after the write of its source needs wait states)
-            auto row_step = [&](auto ctrl) {
+            // (per-channel formats: their down GEMM takes no row sums)
+            if constexpr (GRP) {
+                float *red = reinterpret_cast<float *>(lds + RED);
+                // 16-lane row sums, the 4*MI independent chains interleaved step by
+                // step (a DPP read right after the write of its source needs wait states)
+                auto row_step = [&](auto ctrl) {
+#pragma unroll
+                    for (int mi = 0; mi < MI; mi++)
+#pragma unroll
+                        for (int r = 0; r < 4; r++) hs[mi][r] += dpp_zero<decltype(ctrl)::value, 0xF>(hs[mi][r]);
+                };
+                row_step(std::integral_constant<int, kDppShr1>{});
+                row_step(std::integral_constant<int, kDppShr2>{});
+                row_step(std::integral_constant<int, kDppShr4>{});
+                row_step(std::integral_constant<int, kDppShr8>{});
 #pragma unroll
                 for (int mi = 0; mi < MI; mi++)
 #pragma unroll
-                    for (int r = 0; r < 4; r++) hs[mi][r] += dpp_zero<decltype(ctrl)::value, 0xF>(hs[mi][r]);
-            };
-            row_step(std::integral_constant<int, kDppShr1>{});
-            row_step(std::integral_constant<int, kDppShr2>{});
-            row_step(std::integral_constant<int, kDppShr4>{});
-            row_step(std::integral_constant<int, kDppShr8>{});
+                    for (int r = 0; r < 4; r++)
+                        if ((lane & 15) == 15) red[wave * BM + mi * 16 + lrow + r] = hs[mi][r];
+                // LDS writes done, then the barrier (no wait for the B loads in
+                // flight); the group barriers that follow order these reads
+                // before the next tile's writes
+                wait_vm_lgkm0<63>();
+                raw_barrier();
+                for (int t = threadIdx.x; t < BM * (NW / WPG); t += 64 * NW) {
+                    const int h = t / BM, row = t % BM;
+                    const int grp = n0 / 256 + h;   // 128-wide H group
+                    if (row < nrows && grp < ew.F / 128) {
+                        const float *rr = red + WPG * h * BM + row;
+                        float v = 0.0f;
 #pragma unroll
-            for (int mi = 0; mi < MI; mi++)
-#pragma unroll
-                for (int r = 0; r < 4; r++)
-                    if ((lane & 15) == 15) red[wave * BM + mi * 16 + lrow + r] = hs[mi][r];
-            // LDS writes done, then the barrier (no wait for the B loads in
-            // flight); the group barriers that follow order these reads
-            // before the next tile's writes
-            wait_vm_lgkm0<63>();
-            raw_barrier();
-            for (int t = threadIdx.x; t < BM * (NW / WPG); t += 64 * NW) {
-                const int h = t / BM, row = t % BM;
-                const int grp = n0 / 256 + h;   // 128-wide H group
-                if (row < nrows && grp < ew.F / 128) {
-                    const float *rr = red + WPG * h * BM + row;
-                    float v = 0.0f;
-#pragma unroll
-                    for (int w = 0; w < WPG; w++) v += rr[w * BM];
-                    a.hsum[(size_t)(row0 + row) * (a.ldh / 128) + grp] = -ZC * v;
+                        for (int w = 0; w < WPG; w++) v += rr[w * BM];
+                        a.hsum[(size_t)(row0 + row) * (a.ldh / 128) + grp] = -ZC * v;
+                    }
                 }
             }
         } else {
@@ -1749,119 +1770,6 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm_gpf(GemmArgs a) {
     }
     // no copy into LDS may be in flight when the workgroup ends
     __builtin_amdgcn_s_waitcnt(0);
-}
-
-// Per-channel formats (int8, e4m3): codes convert exactly to bf16 and the
-// per-row scale multiplies the finished accumulator.
-template <int DF, int MODE, int MI>
-__global__ __launch_bounds__(256) void k_gemm_c(GemmArgs a) {
-    constexpr int BM = 16 * MI;
-    constexpr int PITCH = 136;
-    __shared__ __attribute__((aligned(16))) uint16_t As[BM * PITCH];
-
-    TileCtx c;
-    if (!tile_setup<DF, MODE>(a, c)) return;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int KB = c.K / 128;
-    const int lrow = (lane >> 4) * 4;
-    const int c16 = threadIdx.x & 15;
-    const uint16_t *asrc[MI];
-    bool aok[MI];
-#pragma unroll
-    for (int i = 0; i < MI; i++) {
-        const int r = (threadIdx.x >> 4) + 16 * i;
-        aok[i] = r < c.rows;
-        const int gr = c.tl.row0 + (aok[i] ? r : 0);
-        if (MODE == 0) {
-            const int tok = gr < a.P ? a.perm[gr] / a.k : (gr - a.P) % a.T;
-            asrc[i] = a.x + (size_t)tok * a.d + c16 * 8;
-        } else {
-            asrc[i] = a.H + (size_t)gr * a.ldh + c16 * 8;
-        }
-    }
-    const uint8_t *codes = MODE == 0 ? c.ew.c13 : c.ew.c2;
-    const int ib0 = c.n0 / 16 + 4 * wave;
-
-    f32x4 acc[MI][4];
-#pragma unroll
-    for (int mi = 0; mi < MI; mi++)
-#pragma unroll
-        for (int nb = 0; nb < 4; nb++) acc[mi][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    for (int kb = 0; kb < KB; kb++) {
-        uint4 braw[4][2];
-#pragma unroll
-        for (int nb = 0; nb < 4; nb++) {
-            const uint8_t *bp = codes + ((size_t)(ib0 + nb) * KB + kb) * 2048 + lane * 32;
-            braw[nb][0] = *reinterpret_cast<const uint4 *>(bp);
-            braw[nb][1] = *reinterpret_cast<const uint4 *>(bp + 16);
-        }
-#pragma unroll
-        for (int i = 0; i < MI; i++) {
-            const uint4 v = aok[i] ? *reinterpret_cast<const uint4 *>(asrc[i] + kb * 128) : make_uint4(0, 0, 0, 0);
-            *reinterpret_cast<uint4 *>(&As[((threadIdx.x >> 4) + 16 * i) * PITCH + c16 * 8]) = v;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int s = 0; s < 4; s++) {
-            bf16x8 bfr[4];
-#pragma unroll
-            for (int nb = 0; nb < 4; nb++) {
-                const uint4 q = braw[nb][s >> 1];
-                bfr[nb] = codes8_to_bf16<DF>((s & 1) ? q.z : q.x, (s & 1) ? q.w : q.y);
-            }
-#pragma unroll
-            for (int mi = 0; mi < MI; mi++) {
-                const bf16x8 af =
-                    *reinterpret_cast<const bf16x8 *>(&As[(mi * 16 + (lane & 15)) * PITCH + s * 32 + (lane >> 4) * 8]);
-#pragma unroll
-                for (int nb = 0; nb < 4; nb++)
-                    acc[mi][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr[nb], acc[mi][nb], 0, 0, 0);
-            }
-        }
-        __syncthreads();
-    }
-
-    if (MODE == 0) {
-        const float *ps = c.ew.p13;
-#pragma unroll
-        for (int pr = 0; pr < 2; pr++) {
-            const int ibg = ib0 + 2 * pr;
-            const int col = (ibg >> 1) * 16 + (lane & 15);
-            const float sg = ps[ibg * 16 + (lane & 15)];
-            const float su = ps[(ibg + 1) * 16 + (lane & 15)];
-#pragma unroll
-            for (int mi = 0; mi < MI; mi++)
-#pragma unroll
-                for (int r = 0; r < 4; r++) {
-                    const int row = mi * 16 + lrow + r;
-                    if (row < c.rows) {
-                        const float g = acc[mi][2 * pr][r] * sg;
-                        const float u = acc[mi][2 * pr + 1][r] * su;
-                        a.H[(size_t)(c.tl.row0 + row) * a.ldh + col] = to_bf16(silu_mul(g, u));
-                    }
-                }
-        }
-    } else {
-        const float *ps = c.ew.p2;
-        float sn[4];
-#pragma unroll
-        for (int nb = 0; nb < 4; nb++) sn[nb] = ps[c.n0 + 64 * wave + 16 * nb + (lane & 15)];
-#pragma unroll
-        for (int mi = 0; mi < MI; mi++)
-#pragma unroll
-            for (int r = 0; r < 4; r++) {
-                const int row = mi * 16 + lrow + r;
-                if (row >= c.rows) continue;
-                const int gr = c.tl.row0 + row;
-                const float wt = gr < a.P ? a.wrow[gr] : 1.0f;
-#pragma unroll
-                for (int nb = 0; nb < 4; nb++) {
-                    const int n = c.n0 + 64 * wave + 16 * nb + (lane & 15);
-                    a.O[(size_t)gr * a.d + n] = acc[mi][nb][r] * sn[nb] * wt;
-                }
-            }
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -2413,9 +2321,10 @@ constexpr int kGemmGroupTarget = QMOE_GEMM_GROUP_TARGET;
 constexpr long kGemmMinWorkgroups = 6 * 512;
 
 static int gemm_nsub(int df, int bm, int KB, int n_tiles, int max_tiles) {
-    // the 96-row INT4-asym variant has no registers to spare for the
-    // operands in flight while a tile's zero-point correction runs
-    if (df == DF_I4ASYM && bm == 96) return 1;
+    // the 96-row INT4-asym and 8-bit variants have no registers to spare for
+    // the operands in flight while a tile ends (zero-point correction,
+    // 8-bit code words)
+    if (bm == 96 && df != DF_I4SYM) return 1;
     if (const char *env = std::getenv("QMOE_PREFILL_TILES_PER_WG")) {
         const int n = std::atoi(env);
         if (n >= 1) return std::min(n, n_tiles);
@@ -2427,7 +2336,7 @@ static int gemm_nsub(int df, int bm, int KB, int n_tiles, int max_tiles) {
 
 template <int DF, int MODE, int MI>
 static void launch_gpf(bool multi, dim3 grid, const GemmArgs &a, hipStream_t s) {
-    if constexpr (DF == DF_I4ASYM && MI == 6) {
+    if constexpr (DF != DF_I4SYM && MI == 6) {
         hipLaunchKernelGGL((k_gemm_gpf<DF, MODE, MI, 4, 4, false>), grid, dim3(256), 0, s, a);
     } else {
         if (multi) hipLaunchKernelGGL((k_gemm_gpf<DF, MODE, MI, 4, 4, true>), grid, dim3(256), 0, s, a);
@@ -2461,13 +2370,18 @@ static hipError_t launch_gemm(int df, int bm, int max_tiles, int maxN, const Gem
         const int cols = 4 * kDecodeBlocksPerWave * 16;
         return launch_gemm_dec<MODE>(df, dim3((maxN + cols - 1) / cols, max_tiles), a, s);
     }
-    dim3 grid(a.n_tiles, max_tiles);
-    // per-channel formats (8-bit codes): 64-row tiles
-    if (bm != 64) return hipErrorInvalidValue;
-    switch (df) {
-    case DF_INT8: hipLaunchKernelGGL((k_gemm_c<DF_INT8, MODE, 4>), grid, dim3(256), 0, s, a); break;
-    case DF_FP8: hipLaunchKernelGGL((k_gemm_c<DF_FP8, MODE, 4>), grid, dim3(256), 0, s, a); break;
-    default: return hipErrorInvalidValue;
+    // per-channel formats (8-bit codes): the same kernel; e4m3 in 64-row
+    // tiles only (its 96-row variant would spill)
+    if (!((bm == 64 && (df == DF_INT8 || df == DF_FP8)) || (bm == 96 && df == DF_INT8))) return hipErrorInvalidValue;
+    a.nsub = gemm_nsub(df, bm, (MODE == 0 ? a.d : a.ldh) / 128, a.n_tiles, max_tiles);
+    a.n_groups = (a.n_tiles + a.nsub - 1) / a.nsub;
+    const long total = (long)max_tiles * a.n_groups;
+    dim3 grid((unsigned)(8 * ((total + 7) / 8)));
+    if (bm == 64) {
+        if (df == DF_INT8) launch_gpf<DF_INT8, MODE, 4>(a.nsub > 1, grid, a, s);
+        else launch_gpf<DF_FP8, MODE, 4>(a.nsub > 1, grid, a, s);
+    } else {
+        launch_gpf<DF_INT8, MODE, 6>(false, grid, a, s);
     }
     return hipGetLastError();
 }
