@@ -1094,10 +1094,15 @@ __device__ __forceinline__ void dec_tile(const GemmArgs &a, const TileCtx &c, ui
 #pragma unroll
                 for (int j = 0; j < 4; j++) sum += bf16f(u[j] & 0xFFFFu) + bf16f(u[j] >> 16);
             }
-            // the TPG threads of a 128-wide group are consecutive lanes
-#pragma unroll
-            for (int off = 1; off < TPG; off <<= 1) sum += __shfl_xor(sum, off);
-            if ((tid & (TPG - 1)) == 0) Rs[buf][(tid & 15) / TPG][sr] = -ZC * sum;
+            // the TPG threads of a 128-wide group are consecutive lanes of one
+            // 16-lane row: shifted sums (DPP row_shr 1, 2, 4, ...) leave the
+            // group's sum in its last lane
+            static_assert(TPG <= 16 && (TPG & (TPG - 1)) == 0, "groups inside a 16-lane row");
+            if constexpr (TPG > 1) sum += dpp_zero<kDppShr1, 0xF>(sum);
+            if constexpr (TPG > 2) sum += dpp_zero<kDppShr2, 0xF>(sum);
+            if constexpr (TPG > 4) sum += dpp_zero<kDppShr4, 0xF>(sum);
+            if constexpr (TPG > 8) sum += dpp_zero<kDppShr8, 0xF>(sum);
+            if ((tid & (TPG - 1)) == TPG - 1) Rs[buf][(tid & 15) / TPG][sr] = -ZC * sum;
         }
     };
 
