@@ -300,9 +300,10 @@ int rows_per_tile(const qmoe_ctx *c, int T) {
     if (avg <= 16.0) return 16;
     if (c->any_fp8) return 64;   // the e4m3 prefill GEMM takes 64-row tiles (96 would spill)
     // 96-row tiles convert each packed code for 1.5x more MFMA work, which pays
-    // once an expert's rows fill several tiles; below that their ragged tails
-    // cost more than the conversions save
-    if (avg >= 512.0) return 96;
+    // once an expert's rows fill a few tiles (160 rows: two 96-row tiles
+    // against three of 64); below that their ragged tails cost more than the
+    // conversions save
+    if (avg >= 160.0) return 96;
     return c->gemm_bm;
 }
 

@@ -103,7 +103,7 @@ def test_forward_96_row_tiles(oracle_mod, fmt, S):
 
 @pytest.mark.parametrize("fmt", ["int4_asym_g128", "int4_sym_g128", "int3_sym_g128"])
 @pytest.mark.parametrize("T,E,k,d,F,nsub", [(1300, 2, 1, 2048, 384, 8), (1300, 2, 1, 2048, 384, 2),
-                                            (600, 4, 2, 768, 640, 2), (600, 4, 2, 768, 640, 3)])
+                                            (600, 8, 2, 768, 640, 2), (600, 8, 2, 768, 640, 3)])
 def test_forward_multi_tile_workgroups(oracle_mod, monkeypatch, fmt, T, E, k, d, F, nsub):
     # prefill workgroups running through nsub consecutive 256-column tiles of
     # one pipeline (the launcher picks nsub > 1 only for launches with many
@@ -112,14 +112,16 @@ def test_forward_multi_tile_workgroups(oracle_mod, monkeypatch, fmt, T, E, k, d,
     # at odd pipeline positions, and the gate/up product's 3 tiles split into
     # groups of 2 and a lone last tile. d = 768, F = 640 (64-row tiles): 5 K
     # groups per down tile over 3 tiles, 6 per gate/up tile over 5 tiles.
-    # The 96-row INT4-asym kernel keeps one tile per workgroup. With one
-    # expert per token (k = 1) at d = 2048 the outputs are heavy-tailed: the
-    # path's own storage roundings (bf16 H, bf16 y) reach 2.3e-2 RMS there on
-    # the CPU emulation, so the bar applies beyond half a bf16 ulp of y_ref.
+    # The 96-row INT4-asym kernel keeps one tile per workgroup. These outputs
+    # are heavy-tailed (k = 1 at d = 2048; k = 2 of 8 experts at d = 768): the
+    # path's own storage roundings (bf16 H, bf16 y) reach 2.3e-2 and 2.2e-2 RMS
+    # there by CPU emulation, which the GPU results match to four digits, so
+    # where half a bf16 ulp of the largest |y_ref| reaches three quarters of
+    # the bar, the bar applies beyond it.
     monkeypatch.setenv("QMOE_PREFILL_TILES_PER_WG", str(nsub))
     cfg = small(fmt, name=f"multitile_{fmt}_{d}_{F}", T=T, E=E, k=k, d=d, F=F)
     run_and_check(oracle_mod, cfg, seed=d + F + nsub, tag=f"multi-tile x{nsub} {fmt} T={T} E={E} d={d} F={F}",
-                  output_rounding_allowance=(k == 1))
+                  output_rounding_allowance="auto")
 
 
 @pytest.mark.parametrize("T,E,k,fmt", [(64, 256, 8, "int4_sym_g128"), (64, 256, 8, "fp8e4m3_ch"),
