@@ -1319,19 +1319,21 @@ __device__ __forceinline__ bool map_work(int L, int ntiles, int NT, int &tile, i
 
 // ---- prefill tiles: activation ring in LDS ------------------------------------
 //
+// Every prefill format (group formats: 4-bit codes with an fp16 scale per
+// 128-group; per-channel formats: INT8 / e4m3 codes with one scale per column).
 // Tiles of 16*MI rows x 256 columns: each of the NW waves owns all the rows
-// and 16*NB columns. A workgroup computes nsub such tiles side by side (the
-// same rows, consecutive 256-column ranges), running one load pipeline through
-// all of them, so the fixed start and drain of a tile is paid once per
-// workgroup rather than once per tile: the next tile's first operands are in
-// flight while the previous one's results are stored. Per wave and group (128
-// K positions): the gathered activation rows and their row sums travel as
-// asynchronous global -> LDS copies issued from inline assembly (so the
-// compiler neither waits on them before LDS reads nor counts them), one group
-// ahead in a two-stage ring; the wave's own packed codes and scales are
-// ordinary loads into a two-slot register ring, two groups ahead. Every group
-// ends with the next group's copies landed and one barrier that publishes them
-// to the workgroup.
+// and 16*NB columns. With MULTI, a workgroup computes nsub such tiles side by
+// side (the same rows, consecutive 256-column ranges), running one load
+// pipeline through all of them, so the fixed start and drain of a tile is paid
+// once per workgroup rather than once per tile: the next tile's first operands
+// are in flight while the previous one's results are stored. Per wave and
+// group (128 K positions): the gathered activation rows (and, for the group
+// formats, their row sums) travel as asynchronous global -> LDS copies issued
+// from inline assembly (so the compiler neither waits on them before LDS
+// reads nor counts them), one group ahead in a two-stage ring; the wave's own
+// packed codes and scales are ordinary loads into a two-slot register ring,
+// two groups ahead. Every group ends with the next group's copies landed and
+// one barrier that publishes them to the workgroup.
 template <int DF, int MODE, int MI, int NB, int NW, bool MULTI>
 __global__ __launch_bounds__(64 * NW, 2) void k_gemm_gpf(GemmArgs a) {
     constexpr int BM = 16 * MI, RPW = BM / NW;   // activation rows copied per wave
@@ -1339,10 +1341,8 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm_gpf(GemmArgs a) {
     constexpr int ADMA = RPW / 4;                 // 1 KB activation copies per wave
     // Packed codes and scales go straight to registers (each wave owns its B
     // blocks, so nothing would be shared through LDS); the two stages hold only
-    // the activation tile and its row sums.
-    // Group formats (4-bit codes, fp16 scale per 128-group) or per-channel
-    // 8-bit codes (INT8, e4m3; the column scale multiplies the finished
-    // accumulator, no row sums needed)
+    // the activation tile and its row sums. Per-channel 8-bit codes need no
+    // row sums: the column scale multiplies the finished accumulator.
     constexpr bool GRP = DF == DF_I4SYM || DF == DF_I4ASYM;
     constexpr int BW = GRP ? 1 : 2;               // 16-byte code words per lane, block and group
     constexpr int ST_A = 0, ST_R = BM * 256, ST_BYTES = ST_R + (GRP ? BM * 4 : 0);
