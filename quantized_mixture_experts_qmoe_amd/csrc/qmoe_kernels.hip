@@ -1334,8 +1334,19 @@ __device__ __forceinline__ bool map_work(int L, int ntiles, int NT, int &tile, i
 // packed codes and scales are ordinary loads into a two-slot register ring,
 // two groups ahead. Every group ends with the next group's copies landed and
 // one barrier that publishes them to the workgroup.
+// LDS of a workgroup: the two activation stages, then the per-row H sums of
+// each wave (gate/up) or the rows' mixing weights (down)
+template <int DF, int MODE, int MI, int NW>
+constexpr int gpf_lds_bytes() {
+    return 2 * (16 * MI * 256 + ((DF == DF_I4SYM || DF == DF_I4ASYM) ? 16 * MI * 4 : 0)) +
+           (MODE == 0 ? NW * 16 * MI : 16 * MI) * 4;
+}
+
+// The tile(s) of one workgroup with MI 16-row blocks (tl: the task-list tile,
+// ew: its expert's weights, ngrp: the workgroup's group of N-tiles).
 template <int DF, int MODE, int MI, int NB, int NW, bool MULTI>
-__global__ __launch_bounds__(64 * NW, 2) void k_gemm_gpf(GemmArgs a) {
+__device__ __forceinline__ void gpf_tiles(const GemmArgs &a, uint8_t *lds, int ngrp, const Tile &tl,
+                                          const ExpertW &ew) {
     constexpr int BM = 16 * MI, RPW = BM / NW;   // activation rows copied per wave
     static_assert(RPW % 4 == 0 && RPW <= 64, "each wave copies whole 4-row slabs");
     constexpr int ADMA = RPW / 4;                 // 1 KB activation copies per wave
@@ -1357,15 +1368,9 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm_gpf(GemmArgs a) {
     // while a tile ends): gate/up, the per-row H sums of each wave, [NW][BM]
     // floats; down, the rows' mixing weights, [BM] floats
     constexpr int RED = NST * ST_BYTES;
+    static_assert(RED + (MODE == 0 ? NW * BM : BM) * 4 == gpf_lds_bytes<DF, MODE, MI, NW>(), "LDS layout");
     constexpr float ZC = GroupConst<DF>::ZC;
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[RED + (MODE == 0 ? NW * BM : BM) * 4];
 
-    int tile_id, ngrp;
-    if (!map_work(blockIdx.x, *a.num_tiles, a.n_groups, tile_id, ngrp)) return;
-    const Tile tl = a.tiles[tile_id];
-    int efmt;
-    const ExpertW ew = expert_at(a, tl.e, efmt);
-    if (efmt != DF) return;   // another launch computes this expert
     const int N = MODE == 0 ? 2 * ew.F : a.d;
     const int K = MODE == 0 ? a.d : ew.F;
     const int nt0 = ngrp * a.nsub;                // first 256-column tile
@@ -1775,6 +1780,25 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm_gpf(GemmArgs a) {
     }
     // no copy into LDS may be in flight when the workgroup ends
     __builtin_amdgcn_s_waitcnt(0);
+}
+
+// Prefill GEMM: tiles of up to 16*MI rows. The last tile of an expert usually
+// holds fewer rows: such a tile runs only the 32-row steps it needs (MI = 2 or
+// 4), converting the same codes for fewer MFMAs.
+template <int DF, int MODE, int MI, int NB, int NW, bool MULTI>
+__global__ __launch_bounds__(64 * NW, 2) void k_gemm_gpf(GemmArgs a) {
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[gpf_lds_bytes<DF, MODE, MI, NW>()];
+    int tile_id, ngrp;
+    if (!map_work(blockIdx.x, *a.num_tiles, a.n_groups, tile_id, ngrp)) return;
+    const Tile tl = a.tiles[tile_id];
+    int efmt;
+    const ExpertW ew = expert_at(a, tl.e, efmt);
+    if (efmt != DF) return;   // another launch computes this expert
+    const int rows = tl.row_end - tl.row0;
+    static_assert(MI == 4 || MI == 6, "64- or 96-row tiles");
+    if (rows <= 32) gpf_tiles<DF, MODE, 2, NB, NW, MULTI>(a, lds, ngrp, tl, ew);
+    else if (MI == 4 || rows <= 64) gpf_tiles<DF, MODE, 4, NB, NW, MULTI>(a, lds, ngrp, tl, ew);
+    else gpf_tiles<DF, MODE, MI, NB, NW, MULTI>(a, lds, ngrp, tl, ew);
 }
 
 // ---------------------------------------------------------------------------
