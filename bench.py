@@ -16,8 +16,9 @@ median, the per-kernel split, the dominant kernel's roofline fraction (MFMA for
 the prefill shapes, HBM for the decode shapes, whose calls each follow a 1 GiB
 read that evicts the 256 MB MALL), the HBM counter traffic where committed
 counters cover the current kernel code, the sampled GPU clock, and the fp64
-oracle timed on a bounded token sample on the host cores. Prints ONE JSON line
-on stdout; progress goes to stderr.
+oracle timed on a bounded token sample on the host cores. Decode shapes also
+report the same forward recorded once into a HIP graph and replayed
+(`step_us_graph`). Prints ONE JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
 
@@ -255,6 +256,31 @@ def bench_workload(name, steps, warmup, contract_steps, clock, cpu_s, flush_mb):
             warm.append((a, b))
         torch.cuda.synchronize()
         res["step_us_warm_mall_aside"] = float(np.median([1e3 * a.elapsed_time(b) for a, b in warm]))
+    if decode:
+        # the same forward recorded once into a HIP graph and replayed (a
+        # serving loop's form: no per-launch host cost between the kernels);
+        # same flush before each replay
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            layer.forward(x, y=y, stream=side)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            layer.forward(x, y=y, stream=torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for a, b in gev:
+            flush()
+            a.record(stream)
+            graph.replay()
+            b.record(stream)
+        torch.cuda.synchronize()
+        g_us = np.array([1e3 * a.elapsed_time(b) for a, b in gev])
+        res["step_us_graph"] = {"median": float(np.median(g_us)), "min": float(g_us.min()), "calls": steps,
+                                "mall_flushed": bool(fl), "what": "one HIP graph replay of the forward"}
+        del graph
 
     # 3. kernel durations: every kernel launch of n_dom more calls between its
     #    own pair of events on the launch stream (with events on every kernel,
@@ -304,6 +330,9 @@ def bench_workload(name, steps, warmup, contract_steps, clock, cpu_s, flush_mb):
         res["step_hbm"] = {"bytes": step_bytes, "achieved": step_gbs, "unit": "GB/s",
                            "frac": step_gbs / PEAK_HBM_GBS,
                            "what": "packed weights of the selected experts + router weight + x + y"}
+    if "step_us_graph" in res:
+        log(f"{name}: graph replay median {res['step_us_graph']['median']:.1f} us "
+            f"(min {res['step_us_graph']['min']:.1f})")
     log(f"{name}: median {res['step_us']['median']:.1f} us (min {res['step_us']['min']:.1f}), "
         f"{res['tokens_per_s']:.4g} tokens/s, {res['roofline']['kernel']} {res['roofline']['frac']:.3f} of "
         f"{res['roofline']['bound']} peak; clock {res['gpu_clock']}; kernels "
@@ -387,6 +416,9 @@ def main() -> int:
         "workloads": workloads,
     }
     out["layer_mfma_frac"] = out["layer_tflops"] / PEAK_BF16_TFLOPS
+    for key in ("step_us_graph", "step_us_warm_mall_aside", "step_hbm"):
+        if key in hres:
+            out[key] = hres[key]
     print(json.dumps(out), flush=True)
     return 0
 

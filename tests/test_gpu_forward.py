@@ -20,11 +20,22 @@ def run_and_check(O, cfg, seed=0, x_bits=None, tag="", output_rounding_allowance
         inp.x = x_bits
     T = inp.x.shape[0]
     layer = QMoE(inp, max_tokens=max(T, 1))
+    oracle = O.OracleLayer(inp)
+    y = check_batch(O, inp, layer, oracle, tag, output_rounding_allowance)
+    oracle.close()
+    return layer, inp, y
+
+
+def check_batch(O, inp, layer, oracle, tag="", output_rounding_allowance=False):
+    """One forward of the batch inp.x through the layer against the oracle:
+    routing on the GPU's own logits, the dispatch bit for bit, the output to
+    the parity bar. Returns y."""
+    cfg = inp.cfg
+    T = inp.x.shape[0]
     x = to_dev_bf16(inp.x)
     route = QMoE.route_buffers(T, cfg.E, cfg.k)
     y = layer.forward(x, route=route)
     torch.cuda.synchronize()
-    oracle = O.OracleLayer(inp)
     ref = oracle.forward(inp.x)
     idx_gpu = route["topk_idx"].cpu().numpy()
     w_gpu = route["topk_w"].cpu().numpy()
@@ -47,8 +58,7 @@ def run_and_check(O, cfg, seed=0, x_bits=None, tag="", output_rounding_allowance
         output_rounding_allowance = own >= 0.75 * MAX_ABS_RMS
         print(f"[parity] half a bf16 ulp of the largest |y_ref|: {own:.3e} RMS", flush=True)
     assert_output_close(bf16_tensor_to_f64(y), y_ref, tag, output_rounding_allowance)
-    oracle.close()
-    return layer, inp, y
+    return y
 
 
 def small(fmt, **kw):
@@ -132,6 +142,43 @@ def test_forward_small_batch_router_limits(oracle_mod, T, E, k, fmt):
     selects every expert."""
     cfg = small(fmt, T=T, E=E, k=k, d=512, F=256, bias=True)
     run_and_check(oracle_mod, cfg, seed=T * E + k, tag=f"small-batch T={T} E={E} k={k} {fmt}")
+
+
+@pytest.mark.parametrize("T,E,k,S,fmt,renorm", [
+    # a ragged 16-token tile and a ragged 16-expert router tile; shared experts
+    (17, 40, 5, 2, "int4_asym_g128", True),
+    # four 16-token router tiles, sixteen expert tiles, k = 16
+    (64, 256, 16, 0, "int4_sym_g128", True),
+    # k = 17 (more selections than one 16-lane row holds)
+    (33, 24, 17, 1, "int8_sym_ch", True),
+    # full-softmax weights
+    (20, 64, 6, 0, "fp8e4m3_ch", False)])
+def test_small_batch_decode_tiles(oracle_mod, T, E, k, S, fmt, renorm):
+    """Small batches on 16-row decode tiles with the one-workgroup top-k +
+    dispatch, over ragged router tiles, shared experts in the combine, large
+    k and full-softmax weights."""
+    cfg = small(fmt, name=f"small_dec_{T}_{E}_{k}", T=T, E=E, k=k, d=512, F=256, S=S, Fs=256 if S else 0,
+                renormalize=renorm, bias=True)
+    run_and_check(oracle_mod, cfg, seed=T + E + k, tag=f"small-batch decode tiles T={T} E={E} k={k} S={S} {fmt}",
+                  output_rounding_allowance="auto")
+
+
+def test_small_batches_in_sequence(oracle_mod):
+    """Batches of different sizes in a row on one layer (one workspace, every
+    size's tile list and routing rewritten), each against the oracle."""
+    cfg = small("int4_sym_g128", name="sequence", T=64, E=32, k=4, d=512, F=256, S=1, Fs=256)
+    inp = make_inputs(cfg, seed=11)
+    layer = QMoE(inp, max_tokens=cfg.T)
+    oracle = oracle_mod.OracleLayer(inp)
+    try:
+        for i, T in enumerate((64, 1, 37, 64, 16)):
+            inp.x = make_x(cfg, T, seed=200 + i)
+            print(f"[case] sequence call {i} T={T}", flush=True)
+            check_batch(oracle_mod, inp, layer, oracle, tag=f"sequence call {i} T={T}",
+                        output_rounding_allowance="auto")
+    finally:
+        oracle.close()
+        layer.close()
 
 
 @pytest.mark.parametrize("T,E,k,fmt", [(37, 1, 1, "int4_asym_g128"), (300, 1, 1, "int4_sym_g128"),
