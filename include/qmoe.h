@@ -189,7 +189,11 @@ int qmoe_route_topk(qmoe_ctx *ctx, const float *logits, int32_t T, qmoe_route_ou
  *   T       0 <= T <= max_tokens (T = 0 is a no-op)
  *   y       device [T][d] bf16 output (may not alias x)
  *   dbg     NULL, or device buffers that receive this call's routing
- *   stream  hipStream_t (NULL = the null stream) */
+ *   stream  hipStream_t (NULL = the null stream)
+ * The call issues only kernel launches (plus device-to-device copies for dbg)
+ * and allocates nothing, so a caller may record it into a HIP graph on a
+ * capturing stream and replay it (with kernel timing, qmoe_profile_enable,
+ * switched off while capturing). */
 int qmoe_forward(qmoe_ctx *ctx, const uint16_t *x, int32_t T, uint16_t *y, qmoe_route_out *dbg, void *stream);
 
 /* qmoe_forward for callers that cannot allocate device memory (code under HIP
