@@ -1521,9 +1521,23 @@ __device__ __forceinline__ void gpf_tiles(const GemmArgs &a, uint8_t *lds, int n
                 asm volatile("" ::"v"(bh[nb][0]), "v"(bh[nb][1]), "v"(r[nb]));
             if (h == 0) issue(copy_kb, copy_st);
             else load_b(next_j, next_kb, slot);
+            // The rescale of row block mi + 1 runs beside row block mi's
+            // MFMAs, two FMAs after each MFMA (the rescale is the group's
+            // largest VALU block, and an MFMA leaves the VALU free for about
+            // two). The asymmetric down kernel rescales each row block right
+            // before its MFMAs instead: its 96-row body would spill with the
+            // next block's row sums held ahead.
+            constexpr bool SPREAD = GRP && !(DF == DF_I4ASYM && MODE == 1);
+            f32x4 nrs_next;
+            if (SPREAD && h == 0) {
+                const f32x4 nrs = *reinterpret_cast<const f32x4 *>(&Rb[lrow]);
+#pragma unroll
+                for (int nb = 0; nb < NB; nb++) acc[0][nb] = acc[0][nb] * r[nb] + nrs;
+                if (MI > 1) nrs_next = *reinterpret_cast<const f32x4 *>(&Rb[16 + lrow]);
+            }
 #pragma unroll
             for (int mi = 0; mi < MI; mi++) {
-                if (GRP && h == 0) {
+                if (GRP && !SPREAD && h == 0) {
                     const f32x4 nrs = *reinterpret_cast<const f32x4 *>(&Rb[mi * 16 + lrow]);
 #pragma unroll
                     for (int nb = 0; nb < NB; nb++) acc[mi][nb] = acc[mi][nb] * r[nb] + nrs;
@@ -1539,6 +1553,18 @@ __device__ __forceinline__ void gpf_tiles(const GemmArgs &a, uint8_t *lds, int n
 #pragma unroll
                     for (int nb = 0; nb < NB; nb++)
                         acc[mi][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[q & 1], bh[nb][ss], acc[mi][nb], 0, 0, 0);
+                    if (SPREAD && h == 0 && mi + 1 < MI) {
+                        // half of row block mi + 1's columns beside each block of four MFMAs
+#pragma unroll
+                        for (int nb = ss * (NB / 2); nb < (ss + 1) * (NB / 2); nb++)
+                            acc[mi + 1][nb] = acc[mi + 1][nb] * r[nb] + nrs_next;
+                        if (ss == 1 && mi + 2 < MI) nrs_next = *reinterpret_cast<const f32x4 *>(&Rb[(mi + 2) * 16 + lrow]);
+#pragma unroll
+                        for (int i = 0; i < 4; i++) {
+                            __builtin_amdgcn_sched_group_barrier(0x8, 1, 0);   // one MFMA
+                            __builtin_amdgcn_sched_group_barrier(0x2, 2, 0);   // two VALU ops
+                        }
+                    }
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
