@@ -60,7 +60,11 @@ struct QmoeWorkspace {
     int32_t *perm = nullptr, *inv = nullptr, *num_tiles = nullptr;
     Tile *tiles = nullptr;
     uint16_t *H = nullptr;
-    float *O = nullptr, *xsum = nullptr, *xsum_asym = nullptr, *hsum = nullptr;
+    float *xsum = nullptr, *xsum_asym = nullptr, *hsum = nullptr;
+    // expert outputs: fp32 (decode tiles) or 16-bit codes in the same memory
+    // (prefill tiles) with their exponents, one per 16 columns
+    float *O = nullptr;
+    int8_t *Oe = nullptr;
 };
 
 struct qmoe_ctx {
@@ -344,6 +348,7 @@ size_t carve_workspace(const qmoe_ctx *c, size_t T, uint8_t *base, QmoeWorkspace
     take(w.tiles, tiles_cap * sizeof(Tile));
     take(w.H, rows_total * c->ldh * 2);
     take(w.O, rows_total * c->d * 4);
+    take(w.Oe, rows_total * (c->d / 16));
     take(w.xsum, T * (c->d / 128) * 4);
     // layers mixing INT4_SYM / INT3 (row sums scaled by -136) with INT4_ASYM (-128)
     if (both_sums) take(w.xsum_asym, T * (c->d / 128) * 4);
@@ -773,7 +778,9 @@ int run_forward(qmoe_ctx *c, const QmoeWorkspace &w, uint32_t prof, const uint16
     a.xsum = w.xsum;
     a.H = w.H;
     a.hsum = w.hsum;
-    a.O = w.O;
+    a.O = reinterpret_cast<int16_t *>(w.O);
+    a.Oe = w.Oe;
+    a.Of = w.O;
     a.ldh = c->ldh;
     a.d = c->d;
     a.k = c->k;
@@ -800,7 +807,10 @@ int run_forward(qmoe_ctx *c, const QmoeWorkspace &w, uint32_t prof, const uint16
         if (rc) return rc;
         if (one_launch) break;
     }
-    rc = timed(c, prof, K_COMBINE, s, [&] { return launch_combine(w.O, w.inv, T, c->d, c->k, P, c->S, y, s); });
+    rc = timed(c, prof, K_COMBINE, s, [&] {
+        return bm == 16 ? launch_combine_f32(w.O, w.inv, T, c->d, c->k, P, c->S, y, s)
+                        : launch_combine(a.O, w.Oe, w.inv, T, c->d, c->k, P, c->S, y, s);
+    });
     if (rc) return rc;
     if (dbg) {
         rc = copy_out(dbg->logits, w.logits, (size_t)T * c->E * 4, s);
@@ -1091,7 +1101,7 @@ int qmoe_atomic_forward(qmoe_atomic_ctx *c, const uint16_t *x, int32_t T, uint16
         if (!rc)
             rc = ok(launch_atomic_rows(x, c->W, c->V, c->perm, c->idx, c->wrow, P, d, k, c->O, s),
                     "expert-centric experts");
-        if (!rc) rc = ok(launch_combine(c->O, c->inv, T, d, k, P, 0, y, s), "combine");
+        if (!rc) rc = ok(launch_combine_f32(c->O, c->inv, T, d, k, P, 0, y, s), "combine");
     }
     if (!rc && dbg) {
         const size_t ld = (size_t)(Nr + Nc) * 4;

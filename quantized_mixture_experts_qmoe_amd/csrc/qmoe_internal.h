@@ -204,7 +204,9 @@ struct GemmArgs {
     const float *xsum;       // [T][d/128] group sums of x
     uint16_t *H;             // [rows][ldh] bf16 intermediate
     float *hsum;             // [rows][ldh/128] group sums of H (bf16-rounded values)
-    float *O;                // [rows][d] fp32 weighted expert outputs
+    int16_t *O;              // [rows][d] weighted expert outputs of prefill tiles, 16-bit codes (see k_combine)
+    int8_t *Oe;              // [rows][d/16] their exponents, one per 16 columns
+    float *Of;               // [rows][d] fp32 weighted expert outputs of decode tiles (same memory as O)
     int32_t ldh;
     int32_t d;
     int32_t k;               // top-k
@@ -221,8 +223,12 @@ struct GemmArgs {
 constexpr int kDfAllFormats = -1;
 hipError_t launch_gemm13(int df, int bm, const GemmArgs &a, int max_tiles, int maxN13, hipStream_t s);
 hipError_t launch_gemm2(int df, int bm, const GemmArgs &a, int max_tiles, hipStream_t s);
-hipError_t launch_combine(const float *O, const int32_t *inv, int T, int d, int k, int P, int n_shared,
-                          uint16_t *y, hipStream_t s);
+// O: the prefill down GEMM's 16-bit codes and per-16-column exponents; the
+// _f32 variant sums fp32 rows (decode tiles, atomic experts).
+hipError_t launch_combine(const int16_t *O, const int8_t *Oe, const int32_t *inv, int T, int d, int k, int P,
+                          int n_shared, uint16_t *y, hipStream_t s);
+hipError_t launch_combine_f32(const float *O, const int32_t *inv, int T, int d, int k, int P, int n_shared,
+                              uint16_t *y, hipStream_t s);
 hipError_t launch_xsum(const uint16_t *x, int T, int d, float scale, float *xsum, hipStream_t s);
 
 // Shader clock probe: one wave sampling (shader cycles, real-time ticks) pairs.

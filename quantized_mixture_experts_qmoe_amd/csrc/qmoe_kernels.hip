@@ -1034,6 +1034,45 @@ struct DecodeCfg {
 
 // One decode tile: B columns [c.n0, c.n0 + 256) of the tile's expert against
 // its (at most 16) rows, staged through the calling kernel's LDS.
+// Expert outputs O between the down GEMM and the combine: 16-bit codes with
+// one power-of-two scale per row and 16 consecutive columns. For a block whose
+// largest |v| lies in [2^(e-1), 2^e), every v is stored as the signed
+// normalised code q = round(32767 * v / 2^e) (the hardware's fp32 -> snorm16
+// conversion) and e as a signed byte; the combine reads v' = q * (2^e /
+// 32767). |v' - v| <= 2^(e-16): at most 2^-15 of the block's largest |v|.
+// |O| must stay below 2^127.
+constexpr float kOInv = 1.0f / 32767.0f;
+__device__ __forceinline__ int o_exponent(float amax) {
+    return min(max(__builtin_amdgcn_frexp_expf(amax), -126), 127);
+}
+__device__ __forceinline__ float o_scale(int e) { return __builtin_amdgcn_ldexpf(1.0f, -e); }
+// two codes in one dword (a in the low half)
+__device__ __forceinline__ uint32_t o_pack(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pknorm_i16(a, b));
+}
+// Largest |v| over each 16-lane row of the wave (in every lane of the row),
+// for the MFMA output layout: lane i holds column i % 16 of a block.
+__device__ __forceinline__ float row16_absmax(float v) {
+    uint32_t m = __float_as_uint(fabsf(v));   // non-negative floats order as integers
+    m = ror_max<kDppRor1>(m);
+    m = ror_max<kDppRor2>(m);
+    m = ror_max<kDppRor4>(m);
+    m = ror_max<kDppRor8>(m);
+    return __uint_as_float(m);
+}
+// Writes value v of O[gr][n] (MFMA output layout: the 16 lanes of a row hold
+// 16 consecutive columns n) and, from the row's first lane, the block's
+// exponent; every lane of the row takes part (the block maximum), `live`
+// selects the rows that store.
+__device__ __forceinline__ void o_store_lane(int16_t *__restrict__ O, int8_t *__restrict__ Oe, int d, size_t gr, int n,
+                                             float v, bool live, int lane) {
+    const int e = o_exponent(row16_absmax(v));
+    if (live) {
+        O[gr * d + n] = (int16_t)(o_pack(v * o_scale(e), 0.0f) & 0xFFFFu);
+        if ((lane & 15) == 0) Oe[gr * (size_t)(d / 16) + n / 16] = (int8_t)e;
+    }
+}
+
 template <int DF, int MODE>
 __device__ __forceinline__ void dec_tile(const GemmArgs &a, const TileCtx &c, uint16_t (*As)[16 * kDecPitch],
                                          float (*Rs)[kDecKC][16]) {
@@ -1227,6 +1266,8 @@ __device__ __forceinline__ void dec_tile(const GemmArgs &a, const TileCtx &c, ui
 #pragma unroll
         for (int nb = 0; nb < NB; nb++)
             sn[nb] = CF::kGroup ? 1.0f : c.ew.p2[c.n0 + NB * 16 * wave + 16 * nb + (lane & 15)];
+        // (decode tiles: fp32 outputs, read by k_combine_f32; at these
+        // sizes the coding would cost more than the bytes it saves)
 #pragma unroll
         for (int r = 0; r < 4; r++) {
             const int row = lrow + r;
@@ -1236,7 +1277,7 @@ __device__ __forceinline__ void dec_tile(const GemmArgs &a, const TileCtx &c, ui
 #pragma unroll
             for (int nb = 0; nb < NB; nb++) {
                 const int n = c.n0 + NB * 16 * wave + 16 * nb + (lane & 15);
-                a.O[(size_t)gr * a.d + n] = acc[nb][r] * sn[nb] * wt;
+                a.Of[(size_t)gr * a.d + n] = acc[nb][r] * sn[nb] * wt;
             }
         }
     }
@@ -1292,8 +1333,6 @@ __global__ __launch_bounds__(256) void k_gemm_dec_mixed(GemmArgs a) {
     }
 }
 
-// Expert outputs are written once and read once (by the combine).
-__device__ __forceinline__ void store_o(float *p, float v) { *p = v; }
 
 // ---- prefill tiles: XCD-aware work order -----------------------------------
 //
@@ -1593,8 +1632,9 @@ __device__ __forceinline__ void gpf_tiles(const GemmArgs &a, uint8_t *lds, int n
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    // Results of tile j (its columns start at 256 * (nt0 + j)).
-    auto finish = [&](int j) __attribute__((always_inline)) {
+    // Results of tile j (its columns start at 256 * (nt0 + j)); st_free: the
+    // stage the tile's last group read (idle until the next group's copies).
+    auto finish = [&](int j, int st_free) __attribute__((always_inline)) {
         const int n0 = (nt0 + j) * NTILE;
         const int ibj = ib0 + (NTILE / 16) * j;
         // the tile's rows and the output pitches as opaque values here: the
@@ -1747,9 +1787,56 @@ __device__ __forceinline__ void gpf_tiles(const GemmArgs &a, uint8_t *lds, int n
                     }
                 }
             }
-        } else {
-            // the tile's O rows: a uniform base and 32-bit per-lane offsets
+        } else if constexpr (MI >= 4) {
+            // O (16-bit codes, one scale per row and 16 columns) through this
+            // wave's own activation rows of the idle stage (4 KB of at least
+            // 4 KB; the wave's next copies into them come after its reads, in
+            // its own program order), so that each lane holds four
+            // consecutive columns of one row: the 16-column block is a lane
+            // quad, and the stores are 8 bytes per lane.
+            const float *wts = reinterpret_cast<const float *>(lds + RED);
+            float *Sw = reinterpret_cast<float *>(lds + st_free * ST_BYTES + ST_A + wave * RPW * 256);
+            static_assert(RPW * 256 >= 16 * WCOLS * 4, "a 16-row block fits the wave's rows");
+            // rows padded by four floats where they fit (addresses linear in
+            // the row: immediate offsets), else a 16-byte-chunk XOR swizzle
+            constexpr bool PAD = RPW * 256 >= 16 * (WCOLS + 4) * 4;
+            constexpr int OP = PAD ? WCOLS + 4 : WCOLS;
+            auto sidx = [&](int row, int col) __attribute__((always_inline)) {
+                return PAD ? row * OP + col : row * OP + (((col >> 2) ^ row) << 2) + (col & 3);
+            };
+            const int c4 = lane & 15;
+            // the tile's O rows and exponents: uniform bases, 32-bit offsets
             uint8_t *Ob = reinterpret_cast<uint8_t *>(a.O + (size_t)row0 * ld_out);
+            int8_t *Eb = a.Oe + (size_t)row0 * (ld_out / 16);
+            const int col0 = n0 + WCOLS * wave + 4 * c4;
+#pragma unroll
+            for (int mi = 0; mi < MI; mi++) {
+                const f32x4 wt = *reinterpret_cast<const f32x4 *>(&wts[mi * 16 + lrow]);
+#pragma unroll
+                for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+                    for (int r = 0; r < 4; r++) Sw[sidx(lrow + r, 16 * nb + (lane & 15))] = acc[mi][nb][r] * wt[r];
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const int row = 4 * i + (lane >> 4);
+                    const f32x4 v = *reinterpret_cast<const f32x4 *>(&Sw[sidx(row, 4 * c4)]);
+                    uint32_t m = __float_as_uint(fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+                    // quad maximum (DPP quad_perm [1,0,3,2], then [2,3,0,1])
+                    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, false));
+                    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4E, 0xF, 0xF, false));
+                    const int e = o_exponent(__uint_as_float(m));
+                    const float sc = o_scale(e);
+                    const int grow = mi * 16 + row;
+                    if (grow < nrows) {
+                        *reinterpret_cast<uint2 *>(Ob + 2u * (uint32_t)(grow * ld_out + col0)) =
+                            make_uint2(o_pack(v[0] * sc, v[1] * sc), o_pack(v[2] * sc, v[3] * sc));
+                        if ((c4 & 3) == 0) Eb[(uint32_t)(grow * (ld_out / 16) + col0 / 16)] = (int8_t)e;
+                    }
+                }
+            }
+        } else {
+            // (32-row tiles) O straight from the MFMA layout: the 16 lanes of
+            // a row hold a 16-column block
             const float *wts = reinterpret_cast<const float *>(lds + RED);
 #pragma unroll
             for (int mi = 0; mi < MI; mi++) {
@@ -1757,11 +1844,11 @@ __device__ __forceinline__ void gpf_tiles(const GemmArgs &a, uint8_t *lds, int n
 #pragma unroll
                 for (int r = 0; r < 4; r++) {
                     const int row = mi * 16 + lrow + r;
-                    if (row >= nrows) continue;
 #pragma unroll
                     for (int nb = 0; nb < NB; nb++) {
                         const int n = n0 + WCOLS * wave + 16 * nb + (lane & 15);
-                        store_o(reinterpret_cast<float *>(Ob + 4u * (uint32_t)(row * ld_out + n)), acc[mi][nb][r] * wt[r]);
+                        o_store_lane(a.O, a.Oe, ld_out, (size_t)(row0 + row), n, acc[mi][nb][r] * wt[r], row < nrows,
+                                     lane);
                     }
                 }
             }
@@ -1799,7 +1886,7 @@ __device__ __forceinline__ void gpf_tiles(const GemmArgs &a, uint8_t *lds, int n
             step(v + 1, 1, 1, j, vs);
         }
         if (v < vend) step(v++, 0, 0, j, vs);
-        finish(j);
+        finish(j, (v - 1) & 1);
         if (++j == nsub) break;
         vend += KB;
         reset();
@@ -1832,20 +1919,58 @@ __global__ __launch_bounds__(64 * NW, 2) void k_gemm_gpf(GemmArgs a) {
 // ---------------------------------------------------------------------------
 
 // y[t] = sum_j O[inv[t*k+j]] + sum_s O[P + s*T + t], summed in fp32 in slot
-// order, rounded once to bf16. CPT 4-column chunks per thread, 256 columns
-// apart; the rows are loaded eight at a time so that the loads overlap. O is
-// read exactly once: non-temporal loads keep it from displacing cached data.
-constexpr int kCombineCPT = 1;
-constexpr bool kCombineNT = true;
-__device__ __forceinline__ float4 load_o(const float *p) {
-    if (kCombineNT) {
-        const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
-        return make_float4(v[0], v[1], v[2], v[3]);
+// order, rounded once to bf16. Each thread takes four consecutive columns of
+// one token; the rows are loaded eight at a time so that the loads overlap.
+// O is read exactly once: non-temporal loads keep it from displacing cached
+// data. This kernel reads the 16-bit codes of the layer's down GEMM (four
+// codes and their block's exponent per row).
+__global__ __launch_bounds__(256) void k_combine(const int16_t *__restrict__ O, const int8_t *__restrict__ Oe,
+                                                 const int32_t *__restrict__ inv, int T, int d, int k, int P,
+                                                 int n_shared, uint16_t *__restrict__ y) {
+    const int t = blockIdx.x;
+    const int c4 = blockIdx.y * 256 + threadIdx.x;
+    if (c4 >= d / 4) return;
+    const int nrows = k + n_shared;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j0 = 0; j0 < nrows; j0 += 8) {
+        uint2 q[8];
+        int e[8];
+#pragma unroll
+        for (int u = 0; u < 8; u++) {
+            const int j = j0 + u;
+            if (j < nrows) {
+                const size_t row = j < k ? (size_t)inv[(size_t)t * k + j] : (size_t)P + (size_t)(j - k) * T + t;
+                q[u] = __builtin_bit_cast(uint2, __builtin_nontemporal_load(
+                                                     reinterpret_cast<const unsigned long long *>(O + row * d) + c4));
+                e[u] = Oe[row * (size_t)(d / 16) + c4 / 4];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 8; u++)
+            if (j0 + u < nrows) {
+                const float f = __builtin_amdgcn_ldexpf(kOInv, e[u]);
+                acc.x += (float)(int16_t)(q[u].x & 0xFFFFu) * f;
+                acc.y += (float)(int16_t)(q[u].x >> 16) * f;
+                acc.z += (float)(int16_t)(q[u].y & 0xFFFFu) * f;
+                acc.w += (float)(int16_t)(q[u].y >> 16) * f;
+            }
     }
-    return *reinterpret_cast<const float4 *>(p);
+    uint2 out;
+    out.x = (uint32_t)to_bf16(acc.x) | ((uint32_t)to_bf16(acc.y) << 16);
+    out.y = (uint32_t)to_bf16(acc.z) | ((uint32_t)to_bf16(acc.w) << 16);
+    *reinterpret_cast<uint2 *>(y + (size_t)t * d + c4 * 4) = out;
 }
-__global__ __launch_bounds__(256) void k_combine(const float *__restrict__ O, const int32_t *__restrict__ inv, int T,
-                                                 int d, int k, int P, int n_shared, uint16_t *__restrict__ y) {
+
+// The same sum over fp32 rows (the decode GEMM's outputs, the atomic-expert
+// layer's task rows).
+constexpr int kCombineCPT = 1;
+__device__ __forceinline__ float4 load_o(const float *p) {
+    const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
+    return make_float4(v[0], v[1], v[2], v[3]);
+}
+__global__ __launch_bounds__(256) void k_combine_f32(const float *__restrict__ O, const int32_t *__restrict__ inv,
+                                                     int T, int d, int k, int P, int n_shared,
+                                                     uint16_t *__restrict__ y) {
     constexpr int CPT = kCombineCPT;
     const int t = blockIdx.x;
     const int d4 = d / 4;
@@ -2454,9 +2579,15 @@ hipError_t launch_xsum(const uint16_t *x, int T, int d, float scale, float *xsum
     return hipGetLastError();
 }
 
-hipError_t launch_combine(const float *O, const int32_t *inv, int T, int d, int k, int P, int n_shared,
-                          uint16_t *y, hipStream_t s) {
-    hipLaunchKernelGGL(k_combine, dim3(T, (d / 4 + 256 * kCombineCPT - 1) / (256 * kCombineCPT)), dim3(256), 0, s, O, inv,
+hipError_t launch_combine(const int16_t *O, const int8_t *Oe, const int32_t *inv, int T, int d, int k, int P,
+                          int n_shared, uint16_t *y, hipStream_t s) {
+    hipLaunchKernelGGL(k_combine, dim3(T, (d / 4 + 255) / 256), dim3(256), 0, s, O, Oe, inv, T, d, k, P, n_shared, y);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine_f32(const float *O, const int32_t *inv, int T, int d, int k, int P, int n_shared,
+                              uint16_t *y, hipStream_t s) {
+    hipLaunchKernelGGL(k_combine_f32, dim3(T, (d / 4 + 256 * kCombineCPT - 1) / (256 * kCombineCPT)), dim3(256), 0, s, O, inv,
                        T, d, k, P, n_shared, y);
     return hipGetLastError();
 }

@@ -8,8 +8,9 @@ router's softmax probabilities, shared experts added with weight 1) is
 evaluated here per expert over all of its tokens with fp64 matrix products on
 the oracle's dequantized weights. It is tied to the oracle itself by a test
 that compares both on sampled tokens; its only purpose is to emulate the
-roundings the GPU path is allowed (bf16 H before the down projection, bf16 y)
-on complete full-size outputs, where the per-token oracle would take minutes.
+roundings the GPU path is allowed (bf16 H before the down projection, the
+expert outputs' 16-bit block codes, bf16 y) on complete full-size outputs,
+where the per-token oracle would take minutes.
 """
 from __future__ import annotations
 
@@ -26,6 +27,23 @@ def bf16_round(a: np.ndarray) -> np.ndarray:
     u = f.view(np.uint32).astype(np.uint64)
     r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint32) << 16
     return r.view(np.float32).astype(np.float64)
+
+
+def o_code_round(v: np.ndarray) -> np.ndarray:
+    """The expert outputs' storage between the down projection and the sum:
+    per row and 16 consecutive columns, with e the exponent of the block's
+    largest |v| (|v|max in [2^(e-1), 2^e)), the code q = round(32767 * v / 2^e)
+    and the value read back q * (2^e / 32767), in float32 as the path computes
+    it. Rows of v are the outputs of one (token, expert) pair; the column count
+    is a multiple of 16."""
+    f = np.ascontiguousarray(v, dtype=np.float32)
+    b = f.reshape(f.shape[0], -1, 16)
+    amax = np.abs(b).max(axis=2, keepdims=True)
+    e = np.clip(np.frexp(amax)[1], -126, 127).astype(np.int32)
+    scaled = (b * np.ldexp(np.float32(1.0), -e).astype(np.float32)).astype(np.float32)
+    q = np.rint(np.clip(scaled, -1.0, 1.0) * np.float32(32767.0)).astype(np.float32)
+    back = q * np.ldexp(np.float32(1.0 / 32767.0), e).astype(np.float32)
+    return back.reshape(f.shape).astype(np.float64)
 
 
 def half_ulp_bf16(v: np.ndarray) -> np.ndarray:
@@ -51,8 +69,9 @@ def routing(inp):
 
 def exact_and_path(O, layer, inp):
     """(y_exact, y_path): the layer in fp64 on every token, and the same with
-    the path's two storage roundings applied (H rounded to bf16 before the down
-    projection; the summed output rounded once to bf16)."""
+    the path's storage roundings applied (H rounded to bf16 before the down
+    projection; each expert output in its 16-bit block code; the summed output
+    rounded once to bf16)."""
     cfg = inp.cfg
     X, _, idx, w = routing(inp)
     T = X.shape[0]
@@ -80,6 +99,6 @@ def exact_and_path(O, layer, inp):
         Wd = O.dequantize(fe, *layer.codes(e, 2), group=cfg.group)
         # a token picks an expert at most once: tt has no repeats
         y[tt] += mix * (h @ Wd.T)
-        yp[tt] += mix * (bf16_round(h) @ Wd.T)
+        yp[tt] += o_code_round(mix * (bf16_round(h) @ Wd.T))
         del Wd, h
     return y, bf16_round(yp)

@@ -1,7 +1,8 @@
 """The max-abs bar on complete full-size outputs, pinned on the CPU.
 
-The layer's output is bf16 (rounded once from the fp32 sum), and before the
-down projection the path keeps H in bf16. Over a complete output of millions of
+The layer's output is bf16 (rounded once from the fp32 sum); before the down
+projection the path keeps H in bf16, and the expert outputs in 16-bit codes
+with one power-of-two scale per row and 16 columns. Over a complete output of millions of
 elements the largest |y| sits at five to six times RMS(y), where half a bf16
 ulp is already of the order of 1e-2 * RMS(y): the output's own storage
 rounding uses a large share of the plain bar max|err| <= 2e-2 * RMS(y) by
@@ -43,7 +44,7 @@ def test_complete_output_rounding_against_the_bar(oracle_mod, name):
     beyond = float((np.abs(yp - y) - half_ulp_bf16(y)).max()) / rms
     peak = float(np.abs(y).max()) / rms
     print(f"[rounding] {name}: |y|max = {peak:.2f} RMS; bf16(y) alone max|err| = {plain_round:.3e} RMS; "
-          f"bf16 H + bf16 y: max|err| = {plain_path:.3e} RMS, beyond half an ulp {beyond:.3e} RMS, "
+          f"bf16 H + 16-bit O + bf16 y: max|err| = {plain_path:.3e} RMS, beyond half an ulp {beyond:.3e} RMS, "
           f"rel L2 {rel_path:.3e}", flush=True)
     # the storage rounding of y alone takes at least a third of the plain bar
     assert plain_round >= MAX_ABS_RMS / 3
@@ -53,3 +54,23 @@ def test_complete_output_rounding_against_the_bar(oracle_mod, name):
     # 1.30e-2 and 0.82e-2 RMS on the three layers)
     assert rel_path <= REL_L2 / 2
     assert beyond <= 0.7 * MAX_ABS_RMS
+
+
+def test_o_code_error_bound():
+    """The 16-bit block code of the expert outputs: every value comes back
+    within 2^-15 of its block's largest |v| (half a code step, 2^e / 65534,
+    where |v|max lies in [2^(e-1), 2^e)); zeros stay zero; the block maximum
+    itself within 2^-16 of its value."""
+    from layer_emulation import o_code_round
+    rng = np.random.default_rng(7)
+    v = rng.standard_normal((64, 256)) * np.exp(rng.uniform(-8, 8, (64, 1)))
+    v[3, 16:32] = 0.0
+    v[5, :16] = 2.0 ** -3            # a block at an exact power of two
+    back = o_code_round(v)
+    f = v.astype(np.float32).astype(np.float64)
+    bmax = np.abs(f).reshape(64, -1, 16).max(axis=2).repeat(16, axis=1)
+    assert np.all(np.abs(back - f) <= 2.0 ** -15 * bmax * (1 + 2.0 ** -20))
+    assert np.all(back[3, 16:32] == 0.0)
+    assert np.all(np.abs(back[5, :16] - 2.0 ** -3) <= 2.0 ** -16 * 2.0 ** -3 * 2)
+    big = np.abs(f) == bmax
+    assert np.all(np.abs(back[big] - f[big]) <= 2.0 ** -15 * np.abs(f[big]))
