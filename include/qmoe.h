@@ -193,7 +193,13 @@ int qmoe_route_topk(qmoe_ctx *ctx, const float *logits, int32_t T, qmoe_route_ou
  * The call issues only kernel launches (plus device-to-device copies for dbg)
  * and allocates nothing, so a caller may record it into a HIP graph on a
  * capturing stream and replay it (with kernel timing, qmoe_profile_enable,
- * switched off while capturing). */
+ * switched off while capturing).
+ * Numerics: fp32 accumulation throughout; H (the SwiGLU product) is held in
+ * bf16 before the down projection; for batches on the prefill tiles each
+ * weighted expert output is held as a 16-bit code with one power-of-two scale
+ * per 16 consecutive columns until the sum (error at most 2^-15 of the
+ * block's largest magnitude, magnitudes below 2^127); y is rounded once to
+ * bf16. */
 int qmoe_forward(qmoe_ctx *ctx, const uint16_t *x, int32_t T, uint16_t *y, qmoe_route_out *dbg, void *stream);
 
 /* qmoe_forward for callers that cannot allocate device memory (code under HIP
