@@ -215,6 +215,43 @@ def test_forward_group_format_with_fp32_router(oracle_mod, fmt, d):
     run_and_check(oracle_mod, cfg, tag=f"fp32 router {fmt} d={d}")
 
 
+@pytest.mark.parametrize("fmt", ["int4_sym_g128", "int8_sym_ch"])
+def test_forward_expert_output_blocks(oracle_mod, fmt):
+    """The expert outputs' 16-bit block codes (one power-of-two scale per row
+    and 16 output columns) on prefill tiles (150 rows per expert: 64-row tiles
+    and a partial one): output columns whose down rows are zero in every
+    expert (zero blocks: exactly zero for the per-channel format), a block at 2^-8 of
+    the usual magnitude (its own exponent keeps its relative precision; much
+    smaller weights underflow the group formats' fp16 scales to zero rows) and
+    a single column at 2^-30 inside an ordinary block, with a shared expert."""
+    cfg = small(fmt, name=f"oblocks_{fmt}", T=600, d=512, E=8, k=2, F=256, S=1, Fs=256)
+    inp = make_inputs(cfg, seed=21)
+    for wd in inp.w_down:
+        wd[0:16, :] = 0.0
+        wd[64:80, :] *= 2.0 ** -8
+        wd[100, :] *= 2.0 ** -30
+    layer = QMoE(inp, max_tokens=cfg.T)
+    oracle = oracle_mod.OracleLayer(inp)
+    try:
+        print(f"[case] expert-output blocks {fmt}", flush=True)
+        y = bf16_tensor_to_f64(check_batch(oracle_mod, inp, layer, oracle, tag=f"output blocks {fmt}"))
+        ref = oracle.forward(inp.x)["y"]
+        if fmt == "int8_sym_ch":
+            assert np.all(y[:, 0:16] == 0.0)
+        else:
+            # the group formats' integer-code products carry the -Z * row-sum
+            # offset, which zero weights cancel only up to fp32 rounding
+            # (measured 1.5e-3 RMS at most)
+            assert np.abs(y[:, 0:16]).max() <= 5e-3 * np.sqrt(np.mean(ref ** 2))
+        tiny, tref = y[:, 64:80], ref[:, 64:80]
+        rel = np.linalg.norm(tiny - tref) / np.linalg.norm(tref)
+        print(f"[parity] 2^-8 block: rel_l2={rel:.3e}", flush=True)
+        assert rel <= 1e-2
+    finally:
+        oracle.close()
+        layer.close()
+
+
 @pytest.mark.parametrize("fmt", ["int3_sym_g128", "int8_sym_ch", "fp8e4m3_ch"])
 def test_forward_shared_experts_and_bias(oracle_mod, fmt):
     cfg = small(fmt, T=257, E=12, k=3, S=2, Fs=384, bias=True)
