@@ -2404,10 +2404,13 @@ hipError_t launch_router_bf16(const uint16_t *x, const uint16_t *wr, const float
                               int *chunk, hipStream_t s) {
     // 16 x 16 tiles as four independent streams for small batches and few
     // experts (LDS: 4 rings of 3 x 8 KB); wider expert tiles for large batches
-    // (4 rings of 3 x 12 KB; shared rings of 3 x 20 KB and 2 x 40 KB)
+    // (4 rings of 3 x 12 KB; shared rings of 3 x 20 KB, and 3 x 40 KB while
+    // the 32-token tiles fit one round of one workgroup per CU, else 2 x 40 KB
+    // for two per CU)
     if (T < 256 || E <= 16) launch_router_lds<16, 16, 1, 3>(x, wr, rscale, bias, logits, xsum, xscale, T, d, E, rf, chunk, s);
     else if (E <= 32) launch_router_lds<16, 32, 1, 3>(x, wr, rscale, bias, logits, xsum, xscale, T, d, E, rf, chunk, s);
     else if (E <= 64) launch_router_lds<16, 64, 4, 3>(x, wr, rscale, bias, logits, xsum, xscale, T, d, E, rf, chunk, s);
+    else if ((T + 31) / 32 <= 256) launch_router_lds<32, 128, 4, 3>(x, wr, rscale, bias, logits, xsum, xscale, T, d, E, rf, chunk, s);
     else launch_router_lds<32, 128, 4, 2>(x, wr, rscale, bias, logits, xsum, xscale, T, d, E, rf, chunk, s);
     return hipGetLastError();
 }

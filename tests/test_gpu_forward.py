@@ -87,11 +87,13 @@ def test_forward_tile_shapes(oracle_mod, fmt, T, E, k):
                                      (257, 24, "int4_asym_g128"), (700, 48, "int4_sym_g128"),
                                      (513, 64, "int4_asym_g128"), (300, 100, "int4_sym_g128"),
                                      (1000, 128, "int4_asym_g128"), (260, 200, "int4_sym_g128"),
-                                     (300, 300, "fp8e4m3_ch")])
+                                     (300, 300, "fp8e4m3_ch"), (8224, 128, "int4_sym_g128")])
 def test_forward_staged_router_tiles(oracle_mod, T, E, fmt):
     # batches of >= 256 tokens take the router that stages x and router rows
     # through LDS: expert tiles of 16, 32, 64 or 128 rows (several tiles for
-    # E > 128), ragged T and E, fused row sums of x for the group formats
+    # E > 128), ragged T and E, fused row sums of x for the group formats;
+    # 128-expert tiles with three stages up to 256 token tiles of 32, with
+    # two past that (T = 8224: 257 tiles)
     cfg = small(fmt, name=f"router_{T}_{E}_{fmt}", T=T, E=E, k=min(4, E))
     run_and_check(oracle_mod, cfg, tag=f"staged router T={T} E={E} {fmt}")
 
