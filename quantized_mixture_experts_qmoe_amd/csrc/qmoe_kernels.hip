@@ -952,8 +952,9 @@ __device__ __forceinline__ bf16x8 codes8_to_bf16<DF_FP8>(uint32_t d0, uint32_t d
 //
 // MODE 0 (gate/up): A = gathered x rows, B = W13 of the tile's expert; output
 //   H[row][F] = silu(gate) * up in bf16 (+ per-group row sums of H for MODE 1).
-// MODE 1 (down): A = H rows of the tile, B = W2; output O[row][d] (fp32) =
-//   (mixing weight of the row's task) * (H . W2^T).
+// MODE 1 (down): A = H rows of the tile, B = W2; output O[row][d] =
+//   (mixing weight of the row's task) * (H . W2^T), fp32 on decode tiles and
+//   16-bit block codes on prefill tiles.
 // Workgroup = 4 waves; tile = BM rows x 256 columns of B's N dimension (for
 // MODE 0 these are 128 gate/up column pairs = one 128-wide group of H). Wave w
 // owns 64 columns = four 16-row packed blocks, so each packed weight is
