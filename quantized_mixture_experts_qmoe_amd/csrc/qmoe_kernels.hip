@@ -65,6 +65,20 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
     static_assert(VM >= 0 && VM < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | (0 << 8) | ((VM >> 4) << 14));
 }
+// Wait until at most n groups of CPW copies each are outstanding (n uniform,
+// at most NMAX): s_waitcnt takes only an immediate count.
+template <int CPW, int NMAX>
+__device__ __forceinline__ void wait_groups(int n) {
+    if constexpr (NMAX > 0) {
+        if (n >= NMAX) {
+            wait_vm_lgkm0<NMAX * CPW>();
+            return;
+        }
+        wait_groups<CPW, NMAX - 1>(n);
+    } else {
+        wait_vm_lgkm0<0>();
+    }
+}
 // Workgroup barrier without the compiler's fence (which would drain every
 // outstanding load); the memory clobber keeps LDS accesses on their side.
 __device__ __forceinline__ void raw_barrier() { asm volatile("s_barrier" ::: "memory"); }
@@ -199,55 +213,67 @@ __global__ __launch_bounds__(256) void k_router_lds(const uint16_t *__restrict__
     const bool do_sum = xsum != nullptr && et == 0;
     const int we = STREAMS ? 0 : wave;
 
-    if (ng > 0) {   // uniform; a stream with no group (G < 4) only adds zeros
+    // MFMAs (and the row sums) of this wave's q-th group, staged in stage st
+    auto group = [&](int q, int st) __attribute__((always_inline)) {
+        const uint16_t *S = reinterpret_cast<const uint16_t *>(ringp + st * ST);
+#pragma unroll
+        for (int s = 0; s < 4; s++) {
+            const int pc = (s * 4 + (lane >> 4)) ^ (lane & 15);
+            bf16x8 af[MT], bfr[NT];
+#pragma unroll
+            for (int i = 0; i < MT; i++)
+                af[i] = *reinterpret_cast<const bf16x8 *>(&S[(16 * i + (lane & 15)) * 128 + pc * 8]);
+#pragma unroll
+            for (int jj = 0; jj < NT; jj++)
+                bfr[jj] = *reinterpret_cast<const bf16x8 *>(&S[(BT + 16 * (we * NT + jj) + (lane & 15)) * 128 + pc * 8]);
+#pragma unroll
+            for (int i = 0; i < MT; i++)
+#pragma unroll
+                for (int jj = 0; jj < NT; jj++)
+                    acc[i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[jj], acc[i][jj], 0, 0, 0);
+        }
+        if (do_sum) {
+            // 16 lanes per staged x row, one 16-byte chunk each; in shared
+            // mode the workgroup's threads split the rows, in streams mode
+            // each wave sums its own group
+            const int g = gfirst + gstep * q;
+            constexpr int NTH = STREAMS ? 64 : 256;
+            const int tid = STREAMS ? lane : (int)threadIdx.x;
+#pragma unroll
+            for (int c0 = 0; c0 < BT * 16; c0 += NTH) {
+                const int c = c0 + tid;
+                const int row = c >> 4;
+                const uint4 q4 = *reinterpret_cast<const uint4 *>(&S[row * 128 + ((c & 15) ^ (row & 15)) * 8]);
+                const uint32_t qq[4] = {q4.x, q4.y, q4.z, q4.w};
+                float v = 0.0f;
+#pragma unroll
+                for (int k = 0; k < 4; k++) v += bf16f(qq[k] & 0xFFFFu) + bf16f(qq[k] >> 16);
+                // the 16 chunks of a row are one 16-lane DPP row (c & 15 = lane & 15)
+                v = row16_sum_last(v);
+                const int t = t0 + row;
+                if ((c & 15) == 15 && t < T) xsum[(size_t)t * G + g] = v * xscale;
+            }
+        }
+    };
+    if (STREAMS && ng <= NST) {
+        // a stream whose groups all fit its ring (small batches): every copy
+        // in flight at once, then the waits count down group by group
+        for (int q = 0; q < ng; q++) issue(q, q);
+        for (int q = 0; q < ng; q++) {
+            wait_groups<CPW, NST - 1>(ng - 1 - q);
+            group(q, q);
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+    } else if (ng > 0) {   // uniform; a stream with no group (G < 4) only adds zeros
 #pragma unroll
         for (int p = 0; p < NST - 1; p++) issue(p, p);
         for (int q = 0; q < ng; q++) {
             wait_vm_lgkm0<(NST - 2) * CPW>();
             if constexpr (!STREAMS) raw_barrier();
-            const int st = q % NST;
             // refill the stage read one group ago (in shared mode every wave
             // passed this group's barrier, so all are done with it)
             issue(q + NST - 1, (q + NST - 1) % NST);
-            const uint16_t *S = reinterpret_cast<const uint16_t *>(ringp + st * ST);
-#pragma unroll
-            for (int s = 0; s < 4; s++) {
-                const int pc = (s * 4 + (lane >> 4)) ^ (lane & 15);
-                bf16x8 af[MT], bfr[NT];
-#pragma unroll
-                for (int i = 0; i < MT; i++)
-                    af[i] = *reinterpret_cast<const bf16x8 *>(&S[(16 * i + (lane & 15)) * 128 + pc * 8]);
-#pragma unroll
-                for (int jj = 0; jj < NT; jj++)
-                    bfr[jj] = *reinterpret_cast<const bf16x8 *>(&S[(BT + 16 * (we * NT + jj) + (lane & 15)) * 128 + pc * 8]);
-#pragma unroll
-                for (int i = 0; i < MT; i++)
-#pragma unroll
-                    for (int jj = 0; jj < NT; jj++)
-                        acc[i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[jj], acc[i][jj], 0, 0, 0);
-            }
-            if (do_sum) {
-                // 16 lanes per staged x row, one 16-byte chunk each; in shared
-                // mode the workgroup's threads split the rows, in streams mode
-                // each wave sums its own group
-                const int g = gfirst + gstep * q;
-                constexpr int NTH = STREAMS ? 64 : 256;
-                const int tid = STREAMS ? lane : (int)threadIdx.x;
-#pragma unroll
-                for (int c0 = 0; c0 < BT * 16; c0 += NTH) {
-                    const int c = c0 + tid;
-                    const int row = c >> 4;
-                    const uint4 q4 = *reinterpret_cast<const uint4 *>(&S[row * 128 + ((c & 15) ^ (row & 15)) * 8]);
-                    const uint32_t qq[4] = {q4.x, q4.y, q4.z, q4.w};
-                    float v = 0.0f;
-#pragma unroll
-                    for (int k = 0; k < 4; k++) v += bf16f(qq[k] & 0xFFFFu) + bf16f(qq[k] >> 16);
-                    // the 16 chunks of a row are one 16-lane DPP row (c & 15 = lane & 15)
-                    v = row16_sum_last(v);
-                    const int t = t0 + row;
-                    if ((c & 15) == 15 && t < T) xsum[(size_t)t * G + g] = v * xscale;
-                }
-            }
+            group(q, q % NST);
         }
         // no copy may still be writing LDS when the ring is reused or freed
         __builtin_amdgcn_s_waitcnt(0);
@@ -460,10 +486,10 @@ __device__ __forceinline__ int wave_take_max(uint32_t (&hv)[EPL], int lane, uint
 // ties to the lower expert index); lane j ends holding slot j. Weights: softmax over the k selected logits
 // (renorm) or the full-softmax probabilities of the selected. Writes
 // idx_out[0..k) and w_out[0..k); returns this lane's expert (slot = lane) or -1
-// for lanes >= k.
+// for lanes >= k, and this lane's weight in my_w.
 template <int EPL>
 __device__ __forceinline__ int topk_token(const float *__restrict__ lt, int E, int k, int renorm, int lane,
-                                          int32_t *__restrict__ idx_out, float *__restrict__ w_out) {
+                                          int32_t *__restrict__ idx_out, float *__restrict__ w_out, float &my_w) {
     float v[EPL];
     uint32_t hv[EPL];
 #pragma unroll
@@ -495,9 +521,10 @@ __device__ __forceinline__ int topk_token(const float *__restrict__ lt, int E, i
             if (lane + 64 * i < E) part += expf(v[i] - vmax);
     }
     const float denom = wave_sum_f32(part);
+    my_w = ex / denom;
     if (lane < k) {
         idx_out[lane] = my_e;
-        w_out[lane] = ex / denom;
+        w_out[lane] = my_w;
         return my_e;
     }
     return -1;
@@ -583,7 +610,8 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int t = blockIdx.x * 4 + wave;
     if (t >= T) return;   // uniform per wave
-    topk_token<EPL>(logits + (size_t)t * E, E, k, renorm, lane, idx + (size_t)t * k, w + (size_t)t * k);
+    float my_w;
+    topk_token<EPL>(logits + (size_t)t * E, E, k, renorm, lane, idx + (size_t)t * k, w + (size_t)t * k, my_w);
 }
 
 // ---------------------------------------------------------------------------
@@ -772,11 +800,12 @@ __device__ void route_small_body(RouteSmallSmem &sm, const float *__restrict__ l
     for (int i = tid; i < 16 * kSmallRouteMaxE; i += 1024) (&sm.masks[0][0])[i] = 0ull;
     __syncthreads();
     for (int t = wave; t < T; t += 16) {
+        float my_w;
         const int e = topk_token<EPL>(logits + (size_t)t * E, E, k, renorm, lane, idx + (size_t)t * k,
-                                      w + (size_t)t * k);
+                                      w + (size_t)t * k, my_w);
         if (e >= 0) {
             sm.sidx[t * k + lane] = e;
-            sm.sw[t * k + lane] = w[(size_t)t * k + lane];   // written by this lane above
+            sm.sw[t * k + lane] = my_w;
             atomicAdd(&sm.base[e], 1);
         }
     }
@@ -2404,11 +2433,13 @@ hipError_t launch_router_bf16(const uint16_t *x, const uint16_t *wr, const float
                               float *logits, float *xsum, float xscale, int T, int d, int E, const RouteFuse *rf,
                               int *chunk, hipStream_t s) {
     // 16 x 16 tiles as four independent streams for small batches and few
-    // experts (LDS: 4 rings of 3 x 8 KB); wider expert tiles for large batches
+    // experts (LDS: 4 rings of 3 x 8 KB, 4 x 8 KB up to 64 tokens, where a
+    // stream of d <= 2048 has all its groups in flight at once); wider expert tiles for large batches
     // (4 rings of 3 x 12 KB; shared rings of 3 x 20 KB, and 3 x 40 KB while
     // the 32-token tiles fit one round of one workgroup per CU, else 2 x 40 KB
     // for two per CU)
-    if (T < 256 || E <= 16) launch_router_lds<16, 16, 1, 3>(x, wr, rscale, bias, logits, xsum, xscale, T, d, E, rf, chunk, s);
+    if (T <= 64) launch_router_lds<16, 16, 1, 4>(x, wr, rscale, bias, logits, xsum, xscale, T, d, E, rf, chunk, s);
+    else if (T < 256 || E <= 16) launch_router_lds<16, 16, 1, 3>(x, wr, rscale, bias, logits, xsum, xscale, T, d, E, rf, chunk, s);
     else if (E <= 32) launch_router_lds<16, 32, 1, 3>(x, wr, rscale, bias, logits, xsum, xscale, T, d, E, rf, chunk, s);
     else if (E <= 64) launch_router_lds<16, 64, 4, 3>(x, wr, rscale, bias, logits, xsum, xscale, T, d, E, rf, chunk, s);
     else if ((T + 31) / 32 <= 256) launch_router_lds<32, 128, 4, 3>(x, wr, rscale, bias, logits, xsum, xscale, T, d, E, rf, chunk, s);
