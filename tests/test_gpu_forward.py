@@ -429,3 +429,19 @@ def test_injected_allocation_failure(monkeypatch):
     with pytest.raises(QmoeError) as ei:
         QMoE(inp, max_tokens=4)
     assert ei.value.rc == -3
+
+
+@pytest.mark.parametrize("d", [256, 1024, 2048, 4096])
+@pytest.mark.parametrize("T,rq", [(1, "none"), (16, "none"), (64, "none"), (16, "int8")])
+def test_small_batch_router_streams(oracle_mod, T, rq, d):
+    # Up to 64 tokens the bf16 router runs four independent streams per
+    # workgroup (one per wave, every fourth 128-wide K group) through a
+    # four-stage LDS ring: d = 256 leaves two waves without a group, d = 1024
+    # and 2048 put every group of a stream in flight at once (fewer groups than
+    # stages, exactly as many), d = 4096 wraps the ring (eight groups per
+    # stream). Routing on the GPU's own logits is checked against the fp32
+    # dot-product bound, the task list bit for bit, the output to the bar.
+    cfg = small("int4_sym_g128", name=f"router_streams_{T}_{d}_{rq}", T=T, d=d, E=48, k=4, F=256,
+                router_quant=rq)
+    run_and_check(oracle_mod, cfg, seed=T + d, tag=f"small-batch router streams T={T} d={d} router={rq}",
+                  output_rounding_allowance="auto")
